@@ -1,0 +1,186 @@
+"""fp64 CPU oracle for the equivariant linear layers.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the library.  It shares no code with the
+GPU path.  The arithmetic lives in eqref.c (plain C loops, fp64); this module
+builds it with gcc when needed and wraps it for numpy arrays.
+
+What each function computes, and the passage it follows, is stated in eqref.c.
+Counting helpers at the bottom restate the pages' operation counts
+("Flash EQ-Linear", Algorithmic Approach and Specialization for p4;
+"Quick ViTs", key design 2).
+
+Parity status: every function here is pinned by tests/test_oracle.py against
+library routines (numpy FFT, scipy circulant matrices, plain matmul), closed
+forms, hand-derived examples and invariants.  No function is parity unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "eqref.c")
+_LIB = os.path.join(_HERE, "libeqref.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False, sanitize: bool = False, out: str | None = None) -> str:
+    """Compile eqref.c into a shared library with gcc (OpenMP, fp64, no fast-math)."""
+    out = out or _LIB
+    if not force and not sanitize and os.path.exists(out) and \
+            os.path.getmtime(out) >= os.path.getmtime(_SRC):
+        return out
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+           "-fno-fast-math", "-ffp-contract=off"]
+    if sanitize:
+        cmd += ["-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd += [_SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = build()
+        lib = ctypes.CDLL(path)
+        d, i, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.eqref_num_threads.restype = i
+        lib.eqref_cn_expand.argtypes = [i, i, i, d, d]
+        lib.eqref_cn_expand.restype = None
+        lib.eqref_apply_dense.argtypes = [i64, i64, i64, d, d, d]
+        lib.eqref_apply_dense.restype = None
+        lib.eqref_cn_dense.argtypes = [i, i, i, i64, d, d, d]
+        lib.eqref_cn_dense.restype = i
+        lib.eqref_cn_direct.argtypes = [i, i, i, i64, d, d, d]
+        lib.eqref_cn_direct.restype = None
+        lib.eqref_cn_weight_dft.argtypes = [i, i, i, d, d]
+        lib.eqref_cn_weight_dft.restype = None
+        lib.eqref_d8_expand.argtypes = [i, i, d, d]
+        lib.eqref_d8_expand.restype = None
+        lib.eqref_d8_dense.argtypes = [i, i, i64, d, d, d]
+        lib.eqref_d8_dense.restype = i
+        _lib = lib
+        return lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().eqref_num_threads())
+
+
+def cn_expand(w):
+    """Dense group-circulant matrix [(N*C_out), (N*C_in)] from w[C_out][C_in][N]."""
+    w = _f64(w)
+    C_out, C_in, N = w.shape
+    W = np.empty((N * C_out, N * C_in), dtype=np.float64)
+    _load().eqref_cn_expand(N, C_in, C_out, _p(w), _p(W))
+    return W
+
+
+def apply_dense(W, x2d):
+    """y[t] = W @ x[t] for x2d[T][cols]."""
+    W, x2d = _f64(W), _f64(x2d)
+    T, cols = x2d.shape
+    rows = W.shape[0]
+    assert W.shape[1] == cols
+    y = np.empty((T, rows), dtype=np.float64)
+    _load().eqref_apply_dense(T, rows, cols, _p(W), _p(x2d), _p(y))
+    return y
+
+
+def cn_dense(x, w):
+    """C_N layer by replicate-and-multiply; x[T][C_in][N], w[C_out][C_in][N]."""
+    x, w = _f64(x), _f64(w)
+    T, C_in, N = x.shape
+    C_out = w.shape[0]
+    assert w.shape == (C_out, C_in, N)
+    y = np.empty((T, C_out, N), dtype=np.float64)
+    if _load().eqref_cn_dense(N, C_in, C_out, T, _p(x), _p(w), _p(y)) != 0:
+        raise MemoryError("oracle: cannot allocate the dense matrix")
+    return y
+
+
+def cn_direct(x, w):
+    """C_N layer as the direct circular-convolution sum."""
+    x, w = _f64(x), _f64(w)
+    T, C_in, N = x.shape
+    C_out = w.shape[0]
+    assert w.shape == (C_out, C_in, N)
+    y = np.empty((T, C_out, N), dtype=np.float64)
+    _load().eqref_cn_direct(N, C_in, C_out, T, _p(x), _p(w), _p(y))
+    return y
+
+
+def cn_weight_dft(w):
+    """Packed real-DFT planes [N][C_out][C_in] of w[C_out][C_in][N]."""
+    w = _f64(w)
+    C_out, C_in, N = w.shape
+    P = np.empty((N, C_out, C_in), dtype=np.float64)
+    _load().eqref_cn_weight_dft(N, C_out, C_in, _p(w), _p(P))
+    return P
+
+
+def d8_expand(wb, C_in, C_out):
+    wb = _f64(wb)
+    assert wb.size == C_in * C_out // 8
+    W = np.empty((C_out, C_in), dtype=np.float64)
+    _load().eqref_d8_expand(C_in, C_out, _p(wb), _p(W))
+    return W
+
+
+def d8_dense(x, wb, C_out):
+    """D8 Fourier-domain layer; x[T][C_in], wb packed [A1|A2|B1|B2|E]."""
+    x, wb = _f64(x), _f64(wb)
+    T, C_in = x.shape
+    assert wb.size == C_in * C_out // 8
+    y = np.empty((T, C_out), dtype=np.float64)
+    if _load().eqref_d8_dense(C_in, C_out, T, _p(x), _p(wb), _p(y)) != 0:
+        raise MemoryError("oracle: cannot allocate the dense matrix")
+    return y
+
+
+# --- counts -----------------------------------------------------------------
+# Real GEMMs of size T x C_in x C_out in the half-spectrum method: the DC bin
+# (and the Nyquist bin for even N) are real products; every other kept bin is
+# a complex product = four real products.
+
+def cn_kept_bins(N: int) -> int:
+    return N // 2 + 1
+
+
+def cn_real_gemms(N: int) -> int:
+    complex_bins = (N - 1) // 2
+    real_bins = 1 + (1 if N % 2 == 0 else 0)
+    return real_bins + 4 * complex_bins
+
+
+def cn_params(N: int, C_in: int, C_out: int) -> int:
+    return N * C_in * C_out
+
+
+def d8_params(C_in: int, C_out: int) -> int:
+    mi, mo = C_in // 8, C_out // 8
+    return 4 * mi * mo + (2 * mi) * (2 * mo)
+
+
+def d8_mults(C_in: int, C_out: int) -> int:
+    mi, mo = C_in // 8, C_out // 8
+    return 4 * mi * mo + 2 * (2 * mi) * (2 * mo)

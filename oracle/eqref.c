@@ -1,0 +1,165 @@
+/*
+ * eqref.c -- plain fp64 CPU oracle for the equivariant linear layers.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library calls this file; only the
+ * tests, the smoke check and the benchmark's CPU-baseline leg load it.  It
+ * shares no code, header or table with the GPU path.
+ *
+ * Every routine computes a plain definition, with plain loops, in fp64:
+ *
+ *  - C_N layer.  "Flash EQ-Linear" (gist.science summary), Core Insight: the
+ *    layer is a circular convolution along the group axis composed with a
+ *    channel mixing, and its weight matrix is group-circulant, i.e. built by
+ *    cyclically shifting and replicating a small set of learnable parameters.
+ *    Problem Statement: the usual implementation replicates those parameters
+ *    into a dense matrix and multiplies.  Written out:
+ *        W_dense[o*N+g][i*N+h] = w[o][i][(g-h) mod N]
+ *        y[t][o*N+g] = sum_{i,h} W_dense[o*N+g][i*N+h] * x[t][i*N+h]
+ *    (eqref_cn_expand + eqref_apply_dense), and the same sum taken directly
+ *    as a convolution (eqref_cn_direct).
+ *
+ *  - Weight spectrum.  Algorithmic Approach: the group axis is taken to the
+ *    Fourier domain with the DFT; for real data only the non-redundant half
+ *    of the bins is kept.  eqref_cn_weight_dft evaluates
+ *        What[k] = sum_m w[m] * exp(-2*pi*i*m*k/N),  k = 0 .. floor(N/2)
+ *    and packs it into N real planes: plane 0 = Re What[0]; planes 2k-1, 2k =
+ *    Re, Im What[k] for 1 <= k < N/2; plane N-1 = Re What[N/2] when N is even.
+ *
+ *  - D8 Fourier-domain layer.  "Quick ViTs" (papernotes), key design 2
+ *    (Fourier-domain equivariant computation): a width-C map is four square
+ *    blocks of size C/8 (irreps A1, A2, B1, B2) and one square block of size
+ *    C/4 that is applied to both coordinates of the 2-D irrep E.  With the
+ *    feature layout [A1 | A2 | B1 | B2 | E coord 0 | E coord 1] the layer is a
+ *    block-diagonal matrix (eqref_d8_expand) times x.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int eqref_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* W_dense[(o*N+g)*(N*C_in) + i*N+h] = w[(o*C_in+i)*N + (g-h) mod N]. */
+void eqref_cn_expand(int N, int C_in, int C_out, const double* w, double* W) {
+    const int64_t cols = (int64_t)N * C_in;
+    for (int o = 0; o < C_out; ++o)
+        for (int g = 0; g < N; ++g)
+            for (int i = 0; i < C_in; ++i)
+                for (int h = 0; h < N; ++h) {
+                    int m = ((g - h) % N + N) % N;
+                    W[((int64_t)o * N + g) * cols + (int64_t)i * N + h] =
+                        w[((int64_t)o * C_in + i) * N + m];
+                }
+}
+
+/* y[t][r] = sum_c W[r][c] * x[t][c] for every token (rows x cols matrix). */
+void eqref_apply_dense(int64_t T, int64_t rows, int64_t cols, const double* W,
+                       const double* x, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double* xt = x + t * cols;
+        double* yt = y + t * rows;
+        for (int64_t r = 0; r < rows; ++r) {
+            const double* Wr = W + r * cols;
+            double acc = 0.0;
+            for (int64_t c = 0; c < cols; ++c) acc += Wr[c] * xt[c];
+            yt[r] = acc;
+        }
+    }
+}
+
+/* Replicate-and-multiply: the dense definition of the C_N layer.
+ * Returns 0 on success, -1 if the dense matrix cannot be allocated. */
+int eqref_cn_dense(int N, int C_in, int C_out, int64_t T, const double* x,
+                   const double* w, double* y) {
+    const int64_t rows = (int64_t)N * C_out, cols = (int64_t)N * C_in;
+    double* W = (double*)malloc(sizeof(double) * rows * cols);
+    if (!W) return -1;
+    eqref_cn_expand(N, C_in, C_out, w, W);
+    eqref_apply_dense(T, rows, cols, W, x, y);
+    free(W);
+    return 0;
+}
+
+/* The same layer as a direct circular convolution along the group axis:
+ * y[t][o][g] = sum_i sum_m w[o][i][m] * x[t][i][(g-m) mod N]. */
+void eqref_cn_direct(int N, int C_in, int C_out, int64_t T, const double* x,
+                     const double* w, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int o = 0; o < C_out; ++o)
+            for (int g = 0; g < N; ++g) {
+                double acc = 0.0;
+                for (int i = 0; i < C_in; ++i)
+                    for (int m = 0; m < N; ++m) {
+                        int h = ((g - m) % N + N) % N;
+                        acc += w[((int64_t)o * C_in + i) * N + m] *
+                               x[(t * C_in + i) * N + h];
+                    }
+                y[(t * C_out + o) * N + g] = acc;
+            }
+}
+
+/* Real DFT of w along its last axis, packed into N planes [N][C_out][C_in]. */
+void eqref_cn_weight_dft(int N, int C_out, int C_in, const double* w, double* planes) {
+    const double two_pi = 2.0 * acos(-1.0);
+    const int64_t plane = (int64_t)C_out * C_in;
+    for (int64_t oi = 0; oi < plane; ++oi) {
+        const double* wm = w + oi * N;
+        for (int k = 0; k <= N / 2; ++k) {
+            double re = 0.0, im = 0.0;
+            for (int m = 0; m < N; ++m) {
+                double ang = two_pi * (double)((m * k) % N) / (double)N;
+                re += wm[m] * cos(ang);
+                im -= wm[m] * sin(ang);
+            }
+            if (k == 0) {
+                planes[oi] = re;
+            } else if (2 * k == N) {
+                planes[(int64_t)(N - 1) * plane + oi] = re;
+            } else {
+                planes[(int64_t)(2 * k - 1) * plane + oi] = re;
+                planes[(int64_t)(2 * k) * plane + oi] = im;
+            }
+        }
+    }
+}
+
+/* D8 block-diagonal matrix [C_out][C_in] from the packed blocks
+ * wb = [W_A1 | W_A2 | W_B1 | W_B2 | W_E], each row-major [out][in];
+ * 1-D blocks are (C_out/8 x C_in/8), W_E is (C_out/4 x C_in/4). */
+void eqref_d8_expand(int C_in, int C_out, const double* wb, double* W) {
+    const int mi = C_in / 8, mo = C_out / 8;
+    memset(W, 0, sizeof(double) * (size_t)C_in * (size_t)C_out);
+    const double* blk = wb;
+    for (int b = 0; b < 4; ++b) { /* A1, A2, B1, B2 */
+        for (int r = 0; r < mo; ++r)
+            for (int c = 0; c < mi; ++c)
+                W[(int64_t)(b * mo + r) * C_in + b * mi + c] = blk[(int64_t)r * mi + c];
+        blk += (int64_t)mo * mi;
+    }
+    for (int e = 0; e < 2; ++e) /* W_E on E coordinate 0, then coordinate 1 */
+        for (int r = 0; r < 2 * mo; ++r)
+            for (int c = 0; c < 2 * mi; ++c)
+                W[(int64_t)(4 * mo + 2 * e * mo + r) * C_in + 4 * mi + 2 * e * mi + c] =
+                    blk[(int64_t)r * (2 * mi) + c];
+}
+
+int eqref_d8_dense(int C_in, int C_out, int64_t T, const double* x, const double* wb,
+                   double* y) {
+    double* W = (double*)malloc(sizeof(double) * (size_t)C_in * (size_t)C_out);
+    if (!W) return -1;
+    eqref_d8_expand(C_in, C_out, wb, W);
+    eqref_apply_dense(T, C_out, C_in, W, x, y);
+    free(W);
+    return 0;
+}

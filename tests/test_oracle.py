@@ -1,0 +1,459 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+The oracle is checked against things other than itself: library routines
+(numpy's FFT through the convolution theorem, scipy's circulant and
+block-diagonal constructors, plain matmul), hand-derived examples
+(tests/golden/*.json), closed forms, invariants (equivariance, linearity),
+the dimension of the space of equivariant maps, and the operation counts the
+pages state.  test_mutants_are_caught plants plausible mistakes into a copy of
+the oracle's C source and checks that these pins reject every one of them.
+"""
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+import synthetic
+
+RNG = np.random.default_rng(1234)
+
+
+def _rand(*shape):
+    return RNG.standard_normal(shape)
+
+
+def rfft_route(x, w):
+    """Convolution theorem with numpy's FFT: y = irfft(sum_i rfft(w) * rfft(x))."""
+    N = x.shape[-1]
+    X = np.fft.rfft(x, axis=-1)  # [T][C_in][K]
+    W = np.fft.rfft(w, axis=-1)  # [C_out][C_in][K]
+    Y = np.einsum("oik,tik->tok", W, X)
+    return np.fft.irfft(Y, n=N, axis=-1)
+
+
+def pack_rfft(w):
+    """numpy rfft of w[C_out][C_in][N] packed into N planes [N][C_out][C_in]."""
+    N = w.shape[-1]
+    R = np.fft.rfft(w, axis=-1)
+    planes = [R[..., 0].real]
+    for k in range(1, (N - 1) // 2 + 1):
+        planes += [R[..., k].real, R[..., k].imag]
+    if N % 2 == 0:
+        planes.append(R[..., N // 2].real)
+    return np.stack(planes)
+
+
+def rel(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# Pin functions (each raises AssertionError on failure; reused by the mutant test)
+
+def pin_hand_examples(orc, golden_dir):
+    with open(os.path.join(golden_dir, "cn_hand_examples.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        x = np.array(c["x"], float)
+        w = np.array(c["w"], float)
+        y = np.array(c["y"], float)
+        assert np.array_equal(orc.cn_dense(x, w), y), c["name"]
+        assert np.array_equal(orc.cn_direct(x, w), y), c["name"]
+    for c in g["weight_dft_cases"]:
+        w = np.array(c["w"], float)[None, None, :]
+        P = orc.cn_weight_dft(w)[:, 0, 0]
+        np.testing.assert_allclose(P, c["planes"], rtol=0, atol=1e-14, err_msg=c["name"])
+
+
+def pin_rfft_route(orc):
+    for N in range(1, 10):
+        for (C_in, C_out) in [(1, 1), (2, 3), (3, 2)]:
+            for T in (1, 5):
+                x, w = _rand(T, C_in, N), _rand(C_out, C_in, N)
+                ref = rfft_route(x, w)
+                assert rel(orc.cn_dense(x, w), ref) < 1e-13, (N, C_in, C_out, T)
+                assert rel(orc.cn_direct(x, w), ref) < 1e-13, (N, C_in, C_out, T)
+
+
+def pin_weight_dft(orc):
+    for N in range(1, 17):
+        w = _rand(3, 2, N)
+        assert rel(orc.cn_weight_dft(w), pack_rfft(w)) < 1e-14, N
+
+
+def pin_d8_blockdiag(orc, golden_dir):
+    with open(os.path.join(golden_dir, "d8_hand_example.json")) as f:
+        g = json.load(f)
+    order = ["A1", "A2", "B1", "B2", "E"]
+    for c in g["cases"]:
+        C = c["C"]
+        wb = np.concatenate([np.array(c["blocks"][k], float).ravel() for k in order])
+        y = orc.d8_dense(np.array(c["x"], float), wb, C)
+        assert np.array_equal(y, np.array(c["y"], float)), c["name"]
+    # library routine: scipy's block_diag with W_E placed on both E coordinates
+    for (C_in, C_out) in [(8, 16), (16, 8), (24, 24)]:
+        shapes = synthetic.d8_block_shapes(C_in, C_out)
+        blocks = [_rand(*s) for s in shapes]
+        wb = np.concatenate([b.ravel() for b in blocks])
+        ref = scipy.linalg.block_diag(*blocks, blocks[4])
+        assert np.array_equal(orc.d8_expand(wb, C_in, C_out), ref), (C_in, C_out)
+        x = _rand(3, C_in)
+        assert rel(orc.d8_dense(x, wb, C_out), x @ ref.T) < 1e-14
+
+
+def pin_closed_forms(orc):
+    N, C_in, C_out, T = 6, 3, 2, 4
+    x = _rand(T, C_in, N)
+    # weight only at shift 0: the same channel map for every group element
+    w = np.zeros((C_out, C_in, N))
+    w[..., 0] = _rand(C_out, C_in)
+    ref = np.einsum("oi,tig->tog", w[..., 0], x)
+    assert rel(orc.cn_dense(x, w), ref) < 1e-14
+    # w = delta_{o,i} delta_{m,s}: output is the input rolled by s
+    for s in range(N):
+        w = np.zeros((C_in, C_in, N))
+        for i in range(C_in):
+            w[i, i, s] = 1.0
+        assert np.array_equal(orc.cn_dense(x, w), np.roll(x, s, axis=-1)), s
+    # x constant along the group axis: y[t,o,g] = sum_i (sum_m w[o,i,m]) x[t,i]
+    w = _rand(C_out, C_in, N)
+    xc = np.repeat(_rand(T, C_in, 1), N, axis=-1)
+    ref = np.einsum("oi,ti->to", w.sum(-1), xc[..., 0])[..., None].repeat(N, -1)
+    assert rel(orc.cn_dense(xc, w), ref) < 1e-14
+    # alternating input (-1)^h: y[g] = (-1)^g * sum_i (sum_m (-1)^m w[o,i,m]) a[t,i]
+    sgn = (-1.0) ** np.arange(N)
+    a = _rand(T, C_in)
+    xa = a[..., None] * sgn
+    ref = np.einsum("oi,ti->to", (w * sgn).sum(-1), a)[..., None] * sgn
+    assert rel(orc.cn_dense(xa, w), ref) < 1e-14
+    # N = 1 is a plain matrix product
+    x1, w1 = _rand(T, C_in, 1), _rand(C_out, C_in, 1)
+    assert rel(orc.cn_dense(x1, w1)[..., 0], x1[..., 0] @ w1[..., 0].T) < 1e-15
+    # one channel in and out: scipy's circulant matrix (first column w)
+    for n in (2, 3, 5, 8):
+        w11 = _rand(1, 1, n)
+        xs = _rand(2, 1, n)
+        ref = xs[:, 0, :] @ scipy.linalg.circulant(w11[0, 0]).T
+        assert rel(orc.cn_dense(xs, w11)[:, 0, :], ref) < 1e-14
+
+
+def pin_dense_matrix_structure(orc):
+    # the replicated matrix equals the Kronecker-assembled circulant blocks
+    N, C_in, C_out = 5, 2, 3
+    w = _rand(C_out, C_in, N)
+    W = orc.cn_expand(w)
+    for o in range(C_out):
+        for i in range(C_in):
+            blk = W[o * N:(o + 1) * N, i * N:(i + 1) * N]
+            assert np.array_equal(blk, scipy.linalg.circulant(w[o, i])), (o, i)
+
+
+ALL_CN_PINS = [pin_rfft_route, pin_weight_dft, pin_closed_forms, pin_dense_matrix_structure]
+
+
+# ---------------------------------------------------------------------------
+# Tests
+
+def test_hand_examples(golden_dir):
+    pin_hand_examples(oracle, golden_dir)
+
+
+def test_rfft_route():
+    pin_rfft_route(oracle)
+
+
+def test_weight_dft_matches_numpy_rfft():
+    pin_weight_dft(oracle)
+
+
+def test_weight_dft_closed_forms():
+    for N in range(1, 17):
+        d = np.zeros((1, 1, N))
+        d[..., 0] = 1.0  # delta -> every bin is 1
+        P = oracle.cn_weight_dft(d)[:, 0, 0]
+        expect = np.zeros(N)
+        expect[0] = 1.0
+        for k in range(1, (N - 1) // 2 + 1):
+            expect[2 * k - 1] = 1.0
+        if N % 2 == 0 and N > 1:
+            expect[N - 1] = 1.0
+        np.testing.assert_allclose(P, expect, atol=1e-15)
+        c = np.full((1, 1, N), 2.5)  # constant -> DC = N*c, everything else 0
+        P = oracle.cn_weight_dft(c)[:, 0, 0]
+        np.testing.assert_allclose(P, np.r_[2.5 * N, np.zeros(N - 1)], atol=1e-13)
+
+
+def test_closed_forms():
+    pin_closed_forms(oracle)
+
+
+def test_dense_matrix_structure():
+    pin_dense_matrix_structure(oracle)
+
+
+def test_d8_block_diagonal(golden_dir):
+    pin_d8_blockdiag(oracle, golden_dir)
+
+
+@pytest.mark.parametrize("N", [3, 4, 7, 8])
+def test_equivariance_cyclic_roll(N):
+    x, w = _rand(4, 3, N), _rand(2, 3, N)
+    y = oracle.cn_direct(x, w)
+    for s in range(1, N):
+        ys = oracle.cn_direct(np.roll(x, s, axis=-1), w)
+        # the direct sum visits the same products in the same order: bitwise
+        assert np.array_equal(ys, np.roll(y, s, axis=-1))
+        yd = oracle.cn_dense(np.roll(x, s, axis=-1), w)
+        assert rel(yd, np.roll(y, s, axis=-1)) < 1e-13
+
+
+def test_linearity():
+    N, C_in, C_out = 5, 3, 2
+    x1, x2, w1, w2 = _rand(3, C_in, N), _rand(3, C_in, N), _rand(C_out, C_in, N), _rand(C_out, C_in, N)
+    a, b = 0.75, -1.25
+    assert rel(oracle.cn_dense(a * x1 + b * x2, w1),
+               a * oracle.cn_dense(x1, w1) + b * oracle.cn_dense(x2, w1)) < 1e-13
+    assert rel(oracle.cn_dense(x1, a * w1 + b * w2),
+               a * oracle.cn_dense(x1, w1) + b * oracle.cn_dense(x1, w2)) < 1e-13
+
+
+def _commutant_dim(gens_in, gens_out):
+    """dim {M : R_out(g) M = M R_in(g) for all generators g} by SVD."""
+    n_out, n_in = gens_out[0].shape[0], gens_in[0].shape[0]
+    rows = []
+    I_in, I_out = np.eye(n_in), np.eye(n_out)
+    for Rin, Rout in zip(gens_in, gens_out):
+        # vec(R_out M - M R_in) = (I_in (x) R_out - R_in^T (x) I_out) vec(M)  (column-major vec)
+        rows.append(np.kron(I_in, Rout) - np.kron(Rin.T, I_out))
+    L = np.vstack(rows)
+    s = np.linalg.svd(L, compute_uv=False)
+    return int(np.sum(s < 1e-9 * max(s.max(), 1.0))) + max(0, L.shape[1] - len(s))
+
+
+def _cyclic_shift(N, C):
+    P = np.roll(np.eye(N), 1, axis=0)  # (P v)[h] = v[h-1]
+    return np.kron(np.eye(C), P)
+
+
+@pytest.mark.parametrize("N,C_in,C_out", [(3, 1, 1), (3, 2, 1), (4, 2, 2), (5, 1, 3)])
+def test_cn_commutant_dimension(N, C_in, C_out):
+    """Every map that commutes with the cyclic shift is group-circulant, and the
+    oracle's replicated matrices fill that space: dimension = N*C_in*C_out."""
+    dim = _commutant_dim([_cyclic_shift(N, C_in)], [_cyclic_shift(N, C_out)])
+    assert dim == oracle.cn_params(N, C_in, C_out) == N * C_in * C_out
+    P_in, P_out = _cyclic_shift(N, C_in), _cyclic_shift(N, C_out)
+    basis = []
+    for idx in range(N * C_in * C_out):
+        e = np.zeros(N * C_in * C_out)
+        e[idx] = 1.0
+        W = oracle.cn_expand(e.reshape(C_out, C_in, N))
+        assert np.array_equal(P_out @ W, W @ P_in)
+        basis.append(W.ravel())
+    assert np.linalg.matrix_rank(np.array(basis)) == dim
+
+
+def d8_action(C):
+    """Generators r (quarter turn) and s (mirror) acting on D8 Fourier features
+    laid out [A1 | A2 | B1 | B2 | E coord 0 | E coord 1], m = C/8 copies of each
+    1-D irrep and 2m copies of E.  A1: (r,s)=(1,1), A2: (1,-1), B1: (-1,1),
+    B2: (-1,-1); E: r = [[0,-1],[1,0]], s = diag(1,-1) on each copy's
+    (coord 0, coord 1) pair."""
+    m = C // 8
+    r = np.zeros((C, C))
+    s = np.zeros((C, C))
+    for b, (rv, sv) in enumerate([(1, 1), (1, -1), (-1, 1), (-1, -1)]):
+        for j in range(m):
+            r[b * m + j, b * m + j] = rv
+            s[b * m + j, b * m + j] = sv
+    e0, e1 = 4 * m, 6 * m
+    for j in range(2 * m):
+        a, b = e0 + j, e1 + j
+        r[a, b] = -1.0  # new coord0 = -coord1
+        r[b, a] = 1.0   # new coord1 = coord0
+        s[a, a] = 1.0
+        s[b, b] = -1.0
+    return r, s
+
+
+def test_d8_action_is_the_regular_representation():
+    """The feature action is a D8 representation whose character is that of
+    C/8 copies of the regular representation (8m at the identity, 0 elsewhere)."""
+    for C in (8, 16):
+        r, s = d8_action(C)
+        I = np.eye(C)
+        assert np.array_equal(np.linalg.matrix_power(r, 4), I)
+        assert np.array_equal(s @ s, I)
+        assert np.array_equal(s @ r @ s, np.linalg.matrix_power(r, 3))
+        elems = [np.linalg.matrix_power(r, k) @ (s if f else I) for k in range(4) for f in (0, 1)]
+        tr = [np.trace(g) for g in elems]
+        assert tr[0] == C and all(t == 0 for t in tr[1:])
+
+
+@pytest.mark.parametrize("C", [8, 16])
+def test_d8_commutant_dimension(C):
+    """Equivariant maps of the Fourier features are exactly the oracle's block
+    matrices: the commutant has dimension C^2/8 (eight times fewer parameters
+    than a width-C linear), and the oracle's expansion spans it."""
+    r, s = d8_action(C)
+    dim = _commutant_dim([r, s], [r, s])
+    assert dim == C * C // 8 == oracle.d8_params(C, C)
+    basis = []
+    for idx in range(C * C // 8):
+        e = np.zeros(C * C // 8)
+        e[idx] = 1.0
+        W = oracle.d8_expand(e, C, C)
+        assert np.array_equal(r @ W, W @ r) and np.array_equal(s @ W, W @ s)
+        basis.append(W.ravel())
+    assert np.linalg.matrix_rank(np.array(basis)) == dim
+
+
+def test_d8_equivariance_random():
+    C_in, C_out = 16, 24
+    d = synthetic.d8_inputs(C_in, C_out, 5, synthetic.F32, seed=3)
+    x, wb = d["x64"], d["w64"]
+    rin, sin_ = d8_action(C_in)
+    rout, sout = d8_action(C_out)
+    y = oracle.d8_dense(x, wb, C_out)
+    assert rel(oracle.d8_dense(x @ rin.T, wb, C_out), y @ rout.T) < 1e-14
+    assert rel(oracle.d8_dense(x @ sin_.T, wb, C_out), y @ sout.T) < 1e-14
+
+
+def test_p4_transform_is_dyadic():
+    """For N=4 the forward real-DFT matrix has entries in {0, +-1} and the
+    inverse (1/N, doubled non-self-conjugate bins) entries in {0, +-1/4, +-1/2}:
+    only adds, subtracts and power-of-two scalings ("Flash EQ-Linear",
+    Specialization for p4 Rotation Group)."""
+    F = oracle.cn_weight_dft(np.eye(4)[None, :, :])[:, 0, :]  # planes x inputs
+    assert set(np.round(F.ravel(), 14)) <= {0.0, 1.0, -1.0}
+    # inverse: y = G @ planes; find G from the oracle's layer with delta weights
+    G = np.zeros((4, 4))
+    for p in range(4):
+        # a spectrum with one plane set to 1 -> time signal via numpy irfft
+        spec = np.zeros(3, complex)
+        if p == 0:
+            spec[0] = 1
+        elif p == 3:
+            spec[2] = 1
+        elif p == 1:
+            spec[1] = 1
+        else:
+            spec[1] = 1j
+        G[:, p] = np.fft.irfft(spec, n=4)
+    assert set(np.round(np.abs(G.ravel()), 14)) <= {0.0, 0.25, 0.5}
+    assert np.allclose(G @ F, np.eye(4))
+
+
+def test_page_counts(golden_dir):
+    with open(os.path.join(golden_dir, "page_counts.json")) as f:
+        counts = {c["what"][:40]: c for c in json.load(f)["counts"]}
+    vals = [c["value"] for c in counts.values()]
+    # six real products at N=4 against sixteen for the replicated dense matrix
+    assert oracle.cn_real_gemms(4) == vals[0] and 4 * 4 == 16
+    assert abs(16 / oracle.cn_real_gemms(4) - 2.67) < 0.005
+    # parameter reduction against a non-equivariant layer of the same width = N
+    assert (4 * 8) * (4 * 8) // oracle.cn_params(4, 8, 8) == vals[1]
+    # MACs per token: R(N) C_in C_out <= 2/N * (N C_in)(N C_out), -> 2/N as N grows
+    for N in range(2, 65):
+        ratio = oracle.cn_real_gemms(N) / N ** 2
+        assert ratio <= vals[2] / N + 1e-12
+    assert abs(oracle.cn_real_gemms(64) / 64 ** 2 * 64 / 2 - 1) < 0.02
+    # D8: 8x fewer parameters, 5.33x fewer multiplies than a same-width linear
+    for C in (8, 64, 1280):
+        assert C * C / oracle.d8_params(C, C) == vals[3]
+        assert abs(C * C / oracle.d8_mults(C, C) - vals[4]) < 0.005
+    # odd and even orders of the benchmark workloads
+    assert [oracle.cn_real_gemms(n) for n in (4, 7, 8)] == [6, 13, 14]
+
+
+# ---------------------------------------------------------------------------
+# Mutation check: plausible mistakes planted in a copy of the oracle must fail a pin.
+
+MUTANTS = [
+    ("correlation instead of convolution", "int m = ((g - h) % N + N) % N;", "int m = ((h - g) % N + N) % N;"),
+    ("direct sum index sign", "int h = ((g - m) % N + N) % N;", "int h = ((g + m) % N + N) % N;"),
+    ("transposed channel operand", "W[((int64_t)o * N + g) * cols + (int64_t)i * N + h] =\n                        w[((int64_t)o * C_in + i) * N + m];",
+     "W[((int64_t)o * N + g) * cols + (int64_t)i * N + h] =\n                        w[((int64_t)i * C_out + o) * N + m];"),
+    ("dropped last term", "for (int64_t c = 0; c < cols; ++c) acc += Wr[c] * xt[c];",
+     "for (int64_t c = 0; c + 1 < cols; ++c) acc += Wr[c] * xt[c];"),
+    ("imaginary sign", "im -= wm[m] * sin(ang);", "im += wm[m] * sin(ang);"),
+    ("Nyquist plane slot", "planes[(int64_t)(N - 1) * plane + oi] = re;", "planes[(int64_t)(N - 2) * plane + oi] = re;"),
+    ("D8 transposed 1-D block", "blk[(int64_t)r * mi + c];", "blk[(int64_t)c * mi + r];"),
+    ("D8 E weight on coordinate 0 only", "4 * mi + 2 * e * mi + c] =", "4 * mi + c] ="),
+]
+
+
+def _build_mutant(tmp_path, old, new):
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, old
+    mdir = tmp_path / "m"
+    mdir.mkdir(exist_ok=True)
+    msrc = mdir / "eqref.c"
+    msrc.write_text(src.replace(old, new))
+    out = mdir / ("lib%d.so" % abs(hash(new)))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", str(msrc),
+                    "-o", str(out), "-lm"], check=True)
+    return str(out)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutants_are_caught(tmp_path, golden_dir, name, old, new):
+    path = _build_mutant(tmp_path, old, new)
+    saved = oracle._lib
+    try:
+        oracle._lib = None
+        real_build = oracle.build
+        oracle.build = lambda *a, **k: path
+        caught = []
+        checks = [lambda: pin_hand_examples(oracle, golden_dir),
+                  lambda: pin_d8_blockdiag(oracle, golden_dir)] + [
+            (lambda f=f: f(oracle)) for f in ALL_CN_PINS]
+        for chk in checks:
+            try:
+                chk()
+            except AssertionError:
+                caught.append(chk)
+        assert caught, f"mutant '{name}' passed every pin"
+    finally:
+        oracle.build = real_build
+        oracle._lib = saved
+
+
+def _preload_in_use():
+    if os.environ.get("LD_PRELOAD"):
+        return True
+    try:
+        return bool(open("/etc/ld.so.preload").read().strip())
+    except OSError:
+        return False
+
+
+@pytest.mark.skipif(_preload_in_use(), reason="a preload library is already configured; "
+                    "ASan must be loaded first and that library is left alone")
+def test_oracle_under_sanitizers(tmp_path):
+    """Build the oracle with ASan+UBSan and run a small case in a fresh process."""
+    out = oracle.build(sanitize=True, out=str(tmp_path / "libeqref_san.so"))
+    code = (
+        "import ctypes, numpy as np\n"
+        f"lib = ctypes.CDLL({out!r})\n"
+        "x = np.random.default_rng(0).standard_normal((3, 2, 5)); w = np.ones((4, 2, 5))\n"
+        "y = np.zeros((3, 4, 5)); P = np.zeros((5, 4, 2))\n"
+        "p = lambda a: a.ctypes.data_as(ctypes.c_void_p)\n"
+        "lib.eqref_cn_dense.argtypes = [ctypes.c_int]*3 + [ctypes.c_int64] + [ctypes.c_void_p]*3\n"
+        "assert lib.eqref_cn_dense(5, 2, 4, 3, p(x), p(w), p(y)) == 0\n"
+        "lib.eqref_cn_direct.argtypes = lib.eqref_cn_dense.argtypes\n"
+        "lib.eqref_cn_direct(5, 2, 4, 3, p(x), p(w), p(y))\n"
+        "lib.eqref_cn_weight_dft.argtypes = [ctypes.c_int]*3 + [ctypes.c_void_p]*2\n"
+        "lib.eqref_cn_weight_dft(5, 4, 2, p(w), p(P))\n"
+        "wb = np.ones(16*16//8); xd = np.ones((2, 16)); yd = np.zeros((2, 16))\n"
+        "lib.eqref_d8_dense.argtypes = [ctypes.c_int]*2 + [ctypes.c_int64] + [ctypes.c_void_p]*3\n"
+        "assert lib.eqref_d8_dense(16, 16, 2, p(xd), p(wb), p(yd)) == 0\n"
+        "print('SAN-OK')\n"
+    )
+    asan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    env = dict(os.environ, LD_PRELOAD=asan, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1")
+    r = subprocess.run(["python3", "-c", code], capture_output=True, text=True, env=env)
+    assert r.returncode == 0 and "SAN-OK" in r.stdout, r.stderr[-2000:]
