@@ -1,0 +1,252 @@
+"""Python binding of libeqlinear.so, the MI355X (gfx950) equivariant linear layers.
+
+A thin ctypes layer over the C ABI in include/eqlinear.h: every function has the
+C name, turns tensors into device pointers and the current torch stream into a
+hipStream_t, checks shapes and dtypes, and raises EqlError on a non-OK status.
+All arithmetic runs in the library's HIP kernels; there is no fallback path.
+If the library has not been built, loading fails loudly.
+
+Tensor arguments may be torch tensors on a ROCm device, or plain integers
+(raw device addresses, for callers that manage memory themselves).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libeqlinear.so")
+
+EQL_OK, EQL_ERR_INVALID, EQL_ERR_UNSUPPORTED, EQL_ERR_HIP, EQL_ERR_NOMEM = range(5)
+EQL_F32, EQL_BF16 = 0, 1
+EQL_KIND_CN, EQL_KIND_D8 = 0, 1
+
+# Every entry point of include/eqlinear.h.
+ABI_FUNCTIONS = (
+    "eqlinear_status_string", "eqlinear_plan", "eqlinear_d8_plan", "eqlinear_plan_destroy",
+    "eqlinear_plan_info", "eqlinear_w_hat_elems", "eqlinear_weight_fft", "eqlinear_forward",
+    "eqlinear_forward_tiled", "eqlinear_d8_forward", "eqlinear_expand_dense",
+    "eqlinear_dense_forward",
+)
+
+
+class EqlError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {eqlinear_status_string(status)}")
+
+
+class eqlinear_info(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("dtype", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("C_in", ctypes.c_int32), ("C_out", ctypes.c_int32), ("bins", ctypes.c_int32),
+        ("planes", ctypes.c_int32), ("has_nyquist", ctypes.c_int32),
+        ("params", ctypes.c_int64), ("w_hat_elems", ctypes.c_int64),
+        ("real_gemms", ctypes.c_int64), ("macs_per_token", ctypes.c_int64),
+        ("dense_macs_per_token", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str | None = None):
+    """Load libeqlinear.so (raises OSError if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise OSError(f"{p} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(p)
+        vp, i32, i64, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int
+        plan_p = ctypes.POINTER(ctypes.c_void_p)
+        sig = {
+            "eqlinear_status_string": ([st], ctypes.c_char_p),
+            "eqlinear_plan": ([plan_p, i32, i32, i32, i32], st),
+            "eqlinear_d8_plan": ([plan_p, i32, i32, i32], st),
+            "eqlinear_plan_destroy": ([vp], st),
+            "eqlinear_plan_info": ([vp, ctypes.POINTER(eqlinear_info)], st),
+            "eqlinear_w_hat_elems": ([vp], ctypes.c_size_t),
+            "eqlinear_weight_fft": ([vp, vp, vp], st),
+            "eqlinear_forward": ([vp, vp, vp, vp, i64, vp], st),
+            "eqlinear_forward_tiled": ([vp, vp, vp, vp, i64, vp, i32], st),
+            "eqlinear_d8_forward": ([vp, vp, vp, vp, i64, vp], st),
+            "eqlinear_expand_dense": ([vp, vp, vp, vp], st),
+            "eqlinear_dense_forward": ([vp, vp, vp, vp, i64, vp], st),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(lib, name)
+            f.argtypes, f.restype = args, res
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def eqlinear_status_string(status: int) -> str:
+    return load_library().eqlinear_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != EQL_OK:
+        raise EqlError(status, where)
+
+
+class Plan:
+    """Owns an eqlinear_plan_t; destroyed when garbage-collected."""
+
+    def __init__(self, handle: int, lib):
+        self.handle = ctypes.c_void_p(handle)
+        self._lib = lib
+        self.info = eqlinear_plan_info(self)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            self._lib.eqlinear_plan_destroy(h)
+            self.handle = ctypes.c_void_p(0)
+
+    @property
+    def dtype(self):
+        return self.info["dtype"]
+
+
+def eqlinear_plan(N: int, C_in: int, C_out: int, dtype: int) -> Plan:
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.eqlinear_plan(ctypes.byref(h), N, C_in, C_out, int(dtype)), "eqlinear_plan")
+    return Plan(h.value, lib)
+
+
+def eqlinear_d8_plan(C_in: int, C_out: int, dtype: int) -> Plan:
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.eqlinear_d8_plan(ctypes.byref(h), C_in, C_out, int(dtype)), "eqlinear_d8_plan")
+    return Plan(h.value, lib)
+
+
+def eqlinear_plan_destroy(plan: Plan):
+    if plan.handle.value:
+        _check(plan._lib.eqlinear_plan_destroy(plan.handle), "eqlinear_plan_destroy")
+        plan.handle = ctypes.c_void_p(0)
+
+
+def eqlinear_plan_info(plan: Plan) -> dict:
+    inf = eqlinear_info()
+    _check(plan._lib.eqlinear_plan_info(plan.handle, ctypes.byref(inf)), "eqlinear_plan_info")
+    return inf.as_dict()
+
+
+def eqlinear_w_hat_elems(plan: Plan) -> int:
+    return int(plan._lib.eqlinear_w_hat_elems(plan.handle))
+
+
+# --- tensor marshalling --------------------------------------------------------
+
+def _torch_dtype(plan: Plan):
+    import torch
+    return torch.bfloat16 if plan.dtype == EQL_BF16 else torch.float32
+
+
+def _ptr(t, plan: Plan, numel: int | None, name: str):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor or a device address")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: tensor must live on the GPU, got {t.device}")
+    if t.dtype != _torch_dtype(plan):
+        raise ValueError(f"{name}: dtype {t.dtype} does not match the plan ({_torch_dtype(plan)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _widths(plan: Plan):
+    inf = plan.info
+    if inf["kind"] == EQL_KIND_CN:
+        return inf["N"] * inf["C_in"], inf["N"] * inf["C_out"]
+    return inf["C_in"], inf["C_out"]
+
+
+def _tokens(x, T, K):
+    if T is not None:
+        return int(T)
+    if isinstance(x, int):
+        raise ValueError("T is required when x is a raw address")
+    return x.numel() // K
+
+
+def eqlinear_weight_fft(plan: Plan, w, w_hat):
+    n = eqlinear_w_hat_elems(plan)
+    _check(plan._lib.eqlinear_weight_fft(plan.handle, _ptr(w, plan, n, "w"),
+                                         _ptr(w_hat, plan, n, "w_hat")), "eqlinear_weight_fft")
+
+
+def eqlinear_forward(plan: Plan, x, w_hat, y, T: int | None = None, stream=None):
+    K, M = _widths(plan)
+    T = _tokens(x, T, K)
+    n = eqlinear_w_hat_elems(plan)
+    _check(plan._lib.eqlinear_forward(plan.handle, _ptr(x, plan, T * K, "x"),
+                                      _ptr(w_hat, plan, n, "w_hat"), _ptr(y, plan, T * M, "y"),
+                                      T, _stream(stream)), "eqlinear_forward")
+
+
+def eqlinear_forward_tiled(plan: Plan, x, w_hat, y, tile: int, T: int | None = None, stream=None):
+    K, M = _widths(plan)
+    T = _tokens(x, T, K)
+    n = eqlinear_w_hat_elems(plan)
+    _check(plan._lib.eqlinear_forward_tiled(plan.handle, _ptr(x, plan, T * K, "x"),
+                                            _ptr(w_hat, plan, n, "w_hat"),
+                                            _ptr(y, plan, T * M, "y"), T, _stream(stream),
+                                            int(tile)), "eqlinear_forward_tiled")
+
+
+def eqlinear_d8_forward(plan: Plan, x, wb, y, T: int | None = None, stream=None):
+    K, M = _widths(plan)
+    T = _tokens(x, T, K)
+    n = eqlinear_w_hat_elems(plan)
+    _check(plan._lib.eqlinear_d8_forward(plan.handle, _ptr(x, plan, T * K, "x"),
+                                         _ptr(wb, plan, n, "wb"), _ptr(y, plan, T * M, "y"),
+                                         T, _stream(stream)), "eqlinear_d8_forward")
+
+
+def eqlinear_expand_dense(plan: Plan, w, w_dense, stream=None):
+    K, M = _widths(plan)
+    n = eqlinear_w_hat_elems(plan)
+    _check(plan._lib.eqlinear_expand_dense(plan.handle, _ptr(w, plan, n, "w"),
+                                           _ptr(w_dense, plan, K * M, "w_dense"),
+                                           _stream(stream)), "eqlinear_expand_dense")
+
+
+def eqlinear_dense_forward(plan: Plan, x, w_dense, y, T: int | None = None, stream=None):
+    K, M = _widths(plan)
+    T = _tokens(x, T, K)
+    _check(plan._lib.eqlinear_dense_forward(plan.handle, _ptr(x, plan, T * K, "x"),
+                                            _ptr(w_dense, plan, K * M, "w_dense"),
+                                            _ptr(y, plan, T * M, "y"), T, _stream(stream)),
+           "eqlinear_dense_forward")
+
+
+def built() -> bool:
+    return os.path.exists(LIB_PATH)

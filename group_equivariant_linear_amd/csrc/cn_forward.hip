@@ -1,0 +1,32 @@
+// cn_forward.hip -- dispatch of the fused C_N forward over group order and dtype.
+// The kernel instantiations live in cn_fwd_{f32,bf16}_{lo,hi}.hip so they build
+// in parallel.
+#include "eq_launch.h"
+
+namespace eql {
+
+template <int N, typename IO>
+hipError_t launch_n(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
+                    hipStream_t stream, int tile_override);
+
+template <typename IO>
+static hipError_t launch_dt(int N, const void* x, const void* w_hat, void* y, int64_t T,
+                            int C_in, int C_out, hipStream_t stream, int tile) {
+    switch (N) {
+#define EQL_CASE(n) \
+    case n: return launch_n<n, IO>(x, w_hat, y, T, C_in, C_out, stream, tile);
+        EQL_CASE(1) EQL_CASE(2) EQL_CASE(3) EQL_CASE(4) EQL_CASE(5) EQL_CASE(6) EQL_CASE(7)
+        EQL_CASE(8) EQL_CASE(9) EQL_CASE(10) EQL_CASE(11) EQL_CASE(12) EQL_CASE(13)
+        EQL_CASE(14) EQL_CASE(15) EQL_CASE(16)
+#undef EQL_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_cn_forward(int N, int dtype_bf16, const void* x, const void* w_hat, void* y,
+                             int64_t T, int C_in, int C_out, hipStream_t stream, int tile) {
+    if (dtype_bf16) return launch_dt<__bf16>(N, x, w_hat, y, T, C_in, C_out, stream, tile);
+    return launch_dt<float>(N, x, w_hat, y, T, C_in, C_out, stream, tile);
+}
+
+}  // namespace eql

@@ -1,0 +1,43 @@
+// eq_launch.h -- internal host-side launchers of libeqlinear (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eql {
+
+constexpr int kMaxGemmJobs = 6;
+
+// One independent product y[t][y_col+n] = sum_k W[n][k] x[t][x_col+k],
+// n < Nn, k < K, W = w + w_off with row stride ldw (elements).
+struct GemmJob {
+    int x_col, y_col, K, Nn;
+    int64_t w_off;
+    int ldw;
+    int tile_begin;  // first column tile of this job (filled by the launcher)
+    int x_vec_ok, w_vec_ok, y_vec_ok;  // 16-byte (8-byte for bf16 y) access allowed
+};
+
+struct GemmJobs {
+    GemmJob j[kMaxGemmJobs];
+    int njobs;
+    int tiles_per_row;  // column tiles per token tile (filled by the launcher)
+};
+
+// tile: -1 = automatic choice, else a fixed tile configuration (tests, tuning).
+hipError_t launch_cn_forward(int N, int dtype_bf16, const void* x, const void* w_hat, void* y,
+                             int64_t T, int C_in, int C_out, hipStream_t stream, int tile);
+
+hipError_t launch_gemm_rows(int dtype_bf16, GemmJobs jobs, const void* x, const void* w, void* y,
+                            int64_t T, int ldx, int ldy, hipStream_t stream);
+
+hipError_t launch_weight_dft(int N, int dtype_bf16, const void* w, void* w_hat, int C_in,
+                             int C_out, hipStream_t stream);
+
+hipError_t launch_cn_expand(int N, int dtype_bf16, const void* w, void* w_dense, int C_in,
+                            int C_out, hipStream_t stream);
+
+hipError_t launch_d8_expand(int dtype_bf16, const void* wb, void* w_dense, int C_in, int C_out,
+                            hipStream_t stream);
+
+}  // namespace eql

@@ -1,0 +1,222 @@
+// eqlinear_api.hip -- the C ABI of libeqlinear (declared in include/eqlinear.h):
+// plan metadata, argument validation and kernel dispatch.  Validation runs
+// before any HIP call so the error paths can be exercised without a GPU.
+#include <new>
+
+#include "../../include/eqlinear.h"
+#include "eq_launch.h"
+
+struct eqlinear_plan_s {
+    int kind;
+    int dtype;
+    int N;
+    int C_in, C_out;
+};
+
+namespace {
+
+
+bool dtype_ok(int dt) { return dt == EQL_F32 || dt == EQL_BF16; }
+
+size_t elem_size(const eqlinear_plan_s* p) { return p->dtype == EQL_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+eqlinear_status hip_status(hipError_t e) { return e == hipSuccess ? EQL_OK : EQL_ERR_HIP; }
+
+int64_t in_width(const eqlinear_plan_s* p) {
+    return p->kind == EQL_KIND_CN ? (int64_t)p->N * p->C_in : p->C_in;
+}
+int64_t out_width(const eqlinear_plan_s* p) {
+    return p->kind == EQL_KIND_CN ? (int64_t)p->N * p->C_out : p->C_out;
+}
+
+// Widths are capped so every per-row offset fits an int in the kernels.
+constexpr int64_t kMaxWidth = 1 << 20;
+
+}  // namespace
+
+extern "C" {
+
+const char* eqlinear_status_string(eqlinear_status s) {
+    switch (s) {
+        case EQL_OK: return "EQL_OK";
+        case EQL_ERR_INVALID: return "EQL_ERR_INVALID: invalid argument";
+        case EQL_ERR_UNSUPPORTED: return "EQL_ERR_UNSUPPORTED: not supported by this build";
+        case EQL_ERR_HIP: return "EQL_ERR_HIP: HIP runtime or kernel launch error";
+        case EQL_ERR_NOMEM: return "EQL_ERR_NOMEM: host allocation failed";
+    }
+    return "EQL_ERR_UNKNOWN: unknown status code";
+}
+
+eqlinear_status eqlinear_plan(eqlinear_plan_t* out, int N, int C_in, int C_out,
+                              eqlinear_dtype dt) {
+    if (!out) return EQL_ERR_INVALID;
+    *out = nullptr;
+    if (N < 1 || N > 16 || C_in < 1 || C_out < 1 || !dtype_ok((int)dt)) return EQL_ERR_INVALID;
+    if ((int64_t)N * C_in > kMaxWidth || (int64_t)N * C_out > kMaxWidth) return EQL_ERR_INVALID;
+    eqlinear_plan_s* p = new (std::nothrow) eqlinear_plan_s{EQL_KIND_CN, (int)dt, N, C_in, C_out};
+    if (!p) return EQL_ERR_NOMEM;
+    *out = p;
+    return EQL_OK;
+}
+
+eqlinear_status eqlinear_d8_plan(eqlinear_plan_t* out, int C_in, int C_out, eqlinear_dtype dt) {
+    if (!out) return EQL_ERR_INVALID;
+    *out = nullptr;
+    if (C_in < 8 || C_out < 8 || C_in % 8 || C_out % 8 || !dtype_ok((int)dt))
+        return EQL_ERR_INVALID;
+    if (C_in > kMaxWidth || C_out > kMaxWidth) return EQL_ERR_INVALID;
+    eqlinear_plan_s* p = new (std::nothrow) eqlinear_plan_s{EQL_KIND_D8, (int)dt, 8, C_in, C_out};
+    if (!p) return EQL_ERR_NOMEM;
+    *out = p;
+    return EQL_OK;
+}
+
+eqlinear_status eqlinear_plan_destroy(eqlinear_plan_t plan) {
+    if (!plan) return EQL_ERR_INVALID;
+    delete plan;
+    return EQL_OK;
+}
+
+eqlinear_status eqlinear_plan_info(eqlinear_plan_t p, eqlinear_info* out) {
+    if (!p || !out) return EQL_ERR_INVALID;
+    eqlinear_info in{};
+    in.kind = p->kind;
+    in.dtype = p->dtype;
+    in.N = p->N;
+    in.C_in = p->C_in;
+    in.C_out = p->C_out;
+    const int64_t ci = p->C_in, co = p->C_out;
+    if (p->kind == EQL_KIND_CN) {
+        const int N = p->N;
+        const int complex_bins = (N - 1) / 2;
+        const int real_bins = 1 + (N % 2 == 0 && N > 1 ? 1 : 0);
+        in.bins = N / 2 + 1;
+        in.planes = N;
+        in.has_nyquist = (N % 2 == 0 && N > 1) ? 1 : 0;
+        in.params = (int64_t)N * ci * co;
+        in.w_hat_elems = in.params;
+        in.real_gemms = real_bins + 4 * complex_bins;
+        in.macs_per_token = in.real_gemms * ci * co;
+        in.dense_macs_per_token = (int64_t)N * N * ci * co;
+    } else {
+        const int64_t mi = ci / 8, mo = co / 8;
+        in.bins = 5;
+        in.planes = 0;
+        in.has_nyquist = 0;
+        in.params = 4 * mi * mo + (2 * mi) * (2 * mo);
+        in.w_hat_elems = in.params;
+        in.real_gemms = 0;
+        in.macs_per_token = 4 * mi * mo + 2 * (2 * mi) * (2 * mo);
+        in.dense_macs_per_token = ci * co;
+    }
+    *out = in;
+    return EQL_OK;
+}
+
+size_t eqlinear_w_hat_elems(eqlinear_plan_t p) {
+    if (!p) return 0;
+    eqlinear_info in;
+    if (eqlinear_plan_info(p, &in) != EQL_OK) return 0;
+    return (size_t)in.w_hat_elems;
+}
+
+eqlinear_status eqlinear_weight_fft(eqlinear_plan_t p, const void* w, void* w_hat) {
+    if (!p || !w || !w_hat || p->kind != EQL_KIND_CN) return EQL_ERR_INVALID;
+    if (!aligned16(w) || !aligned16(w_hat)) return EQL_ERR_INVALID;
+    const size_t bytes = eqlinear_w_hat_elems(p) * elem_size(p);
+    if (overlaps(w, bytes, w_hat, bytes)) return EQL_ERR_INVALID;
+    hipError_t e = eql::launch_weight_dft(p->N, p->dtype == EQL_BF16, w, w_hat, p->C_in,
+                                          p->C_out, nullptr);
+    if (e != hipSuccess) return EQL_ERR_HIP;
+    return hip_status(hipStreamSynchronize(nullptr));
+}
+
+eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t p, const void* x, const void* w_hat,
+                                      void* y, int64_t T, void* stream, int tile) {
+    if (!p || p->kind != EQL_KIND_CN) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (T == 0) return EQL_OK;
+    if (!x || !w_hat || !y) return EQL_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(w_hat) || !aligned16(y)) return EQL_ERR_INVALID;
+    const size_t es = elem_size(p);
+    const size_t xb = (size_t)T * in_width(p) * es, yb = (size_t)T * out_width(p) * es;
+    const size_t wb = eqlinear_w_hat_elems(p) * es;
+    if (overlaps(x, xb, y, yb) || overlaps(w_hat, wb, y, yb)) return EQL_ERR_INVALID;
+    if (tile < -1 || tile > 2) return EQL_ERR_INVALID;
+    return hip_status(eql::launch_cn_forward(p->N, p->dtype == EQL_BF16, x, w_hat, y, T, p->C_in,
+                                             p->C_out, (hipStream_t)stream, tile));
+}
+
+eqlinear_status eqlinear_forward(eqlinear_plan_t p, const void* x, const void* w_hat, void* y,
+                                 int64_t T, void* stream) {
+    return eqlinear_forward_tiled(p, x, w_hat, y, T, stream, -1);
+}
+
+eqlinear_status eqlinear_d8_forward(eqlinear_plan_t p, const void* x, const void* wb, void* y,
+                                    int64_t T, void* stream) {
+    if (!p || p->kind != EQL_KIND_D8) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (T == 0) return EQL_OK;
+    if (!x || !wb || !y) return EQL_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(wb) || !aligned16(y)) return EQL_ERR_INVALID;
+    const size_t es = elem_size(p);
+    const size_t xb = (size_t)T * p->C_in * es, yb = (size_t)T * p->C_out * es;
+    const size_t wbb = eqlinear_w_hat_elems(p) * es;
+    if (overlaps(x, xb, y, yb) || overlaps(wb, wbb, y, yb)) return EQL_ERR_INVALID;
+    const int mi = p->C_in / 8, mo = p->C_out / 8;
+    eql::GemmJobs jobs{};
+    jobs.njobs = 6;
+    const int64_t e_off = 4LL * mo * mi;
+    for (int b = 0; b < 4; ++b)  // A1, A2, B1, B2
+        jobs.j[b] = eql::GemmJob{b * mi, b * mo, mi, mo, (int64_t)b * mo * mi, mi, 0, 0, 0, 0};
+    for (int c = 0; c < 2; ++c)  // W_E on E coordinate 0 and 1
+        jobs.j[4 + c] = eql::GemmJob{4 * mi + 2 * c * mi, 4 * mo + 2 * c * mo, 2 * mi, 2 * mo,
+                                     e_off, 2 * mi, 0, 0, 0, 0};
+    return hip_status(eql::launch_gemm_rows(p->dtype == EQL_BF16, jobs, x, wb, y, T, p->C_in,
+                                            p->C_out, (hipStream_t)stream));
+}
+
+eqlinear_status eqlinear_expand_dense(eqlinear_plan_t p, const void* w, void* w_dense,
+                                      void* stream) {
+    if (!p || !w || !w_dense) return EQL_ERR_INVALID;
+    if (!aligned16(w) || !aligned16(w_dense)) return EQL_ERR_INVALID;
+    const size_t es = elem_size(p);
+    const size_t wb = eqlinear_w_hat_elems(p) * es;
+    const size_t db = (size_t)in_width(p) * out_width(p) * es;
+    if (overlaps(w, wb, w_dense, db)) return EQL_ERR_INVALID;
+    hipError_t e;
+    if (p->kind == EQL_KIND_CN)
+        e = eql::launch_cn_expand(p->N, p->dtype == EQL_BF16, w, w_dense, p->C_in, p->C_out,
+                                  (hipStream_t)stream);
+    else
+        e = eql::launch_d8_expand(p->dtype == EQL_BF16, w, w_dense, p->C_in, p->C_out,
+                                  (hipStream_t)stream);
+    return hip_status(e);
+}
+
+eqlinear_status eqlinear_dense_forward(eqlinear_plan_t p, const void* x, const void* w_dense,
+                                       void* y, int64_t T, void* stream) {
+    if (!p) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (T == 0) return EQL_OK;
+    if (!x || !w_dense || !y) return EQL_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(w_dense) || !aligned16(y)) return EQL_ERR_INVALID;
+    const int64_t K = in_width(p), M = out_width(p);
+    const size_t es = elem_size(p);
+    const size_t xb = (size_t)T * K * es, yb = (size_t)T * M * es, db = (size_t)K * M * es;
+    if (overlaps(x, xb, y, yb) || overlaps(w_dense, db, y, yb)) return EQL_ERR_INVALID;
+    eql::GemmJobs jobs{};
+    jobs.njobs = 1;
+    jobs.j[0] = eql::GemmJob{0, 0, (int)K, (int)M, 0, (int)K, 0, 0, 0, 0};
+    return hip_status(eql::launch_gemm_rows(p->dtype == EQL_BF16, jobs, x, w_dense, y, T, (int)K,
+                                            (int)M, (hipStream_t)stream));
+}
+
+}  // extern "C"

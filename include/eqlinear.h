@@ -1,0 +1,165 @@
+/*
+ * eqlinear.h -- C ABI of libeqlinear.so, the MI355X (gfx950) equivariant
+ * linear layers.
+ *
+ * Layers
+ *  - C_N layer ("Flash EQ-Linear", gist.science summary, Core Insight and
+ *    Algorithmic Approach):
+ *        y[t][o][g] = sum_{i < C_in} sum_{h < N} w[o][i][(g-h) mod N] * x[t][i][h]
+ *    computed as a real DFT along the group axis, one channel-mixing product per
+ *    kept frequency (floor(N/2)+1 bins; the DC and, for even N, Nyquist bins are
+ *    real products, every other bin is a complex product done as a real 2x2
+ *    block product), and an inverse DFT, in one fused kernel.
+ *  - D8 Fourier-domain layer ("Quick ViTs", papernotes, key design 2): four
+ *    square (C/8) blocks for the 1-D irreps A1, A2, B1, B2 and one (C/4) block
+ *    shared by both coordinates of the 2-D irrep E.
+ *  - The expanded-dense comparator ("Flash EQ-Linear", Problem Statement):
+ *    the weights replicated into the full group-circulant matrix and a dense
+ *    product.
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or keeps them.  Base pointers must be 16-byte aligned.
+ *  - Element type is the plan dtype: EQL_F32 = IEEE fp32, EQL_BF16 = bfloat16
+ *    (accumulation is always fp32).
+ *  - Layouts are row-major with the last index contiguous:
+ *      x [T][C_in][N], y [T][C_out][N], w [C_out][C_in][N]           (C_N)
+ *      x [T][C_in], y [T][C_out] with features [A1|A2|B1|B2|E0|E1]  (D8)
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls that take a stream are asynchronous on it; they do no host
+ *    synchronisation, no allocation and use no workspace.
+ *  - Every call returns an eqlinear_status; nothing is thrown across the ABI and
+ *    there is no global error state.  Argument checks happen before any HIP
+ *    call, so they can be exercised without a GPU.  A kernel launch failure is
+ *    EQL_ERR_HIP; faults inside an asynchronous kernel surface on the stream.
+ *  - A plan is immutable after creation and may be used from several host
+ *    threads and streams at once.  Using a destroyed plan is undefined.
+ */
+#ifndef EQLINEAR_H
+#define EQLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EQL_OK = 0,
+    EQL_ERR_INVALID = 1,     /* bad argument: NULL, size, alignment, aliasing, kind */
+    EQL_ERR_UNSUPPORTED = 2, /* valid request outside what this build implements */
+    EQL_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+    EQL_ERR_NOMEM = 4        /* host allocation failed */
+} eqlinear_status;
+
+typedef enum { EQL_F32 = 0, EQL_BF16 = 1 } eqlinear_dtype;
+
+typedef enum { EQL_KIND_CN = 0, EQL_KIND_D8 = 1 } eqlinear_kind;
+
+typedef struct eqlinear_plan_s* eqlinear_plan_t;
+
+/* Plan metadata.  Counts follow "Flash EQ-Linear", Algorithmic Approach
+ * (kept half spectrum) and Specialization for p4 (six real products at N=4),
+ * and "Quick ViTs", key design 2 (D8 parameter and multiply counts). */
+typedef struct {
+    int32_t kind;               /* eqlinear_kind */
+    int32_t dtype;              /* eqlinear_dtype */
+    int32_t N;                  /* group order (8 for D8) */
+    int32_t C_in, C_out;        /* C_N: channels per group element; D8: full widths */
+    int32_t bins;               /* C_N: floor(N/2)+1 kept frequencies; D8: 5 irrep blocks */
+    int32_t planes;             /* C_N: real frequency planes (= N) */
+    int32_t has_nyquist;        /* C_N: 1 when N is even */
+    int64_t params;             /* learnable parameters */
+    int64_t w_hat_elems;        /* elements of w_hat (C_N) or of the packed blocks (D8) */
+    int64_t real_gemms;         /* C_N: real T x C_in x C_out products (2N-2 even, 2N-1 odd) */
+    int64_t macs_per_token;     /* multiply-adds per token of the layer's products */
+    int64_t dense_macs_per_token; /* same for the expanded dense matrix */
+} eqlinear_info;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* eqlinear_status_string(eqlinear_status s);
+
+/* Create a C_N plan.  1 <= N <= 16, C_in >= 1, C_out >= 1, dt in {EQL_F32,
+ * EQL_BF16}; otherwise EQL_ERR_INVALID and *out is left NULL.  Host metadata
+ * only: needs no GPU.  Release with eqlinear_plan_destroy. */
+eqlinear_status eqlinear_plan(eqlinear_plan_t* out, int N, int C_in, int C_out,
+                              eqlinear_dtype dt);
+
+/* Create a D8 plan ("Quick ViTs", key design 2).  C_in and C_out are full
+ * widths, multiples of 8 (C/8 channels per 1-D irrep, C/4 copies of E). */
+eqlinear_status eqlinear_d8_plan(eqlinear_plan_t* out, int C_in, int C_out,
+                                 eqlinear_dtype dt);
+
+/* Free a plan.  NULL -> EQL_ERR_INVALID. */
+eqlinear_status eqlinear_plan_destroy(eqlinear_plan_t plan);
+
+/* Fill *out with the plan's metadata. */
+eqlinear_status eqlinear_plan_info(eqlinear_plan_t plan, eqlinear_info* out);
+
+/* Number of elements of w_hat for a C_N plan (N*C_out*C_in), or of the packed
+ * D8 blocks (C_in*C_out/8); 0 for a NULL plan. */
+size_t eqlinear_w_hat_elems(eqlinear_plan_t plan);
+
+/* Weight spectrum, computed once per weight ("Flash EQ-Linear", Algorithmic
+ * Approach: DFT along the group axis, non-redundant half kept; Implementation:
+ * a plug-and-play replacement for layers with trained weights).
+ *   w     [C_out][C_in][N]   plan dtype, device
+ *   w_hat [N][C_out][C_in]   plan dtype, device: N real planes of
+ *         What[k] = sum_m w[m] exp(-2 pi i m k / N), unnormalised:
+ *         plane 0 = Re What[0]; planes 2k-1, 2k = Re, Im What[k] (1 <= k < N/2);
+ *         plane N-1 = Re What[N/2] when N is even.
+ * Computed in fp64 and rounded once to the plan dtype.  Runs on the null
+ * stream and returns after it completes (synchronous); the caller must have
+ * finished writing w.  C_N plans only (EQL_ERR_INVALID for D8). */
+eqlinear_status eqlinear_weight_fft(eqlinear_plan_t plan, const void* w, void* w_hat);
+
+/* C_N forward, fused: per token tile, forward real DFT of x along the group
+ * axis, the per-frequency channel products against w_hat (fp32 accumulation),
+ * and the inverse DFT, writing y once ("Flash EQ-Linear", Algorithmic Approach
+ * and Implementation: fused dataflow with no intermediate global writes).
+ *   x     [T][C_in][N]  device, plan dtype
+ *   w_hat [N][C_out][C_in] device, as written by eqlinear_weight_fft
+ *   y     [T][C_out][N] device, plan dtype; must not overlap x or w_hat
+ *   T >= 0 tokens (T == 0: returns EQL_OK, launches nothing)
+ * bf16 plans round the frequency-domain inputs to bf16 before the matrix
+ * cores and round y once from fp32. */
+eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void* w_hat,
+                                 void* y, int64_t T, void* stream);
+
+/* eqlinear_forward with a fixed tile configuration instead of the automatic
+ * choice, for tuning and tests: tile 0 = 64 tokens x 64 output channels
+ * (64 x 32 for N > 8), 1 = 32 x 32, 2 = 16 x 16; -1 = automatic (same as
+ * eqlinear_forward).  Results are identical up to fp32 summation order. */
+eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t plan, const void* x, const void* w_hat,
+                                       void* y, int64_t T, void* stream, int tile);
+
+/* D8 forward: y_rho = W_rho x_rho for rho in A1, A2, B1, B2 and
+ * y_Ec = W_E x_Ec for both E coordinates c ("Quick ViTs", key design 2).
+ *   x  [T][C_in], y [T][C_out], features laid out [A1|A2|B1|B2|E0|E1] with
+ *      widths (m, m, m, m, 2m, 2m), m = C/8
+ *   wb packed [W_A1 | W_A2 | W_B1 | W_B2 | W_E], each row-major [out][in]:
+ *      1-D blocks (C_out/8 x C_in/8), W_E (C_out/4 x C_in/4) */
+eqlinear_status eqlinear_d8_forward(eqlinear_plan_t plan, const void* x, const void* wb,
+                                    void* y, int64_t T, void* stream);
+
+/* Comparator: expand weights into the dense matrix a replicate-and-multiply
+ * implementation would use ("Flash EQ-Linear", Problem Statement).
+ *   C_N: W_dense [N*C_out][N*C_in] with W_dense[o*N+g][i*N+h] = w[o][i][(g-h) mod N]
+ *        from w [C_out][C_in][N]
+ *   D8:  W_dense [C_out][C_in], block-diagonal, from the packed blocks
+ * Asynchronous on stream.  Plan dtype. */
+eqlinear_status eqlinear_expand_dense(eqlinear_plan_t plan, const void* w, void* w_dense,
+                                      void* stream);
+
+/* Comparator: plain dense product y[t] = W_dense x[t] (F.linear without bias)
+ * on the matrix cores, x [T][K], W_dense [M][K], y [T][M] with K, M the full
+ * input and output widths of the plan. */
+eqlinear_status eqlinear_dense_forward(eqlinear_plan_t plan, const void* x,
+                                       const void* w_dense, void* y, int64_t T, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EQLINEAR_H */

@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, validates arguments before any HIP call, and reports the
+plan counts the pages state.  Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eqlinear.h")
+
+
+@pytest.fixture(scope="module")
+def eq():
+    import group_equivariant_linear_amd as eq
+    from group_equivariant_linear_amd import _build
+    if not eq.built():
+        _build.build()
+    eq.load_library()
+    return eq
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(eqlinear_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_set(eq):
+    assert header_functions() == sorted(eq.ABI_FUNCTIONS)
+
+
+def test_library_exports_every_declared_symbol(eq):
+    lib = ctypes.CDLL(eq.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "eqlinear.h"\nint main(void){eqlinear_info i; (void)i; return 0;}\n')
+    import subprocess
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(tmp_path / "t")], check=True)
+
+
+def test_status_strings(eq):
+    for s in range(5):
+        assert eq.eqlinear_status_string(s).startswith("EQL_")
+    assert "UNKNOWN" in eq.eqlinear_status_string(99)
+
+
+@pytest.mark.parametrize("args", [(0, 4, 4, 0), (17, 4, 4, 0), (4, 0, 4, 0), (4, 4, 0, 0),
+                                  (4, 4, 4, 2), (4, 4, 4, -1), (2, 1 << 20, 2, 0)])
+def test_plan_rejects_invalid(eq, args):
+    with pytest.raises(eq.EqlError) as e:
+        eq.eqlinear_plan(*args)
+    assert e.value.status == eq.EQL_ERR_INVALID
+
+
+@pytest.mark.parametrize("args", [(12, 16, 0), (16, 12, 0), (0, 8, 0), (8, 8, 7)])
+def test_d8_plan_rejects_invalid(eq, args):
+    with pytest.raises(eq.EqlError):
+        eq.eqlinear_d8_plan(*args)
+
+
+def test_null_out_and_null_plan(eq):
+    lib = eq.load_library()
+    assert lib.eqlinear_plan(None, 4, 4, 4, 0) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_plan_destroy(None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_plan_info(None, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_w_hat_elems(None) == 0
+    assert lib.eqlinear_forward(None, 16, 16, 16, 1, None) == eq.EQL_ERR_INVALID
+
+
+@pytest.mark.parametrize("N", range(1, 17))
+def test_plan_info_counts(eq, N):
+    C_in, C_out = 3, 5
+    p = eq.eqlinear_plan(N, C_in, C_out, eq.EQL_F32)
+    inf = p.info
+    assert inf["bins"] == N // 2 + 1 == oracle.cn_kept_bins(N)
+    assert inf["planes"] == N
+    assert inf["has_nyquist"] == (1 if N % 2 == 0 and N > 1 else 0)
+    assert inf["params"] == inf["w_hat_elems"] == oracle.cn_params(N, C_in, C_out)
+    assert inf["real_gemms"] == oracle.cn_real_gemms(N) == (2 * N - 2 if N % 2 == 0 else 2 * N - 1)
+    assert inf["macs_per_token"] == inf["real_gemms"] * C_in * C_out
+    assert inf["dense_macs_per_token"] == N * N * C_in * C_out
+    assert eq.eqlinear_w_hat_elems(p) == N * C_in * C_out
+
+
+def test_page_counts_through_the_abi(eq):
+    # six real products instead of sixteen for the p4 group
+    p = eq.eqlinear_plan(4, 8, 8, eq.EQL_F32).info
+    assert p["real_gemms"] == 6 and p["dense_macs_per_token"] // (8 * 8) == 16
+    # the D8 layer: eight times fewer parameters, 5.33 times fewer multiplies
+    d = eq.eqlinear_d8_plan(1280, 1280, eq.EQL_BF16).info
+    assert d["dense_macs_per_token"] / d["params"] == 8
+    assert abs(d["dense_macs_per_token"] / d["macs_per_token"] - 16 / 3) < 1e-12
+    assert d["params"] == oracle.d8_params(1280, 1280)
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="uses fake device addresses; kept off machines with a GPU")
+def test_forward_validation_before_any_hip_call(eq):
+    lib = eq.load_library()
+    p = eq.eqlinear_plan(8, 32, 32, eq.EQL_F32)
+    h = p.handle
+    A, B, W = 1 << 20, 1 << 30, 1 << 34  # aligned, disjoint fake addresses (never dereferenced)
+    assert lib.eqlinear_forward(h, A, W, B, -1, None) == eq.EQL_ERR_INVALID  # T < 0
+    assert lib.eqlinear_forward(h, None, None, None, 0, None) == eq.EQL_OK    # T == 0: no-op
+    assert lib.eqlinear_forward(h, None, W, B, 5, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_forward(h, A, None, B, 5, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_forward(h, A, W, None, 5, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_forward(h, A + 4, W, B, 5, None) == eq.EQL_ERR_INVALID  # misaligned
+    assert lib.eqlinear_forward(h, A, W, B + 8, 5, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_forward(h, A, W, A, 5, None) == eq.EQL_ERR_INVALID      # y aliases x
+    assert lib.eqlinear_forward(h, A, W, A + 256, 5, None) == eq.EQL_ERR_INVALID  # overlap
+    assert lib.eqlinear_forward(h, A, W, W, 5, None) == eq.EQL_ERR_INVALID      # y aliases w_hat
+    assert lib.eqlinear_forward_tiled(h, A, W, B, 5, None, 3) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_forward_tiled(h, A, W, B, 5, None, -2) == eq.EQL_ERR_INVALID
+    d8 = eq.eqlinear_d8_plan(16, 16, eq.EQL_F32)
+    assert lib.eqlinear_forward(d8.handle, A, W, B, 5, None) == eq.EQL_ERR_INVALID  # wrong kind
+    assert lib.eqlinear_d8_forward(h, A, W, B, 5, None) == eq.EQL_ERR_INVALID       # wrong kind
+    assert lib.eqlinear_weight_fft(d8.handle, A, W) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_weight_fft(h, A, A) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_weight_fft(h, A + 2, W) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_d8_forward(d8.handle, A, W, A, 5, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_d8_forward(d8.handle, A, W, B, -3, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_d8_forward(d8.handle, None, None, None, 0, None) == eq.EQL_OK
+    assert lib.eqlinear_expand_dense(h, A, A, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_expand_dense(h, None, B, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_dense_forward(h, A, W, A, 5, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_dense_forward(h, A, W, B, -1, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_dense_forward(h, None, None, None, 0, None) == eq.EQL_OK
+
+
+def test_binding_checks_tensors_without_gpu(eq):
+    import torch
+    p = eq.eqlinear_plan(4, 2, 2, eq.EQL_F32)
+    x = torch.zeros(3, 2, 4)  # host tensor: rejected before the C call
+    with pytest.raises(ValueError):
+        eq.eqlinear_forward(p, x, x, x)
+
+
+def test_plan_is_freed(eq):
+    p = eq.eqlinear_plan(4, 2, 2, eq.EQL_F32)
+    eq.eqlinear_plan_destroy(p)
+    assert p.handle.value is None or p.handle.value == 0
+    eq.eqlinear_plan_destroy(p)  # second destroy through the binding is a no-op
