@@ -1,0 +1,322 @@
+"""Benchmark of the EQ-Linear forward on one MI355X.
+
+Prints ONE JSON line.  A step is one forward of the layer over one batch of
+synthetic tokens already resident in device memory: for a C_N workload the
+fused eqlinear_forward (group DFT, per-bin matrix-core products, inverse DFT),
+for the D8 workload eqlinear_d8_forward.  The weight spectrum (eqlinear_weight_fft)
+is computed once per weight, before the timed region, and timed on its own.
+
+Beside the step the run times, on the same inputs:
+  - the expanded-dense comparator: the replicated dense matrix multiplied by
+    this library's own MFMA GEMM and by torch's F.linear (hipBLASLt); the
+    faster of the two is the bar ("Flash EQ-Linear", Problem Statement and
+    Experimental Results / Operator Level compare against F.linear);
+  - a cache-cold variant of the step (a 512 MiB write evicts the 256 MiB
+    Infinity Cache before each launch);
+  - the fp64 CPU oracle on the host cores (rank 0, N=1 only, bounded sample).
+
+Default workload: C_8 EQ-Linear, fp32, T=4096, C_in=C_out=32 (c2).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "EQ-Linear fwd tokens/sec + TFLOP/s and % roofline vs expanded-dense GEMM"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+KERNEL_SOURCES = {
+    "C": ["group_equivariant_linear_amd/csrc/cn_fused.h",
+          "group_equivariant_linear_amd/csrc/eq_device.h"],
+    "D8": ["group_equivariant_linear_amd/csrc/gemm_rows.hip",
+           "group_equivariant_linear_amd/csrc/eq_device.h"],
+}
+
+
+def kernel_source_hash(group):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[group]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="c2",
+                    help="c1, c2, c3a, c3b, c3c, c3 (the three MLP layers), c4, c5")
+    ap.add_argument("--cold-steps", type=int, default=100)
+    ap.add_argument("--tile", type=int, default=-1,
+                    help="fixed tile configuration of the C_N kernel (eqlinear_forward_tiled); -1 = automatic")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle sample (0 disables)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "traffic"],
+                    help="traffic: a few forwards and a copy of known size, for rocprofv3 --pmc")
+    return ap.parse_args()
+
+
+class Layer:
+    """One layer of a workload: device buffers, plan, and the step callables."""
+
+    def __init__(self, eq, wl, seed=0, tile=-1):
+        import numpy as np
+        import torch
+
+        import synthetic
+        self.wl = wl
+        self.dt = wl.dtype
+        self.tdt = torch.float32 if wl.dtype == synthetic.F32 else torch.bfloat16
+        eqdt = eq.EQL_F32 if wl.dtype == synthetic.F32 else eq.EQL_BF16
+        d = synthetic.workload_inputs(wl, seed=seed)
+        self.inputs = d
+
+        def dev(a):
+            if wl.dtype == synthetic.F32:
+                return torch.from_numpy(a).cuda()
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+        self.x = dev(d["x"]).reshape(wl.T, -1)
+        w = dev(d["w"])
+        if wl.group == "C":
+            self.plan = eq.eqlinear_plan(wl.N, wl.C_in, wl.C_out, eqdt)
+            self.w_hat = torch.empty(eq.eqlinear_w_hat_elems(self.plan), dtype=self.tdt, device="cuda")
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            eq.eqlinear_weight_fft(self.plan, w, self.w_hat)
+            self.weight_fft_ms = (time.perf_counter() - t0) * 1e3
+            self.K, self.M = wl.N * wl.C_in, wl.N * wl.C_out
+            if tile < 0:
+                self.step = lambda: eq.eqlinear_forward(self.plan, self.x, self.w_hat, self.y, T=wl.T)
+            else:
+                self.step = lambda: eq.eqlinear_forward_tiled(self.plan, self.x, self.w_hat, self.y, tile, T=wl.T)
+        else:
+            self.plan = eq.eqlinear_d8_plan(wl.C_in, wl.C_out, eqdt)
+            self.w_hat = w
+            self.weight_fft_ms = None
+            self.K, self.M = wl.C_in, wl.C_out
+            self.step = lambda: eq.eqlinear_d8_forward(self.plan, self.x, self.w_hat, self.y, T=wl.T)
+        self.y = torch.empty(wl.T, self.M, dtype=self.tdt, device="cuda")
+        self.w = w
+        info = self.plan.info
+        self.macs_per_token = info["macs_per_token"]
+        self.dense_macs_per_token = info["dense_macs_per_token"]
+        es = 4 if wl.dtype == synthetic.F32 else 2
+        self.bytes_per_token = (self.K + self.M) * es
+        self.w_hat_bytes = info["w_hat_elems"] * es
+        self.bytes_per_launch = wl.T * self.bytes_per_token + self.w_hat_bytes
+
+        # comparator: replicated dense matrix, own MFMA GEMM and torch F.linear
+        self.W_dense = torch.empty(self.M, self.K, dtype=self.tdt, device="cuda")
+        t0 = time.perf_counter()
+        eq.eqlinear_expand_dense(self.plan, w, self.W_dense)
+        torch.cuda.synchronize()
+        self.expand_ms = (time.perf_counter() - t0) * 1e3
+        self.y_dense = torch.empty_like(self.y)
+        self.dense_own = lambda: eq.eqlinear_dense_forward(self.plan, self.x, self.W_dense, self.y_dense, T=wl.T)
+        self.dense_torch = lambda: torch.nn.functional.linear(self.x, self.W_dense)
+
+
+def time_loop(fns, steps, warmup):
+    """Average ms per step of running every fn once per step, by events on the
+    current stream (where the library launches)."""
+    import torch
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        for f in fns:
+            f()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def time_cold(fns, steps):
+    """Median ms of one step launched right after a 512 MiB write (cache-cold)."""
+    import torch
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for _ in range(steps):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for f in fns:
+            f()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del flush
+    times.sort()
+    return times[len(times) // 2]
+
+
+def cpu_baseline(layers, target_s):
+    """The fp64 oracle (replicate-and-multiply) on the host cores, on a bounded
+    sample: passes over the first n tokens of the batch, n sized so that a pass
+    takes at most about target_s, repeated until target_s has elapsed."""
+    import oracle  # CPU-baseline leg only
+    per_token = 0.0
+    for L in layers:
+        p = min(L.wl.T, 64)
+        ts = time.perf_counter()
+        _run_oracle(L.wl, L.inputs, p)
+        per_token += (time.perf_counter() - ts) / p
+    n = max(1, min(layers[0].wl.T, int(target_s / max(per_token, 1e-12))))
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for L in layers:
+            _run_oracle(L.wl, L.inputs, n)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    names = "+".join(L.wl.name for L in layers)
+    return {"value": passes * n / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{names}: {passes} pass(es) over the first {n} of {layers[0].wl.T} tokens, "
+                      f"fp64 replicate-and-multiply, {el:.1f} s"}
+
+
+def _run_oracle(wl, d, n):
+    import oracle
+    if wl.group == "C":
+        oracle.cn_dense(d["x64"][:n], d["w64"])
+    else:
+        oracle.d8_dense(d["x64"][:n], d["w64"], wl.C_out)
+
+
+def load_traffic(workload, group):
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_hash(group):
+        return None  # the kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(tokens shard across GPUs with no exchange; see the sharding notes). "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import group_equivariant_linear_amd as eq
+    import synthetic
+    if not eq.built():
+        from group_equivariant_linear_amd import _build
+        _build.build()
+    eq.load_library()
+    torch.cuda.set_device(0)
+
+    names = ["c3a", "c3b", "c3c"] if args.workload == "c3" else [args.workload]
+    wls = [synthetic.WORKLOADS[n] for n in names]
+    layers = [Layer(eq, wl, tile=args.tile) for wl in wls]
+    torch.cuda.synchronize()
+
+    if args.mode == "traffic":
+        # a few forwards, then a plain copy of known size (calibrates the counters)
+        for _ in range(5):
+            for L in layers:
+                L.step()
+        n = 256 * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "workload": args.workload}))
+        return
+
+    steps = [L.step for L in layers]
+    ms = time_loop(steps, args.steps, args.warmup)
+    ms_cold = time_cold(steps, args.cold_steps) if args.cold_steps > 0 else None
+    ms_own = time_loop([L.dense_own for L in layers], max(args.steps // 4, 10), max(args.warmup // 4, 5))
+    ms_lin = time_loop([L.dense_torch for L in layers], max(args.steps // 4, 10), max(args.warmup // 4, 5))
+    # agreement of the fused path with the dense comparator on this very batch
+    for L in layers:
+        L.step()
+        L.dense_own()
+    torch.cuda.synchronize()
+    agree = max(float(torch.linalg.vector_norm((L.y.float() - L.y_dense.float())) /
+                      torch.linalg.vector_norm(L.y_dense.float())) for L in layers)
+
+    tokens = wls[0].T
+    flops = sum(2 * L.macs_per_token * L.wl.T for L in layers)
+    dense_flops = sum(2 * L.dense_macs_per_token * L.wl.T for L in layers)
+    bytes_launch = sum(L.bytes_per_launch for L in layers)
+    dt = wls[0].dtype
+    achieved = bytes_launch / (ms * 1e-3) / 1e9
+    best_dense = min(ms_own, ms_lin)
+    group = wls[0].group
+
+    traffic = load_traffic(args.workload, group)
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {
+            "workload": "; ".join(f"{wl.name}: {wl.note}, {'C' if wl.group == 'C' else ''}"
+                                  f"{wl.N if wl.group == 'C' else 'D8'} T={wl.T} "
+                                  f"C_in={wl.C_in} C_out={wl.C_out} {wl.dtype}" for wl in wls),
+            "tokens_per_step": tokens,
+            "layers_per_step": len(layers),
+            "tile": args.tile,
+        },
+        "tflops_actual": flops / (ms * 1e-3) / 1e12,
+        "tflops_dense_equiv": dense_flops / (ms * 1e-3) / 1e12,
+        "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[dt],
+        "cold": {"ms_per_step": ms_cold,
+                 "gbs": bytes_launch / (ms_cold * 1e-3) / 1e9 if ms_cold else None,
+                 "frac_hbm": bytes_launch / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS if ms_cold else None},
+        "expanded_dense": {"ms_own_mfma": ms_own, "ms_torch_linear": ms_lin, "ms_best": best_dense,
+                           "speedup_vs_best": best_dense / ms, "expand_ms_once": sum(L.expand_ms for L in layers),
+                           "agreement_rel_l2": agree},
+        "weight_fft_ms_once": [L.weight_fft_ms for L in layers],
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "cn_forward_kernel" if group == "C" else "gemm_rows_kernel",
+            "bytes_per_launch": bytes_launch,
+            "kernel_source_sha": kernel_source_hash(group),
+        },
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,20 +1,20 @@
 // cn_forward.hip -- dispatch of the fused C_N forward over group order and dtype.
-// The kernel instantiations live in cn_fwd_{f32,bf16}_{lo,hi}.hip so they build
-// in parallel.
+// The kernel (cn_fused.h) is instantiated in cn_fused_{f32,bf16}_nXX.hip so the
+// instantiations build in parallel.
 #include "eq_launch.h"
 
 namespace eql {
 
 template <int N, typename IO>
-hipError_t launch_n(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
-                    hipStream_t stream, int tile_override);
+hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
+                        hipStream_t stream, int tile);
 
 template <typename IO>
 static hipError_t launch_dt(int N, const void* x, const void* w_hat, void* y, int64_t T,
                             int C_in, int C_out, hipStream_t stream, int tile) {
     switch (N) {
 #define EQL_CASE(n) \
-    case n: return launch_n<n, IO>(x, w_hat, y, T, C_in, C_out, stream, tile);
+    case n: return launch_fused<n, IO>(x, w_hat, y, T, C_in, C_out, stream, tile);
         EQL_CASE(1) EQL_CASE(2) EQL_CASE(3) EQL_CASE(4) EQL_CASE(5) EQL_CASE(6) EQL_CASE(7)
         EQL_CASE(8) EQL_CASE(9) EQL_CASE(10) EQL_CASE(11) EQL_CASE(12) EQL_CASE(13)
         EQL_CASE(14) EQL_CASE(15) EQL_CASE(16)

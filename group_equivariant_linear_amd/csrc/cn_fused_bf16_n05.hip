@@ -1,0 +1,15 @@
+// cn_fused_bf16_n5.hip -- fused C_N forward instantiations, bf16, N = 5..8.
+#include "cn_fused.h"
+
+namespace eql {
+
+template hipError_t launch_fused<5, __bf16>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<6, __bf16>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<7, __bf16>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<8, __bf16>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+
+}  // namespace eql

@@ -1,0 +1,15 @@
+// cn_fused_f32_n1.hip -- fused C_N forward instantiations, f32, N = 1..4.
+#include "cn_fused.h"
+
+namespace eql {
+
+template hipError_t launch_fused<1, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<2, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<3, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<4, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+
+}  // namespace eql

@@ -1,0 +1,15 @@
+// cn_fused_f32_n5.hip -- fused C_N forward instantiations, f32, N = 5..8.
+#include "cn_fused.h"
+
+namespace eql {
+
+template hipError_t launch_fused<5, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<6, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<7, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<8, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+
+}  // namespace eql

@@ -1,0 +1,15 @@
+// cn_fused_f32_n13.hip -- fused C_N forward instantiations, f32, N = 13..16.
+#include "cn_fused.h"
+
+namespace eql {
+
+template hipError_t launch_fused<13, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<14, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<15, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+template hipError_t launch_fused<16, float>(const void*, const void*, void*, int64_t, int, int,
+                                            hipStream_t, int);
+
+}  // namespace eql

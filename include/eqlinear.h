@@ -128,9 +128,11 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
                                  void* y, int64_t T, void* stream);
 
 /* eqlinear_forward with a fixed tile configuration instead of the automatic
- * choice, for tuning and tests: tile 0 = 64 tokens x 64 output channels
- * (64 x 32 for N > 8), 1 = 32 x 32, 2 = 16 x 16; -1 = automatic (same as
- * eqlinear_forward).  Results are identical up to fp32 summation order. */
+ * choice, for tuning and tests.  A workgroup covers 16*W tokens and 16*B output
+ * channels (B is capped so that 4*N*B <= 192 accumulators per lane):
+ *   tile 0: W=4 B=6   1: W=4 B=5   2: W=4 B=4   3: W=4 B=3   4: W=4 B=2
+ *   tile 5: W=1 B=2   6: W=1 B=1   -1: automatic (same as eqlinear_forward).
+ * Results agree to fp32 rounding; other values -> EQL_ERR_INVALID. */
 eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                        void* y, int64_t T, void* stream, int tile);
 

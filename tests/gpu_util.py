@@ -69,11 +69,3 @@ def assert_close(y, ref, dt, what=""):
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
     assert r <= bar and m <= mbar, f"{what}: rel-L2 {r:.3e} (bar {bar:g}), max/rms {m:.3e} (bar {mbar:g})"
     return r, m
-
-
-def f64_to_bf16_rne(a):
-    """Correctly rounded fp64 -> bf16 (8 significant bits, ties to even), as fp64."""
-    a = np.asarray(a, dtype=np.float64)
-    _, e = np.frexp(a)  # a = m * 2**e with 0.5 <= |m| < 1, exact
-    ulp = np.ldexp(1.0, e - 8)
-    return np.rint(a / ulp) * ulp

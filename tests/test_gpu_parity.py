@@ -12,8 +12,7 @@ import pytest
 
 import oracle
 import synthetic
-from gpu_util import (Guarded, assert_close, f64_to_bf16_rne, rel_l2, to_dev, to_f64,
-                      torch_dtype)
+from gpu_util import Guarded, assert_close, rel_l2, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -67,11 +66,15 @@ def test_weight_fft_matches_oracle(eq, N, dt):
     wh.check_guards()
     got = to_f64(wh.t).reshape(N, C_out, C_in)
     ref = oracle.cn_weight_dft(d["w64"])
-    # computed in fp64 and rounded once: equal to the correctly rounded oracle
-    # value except where the exact value sits within fp64 noise of a tie
-    want = ref.astype(np.float32).astype(np.float64) if dt == F32 else f64_to_bf16_rne(ref)
-    mismatch = np.mean(got != want)
-    assert mismatch <= 0.01, f"{mismatch:.3%} of planes not correctly rounded"
+    # computed in fp64 with exact special twiddles and rounded once: the GPU
+    # value is a correctly rounded neighbour of the exact DFT, which the oracle
+    # gives up to fp64 noise (libm's cos(pi/2) is 6e-17, not 0, so exact ties
+    # of sums of fp32 values may fall either way in the oracle).
+    bits = 24 if dt == F32 else 8
+    _, e = np.frexp(ref)
+    half_ulp = np.ldexp(0.5, e - bits)
+    noise = 1e-13 * np.abs(d["w64"]).max()
+    assert np.all(np.abs(got - ref) <= half_ulp * (1 + 1e-9) + noise)
     assert rel_l2(got, ref) <= (1e-6 if dt == F32 else 4e-3)
 
 
@@ -86,7 +89,7 @@ def test_forward_sweep(eq, N, dt):
     for (C_in, C_out, T) in SHAPES:
         d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=N * 100 + C_in)
         ref = oracle.cn_dense(d["x64"], d["w64"])
-        for tile in (-1, 0, 1, 2):
+        for tile in (-1, 0, 1, 2, 3, 4, 5, 6):
             y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
             assert_close(y, ref, dt, f"N={N} {dt} C_in={C_in} C_out={C_out} T={T} tile={tile}")
 
@@ -99,7 +102,7 @@ def test_forward_sweep(eq, N, dt):
 def test_forward_multi_tile_shapes(eq, N, C_in, C_out, T, dt):
     d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=7)
     ref = oracle.cn_dense(d["x64"], d["w64"])
-    for tile in (-1, 0, 1, 2):
+    for tile in (-1, 0, 1, 2, 3, 4, 5, 6):
         y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
         assert_close(y, ref, dt, f"N={N} {dt} {C_in}->{C_out} T={T} tile={tile}")
 
