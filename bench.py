@@ -121,7 +121,9 @@ class Layer:
         self.expand_ms = (time.perf_counter() - t0) * 1e3
         self.y_dense = torch.empty_like(self.y)
         self.dense_own = lambda: eq.eqlinear_dense_forward(self.plan, self.x, self.W_dense, self.y_dense, T=wl.T)
-        self.dense_torch = lambda: torch.nn.functional.linear(self.x, self.W_dense)
+        self.y_lin = torch.empty_like(self.y)
+        # F.linear(x, W) without a bias is x @ W^T: the same GEMM, written into a fixed buffer
+        self.dense_torch = lambda: torch.mm(self.x, self.W_dense.t(), out=self.y_lin)
 
 
 def time_loop(fns, steps, warmup):
@@ -140,6 +142,44 @@ def time_loop(fns, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def time_graph(fns, outs, steps, warmup, per_graph=50):
+    """Average ms per step with the steps captured into a HIP graph (per_graph
+    steps per graph, replayed until `steps` steps ran), or None if a replay does
+    not reproduce the eager outputs bit for bit (then the path stays eager).
+    Launch-bound steps are measured this way because host-side launch cost is
+    not part of the layer."""
+    import torch
+    for _ in range(max(warmup, 3)):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            for f in fns:
+                f()
+    for _ in range(3):  # replays with eager work in between, each checked
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(o, r) for o, r in zip(outs, ref)):
+            return None
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+    reps = max(1, steps // per_graph)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * per_graph)
 
 
 def time_cold(fns, steps):
@@ -246,10 +286,17 @@ def main():
         return
 
     steps = [L.step for L in layers]
-    ms = time_loop(steps, args.steps, args.warmup)
+    ms_eager = time_loop(steps, args.steps, args.warmup)
+    ms_graph = time_graph(steps, [L.y for L in layers], args.steps, args.warmup)
+    ms = ms_graph if ms_graph is not None else ms_eager
     ms_cold = time_cold(steps, args.cold_steps) if args.cold_steps > 0 else None
-    ms_own = time_loop([L.dense_own for L in layers], max(args.steps // 4, 10), max(args.warmup // 4, 5))
-    ms_lin = time_loop([L.dense_torch for L in layers], max(args.steps // 4, 10), max(args.warmup // 4, 5))
+    dsteps, dwarm = max(args.steps // 4, 50), max(args.warmup // 4, 5)
+    ms_own_eager = time_loop([L.dense_own for L in layers], dsteps, dwarm)
+    ms_own_graph = time_graph([L.dense_own for L in layers], [L.y_dense for L in layers], dsteps, dwarm)
+    ms_lin_eager = time_loop([L.dense_torch for L in layers], dsteps, dwarm)
+    ms_lin_graph = time_graph([L.dense_torch for L in layers], [L.y_lin for L in layers], dsteps, dwarm)
+    ms_own = min(t for t in (ms_own_eager, ms_own_graph) if t is not None)
+    ms_lin = min(t for t in (ms_lin_eager, ms_lin_graph) if t is not None)
     # agreement of the fused path with the dense comparator on this very batch
     for L in layers:
         L.step()
@@ -295,7 +342,11 @@ def main():
         "cold": {"ms_per_step": ms_cold,
                  "gbs": bytes_launch / (ms_cold * 1e-3) / 1e9 if ms_cold else None,
                  "frac_hbm": bytes_launch / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS if ms_cold else None},
+        "timing": {"ms_eager": ms_eager, "ms_graph": ms_graph,
+                   "method": "graph" if ms_graph is not None else "eager"},
         "expanded_dense": {"ms_own_mfma": ms_own, "ms_torch_linear": ms_lin, "ms_best": best_dense,
+                           "ms_own_eager": ms_own_eager, "ms_own_graph": ms_own_graph,
+                           "ms_torch_eager": ms_lin_eager, "ms_torch_graph": ms_lin_graph,
                            "speedup_vs_best": best_dense / ms, "expand_ms_once": sum(L.expand_ms for L in layers),
                            "agreement_rel_l2": agree},
         "weight_fft_ms_once": [L.weight_fft_ms for L in layers],
@@ -306,7 +357,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "cn_forward_kernel" if group == "C" else "gemm_rows_kernel",
+            "kernel": "cn_fast_kernel" if group == "C" else "gemm_rows_kernel",
             "bytes_per_launch": bytes_launch,
             "kernel_source_sha": kernel_source_hash(group),
         },

@@ -205,6 +205,68 @@ __device__ __forceinline__ void rdft_inverse(const float (&P)[N], float (&y)[N])
     });
 }
 
+// Minimal-operation forms for the orders the workloads use most (same
+// results as the generic forms up to fp32 rounding order).
+//   N = 8: 20 adds/FMAs forward, 25 inverse (radix-2 split of the symmetric
+//          form; c = cos(pi/4)).
+//   N = 4: 6 adds forward, 7 inverse -- every coefficient is 0, +-1 or a power
+//          of two ("Flash EQ-Linear", Specialization for p4 Rotation Group).
+template <>
+__device__ __forceinline__ void rdft_forward<8>(const float (&x)[8], float (&P)[8]) {
+    constexpr float c = Tw<8>::fwd.cs[1];
+    const float a0 = x[0] + x[4], a1 = x[0] - x[4];
+    const float s1 = x[1] + x[7], d1 = x[1] - x[7];
+    const float s2 = x[2] + x[6], d2 = x[2] - x[6];
+    const float s3 = x[3] + x[5], d3 = x[3] - x[5];
+    const float b0 = a0 + s2, c0 = s1 + s3, c1 = s1 - s3, e = d1 + d3;
+    P[0] = b0 + c0;                          // Re X0
+    P[7] = b0 - c0;                          // Re X4 (Nyquist)
+    P[1] = __builtin_fmaf(c, c1, a1);        // Re X1
+    P[5] = __builtin_fmaf(-c, c1, a1);       // Re X3
+    P[2] = __builtin_fmaf(-c, e, -d2);       // Im X1
+    P[6] = __builtin_fmaf(-c, e, d2);        // Im X3
+    P[3] = a0 - s2;                          // Re X2
+    P[4] = d3 - d1;                          // Im X2
+}
+
+template <>
+__device__ __forceinline__ void rdft_inverse<8>(const float (&P)[8], float (&y)[8]) {
+    constexpr float c = Tw<8>::fwd.cs[1];
+    const float R1 = P[1], I1 = P[2], R2 = P[3], I2 = P[4], R3 = P[5], I3 = P[6];
+    const float t = P[0] * 0.125f;
+    const float u0 = __builtin_fmaf(P[7], 0.125f, t), u1 = __builtin_fmaf(P[7], -0.125f, t);
+    const float p = R1 - R3, m = R1 + R3, n = I1 + I3, k2 = I1 - I3;
+    y[0] = __builtin_fmaf(m + R2, 0.25f, u0);
+    y[4] = __builtin_fmaf(R2 - m, 0.25f, u0);
+    y[2] = __builtin_fmaf(R2 + k2, -0.25f, u0);
+    y[6] = __builtin_fmaf(k2 - R2, 0.25f, u0);
+    const float pm = p - n, pp = p + n;
+    y[1] = __builtin_fmaf(__builtin_fmaf(c, pm, -I2), 0.25f, u1);
+    y[7] = __builtin_fmaf(__builtin_fmaf(c, pp, I2), 0.25f, u1);
+    y[3] = __builtin_fmaf(__builtin_fmaf(-c, pp, I2), 0.25f, u1);
+    y[5] = __builtin_fmaf(__builtin_fmaf(-c, pm, -I2), 0.25f, u1);
+}
+
+template <>
+__device__ __forceinline__ void rdft_forward<4>(const float (&x)[4], float (&P)[4]) {
+    const float a0 = x[0] + x[2];
+    const float s1 = x[1] + x[3];
+    P[0] = a0 + s1;       // Re X0
+    P[3] = a0 - s1;       // Re X2 (Nyquist)
+    P[1] = x[0] - x[2];   // Re X1
+    P[2] = x[3] - x[1];   // Im X1
+}
+
+template <>
+__device__ __forceinline__ void rdft_inverse<4>(const float (&P)[4], float (&y)[4]) {
+    const float t = P[0] * 0.25f;
+    const float u0 = __builtin_fmaf(P[3], 0.25f, t), u1 = __builtin_fmaf(P[3], -0.25f, t);
+    y[0] = __builtin_fmaf(P[1], 0.5f, u0);
+    y[2] = __builtin_fmaf(P[1], -0.5f, u0);
+    y[1] = __builtin_fmaf(P[2], -0.5f, u1);
+    y[3] = __builtin_fmaf(P[2], 0.5f, u1);
+}
+
 // ---------------------------------------------------------------------------
 // bf16 helpers.
 
@@ -212,11 +274,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16, two values packed in one dword.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16, two values packed in one dword
+// (a single v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    uint16_t ua = __builtin_bit_cast(uint16_t, a), ub = __builtin_bit_cast(uint16_t, b);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // ---------------------------------------------------------------------------
