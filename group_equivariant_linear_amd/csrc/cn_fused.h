@@ -62,34 +62,6 @@ struct FusedCfg {
     static constexpr int DMA_ITERS = (SLOTS + kThreads - 1) / kThreads;
 };
 
-// Fast-path shape: WAVES token slabs of 16 tokens, CB output blocks of 16
-// channels, and KS waves per slab that split the input channels (wave group kw
-// takes chunks kw, kw+KS, ...; their accumulators are summed through LDS).
-template <int N_, typename IO_, int WAVES_, int CB_, int KS_, int PD_ = 1>
-struct FastCfg : FusedCfg<N_, IO_, WAVES_, CB_> {
-    using Base = FusedCfg<N_, IO_, WAVES_, CB_>;
-    static constexpr int KS = KS_;
-    static constexpr int PD = PD_;             // chunks in flight ahead of the one being multiplied
-    static constexpr int NBUF = PD_ + 1;       // w_hat tile buffers per K group
-    static constexpr int kThreads = 64 * WAVES_ * KS_;
-    static constexpr int DMA_ITERS = (Base::SLOTS + 64 * WAVES_ - 1) / (64 * WAVES_);
-    // every wave issues exactly DMA_ITERS tile loads per chunk (the counted wait
-    // relies on it): the buffer is padded to a whole number of wave loads
-    static constexpr int BUF_BYTES = DMA_ITERS * WAVES_ * 64 * 16;
-    static constexpr int LDS_BYTES = NBUF * KS_ * BUF_BYTES;
-    // the K-group reduction reuses the tile buffers: (KS-1)*WAVES*64 lanes*N*CB*16 B
-    static_assert((KS_ - 1) * WAVES_ * 64 * N_ * CB_ * 16 <= LDS_BYTES, "reduction does not fit");
-    static_assert(PD_ == 1 || PD_ == 2, "prefetch depth");
-};
-
-// s_waitcnt vmcnt(K) leaving the other counters alone (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
-template <int K>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(K >= 0 && K < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((K & 15) | (7 << 4) | (15 << 8) | ((K >> 4) << 14));
-}
-
 // 16-byte slot of (row o, part q) inside one plane of a w_hat chunk.
 __device__ __forceinline__ int wslot(int o, int q) { return o * 4 + (q ^ ((o >> 1) & 3)); }
 
@@ -383,15 +355,22 @@ __global__ __launch_bounds__(C::kThreads) void cn_fused_kernel(
     store_y<C>(acc, y, T, C_out, tw0, o0);
 }
 
-// --- fast path: buffer-resource loads and stores -------------------------------
+// --- fast path: buffer-resource traffic, coalesced through LDS -----------------
 //
 // Used when C_in is a multiple of R (every x record group and every w_hat row
 // chunk is a whole, 16-byte aligned vector).  All global traffic goes through
-// buffer resources: one SGPR base per tensor and a 32-bit VGPR offset per lane.
-// Offsets past the resource's extent read as zero and drop writes, which covers
-// the token tail, rows past C_out and the input-channel tail without branches.
-// Every lane issues the same loads in every chunk; the next chunk's x lands in
-// the registers of the current one as soon as they are transformed.
+// buffer resources: one SGPR base per tensor and a 32-bit VGPR offset per lane,
+// with the chunk advance in the SGPR offset.  Offsets past the resource's extent
+// read as zero and drop writes, which covers the token tail, rows past C_out and
+// the input-channel tail without branches; every lane issues the same loads.
+//
+// x reaches the MFMA A layout in two moves: a coalesced load (each wave
+// instruction reads whole 16-byte pieces of consecutive token rows) and an
+// exchange through a per-wave LDS region, read back as each lane's records.
+// y leaves the same way: the tile is staged in LDS by (token, channel) record and
+// written as contiguous 16-byte pieces.  Both LDS layouts are conflict-free: row
+// pitches that are multiples of 8 pieces rotate each row by its index, other
+// pitches are made odd.
 
 constexpr uint32_t kOOB = 0x80000000u;  // offset past every resource (extents < 2^31)
 
@@ -400,18 +379,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// off: per-lane offset (kOOB for no data); soff: wave-uniform chunk offset.
-template <class C>
-__device__ __forceinline__ void fast_load_x(__amdgpu_buffer_rsrc_t rx, uint32_t off, uint32_t soff,
-                                            uint32_t (&xr)[C::XW]) {
-#pragma unroll
-    for (int j = 0; j < C::N; ++j) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16u * j, soff, 0);
-        xr[4 * j + 0] = v.x;
-        xr[4 * j + 1] = v.y;
-        xr[4 * j + 2] = v.z;
-        xr[4 * j + 3] = v.w;
-    }
+template <int N_, typename IO_, int WAVES_, int CB_>
+struct FastCfg : FusedCfg<N_, IO_, WAVES_, CB_> {
+    using Base = FusedCfg<N_, IO_, WAVES_, CB_>;
+    static constexpr int kThreads = 64 * WAVES_;
+    static constexpr int DMA_ITERS = (Base::SLOTS + kThreads - 1) / kThreads;
+    // w_hat tile buffer, padded so every wave issues exactly DMA_ITERS loads
+    static constexpr int BUF_BYTES = DMA_ITERS * kThreads * 16;
+    // x exchange: 16 token rows x XP pieces (one chunk of one wave)
+    static constexpr int XP = 4 * N_;  // KC * N * sizeof / 16
+    static constexpr bool XROT = (XP % 8) == 0;
+    static constexpr int XPITCH = XROT ? XP : (XP | 1);
+    static constexpr int XEX_BYTES = 16 * XPITCH * 16;
+    static constexpr int W_REGION = 2 * BUF_BYTES;
+    static constexpr int X_REGION = WAVES_ * XEX_BYTES;
+    // y staging: 16 token rows x YP pieces per wave, after the main loop
+    static constexpr int YROW = Base::CT * N_ * Base::S;  // bytes of one token row of the tile
+    static constexpr int YP = YROW / 16;
+    static constexpr bool YROT = (YP % 8) == 0;
+    static constexpr int YPITCH = YROT ? YP : (YP | 1);
+    static constexpr int YST_BYTES = 16 * YPITCH * 16;
+    static constexpr int MAIN_BYTES = W_REGION + X_REGION;
+    static constexpr int LDS_BYTES =
+        MAIN_BYTES > WAVES_ * YST_BYTES ? MAIN_BYTES : WAVES_ * YST_BYTES;
+    static_assert(YROW % 16 == 0, "tile rows are whole pieces");
+};
+
+// LDS piece index of piece k of row r in a region with pitch P and X pieces per row.
+template <bool ROT, int X, int P>
+__device__ __forceinline__ int xpiece(int r, int k) {
+    if constexpr (ROT) return r * P + ((k + r) % X);
+    else return r * P + k;
 }
 
 // slot s of a w_hat chunk -> plane p, row o, channel part q (inverse of wslot)
@@ -423,15 +421,14 @@ __device__ __forceinline__ void slot_coords(int s, int& p, int& o, int& q) {
     q = (sp & 3) ^ ((o >> 1) & 3);
 }
 
-// The WAVES waves of one K group load one chunk together; tw = wave within the group.
 template <class C>
 __device__ __forceinline__ void fast_dma_w(__amdgpu_buffer_rsrc_t rw, const uint32_t (&woff)[C::DMA_ITERS],
-                                           uint32_t chunk_off, bool tail, int k0, int C_in, int tw,
+                                           uint32_t chunk_off, bool tail, int k0, int C_in,
                                            char* lds_buf) {
-    const int lane = (int)threadIdx.x & 63;
+    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
 #pragma unroll
     for (int it = 0; it < C::DMA_ITERS; ++it) {
-        const int base = (it * C::WAVES + tw) * 64;  // slots past SLOTS land in the padding
+        const int base = (it * C::WAVES + wave) * 64;  // slots past SLOTS land in the padding
         uint32_t off = woff[it];
         if (tail) {
             int p, o, q;
@@ -477,76 +474,19 @@ __device__ __forceinline__ void fast_products(const typename AFrag<typename C::I
 }
 
 template <class C>
-__device__ __forceinline__ void fast_store_y(const f32x4 (&acc)[C::N][C::CB], __amdgpu_buffer_rsrc_t ry,
-                                             uint32_t row_y, int C_out, int o0, int wave) {
-    using IO = typename C::IO;
-    constexpr int N = C::N;
-    const int lane = (int)threadIdx.x & 63;
-#pragma unroll
-    for (int b = 0; b < C::CB; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t tl = (uint32_t)(wave * 16 + (lane >> 4) * 4 + r);
-            const int o = o0 + b * 16 + (lane & 15);
-            const uint32_t off = o < C_out ? tl * row_y + (uint32_t)o * (N * C::S) : kOOB;
-            float P[N], yv[N];
-#pragma unroll
-            for (int p = 0; p < N; ++p) P[p] = acc[p][b][r];
-            rdft_inverse<N>(P, yv);
-            if constexpr (sizeof(IO) == 4) {
-                if constexpr (N % 4 == 0) {
-#pragma unroll
-                    for (int j = 0; j < N / 4; ++j) {
-                        const u32x4 v = {__float_as_uint(yv[4 * j]), __float_as_uint(yv[4 * j + 1]),
-                                         __float_as_uint(yv[4 * j + 2]), __float_as_uint(yv[4 * j + 3])};
-                        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off + 16u * j, 0, 0);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < N; ++j)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[j]), ry, off + 4u * j, 0, 0);
-                }
-            } else {
-                if constexpr (N % 8 == 0) {
-#pragma unroll
-                    for (int j = 0; j < N / 8; ++j) {
-                        const u32x4 v = {pack_bf16x2(yv[8 * j], yv[8 * j + 1]), pack_bf16x2(yv[8 * j + 2], yv[8 * j + 3]),
-                                         pack_bf16x2(yv[8 * j + 4], yv[8 * j + 5]), pack_bf16x2(yv[8 * j + 6], yv[8 * j + 7])};
-                        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off + 16u * j, 0, 0);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < N; j += 2) {
-                        if (j + 1 < N) {
-                            const uint32_t pk = pack_bf16x2(yv[j], yv[j + 1]);
-                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pk & 0xffffu), ry, off + 2u * j, 0, 0);
-                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pk >> 16), ry, off + 2u * (j + 1), 0, 0);
-                        } else {
-                            const uint32_t pk = pack_bf16x2(yv[j], 0.0f);
-                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pk & 0xffffu), ry, off + 2u * j, 0, 0);
-                        }
-                    }
-                }
-            }
-        }
-}
-
-template <class C>
 __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
     const typename C::IO* __restrict__ x, const typename C::IO* __restrict__ w_hat,
     typename C::IO* __restrict__ y, int64_t T, int C_in, int C_out, int n_c_tiles,
-    uint32_t total_tiles, uint32_t w_bytes) {
+    uint32_t total_tiles, uint32_t w_bytes, int y_coalesced) {
     using IO = typename C::IO;
     using F = typename AFrag<IO>::T;
-    constexpr int N = C::N, S = C::S, KS = C::KS;
+    constexpr int N = C::N, S = C::S, XP = C::XP;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
     const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
     const int64_t t0 = (int64_t)(tile / n_c_tiles) * C::TT;
     const int o0 = (int)(tile % n_c_tiles) * C::CT;
     const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
-    const int tw = wave % C::WAVES;  // token slab of this wave
-    const int kw = wave / C::WAVES;  // input-channel group of this wave
     const int q = lane >> 4;
 
     const uint32_t row_x = (uint32_t)C_in * (N * S), row_y = (uint32_t)C_out * (N * S);
@@ -556,13 +496,22 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + t0 * C_out * N, rows * row_y);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_hat, w_bytes);
 
-    // loop-invariant offsets
-    const uint32_t xoff = (uint32_t)(tw * 16 + (lane & 15)) * row_x + (uint32_t)(q * C::R) * (N * S);
+    char* wbuf = smem;                                         // two w_hat tile buffers
+    char* xex = smem + C::W_REGION + wave * C::XEX_BYTES;      // this wave's x exchange region
+
+    // loop-invariant offsets of the coalesced x loads: instruction j, lane l
+    // fetches piece k of row r of this wave's 16 rows (pc = 64 j + l = r XP + k)
+    uint32_t xoff[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const int pc = 64 * j + lane, r = pc / XP, k = pc % XP;
+        xoff[j] = (uint32_t)(wave * 16 + r) * row_x + (uint32_t)k * 16u;
+    }
     uint32_t woff[C::DMA_ITERS];
 #pragma unroll
     for (int it = 0; it < C::DMA_ITERS; ++it) {
         int p, o, qq;
-        slot_coords<C>((it * C::WAVES + tw) * 64 + lane, p, o, qq);
+        slot_coords<C>((it * C::WAVES + wave) * 64 + lane, p, o, qq);
         woff[it] = (o0 + o < C_out && p < N)
                        ? (uint32_t)((((int64_t)p * C_out + o0 + o) * C_in + qq * C::R) * S)
                        : kOOB;
@@ -575,100 +524,136 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
         for (int b = 0; b < C::CB; ++b) acc[p][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nch = (C_in + C::KC - 1) / C::KC;
-    const int nsteps = (nch + KS - 1) / KS;
-    // input-channel tail: only a partial (or absent) last chunk has lanes without data
-    auto x_off = [&](int c) -> uint32_t {
-        return (c * C::KC + C::KC <= C_in || c * C::KC + q * C::R < C_in) ? xoff : kOOB;
+    const uint32_t chunk_x = (uint32_t)C::KC * (N * S);
+    auto load_x = [&](int c, uint32_t(&xr)[C::XW]) {
+        const bool tail = c * C::KC + C::KC > C_in;
+        const uint32_t valid = tail ? (uint32_t)(C_in - c * C::KC) * (N * S) : 0xffffffffu;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int k = (64 * j + lane) % XP;
+            const uint32_t off = (c < nch && (uint32_t)k * 16u < valid) ? xoff[j] : kOOB;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, (uint32_t)c * chunk_x, 0);
+            xr[4 * j + 0] = v.x;
+            xr[4 * j + 1] = v.y;
+            xr[4 * j + 2] = v.z;
+            xr[4 * j + 3] = v.w;
+        }
     };
-    auto x_soff = [&](int c) -> uint32_t { return (uint32_t)(c * C::KC) * (N * S); };
-    // this K group's tile buffers
-    char* gbuf = smem + kw * C::NBUF * C::BUF_BYTES;
     auto dma = [&](int c, char* buf) {
         if (c < nch)
-            fast_dma_w<C>(rw, woff, (uint32_t)(c * C::KC * S), c * C::KC + C::KC > C_in, c * C::KC, C_in,
-                          tw, buf);
+            fast_dma_w<C>(rw, woff, (uint32_t)(c * C::KC * S), c * C::KC + C::KC > C_in, c * C::KC, C_in, buf);
+    };
+    // coalesced pieces -> LDS -> this lane's records (A layout: row = lane%16,
+    // pieces q*N .. q*N+N-1 of that row)
+    auto exchange = [&](const uint32_t(&xr)[C::XW], uint32_t(&xa)[C::XW]) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int pc = 64 * j + lane, r = pc / XP, k = pc % XP;
+            *reinterpret_cast<u32x4*>(xex + xpiece<C::XROT, XP, C::XPITCH>(r, k) * 16) =
+                u32x4{xr[4 * j], xr[4 * j + 1], xr[4 * j + 2], xr[4 * j + 3]};
+        }
+        const int r = lane & 15;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(xex + xpiece<C::XROT, XP, C::XPITCH>(r, q * N + j) * 16);
+            xa[4 * j + 0] = v.x;
+            xa[4 * j + 1] = v.y;
+            xa[4 * j + 2] = v.z;
+            xa[4 * j + 3] = v.w;
+        }
     };
 
-    // Step st: group kw handles chunk c = st*KS + kw, kept in tile buffer st % NBUF.
-    // Wait for that chunk's w_hat (LDS) and x (VGPRs); start the w_hat DMA of the
-    // group's chunk PD steps ahead; transform x; start that chunk's x loads into
-    // the registers just freed; multiply while the loads are in flight.
-    auto tbuf = [&](int st) -> char* { return gbuf + (st % C::NBUF) * C::BUF_BYTES; };
-    if constexpr (KS > 1) {
-        // A group whose chunks run out multiplies zeros (out-of-range x) by a
-        // tile buffer it may never have written: clear every buffer first so
-        // never-written LDS cannot inject NaN, then order the clear before any DMA.
-        for (int i = (int)threadIdx.x * 16; i < C::LDS_BYTES; i += C::kThreads * 16)
-            *reinterpret_cast<u32x4*>(smem + i) = u32x4{0u, 0u, 0u, 0u};
+    // Per chunk c: wait for w_hat chunk c (LDS) and x chunk c (VGPRs); start the
+    // w_hat DMA of chunk c+1; move x through the exchange; transform; start the
+    // x loads of chunk c+1 into the registers just freed; multiply while those
+    // loads are in flight.
+    uint32_t xr[C::XW];
+    dma(0, wbuf);
+    load_x(0, xr);
+    for (int c = 0; c < nch; ++c) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        dma(c + 1, wbuf + ((c + 1) & 1) * C::BUF_BYTES);
+        uint32_t xa[C::XW];
+        exchange(xr, xa);
+        F A[N];
+        x_to_planes<C>(xa, A);
+        // unconditional: past the last chunk the offsets are out of range (zeros,
+        // no memory access), and the registers keep a single definition
+        load_x(c + 1, xr);
+        fast_products<C>(A, wbuf + (c & 1) * C::BUF_BYTES, acc);
     }
-    uint32_t xa[C::XW];
-    if constexpr (C::PD == 1) {
-        dma(kw, tbuf(0));
-        fast_load_x<C>(rx, x_off(kw), x_soff(kw), xa);
-        for (int st = 0; st < nsteps; ++st) {
-            const int c = st * KS + kw;
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            dma(c + KS, tbuf(st + 1));
-            F A[N];
-            x_to_planes<C>(xa, A);
-            // unconditional: past the last chunk the offset is out of range (zeros,
-            // no memory access), and the registers keep a single definition
-            fast_load_x<C>(rx, x_off(c + KS), x_soff(c + KS), xa);
-            // past the last chunk A is zero (out-of-range x loads), so the products
-            // add nothing; the group's tile holds finite values (see above)
-            fast_products<C>(A, tbuf(st), acc);
+
+    // Epilogue: inverse DFT of each (token, channel) record, then y written once.
+    if (y_coalesced) {
+        __syncthreads();  // the staging area overlaps the tile and exchange buffers
+        char* yst = smem + wave * C::YST_BYTES;
+#pragma unroll
+        for (int b = 0; b < C::CB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tl = (lane >> 4) * 4 + r, ol = b * 16 + (lane & 15);
+                float P[N], yv[N];
+#pragma unroll
+                for (int p = 0; p < N; ++p) P[p] = acc[p][b][r];
+                rdft_inverse<N>(P, yv);
+                // record bytes [ol*N*S, ol*N*S + N*S) of row tl, piece-rotated like x
+                const int byte0 = ol * N * S;
+                if constexpr ((N * S) % 16 == 0) {
+#pragma unroll
+                    for (int j = 0; j < N * S / 16; ++j) {
+                        u32x4 v;
+                        if constexpr (sizeof(IO) == 4) {
+                            v = u32x4{__float_as_uint(yv[4 * j]), __float_as_uint(yv[4 * j + 1]),
+                                      __float_as_uint(yv[4 * j + 2]), __float_as_uint(yv[4 * j + 3])};
+                        } else {
+                            v = u32x4{pack_bf16x2(yv[8 * j], yv[8 * j + 1]), pack_bf16x2(yv[8 * j + 2], yv[8 * j + 3]),
+                                      pack_bf16x2(yv[8 * j + 4], yv[8 * j + 5]), pack_bf16x2(yv[8 * j + 6], yv[8 * j + 7])};
+                        }
+                        *reinterpret_cast<u32x4*>(yst + xpiece<C::YROT, C::YP, C::YPITCH>(tl, byte0 / 16 + j) * 16) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < N; ++e) {
+                        const int by = byte0 + e * S;
+                        char* dst = yst + xpiece<C::YROT, C::YP, C::YPITCH>(tl, by / 16) * 16 + (by % 16);
+                        if constexpr (sizeof(IO) == 4) *reinterpret_cast<float*>(dst) = yv[e];
+                        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16x2(yv[e], 0.f) & 0xffffu);
+                    }
+                }
+            }
+        // wave-local: its own rows, written and read by the same wave
+        const uint32_t cols = (uint32_t)(C_out - o0) * (N * S);  // valid bytes of a tile row
+        for (int pc = lane; pc < 16 * C::YP; pc += 64) {
+            const int r = pc / C::YP, k = pc % C::YP;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(yst + xpiece<C::YROT, C::YP, C::YPITCH>(r, k) * 16);
+            const uint32_t off = ((uint32_t)k * 16u < cols)
+                                     ? (uint32_t)(wave * 16 + r) * row_y + (uint32_t)o0 * (N * S) + (uint32_t)k * 16u
+                                     : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
         }
     } else {
-        // Two chunks in flight: x alternates between two register sets.  The wait
-        // for chunk c counts the loads issued for the next chunk (N x loads plus,
-        // if that chunk exists, DMA_ITERS tile loads); barriers separate the
-        // chunks' issue groups, so those are exactly the loads younger than c's.
-        uint32_t xb[C::XW];
-        dma(kw, tbuf(0));
-        fast_load_x<C>(rx, x_off(kw), x_soff(kw), xa);
-        __syncthreads();
-        dma(kw + KS, tbuf(1));
-        fast_load_x<C>(rx, x_off(kw + KS), x_soff(kw + KS), xb);
-        auto step = [&](int st, uint32_t(&xc)[C::XW]) {
-            const int c = st * KS + kw;
-            if (c + KS < nch) wait_vmcnt<C::N + C::DMA_ITERS>();
-            else wait_vmcnt<C::N>();
-            __syncthreads();
-            dma(c + 2 * KS, tbuf(st + 2));
-            F A[N];
-            x_to_planes<C>(xc, A);
-            fast_load_x<C>(rx, x_off(c + 2 * KS), x_soff(c + 2 * KS), xc);
-            fast_products<C>(A, tbuf(st), acc);
-        };
-        for (int st = 0; st < nsteps; st += 2) {
-            step(st, xa);
-            if (st + 1 < nsteps) step(st + 1, xb);
-        }
+#pragma unroll
+        for (int b = 0; b < C::CB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t tl = (uint32_t)(wave * 16 + (lane >> 4) * 4 + r);
+                const int o = o0 + b * 16 + (lane & 15);
+                const uint32_t off = o < C_out ? tl * row_y + (uint32_t)o * (N * S) : kOOB;
+                float P[N], yv[N];
+#pragma unroll
+                for (int p = 0; p < N; ++p) P[p] = acc[p][b][r];
+                rdft_inverse<N>(P, yv);
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    if constexpr (sizeof(IO) == 4)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[e]), ry, off + 4u * e, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(yv[e], 0.f) & 0xffffu), ry,
+                                                             off + 2u * e, 0, 0);
+                }
+            }
     }
-    if constexpr (KS > 1) {
-        // sum the K groups' accumulators into group 0 through LDS
-        __syncthreads();
-        f32x4* red = reinterpret_cast<f32x4*>(smem);
-        if (kw > 0) {
-#pragma unroll
-            for (int p = 0; p < N; ++p)
-#pragma unroll
-                for (int b = 0; b < C::CB; ++b)
-                    red[((((kw - 1) * C::WAVES + tw) * N + p) * C::CB + b) * 64 + lane] = acc[p][b];
-        }
-        __syncthreads();
-        if (kw > 0) return;
-#pragma unroll
-        for (int g = 1; g < KS; ++g)
-#pragma unroll
-            for (int p = 0; p < N; ++p)
-#pragma unroll
-                for (int b = 0; b < C::CB; ++b)
-                    acc[p][b] += red[((((g - 1) * C::WAVES + tw) * N + p) * C::CB + b) * 64 + lane];
-    }
-    fast_store_y<C>(acc, ry, row_y, C_out, o0, tw);
 }
 
 // --- host side ----------------------------------------------------------------------
@@ -699,9 +684,11 @@ hipError_t launch_fast_cfg(const void* x, const void* w_hat, void* y, int64_t T,
     const int64_t total = n_t * n_c;
     if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
     const int64_t w_bytes = (int64_t)C::N * C_out * C_in * (int64_t)sizeof(IO);
+    // staged, coalesced y stores need whole 16-byte pieces in every row of y
+    const int y_coalesced = ((int64_t)C_out * C::N * (int64_t)sizeof(IO)) % 16 == 0;
     hipLaunchKernelGGL((cn_fast_kernel<C>), dim3((uint32_t)total), dim3(C::kThreads), 0, stream,
                        (const IO*)x, (const IO*)w_hat, (IO*)y, T, C_in, C_out, n_c, (uint32_t)total,
-                       (uint32_t)w_bytes);
+                       (uint32_t)w_bytes, y_coalesced);
     return hipGetLastError();
 }
 
@@ -720,11 +707,9 @@ bool fast_ok(int C_in, int C_out, int TT) {
 // lane = 4 * N * CB.
 template <int N, typename IO>
 struct FusedMenu {
-    static constexpr int kCount = 14;
-    static constexpr int waves[kCount] = {4, 4, 4, 4, 4, 1, 1, 1, 4, 4, 4, 4, 1, 1};
-    static constexpr int cb[kCount] = {6, 5, 4, 3, 2, 2, 1, 1, 3, 4, 3, 2, 2, 1};
-    static constexpr int ks[kCount] = {1, 1, 1, 1, 1, 1, 1, 2, 2, 1, 1, 1, 1, 1};
-    static constexpr int pd[kCount] = {1, 1, 1, 1, 1, 1, 1, 1, 1, 2, 2, 2, 2, 2};
+    static constexpr int kCount = 7;
+    static constexpr int waves[kCount] = {4, 4, 4, 4, 4, 1, 1};
+    static constexpr int cb[kCount] = {6, 5, 4, 3, 2, 2, 1};
 };
 
 template <int N, typename IO, int I>
@@ -732,14 +717,16 @@ hipError_t launch_menu_entry(const void* x, const void* w_hat, void* y, int64_t 
                              int C_out, hipStream_t stream) {
     constexpr int W = FusedMenu<N, IO>::waves[I];
     constexpr int CBr = FusedMenu<N, IO>::cb[I];
-    constexpr int KS = FusedMenu<N, IO>::ks[I];
-    constexpr int PD = FusedMenu<N, IO>::pd[I];
-    // keep the accumulators within 192 registers per lane and the 2*KS chunk
-    // buffers (N*CB KiB each) within the 160 KiB of LDS
+    // keep the accumulators within 192 registers per lane and the LDS tiles
+    // (two w_hat buffers of N*CB KiB plus the x exchange) within 160 KiB
+    // (two w_hat buffers of N*CB KiB plus the x exchange, and afterwards the
+    // y staging of 16 rows x 16*CB*N*sizeof bytes per wave) within 160 KiB
     constexpr int cap_acc = 48 / N > 0 ? 48 / N : 1;
-    constexpr int cap_lds = 160 / ((PD + 1) * KS * N) > 0 ? 160 / ((PD + 1) * KS * N) : 1;
-    constexpr int CB = CBr < cap_acc ? (CBr < cap_lds ? CBr : cap_lds) : (cap_acc < cap_lds ? cap_acc : cap_lds);
-    using Cfg = FastCfg<N, IO, W, CB, KS, PD>;
+    constexpr int cap_lds = 64 / N > 0 ? 64 / N : 1;
+    constexpr int cap_y = 163840 / (W * 256 * N * (int)sizeof(IO)) > 0 ? 163840 / (W * 256 * N * (int)sizeof(IO)) : 1;
+    constexpr int cap = cap_acc < cap_lds ? (cap_acc < cap_y ? cap_acc : cap_y) : (cap_lds < cap_y ? cap_lds : cap_y);
+    constexpr int CB = CBr < cap ? CBr : cap;
+    using Cfg = FastCfg<N, IO, W, CB>;
     if (fast_ok<N, IO>(C_in, C_out, Cfg::TT))
         return launch_fast_cfg<Cfg>(x, w_hat, y, T, C_in, C_out, stream);
     // generic path (ragged channel groups): two shapes only
@@ -748,14 +735,15 @@ hipError_t launch_menu_entry(const void* x, const void* w_hat, void* y, int64_t 
 }
 
 // Automatic choice (from tile sweeps on MI355X): 4-wave workgroups with the
-// widest output tile that keeps two waves per SIMD (about 28/N output blocks:
-// 4*N*CB accumulators plus ~110 other registers within 256) while the grid still
-// gives every CU a workgroup; one-wave workgroups for small problems.
+// widest output tile that keeps two workgroups per CU (about 24/N output blocks:
+// 4*N*CB accumulators plus ~130 other registers within 256, and the LDS tiles
+// within half the CU's 160 KiB) while the grid still gives every CU a
+// workgroup; one-wave workgroups for small problems.
 template <int N, typename IO>
 int choose_fused(int64_t T, int C_in, int C_out) {
     (void)C_in;
     const int nblk = (C_out + 15) / 16;
-    int cb = 28 / N;
+    int cb = 24 / N;
     cb = cb < 2 ? 2 : (cb > 6 ? 6 : cb);
     if (cb > nblk) cb = nblk < 2 ? 2 : nblk;
     for (; cb >= 2; --cb) {
@@ -772,10 +760,9 @@ hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, in
     switch (i) {
 #define EQL_ENTRY(k) \
     case k: return launch_menu_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream);
-        EQL_ENTRY(0) EQL_ENTRY(1) EQL_ENTRY(2) EQL_ENTRY(3) EQL_ENTRY(4) EQL_ENTRY(5) EQL_ENTRY(6)
-        EQL_ENTRY(7) EQL_ENTRY(8) EQL_ENTRY(9) EQL_ENTRY(10) EQL_ENTRY(11) EQL_ENTRY(12)
+        EQL_ENTRY(0) EQL_ENTRY(1) EQL_ENTRY(2) EQL_ENTRY(3) EQL_ENTRY(4) EQL_ENTRY(5)
 #undef EQL_ENTRY
-        default: return launch_menu_entry<N, IO, 13>(x, w_hat, y, T, C_in, C_out, stream);
+        default: return launch_menu_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream);
     }
 }
 

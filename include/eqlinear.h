@@ -129,11 +129,10 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
 
 /* eqlinear_forward with a fixed tile configuration instead of the automatic
  * choice, for tuning and tests.  A workgroup covers 16*W tokens and 16*B output
- * channels (B is capped so that 4*N*B <= 192 accumulators per lane), with K
- * waves per 16-token slab splitting the input channels:
+ * channels (B is capped so that 4*N*B <= 192 accumulators per lane and the LDS
+ * tiles fit):
  *   tile 0: W=4 B=6   1: W=4 B=5   2: W=4 B=4   3: W=4 B=3   4: W=4 B=2
- *   tile 5: W=1 B=2   6: W=1 B=1   7: W=1 B=1 K=2   8: W=4 B=3 K=2
- *   (K=1 where not given); -1: automatic (same as eqlinear_forward).
+ *   tile 5: W=1 B=2   6: W=1 B=1   -1: automatic (same as eqlinear_forward).
  * Shapes with C_in not a multiple of 16 bytes of channels use a generic kernel
  * with fewer shapes.  Results agree to fp32 rounding; other values ->
  * EQL_ERR_INVALID. */
