@@ -32,10 +32,19 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 KERNEL_SOURCES = {
     "C": ["group_equivariant_linear_amd/csrc/cn_fused.h",
+          "group_equivariant_linear_amd/csrc/cn_mf.h",
+          "group_equivariant_linear_amd/csrc/cn_dispatch.h",
           "group_equivariant_linear_amd/csrc/eq_device.h"],
     "D8": ["group_equivariant_linear_amd/csrc/gemm_rows.hip",
            "group_equivariant_linear_amd/csrc/eq_device.h"],
 }
+
+
+def step_kernel_name(wl):
+    """The kernel one forward of this workload launches (automatic tile choice)."""
+    if wl.group != "C":
+        return "gemm_rows_kernel"
+    return "cn_mf_kernel" if wl.dtype == "bf16" and 2 <= wl.N <= 8 else "cn_fast_kernel"
 
 
 def kernel_source_hash(group):
@@ -60,6 +69,9 @@ def parse():
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--mode", default="bench", choices=["bench", "traffic"],
                     help="traffic: a few forwards and a copy of known size, for rocprofv3 --pmc")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="read the counter CSVs of a FETCH_SIZE and a WRITE_SIZE run of "
+                         "--mode traffic and write profiles/traffic_<workload>.{json,md}")
     return ap.parse_args()
 
 
@@ -237,6 +249,114 @@ def _run_oracle(wl, d, n):
         oracle.d8_dense(d["x64"][:n], d["w64"], wl.C_out)
 
 
+STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "gemm_rows_kernel")
+TRAFFIC_WARM = 5   # back-to-back forwards (inputs partly cached from the previous launch)
+TRAFFIC_COLD = 5   # forwards each after a 512 MiB read that evicts the L2s
+TRAFFIC_COPIES = 5
+TRAFFIC_COPY_BYTES = 256 * 1024 * 1024
+
+
+def traffic_run(layers):
+    """The launches the FETCH_SIZE / WRITE_SIZE passes count: warm forwards, cold
+    forwards, and device copies of known size that calibrate the counters."""
+    import torch
+    for _ in range(TRAFFIC_WARM):
+        for L in layers:
+            L.step()
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    for _ in range(TRAFFIC_COLD):
+        flush.sum()  # reads only: leaves clean lines, so no write-back is charged to the forward
+        for L in layers:
+            L.step()
+    del flush
+    n = TRAFFIC_COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(TRAFFIC_COPIES):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _counter_rows(d, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {files}")
+    rows = [r for r in csv.DictReader(open(files[0])) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def algorithmic_bytes(wl):
+    """x read once, y written once, the weight operand (w_hat, or the D8 blocks) read once."""
+    es = 4 if wl.dtype == "f32" else 2
+    if wl.group == "C":
+        K, M, w = wl.N * wl.C_in, wl.N * wl.C_out, wl.N * wl.C_in * wl.C_out
+    else:
+        K, M = wl.C_in, wl.C_out
+        w = 4 * (wl.C_in // 8) * (wl.C_out // 8) + (wl.C_in // 4) * (wl.C_out // 4)
+    return es * (wl.T * (K + M) + w)
+
+
+def summarize_traffic(args, wls):
+    """Calibrated HBM bytes per launch of the step kernel from two rocprofv3 --pmc runs
+    of --mode traffic (FETCH_SIZE, then WRITE_SIZE; both count KiB per dispatch)."""
+    wl = args.workload
+    layers = wls
+    res = {}
+    for counter, d in zip(("FETCH_SIZE", "WRITE_SIZE"), args.traffic_from):
+        rows = _counter_rows(d, counter)
+        steps = [r for r in rows if any(k in r["Kernel_Name"] for k in STEP_KERNELS)]
+        copies = [r for r in rows if "copy" in r["Kernel_Name"].lower() and int(r["Grid_Size"]) >= 65536]
+        nl = len(layers)
+        if len(steps) != (TRAFFIC_WARM + TRAFFIC_COLD) * nl or len(copies) < TRAFFIC_COPIES:
+            raise SystemExit(f"{counter}: {len(steps)} step dispatches, {len(copies)} copies; "
+                             f"expected {(TRAFFIC_WARM + TRAFFIC_COLD) * nl} and {TRAFFIC_COPIES}")
+        kib = [float(r["Counter_Value"]) for r in steps]
+        warm = sum(kib[:TRAFFIC_WARM * nl]) / TRAFFIC_WARM
+        cold = sum(kib[TRAFFIC_WARM * nl:]) / TRAFFIC_COLD
+        copy = sum(float(r["Counter_Value"]) for r in copies[-TRAFFIC_COPIES:]) / TRAFFIC_COPIES
+        factor = TRAFFIC_COPY_BYTES / (copy * 1024.0)
+        res[counter] = {"kib_warm": warm, "kib_cold": cold, "copy_kib": copy, "scale": factor,
+                        "kernel": steps[0]["Kernel_Name"]}
+    f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
+    cold = f["kib_cold"] * 1024 * f["scale"] + w["kib_cold"] * 1024 * w["scale"]
+    warm = f["kib_warm"] * 1024 * f["scale"] + w["kib_warm"] * 1024 * w["scale"]
+    algo = sum(algorithmic_bytes(w) for w in wls)
+    group = wls[0].group
+    rec = {"workload": wl, "kernel": f["kernel"], "kernel_source_sha": kernel_source_hash(group),
+           "hbm_bytes_per_launch": cold, "hbm_bytes_per_launch_warm": warm,
+           "algorithmic_bytes_per_launch": algo, "traffic_over_algorithmic": cold / algo,
+           "fetch": f, "write": w, "copy_bytes": TRAFFIC_COPY_BYTES,
+           "command_fetch": f"rocprofv3 --pmc FETCH_SIZE -d {args.traffic_from[0]} -o run -f csv -- "
+                            f"python3 bench.py --workload {wl} --mode traffic",
+           "command_write": f"rocprofv3 --pmc WRITE_SIZE -d {args.traffic_from[1]} -o run -f csv -- "
+                            f"python3 bench.py --workload {wl} --mode traffic",
+           "command_summary": f"python3 bench.py --workload {wl} --traffic-from "
+                              f"{args.traffic_from[0]} {args.traffic_from[1]}"}
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl}.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    md = [f"# HBM traffic of the step kernel, workload {wl}", "",
+          f"Kernel: `{f['kernel']}`", "",
+          "Commands (each counter in its own pass):", "",
+          "```", rec["command_fetch"], rec["command_write"], rec["command_summary"], "```", "",
+          f"`--mode traffic` launches {TRAFFIC_WARM} back-to-back forwards, {TRAFFIC_COLD} forwards "
+          f"each after a 512 MiB read (L2s evicted, clean), then {TRAFFIC_COPIES} device copies of "
+          f"{TRAFFIC_COPY_BYTES >> 20} MiB that calibrate the counters.", "",
+          "| counter | KiB/launch warm | KiB/launch cold | copy KiB (expected "
+          f"{TRAFFIC_COPY_BYTES >> 10}) | scale |", "|---|---|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = res[c]
+        md.append(f"| {c} | {r['kib_warm']:.1f} | {r['kib_cold']:.1f} | {r['copy_kib']:.1f} | {r['scale']:.4f} |")
+    md += ["", f"Calibrated HBM bytes per launch: cold {cold:.0f}, warm {warm:.0f}; "
+               f"algorithmic {algo} (x once, y once, w_hat once): cold/algorithmic = {cold / algo:.3f}.",
+           f"Kernel source sha (cn path headers): `{rec['kernel_source_sha']}`."]
+    with open(os.path.join(ROOT, "profiles", f"traffic_{wl}.md"), "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print(json.dumps({"hbm_bytes_per_launch": cold, "algorithmic": algo, "ratio": cold / algo}))
+
+
 def load_traffic(workload, group):
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
@@ -256,33 +376,29 @@ def main():
               f"--gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 
+    import synthetic
+    names = ["c3a", "c3b", "c3c"] if args.workload == "c3" else [args.workload]
+    wls = [synthetic.WORKLOADS[n] for n in names]
+    if args.traffic_from:
+        summarize_traffic(args, wls)
+        return
+
     import torch
 
     import group_equivariant_linear_amd as eq
-    import synthetic
     if not eq.built():
         from group_equivariant_linear_amd import _build
         _build.build()
     eq.load_library()
     torch.cuda.set_device(0)
 
-    names = ["c3a", "c3b", "c3c"] if args.workload == "c3" else [args.workload]
-    wls = [synthetic.WORKLOADS[n] for n in names]
     layers = [Layer(eq, wl, tile=args.tile) for wl in wls]
     torch.cuda.synchronize()
-
+    for L in layers:
+        assert L.bytes_per_launch == algorithmic_bytes(L.wl)
     if args.mode == "traffic":
-        # a few forwards, then a plain copy of known size (calibrates the counters)
-        for _ in range(5):
-            for L in layers:
-                L.step()
-        n = 256 * 1024 * 1024 // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n * 4, "workload": args.workload}))
+        traffic_run(layers)
+        print(json.dumps({"copy_bytes": TRAFFIC_COPY_BYTES, "workload": args.workload}))
         return
 
     steps = [L.step for L in layers]
@@ -295,6 +411,15 @@ def main():
     ms_own_graph = time_graph([L.dense_own for L in layers], [L.y_dense for L in layers], dsteps, dwarm)
     ms_lin_eager = time_loop([L.dense_torch for L in layers], dsteps, dwarm)
     ms_lin_graph = time_graph([L.dense_torch for L in layers], [L.y_lin for L in layers], dsteps, dwarm)
+    # a device copy moving the same number of bytes (half read, half written): the
+    # practical floor of a launch of this size
+    bytes_launch = sum(L.bytes_per_launch for L in layers)
+    csrc = torch.ones(bytes_launch // 8, dtype=torch.float32, device="cuda")
+    cdst = torch.empty_like(csrc)
+    ms_copy = time_graph([lambda: cdst.copy_(csrc)], [cdst], dsteps, dwarm)
+    if ms_copy is None:
+        ms_copy = time_loop([lambda: cdst.copy_(csrc)], dsteps, dwarm)
+    del csrc, cdst
     ms_own = min(t for t in (ms_own_eager, ms_own_graph) if t is not None)
     ms_lin = min(t for t in (ms_lin_eager, ms_lin_graph) if t is not None)
     # agreement of the fused path with the dense comparator on this very batch
@@ -349,6 +474,8 @@ def main():
                            "ms_torch_eager": ms_lin_eager, "ms_torch_graph": ms_lin_graph,
                            "speedup_vs_best": best_dense / ms, "expand_ms_once": sum(L.expand_ms for L in layers),
                            "agreement_rel_l2": agree},
+        "copy_same_bytes": {"ms": ms_copy, "gbs": bytes_launch / (ms_copy * 1e-3) / 1e9,
+                            "frac_hbm": bytes_launch / (ms_copy * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "weight_fft_ms_once": [L.weight_fft_ms for L in layers],
         "roofline": {
             "bound": "hbm",
@@ -357,7 +484,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "cn_fast_kernel" if group == "C" else "gemm_rows_kernel",
+            "kernel": step_kernel_name(wls[0]),
             "bytes_per_launch": bytes_launch,
             "kernel_source_sha": kernel_source_hash(group),
         },

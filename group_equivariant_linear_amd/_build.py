@@ -15,9 +15,12 @@ OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
 ARCH = "gfx950"
 # Packed-fp32 VALU ops are disabled: the plain scalar forms are used everywhere.
+# MFMA results live in ordinary VGPRs (gfx950 allows it): no copies between the
+# accumulation registers and the VALU, and fewer registers in all.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -1,0 +1,67 @@
+// cn_dispatch.h -- tile choice and dispatch of the C_N forward kernels.
+#pragma once
+
+#include "cn_fused.h"
+#include "cn_mf.h"
+
+namespace eql {
+
+constexpr int kMfFirstTile = 7;  // tiles 7..13: entries 0..6 on the matrix-core transform kernel
+
+// Automatic choice (from tile sweeps on MI355X): 4-wave workgroups with the
+// widest output tile that keeps two workgroups per CU (about 24/N output blocks:
+// 4*N*CB accumulators plus ~130 other registers within 256, and the LDS tiles
+// within half the CU's 160 KiB) while the grid still gives every CU a
+// workgroup; one-wave workgroups for small problems.
+template <int N>
+int choose_shape(int64_t T, int C_in, int C_out) {
+    (void)C_in;
+    const int nblk = (C_out + 15) / 16;
+    int cb = 24 / N;
+    cb = cb < 2 ? 2 : (cb > 6 ? 6 : cb);
+    if (cb > nblk) cb = nblk < 2 ? 2 : nblk;
+    for (; cb >= 2; --cb) {
+        const int64_t tiles = ((T + 63) / 64) * ((nblk + cb - 1) / cb);
+        if (tiles >= 256) return 6 - cb;  // menu entries 0..4 hold CB = 6..2
+    }
+    return 6;  // one wave, one output block
+}
+
+template <int N, typename IO>
+int choose_fused(int64_t T, int C_in, int C_out) {
+    // bf16 orders up to 8 take the matrix-core transform kernel, same shapes
+    if constexpr (mf_supported<N, IO>) return kMfFirstTile + choose_shape<N>(T, C_in, C_out);
+    else return choose_shape<N>(T, C_in, C_out);
+}
+
+template <int N, typename IO>
+hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
+                        hipStream_t stream, int tile) {
+    const int i = tile >= 0 ? tile : choose_fused<N, IO>(T, C_in, C_out);
+    if (i >= kMfFirstTile) {
+        switch (i - kMfFirstTile) {
+#define EQL_MF(k)                                                                       \
+    case k:                                                                             \
+        if constexpr (mf_supported<N, IO>)                                              \
+            return launch_mf_entry<N, k>(x, w_hat, y, T, C_in, C_out, stream);          \
+        else                                                                            \
+            return launch_menu_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream);
+            EQL_MF(0) EQL_MF(1) EQL_MF(2) EQL_MF(3) EQL_MF(4) EQL_MF(5)
+#undef EQL_MF
+            default:
+                if constexpr (mf_supported<N, IO>)
+                    return launch_mf_entry<N, 6>(x, w_hat, y, T, C_in, C_out, stream);
+                else
+                    return launch_menu_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream);
+        }
+    }
+    switch (i) {
+#define EQL_ENTRY(k) \
+    case k: return launch_menu_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream);
+        EQL_ENTRY(0) EQL_ENTRY(1) EQL_ENTRY(2) EQL_ENTRY(3) EQL_ENTRY(4) EQL_ENTRY(5)
+#undef EQL_ENTRY
+        default: return launch_menu_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream);
+    }
+}
+
+}  // namespace eql

@@ -734,36 +734,4 @@ hipError_t launch_menu_entry(const void* x, const void* w_hat, void* y, int64_t 
     else return launch_fused_cfg<FusedCfg<N, IO, 1, 1>>(x, w_hat, y, T, C_in, C_out, stream);
 }
 
-// Automatic choice (from tile sweeps on MI355X): 4-wave workgroups with the
-// widest output tile that keeps two workgroups per CU (about 24/N output blocks:
-// 4*N*CB accumulators plus ~130 other registers within 256, and the LDS tiles
-// within half the CU's 160 KiB) while the grid still gives every CU a
-// workgroup; one-wave workgroups for small problems.
-template <int N, typename IO>
-int choose_fused(int64_t T, int C_in, int C_out) {
-    (void)C_in;
-    const int nblk = (C_out + 15) / 16;
-    int cb = 24 / N;
-    cb = cb < 2 ? 2 : (cb > 6 ? 6 : cb);
-    if (cb > nblk) cb = nblk < 2 ? 2 : nblk;
-    for (; cb >= 2; --cb) {
-        const int64_t tiles = ((T + 63) / 64) * ((nblk + cb - 1) / cb);
-        if (tiles >= 256) return 6 - cb;  // menu entries 0..4 hold CB = 6..2
-    }
-    return 6;  // one wave, one output block
-}
-
-template <int N, typename IO>
-hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
-                        hipStream_t stream, int tile) {
-    const int i = tile >= 0 ? tile : choose_fused<N, IO>(T, C_in, C_out);
-    switch (i) {
-#define EQL_ENTRY(k) \
-    case k: return launch_menu_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream);
-        EQL_ENTRY(0) EQL_ENTRY(1) EQL_ENTRY(2) EQL_ENTRY(3) EQL_ENTRY(4) EQL_ENTRY(5)
-#undef EQL_ENTRY
-        default: return launch_menu_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream);
-    }
-}
-
 }  // namespace eql

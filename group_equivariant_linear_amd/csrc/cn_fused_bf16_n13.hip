@@ -1,5 +1,5 @@
 // cn_fused_bf16_n13.hip -- fused C_N forward instantiations, bf16, N = 13..16.
-#include "cn_fused.h"
+#include "cn_dispatch.h"
 
 namespace eql {
 

@@ -1,5 +1,5 @@
 // cn_fused_f32_n1.hip -- fused C_N forward instantiations, f32, N = 1..4.
-#include "cn_fused.h"
+#include "cn_dispatch.h"
 
 namespace eql {
 

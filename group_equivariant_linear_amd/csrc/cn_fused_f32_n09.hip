@@ -1,5 +1,5 @@
 // cn_fused_f32_n9.hip -- fused C_N forward instantiations, f32, N = 9..12.
-#include "cn_fused.h"
+#include "cn_dispatch.h"
 
 namespace eql {
 

@@ -123,7 +123,9 @@ eqlinear_status eqlinear_weight_fft(eqlinear_plan_t plan, const void* w, void* w
  *   y     [T][C_out][N] device, plan dtype; must not overlap x or w_hat
  *   T >= 0 tokens (T == 0: returns EQL_OK, launches nothing)
  * bf16 plans round the frequency-domain inputs to bf16 before the matrix
- * cores and round y once from fp32. */
+ * cores and round y once from fp32; for 2 <= N <= 8 the transforms run on the
+ * matrix cores too, with bf16 coefficients, and the frequency-domain outputs
+ * are rounded to bf16 before the inverse transform. */
 eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                  void* y, int64_t T, void* stream);
 
@@ -133,9 +135,13 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
  * tiles fit):
  *   tile 0: W=4 B=6   1: W=4 B=5   2: W=4 B=4   3: W=4 B=3   4: W=4 B=2
  *   tile 5: W=1 B=2   6: W=1 B=1   -1: automatic (same as eqlinear_forward).
- * Shapes with C_in not a multiple of 16 bytes of channels use a generic kernel
- * with fewer shapes.  Results agree to fp32 rounding; other values ->
- * EQL_ERR_INVALID. */
+ * Tiles 7..13 are the shapes of tiles 0..6 on the kernel that runs the group
+ * DFT and its inverse as block-diagonal matrix-core products (bf16 plans with
+ * 2 <= N <= 8; other plans run tile - 7).  It rounds the transform
+ * coefficients and the Fourier-domain outputs to bf16, so its results differ
+ * from the other tiles by bf16 rounding; the automatic choice uses it where
+ * it applies.  Shapes with C_in not a multiple of 16 bytes of channels use a
+ * generic kernel with fewer shapes.  Other tile values -> EQL_ERR_INVALID. */
 eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                        void* y, int64_t T, void* stream, int tile);
 

@@ -89,7 +89,7 @@ def test_forward_sweep(eq, N, dt):
     for (C_in, C_out, T) in SHAPES:
         d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=N * 100 + C_in)
         ref = oracle.cn_dense(d["x64"], d["w64"])
-        for tile in range(-1, 7):
+        for tile in range(-1, 14):
             y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
             assert_close(y, ref, dt, f"N={N} {dt} C_in={C_in} C_out={C_out} T={T} tile={tile}")
 
@@ -98,11 +98,12 @@ def test_forward_sweep(eq, N, dt):
 @pytest.mark.parametrize("N,C_in,C_out,T", [
     (8, 96, 96, 1000), (7, 160, 160, 777), (8, 96, 384, 300), (8, 384, 96, 300),
     (4, 8, 8, 64), (8, 32, 32, 4096), (5, 64, 64, 129), (16, 48, 80, 97), (12, 20, 36, 200),
+    (6, 48, 40, 150), (3, 64, 24, 90), (2, 16, 48, 70),
 ])
 def test_forward_multi_tile_shapes(eq, N, C_in, C_out, T, dt):
     d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=7)
     ref = oracle.cn_dense(d["x64"], d["w64"])
-    for tile in range(-1, 7):
+    for tile in range(-1, 14):
         y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
         assert_close(y, ref, dt, f"N={N} {dt} {C_in}->{C_out} T={T} tile={tile}")
 
