@@ -31,6 +31,12 @@ hipError_t launch_cn_forward(int N, int dtype_bf16, const void* x, const void* w
 hipError_t launch_gemm_rows(int dtype_bf16, GemmJobs jobs, const void* x, const void* w, void* y,
                             int64_t T, int ldx, int ldy, hipStream_t stream);
 
+// bf16 D8 jobs on the dedicated kernel (16*cb output channels per workgroup);
+// hipErrorNotSupported when a job column, width or W row is not a whole number
+// of 16-byte pieces (then use launch_gemm_rows).
+hipError_t launch_d8_fast(GemmJobs jobs, const void* x, const void* w, void* y, int64_t T, int ldx, int ldy,
+                          int64_t w_elems, int cb, hipStream_t stream);
+
 hipError_t launch_weight_dft(int N, int dtype_bf16, const void* w, void* w_hat, int C_in,
                              int C_out, hipStream_t stream);
 

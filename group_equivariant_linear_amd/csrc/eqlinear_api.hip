@@ -179,6 +179,13 @@ eqlinear_status eqlinear_d8_forward(eqlinear_plan_t p, const void* x, const void
     for (int c = 0; c < 2; ++c)  // W_E on E coordinate 0 and 1
         jobs.j[4 + c] = eql::GemmJob{4 * mi + 2 * c * mi, 4 * mo + 2 * c * mo, 2 * mi, 2 * mo,
                                      e_off, 2 * mi, 0, 0, 0, 0};
+    if (p->dtype == EQL_BF16) {
+        // widest output tile that the 1-D blocks fill: 160, 80 or 32 channels
+        const int cb = mo % 160 == 0 ? 10 : (mo % 80 == 0 ? 5 : 2);
+        const hipError_t e = eql::launch_d8_fast(jobs, x, wb, y, T, p->C_in, p->C_out,
+                                                 (int64_t)eqlinear_w_hat_elems(p), cb, (hipStream_t)stream);
+        if (e != hipErrorNotSupported) return hip_status(e);
+    }
     return hip_status(eql::launch_gemm_rows(p->dtype == EQL_BF16, jobs, x, wb, y, T, p->C_in,
                                             p->C_out, (hipStream_t)stream));
 }

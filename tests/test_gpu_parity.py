@@ -207,7 +207,8 @@ def run_d8(eq, C_in, C_out, T, dt, seed=0, inputs=None):
 
 @pytest.mark.parametrize("dt", [F32, BF16])
 @pytest.mark.parametrize("C_in,C_out,T", [(8, 8, 1), (16, 24, 33), (64, 64, 130), (160, 96, 257),
-                                          (256, 512, 100), (1280, 1280, 77)])
+                                          (256, 512, 100), (1280, 1280, 77), (512, 320, 97),
+                                          (192, 640, 200)])
 def test_d8_forward(eq, C_in, C_out, T, dt):
     y, d = run_d8(eq, C_in, C_out, T, dt, seed=C_in)
     ref = oracle.d8_dense(d["x64"], d["w64"], C_out)
