@@ -35,7 +35,8 @@ KERNEL_SOURCES = {
           "group_equivariant_linear_amd/csrc/cn_mf.h",
           "group_equivariant_linear_amd/csrc/cn_dispatch.h",
           "group_equivariant_linear_amd/csrc/eq_device.h"],
-    "D8": ["group_equivariant_linear_amd/csrc/gemm_rows.hip",
+    "D8": ["group_equivariant_linear_amd/csrc/d8_forward.hip",
+           "group_equivariant_linear_amd/csrc/gemm_rows.hip",
            "group_equivariant_linear_amd/csrc/eq_device.h"],
 }
 
@@ -43,7 +44,8 @@ KERNEL_SOURCES = {
 def step_kernel_name(wl):
     """The kernel one forward of this workload launches (automatic tile choice)."""
     if wl.group != "C":
-        return "gemm_rows_kernel"
+        whole = (wl.C_in // 8) % 8 == 0 and (wl.C_out // 8) % 8 == 0  # block columns in 16-byte pieces
+        return "d8_kernel" if wl.dtype == "bf16" and whole else "gemm_rows_kernel"
     return "cn_mf_kernel" if wl.dtype == "bf16" and 2 <= wl.N <= 8 else "cn_fast_kernel"
 
 
@@ -249,7 +251,7 @@ def _run_oracle(wl, d, n):
         oracle.d8_dense(d["x64"][:n], d["w64"], wl.C_out)
 
 
-STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "gemm_rows_kernel")
+STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "d8_kernel", "gemm_rows_kernel")
 TRAFFIC_WARM = 5   # back-to-back forwards (inputs partly cached from the previous launch)
 TRAFFIC_COLD = 5   # forwards each after a 512 MiB read that evicts the L2s
 TRAFFIC_COPIES = 5
