@@ -77,23 +77,12 @@ __device__ __forceinline__ int ypiece(int r, int k) {
     else return r * P + k;
 }
 
+// One tile: tokens t0 .. t0+TT-1, output channels n0 .. n0+CT-1 of job.
 template <class C>
-__global__ __launch_bounds__(C::kThreads) void d8_kernel(GemmJobs jobs, const __bf16* __restrict__ x,
-                                                         const __bf16* __restrict__ w, __bf16* __restrict__ y,
-                                                         int64_t T, int ldx, int ldy, uint32_t total_tiles,
-                                                         uint32_t w_bytes) {
+__device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, const __bf16* __restrict__ x,
+                                        const __bf16* __restrict__ w, __bf16* __restrict__ y, int64_t T, int ldx,
+                                        int ldy, uint32_t w_bytes, char* smem) {
     constexpr int TPW = C::TPW, NPW = C::NPW;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-
-    const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
-    const int64_t t0 = (int64_t)(tile / jobs.tiles_per_row) * C::TT;
-    const int jt = (int)(tile % jobs.tiles_per_row);
-    int ji = 0;
-#pragma unroll
-    for (int j = 1; j < kMaxGemmJobs; ++j)
-        if (j < jobs.njobs && jt >= jobs.j[j].tile_begin) ji = j;
-    const GemmJob job = jobs.j[ji];
-    const int n0 = (jt - job.tile_begin) * C::CT;
     const int K = job.K, Nn = job.Nn;
 
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -225,19 +214,47 @@ __global__ __launch_bounds__(C::kThreads) void d8_kernel(GemmJobs jobs, const __
     }
 }
 
-template <class C>
+// Workgroups take one tile each.  Jobs flagged narrow (the ones with twice the
+// input channels: W_E on an E coordinate) use the CN shape, the others CW, so
+// that every workgroup has the same number of products.
+template <class CW, class CN>
+__global__ __launch_bounds__(CW::kThreads) void d8_kernel(GemmJobs jobs, const __bf16* __restrict__ x,
+                                                          const __bf16* __restrict__ w, __bf16* __restrict__ y,
+                                                          int64_t T, int ldx, int ldy, uint32_t total_tiles,
+                                                          uint32_t w_bytes) {
+    static_assert(CW::TT == CN::TT && CW::kThreads == CN::kThreads, "one workgroup shape");
+    __shared__ __attribute__((aligned(16))) char smem[CW::LDS > CN::LDS ? CW::LDS : CN::LDS];
+
+    const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
+    const int64_t t0 = (int64_t)(tile / jobs.tiles_per_row) * CW::TT;
+    const int jt = (int)(tile % jobs.tiles_per_row);
+    int ji = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxGemmJobs; ++j)
+        if (j < jobs.njobs && jt >= jobs.j[j].tile_begin) ji = j;
+    const GemmJob job = jobs.j[ji];
+    if (job.narrow)
+        d8_tile<CN>(job, (jt - job.tile_begin) * CN::CT, t0, x, w, y, T, ldx, ldy, w_bytes, smem);
+    else
+        d8_tile<CW>(job, (jt - job.tile_begin) * CW::CT, t0, x, w, y, T, ldx, ldy, w_bytes, smem);
+}
+
+template <class CW, class CN>
 hipError_t launch_d8_cfg(GemmJobs jobs, const void* x, const void* w, void* y, int64_t T, int ldx, int ldy,
                          int64_t w_elems, hipStream_t stream) {
+    int kmin = jobs.j[0].K;
+    for (int j = 1; j < jobs.njobs; ++j) kmin = jobs.j[j].K < kmin ? jobs.j[j].K : kmin;
     int tiles = 0;
     for (int j = 0; j < jobs.njobs; ++j) {
+        jobs.j[j].narrow = (kmin > 0 && jobs.j[j].K >= 2 * kmin) ? 1 : 0;
         jobs.j[j].tile_begin = tiles;
-        tiles += (jobs.j[j].Nn + C::CT - 1) / C::CT;
+        tiles += (jobs.j[j].Nn + (jobs.j[j].narrow ? CN::CT : CW::CT) - 1) / (jobs.j[j].narrow ? CN::CT : CW::CT);
     }
     for (int j = jobs.njobs; j < kMaxGemmJobs; ++j) jobs.j[j] = jobs.j[0];
     jobs.tiles_per_row = tiles;
-    const int64_t total = (T + C::TT - 1) / C::TT * tiles;
+    const int64_t total = (T + CW::TT - 1) / CW::TT * tiles;
     if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((d8_kernel<C>), dim3((uint32_t)total), dim3(C::kThreads), 0, stream, jobs,
+    hipLaunchKernelGGL((d8_kernel<CW, CN>), dim3((uint32_t)total), dim3(CW::kThreads), 0, stream, jobs,
                        (const __bf16*)x, (const __bf16*)w, (__bf16*)y, T, ldx, ldy, (uint32_t)total,
                        (uint32_t)(w_elems * 2));
     return hipGetLastError();
@@ -257,10 +274,16 @@ hipError_t launch_d8_fast(GemmJobs jobs, const void* x, const void* w, void* y, 
         const GemmJob& g = jobs.j[j];
         if (g.x_col % 8 || g.y_col % 8 || g.K % 8 || g.Nn % 8 || g.ldw % 8 || g.w_off % 8) return hipErrorNotSupported;
     }
+    // 128 tokens x 160 channels (2x2 waves), or x 80 channels (4x1 waves) for
+    // the jobs with twice the input channels; the smaller shapes use one tile
+    // for every job
+    using Wide = D8Cfg<2, 2, 4, 5, 2>;
+    using Narrow = D8Cfg<4, 1, 2, 5, 2>;
+    using Small = D8Cfg<4, 1, 1, 2, 2>;
     switch (cb) {
-        case 5: return launch_d8_cfg<D8Cfg<2, 1, 4, 5, 2>>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
-        case 2: return launch_d8_cfg<D8Cfg<4, 1, 1, 2, 2>>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
-        default: return launch_d8_cfg<D8Cfg<2, 2, 4, 5, 2>>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
+        case 5: return launch_d8_cfg<D8Cfg<2, 1, 4, 5, 2>, D8Cfg<2, 1, 4, 5, 2>>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
+        case 2: return launch_d8_cfg<Small, Small>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
+        default: return launch_d8_cfg<Wide, Narrow>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
     }
 }
 

@@ -16,6 +16,7 @@ struct GemmJob {
     int ldw;
     int tile_begin;  // first column tile of this job (filled by the launcher)
     int x_vec_ok, w_vec_ok, y_vec_ok;  // 16-byte (8-byte for bf16 y) access allowed
+    int narrow;      // D8 kernel: narrower output tile for this job (filled by the launcher)
 };
 
 struct GemmJobs {
