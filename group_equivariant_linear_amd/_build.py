@@ -17,10 +17,15 @@ ARCH = "gfx950"
 # Packed-fp32 VALU ops are disabled: the plain scalar forms are used everywhere.
 # MFMA results live in ordinary VGPRs (gfx950 allows it): no copies between the
 # accumulation registers and the VALU, and fewer registers in all.
+# The first 16 dwords of kernel arguments are preloaded into SGPRs at wave
+# launch (gfx950 supports it; the code object keeps a loading prologue for
+# firmware that does not), instead of scalar loads whose round trips the
+# compiler otherwise spreads over the kernel's first instructions.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

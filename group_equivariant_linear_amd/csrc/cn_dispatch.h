@@ -1,12 +1,20 @@
 // cn_dispatch.h -- tile choice and dispatch of the C_N forward kernels.
 #pragma once
 
+#include <type_traits>
+
 #include "cn_fused.h"
 #include "cn_mf.h"
+#include "cn_split.h"
 
 namespace eql {
 
-constexpr int kMfFirstTile = 7;  // tiles 7..13: entries 0..6 on the matrix-core transform kernel
+constexpr int kMfFirstTile = 7;     // tiles 7..13: entries 0..6 on the matrix-core transform kernel
+constexpr int kSplitFirstTile = 14;  // tiles 14, 15: fp32, input channels split over 2 or 4 waves
+
+#ifndef EQL_SPLIT_AUTO_KS
+#define EQL_SPLIT_AUTO_KS 2
+#endif
 
 // Automatic choice (from tile sweeps on MI355X): 4-wave workgroups with the
 // widest output tile that keeps two workgroups per CU (about 24/N output blocks:
@@ -30,14 +38,32 @@ int choose_shape(int64_t T, int C_in, int C_out) {
 template <int N, typename IO>
 int choose_fused(int64_t T, int C_in, int C_out) {
     // bf16 orders up to 8 take the matrix-core transform kernel, same shapes
-    if constexpr (mf_supported<N, IO>) return kMfFirstTile + choose_shape<N>(T, C_in, C_out);
-    else return choose_shape<N>(T, C_in, C_out);
+    if constexpr (mf_supported<N, IO>) {
+        return kMfFirstTile + choose_shape<N>(T, C_in, C_out);
+    } else {
+        const int s = choose_shape<N>(T, C_in, C_out);
+        // fp32 layers too small for one wave per SIMD at 16 x 16 per wave: split
+        // the input channels of each such tile over 2 or 4 waves
+        if constexpr (std::is_same_v<IO, float>)
+            if (s == 6 && split_ok<N>(C_in, C_out)) return kSplitFirstTile + (EQL_SPLIT_AUTO_KS == 4 ? 1 : 0);
+        return s;
+    }
 }
 
 template <int N, typename IO>
 hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
                         hipStream_t stream, int tile) {
-    const int i = tile >= 0 ? tile : choose_fused<N, IO>(T, C_in, C_out);
+    int i = tile >= 0 ? tile : choose_fused<N, IO>(T, C_in, C_out);
+    if (i >= kSplitFirstTile) {
+        if constexpr (std::is_same_v<IO, float>) {
+            if (split_ok<N>(C_in, C_out)) {
+                // four channels per lane run out of registers past N = 12
+                if (i == kSplitFirstTile && N <= 12) return launch_split<N, 2>(x, w_hat, y, T, C_in, C_out, stream);
+                return launch_split<N, 4>(x, w_hat, y, T, C_in, C_out, stream);
+            }
+        }
+        i = kMfFirstTile + 6;  // one-wave shape of the other kernels
+    }
     if (i >= kMfFirstTile) {
         switch (i - kMfFirstTile) {
 #define EQL_MF(k)                                                                       \

@@ -1,0 +1,336 @@
+// cn_split.h -- fp32 C_N forward with the input channels split over waves.
+//
+// Same computation as the fused kernels ("Flash EQ-Linear", Algorithmic Approach
+// and Implementation: real DFT along the group axis, per-frequency channel
+// products over the kept bins, inverse DFT, all in one launch), arranged for
+// layers too small to give every SIMD a wave when one wave owns a 16-token x
+// 16-channel tile (few tokens, few output channels; fp32 products on the matrix
+// cores run at 1/16 of the bf16 rate, so they dominate such layers).
+//
+// A workgroup owns 16 tokens and CT = 16*OB output channels.  Its OB*KS waves
+// each take one 16-channel output block and one of KS slices of every step of
+// input channels: a wave loads (through a shared, coalesced LDS tile) and
+// transforms only its slice of the x records, and multiplies it with its block's
+// weights.  The KS partial spectra of a block are then summed through LDS in a
+// fixed order (each wave finishes 4/KS of the accumulator rows of its block),
+// inverse-transformed, staged in LDS and written as contiguous 16-byte pieces.
+//
+// Complex bins use three real products instead of four (Gauss's method):
+//   t1 = Xr Wr^T, t2 = Xi Wi^T, t3 = (Xr + Xi)(Wr + Wi)^T,
+//   Re = t1 - t2, Im = t3 - t1 - t2.
+#pragma once
+
+#include "cn_fused.h"
+
+namespace eql {
+
+#ifndef EQL_SPLIT_GAUSS
+#define EQL_SPLIT_GAUSS 1
+#endif
+
+template <int N_, int OB_, int KS_, int R_>
+struct SplitCfg {
+    static constexpr int N = N_, OB = OB_, KS = KS_, R = R_;
+    static constexpr int H = (N - 1) / 2;  // complex bins
+    static constexpr bool GAUSS = EQL_SPLIT_GAUSS != 0 && H > 0;
+    static constexpr int kWaves = OB * KS, kThreads = 64 * kWaves;
+    static constexpr int TT = 16, CT = 16 * OB;
+    static constexpr int KW = 4 * R;          // channels of one wave per step (R per lane)
+    static constexpr int KSTEP = KS * KW;     // channels per step
+    static constexpr int XP = KSTEP * N / 4;  // 16-byte pieces of one token row of a step
+    static constexpr bool XROT = XP % 8 == 0;
+    static constexpr int XPITCH = XROT ? XP : (XP | 1);
+    static constexpr int XBUF = 16 * XPITCH * 16;
+    static constexpr int XL = (16 * XP + kThreads - 1) / kThreads;  // x loads per thread per step
+    static constexpr int ROWS = 4 / KS;                // accumulator rows each wave finishes
+    static constexpr int RED = N * 4 * 64 * 4;           // one wave's partial spectra
+    static constexpr int YOFF = kWaves * RED;            // y staging, after the partials
+    static constexpr int YROW = CT * N * 4;
+    static constexpr int YP = YROW / 16;
+    static constexpr bool YROT = YP % 8 == 0;
+    static constexpr int YPITCH = YROT ? YP : (YP | 1);
+    static constexpr int YST = 16 * YPITCH * 16;
+    // the x tiles of the main loop overlap the partials and the y staging
+    static constexpr int LDS = 2 * XBUF > YOFF + YST ? 2 * XBUF : YOFF + YST;
+    static_assert(4 % KS == 0, "KS divides the 4 accumulator rows");
+    static_assert(R == 2 || R == 4, "two or four channels per lane");
+    static_assert(YROW % 16 == 0, "tile rows are whole pieces");
+};
+
+// LDS barrier without the wait on outstanding global loads that __syncthreads
+// implies (those loads are the next step's prefetch).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
+    const float* __restrict__ x, const float* __restrict__ w_hat, float* __restrict__ y, int64_t T,
+    int C_in, int C_out, int n_c_tiles, uint32_t total_tiles, uint32_t w_bytes, int y_coalesced) {
+    constexpr int N = C::N, R = C::R, H = C::H, XP = C::XP;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+    const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
+    const int64_t t0 = (int64_t)(tile / n_c_tiles) * C::TT;
+    const int o0 = (int)(tile % n_c_tiles) * C::CT;
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ob = wave % C::OB, kh = wave / C::OB;
+    const int q = lane >> 4, l16 = lane & 15;
+
+    const uint32_t row_x = (uint32_t)C_in * (N * 4), row_y = (uint32_t)C_out * (N * 4);
+    const int64_t rem = T - t0;
+    const uint32_t rows = (uint32_t)(rem < C::TT ? rem : C::TT);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + t0 * C_in * N, rows * row_x);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + t0 * C_out * N, rows * row_y);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_hat, w_bytes);
+
+    const int steps = (C_in + C::KSTEP - 1) / C::KSTEP;
+    const uint32_t step_x = (uint32_t)C::KSTEP * (N * 4);
+
+    // x tile of a step: piece pc = tid + j*kThreads is piece k of token row r
+    uint32_t xoff[C::XL];
+#pragma unroll
+    for (int j = 0; j < C::XL; ++j) {
+        const int pc = tid + j * C::kThreads, r = pc / XP, k = pc % XP;
+        xoff[j] = pc < 16 * XP ? (uint32_t)r * row_x + (uint32_t)k * 16u : kOOB;
+    }
+    auto load_x = [&](int s, u32x4 (&xr)[C::XL]) {
+        const int left = C_in - s * C::KSTEP;  // channels of this step that exist
+        const uint32_t valid = left > 0 ? (uint32_t)left * (N * 4) : 0u;
+#pragma unroll
+        for (int j = 0; j < C::XL; ++j) {
+            const int k = (tid + j * C::kThreads) % XP;
+            const uint32_t off = (uint32_t)k * 16u < valid ? xoff[j] : kOOB;
+            xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, (uint32_t)s * step_x, 0);
+        }
+    };
+
+    // B fragments (weights): lane (column l16, k-group q) holds channels
+    // ch .. ch+R-1 of output row orow in every plane
+    const int orow = o0 + ob * 16 + l16;
+    const int ch_lane = kh * C::KW + q * R;
+    const uint32_t plane_w = (uint32_t)C_out * (uint32_t)C_in * 4u;
+    const uint32_t wbase = (uint32_t)orow * (uint32_t)C_in * 4u + (uint32_t)ch_lane * 4u;
+    auto load_w = [&](int s, float (&B)[N][R]) {
+        const bool ok = orow < C_out && s * C::KSTEP + ch_lane < C_in;
+        const uint32_t soff = (uint32_t)(s * C::KSTEP) * 4u;
+#pragma unroll
+        for (int p = 0; p < N; ++p) {
+            const uint32_t off = ok ? wbase + (uint32_t)p * plane_w : kOOB;
+            if constexpr (R == 4) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off, soff, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) B[p][r] = __uint_as_float(v[r]);
+            } else {
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, off, soff, 0);
+                B[p][0] = __uint_as_float(v[0]);
+                B[p][1] = __uint_as_float(v[1]);
+            }
+        }
+    };
+
+    f32x4 acc[N];
+    f32x4 gs[H > 0 ? H : 1];  // Gauss: (Xr + Xi)(Wr + Wi) per complex bin
+#pragma unroll
+    for (int p = 0; p < N; ++p) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < (H > 0 ? H : 1); ++k) gs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 xr[C::XL];
+    float Bn[N][R];
+    load_x(0, xr);
+    __builtin_amdgcn_sched_barrier(0);  // x first: it is needed first
+    load_w(0, Bn);
+    int s = 0;  // C_in >= 1: at least one step, no branch ahead of the first loads
+    do {
+        char* xbuf = smem + (s & 1) * C::XBUF;
+#pragma unroll
+        for (int j = 0; j < C::XL; ++j) {
+            const int pc = tid + j * C::kThreads;
+            if (16 * XP % C::kThreads != 0 && pc >= 16 * XP) continue;
+            *reinterpret_cast<u32x4*>(xbuf + xpiece<C::XROT, XP, C::XPITCH>(pc / XP, pc % XP) * 16) = xr[j];
+        }
+        float B[N][R];
+#pragma unroll
+        for (int p = 0; p < N; ++p)
+#pragma unroll
+            for (int r = 0; r < R; ++r) B[p][r] = Bn[p][r];
+        // next step's loads (past the last step: offsets out of range, no access)
+        load_x(s + 1, xr);
+        if (s + 1 < steps) load_w(s + 1, Bn);
+        lds_barrier();
+
+        // this lane's records: token row l16, channels ch_lane .. ch_lane+R-1
+        float rec[R * N];
+        const int byte0 = ch_lane * N * 4;
+        if constexpr ((R * N) % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < R * N / 4; ++j) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(
+                    xbuf + xpiece<C::XROT, XP, C::XPITCH>(l16, byte0 / 16 + j) * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rec[4 * j + e] = __uint_as_float(v[e]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < R * N / 2; ++j) {
+                const int b = byte0 + 8 * j;
+                const u32x2 v = *reinterpret_cast<const u32x2*>(
+                    xbuf + xpiece<C::XROT, XP, C::XPITCH>(l16, b / 16) * 16 + (b % 16));
+                rec[2 * j] = __uint_as_float(v[0]);
+                rec[2 * j + 1] = __uint_as_float(v[1]);
+            }
+        }
+        float A[N][R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float xv[N], P[N];
+#pragma unroll
+            for (int h = 0; h < N; ++h) xv[h] = rec[r * N + h];
+            rdft_forward<N>(xv, P);
+#pragma unroll
+            for (int p = 0; p < N; ++p) A[p][r] = P[p];
+        }
+        // all records transformed before the products start: the MFMAs then
+        // issue back to back instead of waiting on each record's LDS read
+        __builtin_amdgcn_sched_barrier(0);
+
+        // products: consecutive MFMAs go to different accumulators
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[0][r], B[0][r], acc[0], 0, 0, 0);
+            if constexpr (N % 2 == 0 && N > 1)
+                acc[N - 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[N - 1][r], B[N - 1][r], acc[N - 1], 0, 0, 0);
+#pragma unroll
+            for (int k = 1; k <= H; ++k) {
+                const int pr = 2 * k - 1, pi = 2 * k;
+                if constexpr (C::GAUSS) {
+                    acc[pr] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pr][r], B[pr][r], acc[pr], 0, 0, 0);
+                    acc[pi] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pi][r], B[pi][r], acc[pi], 0, 0, 0);
+                    gs[k - 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pr][r] + A[pi][r], B[pr][r] + B[pi][r],
+                                                                     gs[k - 1], 0, 0, 0);
+                } else {
+                    acc[pr] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pr][r], B[pr][r], acc[pr], 0, 0, 0);
+                    acc[pi] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pr][r], B[pi][r], acc[pi], 0, 0, 0);
+                    acc[pr] = __builtin_amdgcn_mfma_f32_16x16x4f32(-A[pi][r], B[pi][r], acc[pr], 0, 0, 0);
+                    acc[pi] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pi][r], B[pr][r], acc[pi], 0, 0, 0);
+                }
+            }
+        }
+    } while (++s < steps);
+    if constexpr (C::GAUSS) {
+#pragma unroll
+        for (int k = 1; k <= H; ++k) {
+            const f32x4 t1 = acc[2 * k - 1], t2 = acc[2 * k];
+            acc[2 * k - 1] = t1 - t2;
+            acc[2 * k] = gs[k - 1] - t1 - t2;
+        }
+    }
+
+    // Sum the KS partial spectra of each block through LDS: every wave leaves
+    // all its accumulator rows there, and row i is finished by the wave with
+    // kh == i / ROWS, adding the KS partials in order (no per-lane selects).
+    __syncthreads();  // the partials and the y staging overwrite the x tiles
+    {
+        float* mine = reinterpret_cast<float*>(smem + wave * C::RED);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int p = 0; p < N; ++p) mine[(i * N + p) * 64 + lane] = acc[p][i];
+    }
+    __syncthreads();
+    const float* red = reinterpret_cast<const float*>(smem) + ob * (C::RED / 4) + kh * C::ROWS * N * 64 + lane;
+    float P[C::ROWS][N];
+#pragma unroll
+    for (int ii = 0; ii < C::ROWS; ++ii)
+#pragma unroll
+        for (int p = 0; p < N; ++p) {
+            float v = red[(ii * N + p) * 64];
+#pragma unroll
+            for (int src = 1; src < C::KS; ++src) v += red[src * C::OB * (C::RED / 4) + (ii * N + p) * 64];
+            P[ii][p] = v;
+        }
+
+    // Epilogue: inverse DFT of each finished (token, channel) record, y written once.
+    if (y_coalesced) {
+        char* yst = smem + C::YOFF;
+#pragma unroll
+        for (int ii = 0; ii < C::ROWS; ++ii) {
+            const int tl = q * 4 + kh * C::ROWS + ii, ol = ob * 16 + l16;
+            float yv[N];
+            rdft_inverse<N>(P[ii], yv);
+            const int byte0 = ol * N * 4;
+            if constexpr (N % 4 == 0) {
+#pragma unroll
+                for (int j = 0; j < N / 4; ++j)
+                    *reinterpret_cast<u32x4*>(yst + xpiece<C::YROT, C::YP, C::YPITCH>(tl, byte0 / 16 + j) * 16) =
+                        u32x4{__float_as_uint(yv[4 * j]), __float_as_uint(yv[4 * j + 1]),
+                              __float_as_uint(yv[4 * j + 2]), __float_as_uint(yv[4 * j + 3])};
+            } else {
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    const int b = byte0 + 4 * e;
+                    *reinterpret_cast<float*>(yst + xpiece<C::YROT, C::YP, C::YPITCH>(tl, b / 16) * 16 + (b % 16)) =
+                        yv[e];
+                }
+            }
+        }
+        __syncthreads();
+        const int left = C_out - o0;
+        const uint32_t cols = (uint32_t)(left < C::CT ? left : C::CT) * (N * 4);  // valid bytes of a tile row
+        for (int pc = tid; pc < 16 * C::YP; pc += C::kThreads) {
+            const int r = pc / C::YP, k = pc % C::YP;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(yst + xpiece<C::YROT, C::YP, C::YPITCH>(r, k) * 16);
+            const uint32_t off = (uint32_t)k * 16u < cols
+                                     ? (uint32_t)r * row_y + (uint32_t)o0 * (N * 4) + (uint32_t)k * 16u
+                                     : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int ii = 0; ii < C::ROWS; ++ii) {
+            const uint32_t tl = (uint32_t)(q * 4 + kh * C::ROWS + ii);
+            const uint32_t off = orow < C_out ? tl * row_y + (uint32_t)orow * (N * 4) : kOOB;
+            float yv[N];
+            rdft_inverse<N>(P[ii], yv);
+#pragma unroll
+            for (int e = 0; e < N; ++e)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[e]), ry, off + 4u * e, 0, 0);
+        }
+    }
+}
+
+// Whole 16-byte pieces of x rows and 32-bit buffer offsets.
+template <int N>
+bool split_ok(int C_in, int C_out) {
+    const int64_t lim = (int64_t)1 << 30;
+    return C_in % 4 == 0 && (int64_t)N * C_out * C_in * 4 < lim && (int64_t)16 * C_in * N * 4 < lim &&
+           (int64_t)16 * C_out * N * 4 < lim;
+}
+
+template <class C>
+hipError_t launch_split_cfg(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
+                            hipStream_t stream) {
+    const int64_t n_t = (T + C::TT - 1) / C::TT;
+    const int n_c = (C_out + C::CT - 1) / C::CT;
+    const int64_t total = n_t * n_c;
+    if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int64_t w_bytes = (int64_t)C::N * C_out * C_in * 4;
+    const int y_coalesced = ((int64_t)C_out * C::N * 4) % 16 == 0;
+    hipLaunchKernelGGL((cn_split_kernel<C>), dim3((uint32_t)total), dim3(C::kThreads), 0, stream,
+                       (const float*)x, (const float*)w_hat, (float*)y, T, C_in, C_out, n_c, (uint32_t)total,
+                       (uint32_t)w_bytes, y_coalesced);
+    return hipGetLastError();
+}
+
+// KS input-channel slices: 2 (four channels per lane) or 4 (two per lane); one
+// output block per workgroup when C_out fits in 16 channels, else two.
+template <int N, int KS>
+hipError_t launch_split(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
+                        hipStream_t stream) {
+    constexpr int R = KS == 2 ? 4 : 2;
+    if (C_out <= 16) return launch_split_cfg<SplitCfg<N, 1, KS, R>>(x, w_hat, y, T, C_in, C_out, stream);
+    return launch_split_cfg<SplitCfg<N, 2, KS, R>>(x, w_hat, y, T, C_in, C_out, stream);
+}
+
+}  // namespace eql

@@ -291,7 +291,8 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t id, uint32_t total) {
     constexpr uint32_t kXcd = 8;
     uint32_t xcd = id % kXcd, local = id / kXcd;
     uint32_t q = total / kXcd, r = total % kXcd;
-    uint32_t base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+    // XCDs below r take q + 1 tiles, the others q (branch-free form)
+    uint32_t base = xcd * q + (xcd < r ? xcd : r);
     return base + local;
 }
 

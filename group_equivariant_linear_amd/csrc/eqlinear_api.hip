@@ -149,7 +149,7 @@ eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t p, const void* x, const v
     const size_t xb = (size_t)T * in_width(p) * es, yb = (size_t)T * out_width(p) * es;
     const size_t wb = eqlinear_w_hat_elems(p) * es;
     if (overlaps(x, xb, y, yb) || overlaps(w_hat, wb, y, yb)) return EQL_ERR_INVALID;
-    if (tile < -1 || tile > 13) return EQL_ERR_INVALID;
+    if (tile < -1 || tile > 15) return EQL_ERR_INVALID;
     return hip_status(eql::launch_cn_forward(p->N, p->dtype == EQL_BF16, x, w_hat, y, T, p->C_in,
                                              p->C_out, (hipStream_t)stream, tile));
 }

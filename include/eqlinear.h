@@ -140,8 +140,15 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
  * 2 <= N <= 8; other plans run tile - 7).  It rounds the transform
  * coefficients and the Fourier-domain outputs to bf16, so its results differ
  * from the other tiles by bf16 rounding; the automatic choice uses it where
- * it applies.  Shapes with C_in not a multiple of 16 bytes of channels use a
- * generic kernel with fewer shapes.  Other tile values -> EQL_ERR_INVALID. */
+ * it applies.  Tiles 14 and 15 (fp32 plans, C_in a multiple of 4; other
+ * plans and shapes run tile 13) cover 16 tokens and 32 output channels (16
+ * when C_out <= 16) with the input channels of every step split over 2 or 4
+ * waves per output block, whose partial spectra are summed in a fixed order;
+ * complex bins use three real products instead of four (Gauss's method), so
+ * their results differ from the other tiles by fp32 rounding.  The automatic
+ * choice uses tile 14 for fp32 layers too small for one wave per SIMD.  Shapes
+ * with C_in not a multiple of 16 bytes of channels use a generic kernel with
+ * fewer shapes.  Other tile values -> EQL_ERR_INVALID. */
 eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                        void* y, int64_t T, void* stream, int tile);
 

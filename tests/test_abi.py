@@ -119,7 +119,7 @@ def test_forward_validation_before_any_hip_call(eq):
     assert lib.eqlinear_forward(h, A, W, A, 5, None) == eq.EQL_ERR_INVALID      # y aliases x
     assert lib.eqlinear_forward(h, A, W, A + 256, 5, None) == eq.EQL_ERR_INVALID  # overlap
     assert lib.eqlinear_forward(h, A, W, W, 5, None) == eq.EQL_ERR_INVALID      # y aliases w_hat
-    assert lib.eqlinear_forward_tiled(h, A, W, B, 5, None, 14) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_forward_tiled(h, A, W, B, 5, None, 16) == eq.EQL_ERR_INVALID
     assert lib.eqlinear_forward_tiled(h, A, W, B, 5, None, -2) == eq.EQL_ERR_INVALID
     d8 = eq.eqlinear_d8_plan(16, 16, eq.EQL_F32)
     assert lib.eqlinear_forward(d8.handle, A, W, B, 5, None) == eq.EQL_ERR_INVALID  # wrong kind

@@ -89,7 +89,7 @@ def test_forward_sweep(eq, N, dt):
     for (C_in, C_out, T) in SHAPES:
         d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=N * 100 + C_in)
         ref = oracle.cn_dense(d["x64"], d["w64"])
-        for tile in range(-1, 14):
+        for tile in range(-1, 16):
             y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
             assert_close(y, ref, dt, f"N={N} {dt} C_in={C_in} C_out={C_out} T={T} tile={tile}")
 
@@ -103,7 +103,7 @@ def test_forward_sweep(eq, N, dt):
 def test_forward_multi_tile_shapes(eq, N, C_in, C_out, T, dt):
     d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=7)
     ref = oracle.cn_dense(d["x64"], d["w64"])
-    for tile in range(-1, 14):
+    for tile in range(-1, 16):
         y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
         assert_close(y, ref, dt, f"N={N} {dt} {C_in}->{C_out} T={T} tile={tile}")
 
