@@ -11,6 +11,7 @@ namespace eql {
 
 constexpr int kMfFirstTile = 7;     // tiles 7..13: entries 0..6 on the matrix-core transform kernel
 constexpr int kSplitFirstTile = 14;  // tiles 14, 15: fp32, input channels split over 2 or 4 waves
+constexpr int kSplitMaxN = 10;       // larger orders: the split kernel's registers do not fit
 
 #ifndef EQL_SPLIT_AUTO_KS
 #define EQL_SPLIT_AUTO_KS 2
@@ -44,7 +45,7 @@ int choose_fused(int64_t T, int C_in, int C_out) {
         const int s = choose_shape<N>(T, C_in, C_out);
         // fp32 layers too small for one wave per SIMD at 16 x 16 per wave: split
         // the input channels of each such tile over 2 or 4 waves
-        if constexpr (std::is_same_v<IO, float>)
+        if constexpr (std::is_same_v<IO, float> && N <= kSplitMaxN)
             if (s == 6 && split_ok<N>(C_in, C_out)) return kSplitFirstTile + (EQL_SPLIT_AUTO_KS == 4 ? 1 : 0);
         return s;
     }
@@ -55,10 +56,9 @@ hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, in
                         hipStream_t stream, int tile) {
     int i = tile >= 0 ? tile : choose_fused<N, IO>(T, C_in, C_out);
     if (i >= kSplitFirstTile) {
-        if constexpr (std::is_same_v<IO, float>) {
+        if constexpr (std::is_same_v<IO, float> && N <= kSplitMaxN) {
             if (split_ok<N>(C_in, C_out)) {
-                // four channels per lane run out of registers past N = 12
-                if (i == kSplitFirstTile && N <= 12) return launch_split<N, 2>(x, w_hat, y, T, C_in, C_out, stream);
+                if (i == kSplitFirstTile) return launch_split<N, 2>(x, w_hat, y, T, C_in, C_out, stream);
                 return launch_split<N, 4>(x, w_hat, y, T, C_in, C_out, stream);
             }
         }

@@ -44,14 +44,14 @@ struct SplitCfg {
     static constexpr int XL = (16 * XP + kThreads - 1) / kThreads;  // x loads per thread per step
     static constexpr int ROWS = 4 / KS;                // accumulator rows each wave finishes
     static constexpr int RED = N * 4 * 64 * 4;           // one wave's partial spectra
-    static constexpr int YOFF = kWaves * RED;            // y staging, after the partials
     static constexpr int YROW = CT * N * 4;
     static constexpr int YP = YROW / 16;
     static constexpr bool YROT = YP % 8 == 0;
     static constexpr int YPITCH = YROT ? YP : (YP | 1);
     static constexpr int YST = 16 * YPITCH * 16;
-    // the x tiles of the main loop overlap the partials and the y staging
-    static constexpr int LDS = 2 * XBUF > YOFF + YST ? 2 * XBUF : YOFF + YST;
+    // the y staging overlaps the x tiles (both at offset 0); the partials follow
+    static constexpr int PART_OFF = 2 * XBUF > YST ? 2 * XBUF : YST;
+    static constexpr int LDS = PART_OFF + kWaves * RED;
     static_assert(4 % KS == 0, "KS divides the 4 accumulator rows");
     static_assert(R == 2 || R == 4, "two or four channels per lane");
     static_assert(YROW % 16 == 0, "tile rows are whole pieces");
@@ -137,12 +137,16 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
     for (int k = 0; k < (H > 0 ? H : 1); ++k) gs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x4 xr[C::XL];
-    float Bn[N][R];
+    float B0[N][R], B1[N][R];
     load_x(0, xr);
     __builtin_amdgcn_sched_barrier(0);  // x first: it is needed first
-    load_w(0, Bn);
-    int s = 0;  // C_in >= 1: at least one step, no branch ahead of the first loads
-    do {
+    load_w(0, B0);
+
+    // One step with weights B; the next step's weights load into Bnext.  VALU
+    // work placed between fp32 MFMAs stretches each of them by about half, so
+    // everything the products read (transforms, Gauss sums) is computed first
+    // and the products issue as one uninterrupted run.
+    auto step = [&](int s, const float (&B)[N][R], float (&Bnext)[N][R]) {
         char* xbuf = smem + (s & 1) * C::XBUF;
 #pragma unroll
         for (int j = 0; j < C::XL; ++j) {
@@ -150,14 +154,9 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
             if (16 * XP % C::kThreads != 0 && pc >= 16 * XP) continue;
             *reinterpret_cast<u32x4*>(xbuf + xpiece<C::XROT, XP, C::XPITCH>(pc / XP, pc % XP) * 16) = xr[j];
         }
-        float B[N][R];
-#pragma unroll
-        for (int p = 0; p < N; ++p)
-#pragma unroll
-            for (int r = 0; r < R; ++r) B[p][r] = Bn[p][r];
         // next step's loads (past the last step: offsets out of range, no access)
         load_x(s + 1, xr);
-        if (s + 1 < steps) load_w(s + 1, Bn);
+        if (s + 1 < steps) load_w(s + 1, Bnext);
         lds_barrier();
 
         // this lane's records: token row l16, channels ch_lane .. ch_lane+R-1
@@ -191,8 +190,22 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
 #pragma unroll
             for (int p = 0; p < N; ++p) A[p][r] = P[p];
         }
-        // all records transformed before the products start: the MFMAs then
-        // issue back to back instead of waiting on each record's LDS read
+        constexpr int HG = H > 0 ? H : 1;
+        float SA[HG][R], SB[HG][R];  // Gauss: Xr + Xi and Wr + Wi per complex bin (else -Xi in SA)
+        if constexpr (C::GAUSS) {
+#pragma unroll
+            for (int k = 1; k <= H; ++k)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    SA[k - 1][r] = A[2 * k - 1][r] + A[2 * k][r];
+                    SB[k - 1][r] = B[2 * k - 1][r] + B[2 * k][r];
+                }
+        } else {
+#pragma unroll
+            for (int k = 1; k <= H; ++k)
+#pragma unroll
+                for (int r = 0; r < R; ++r) SA[k - 1][r] = -A[2 * k][r];
+        }
         __builtin_amdgcn_sched_barrier(0);
 
         // products: consecutive MFMAs go to different accumulators
@@ -207,17 +220,26 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
                 if constexpr (C::GAUSS) {
                     acc[pr] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pr][r], B[pr][r], acc[pr], 0, 0, 0);
                     acc[pi] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pi][r], B[pi][r], acc[pi], 0, 0, 0);
-                    gs[k - 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pr][r] + A[pi][r], B[pr][r] + B[pi][r],
-                                                                     gs[k - 1], 0, 0, 0);
+                    gs[k - 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(SA[k - 1][r], SB[k - 1][r], gs[k - 1], 0, 0, 0);
                 } else {
+                    // Yr += Xr Wr - Xi Wi, Yi += Xr Wi + Xi Wr (SA holds -Xi)
                     acc[pr] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pr][r], B[pr][r], acc[pr], 0, 0, 0);
                     acc[pi] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pr][r], B[pi][r], acc[pi], 0, 0, 0);
-                    acc[pr] = __builtin_amdgcn_mfma_f32_16x16x4f32(-A[pi][r], B[pi][r], acc[pr], 0, 0, 0);
+                    acc[pr] = __builtin_amdgcn_mfma_f32_16x16x4f32(SA[k - 1][r], B[pi][r], acc[pr], 0, 0, 0);
                     acc[pi] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[pi][r], B[pr][r], acc[pi], 0, 0, 0);
                 }
             }
         }
-    } while (++s < steps);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // C_in >= 1: at least one step, no branch ahead of the first loads; the two
+    // weight buffers alternate without register copies
+    for (int s = 0;;) {
+        step(s, B0, B1);
+        if (++s >= steps) break;
+        step(s, B1, B0);
+        if (++s >= steps) break;
+    }
     if constexpr (C::GAUSS) {
 #pragma unroll
         for (int k = 1; k <= H; ++k) {
@@ -230,16 +252,19 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
     // Sum the KS partial spectra of each block through LDS: every wave leaves
     // all its accumulator rows there, and row i is finished by the wave with
     // kh == i / ROWS, adding the KS partials in order (no per-lane selects).
-    __syncthreads();  // the partials and the y staging overwrite the x tiles
+    // The partials have a region of their own, so they are written as soon as
+    // the products are done; the barrier after them also ends every wave's use
+    // of the x tiles, which the y staging then overwrites.
     {
-        float* mine = reinterpret_cast<float*>(smem + wave * C::RED);
+        float* mine = reinterpret_cast<float*>(smem + C::PART_OFF + wave * C::RED);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int p = 0; p < N; ++p) mine[(i * N + p) * 64 + lane] = acc[p][i];
     }
     __syncthreads();
-    const float* red = reinterpret_cast<const float*>(smem) + ob * (C::RED / 4) + kh * C::ROWS * N * 64 + lane;
+    const float* red =
+        reinterpret_cast<const float*>(smem + C::PART_OFF) + ob * (C::RED / 4) + kh * C::ROWS * N * 64 + lane;
     float P[C::ROWS][N];
 #pragma unroll
     for (int ii = 0; ii < C::ROWS; ++ii)
@@ -253,7 +278,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
 
     // Epilogue: inverse DFT of each finished (token, channel) record, y written once.
     if (y_coalesced) {
-        char* yst = smem + C::YOFF;
+        char* yst = smem;
 #pragma unroll
         for (int ii = 0; ii < C::ROWS; ++ii) {
             const int tl = q * 4 + kh * C::ROWS + ii, ol = ob * 16 + l16;
@@ -323,12 +348,13 @@ hipError_t launch_split_cfg(const void* x, const void* w_hat, void* y, int64_t T
     return hipGetLastError();
 }
 
-// KS input-channel slices: 2 (four channels per lane) or 4 (two per lane); one
-// output block per workgroup when C_out fits in 16 channels, else two.
+// KS input-channel slices: 2 (four channels per lane up to N = 8, else two) or
+// 4 (two per lane); one output block per workgroup when C_out fits in 16
+// channels, else two.
 template <int N, int KS>
 hipError_t launch_split(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
                         hipStream_t stream) {
-    constexpr int R = KS == 2 ? 4 : 2;
+    constexpr int R = (KS == 2 && N <= 8) ? 4 : 2;
     if (C_out <= 16) return launch_split_cfg<SplitCfg<N, 1, KS, R>>(x, w_hat, y, T, C_in, C_out, stream);
     return launch_split_cfg<SplitCfg<N, 2, KS, R>>(x, w_hat, y, T, C_in, C_out, stream);
 }

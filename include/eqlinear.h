@@ -140,8 +140,8 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
  * 2 <= N <= 8; other plans run tile - 7).  It rounds the transform
  * coefficients and the Fourier-domain outputs to bf16, so its results differ
  * from the other tiles by bf16 rounding; the automatic choice uses it where
- * it applies.  Tiles 14 and 15 (fp32 plans, C_in a multiple of 4; other
- * plans and shapes run tile 13) cover 16 tokens and 32 output channels (16
+ * it applies.  Tiles 14 and 15 (fp32 plans with N <= 10, C_in a multiple of
+ * 4; other plans and shapes run tile 13) cover 16 tokens and 32 output channels (16
  * when C_out <= 16) with the input channels of every step split over 2 or 4
  * waves per output block, whose partial spectra are summed in a fixed order;
  * complex bins use three real products instead of four (Gauss's method), so
