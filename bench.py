@@ -33,6 +33,7 @@ MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 KERNEL_SOURCES = {
     "C": ["group_equivariant_linear_amd/csrc/cn_fused.h",
           "group_equivariant_linear_amd/csrc/cn_mf.h",
+          "group_equivariant_linear_amd/csrc/cn_split.h",
           "group_equivariant_linear_amd/csrc/cn_dispatch.h",
           "group_equivariant_linear_amd/csrc/eq_device.h"],
     "D8": ["group_equivariant_linear_amd/csrc/d8_forward.hip",
@@ -46,7 +47,26 @@ def step_kernel_name(wl):
     if wl.group != "C":
         whole = (wl.C_in // 8) % 8 == 0 and (wl.C_out // 8) % 8 == 0  # block columns in 16-byte pieces
         return "d8_kernel" if wl.dtype == "bf16" and whole else "gemm_rows_kernel"
-    return "cn_mf_kernel" if wl.dtype == "bf16" and 2 <= wl.N <= 8 else "cn_fast_kernel"
+    if wl.dtype == "bf16" and 2 <= wl.N <= 8:
+        return "cn_mf_kernel"
+    if wl.dtype != "bf16" and wl.N <= 10 and wl.C_in % 4 == 0 and _one_wave_shape(wl):
+        return "cn_split_kernel"
+    return "cn_fast_kernel"
+
+
+def _one_wave_shape(wl):
+    """True where the automatic choice falls to one-wave tiles (the layer is too
+    small to give every CU a 4-wave workgroup); fp32 layers then run the
+    input-channel split kernel.  Mirrors choose_shape in cn_dispatch.h."""
+    nblk = (wl.C_out + 15) // 16
+    cb = min(max(24 // wl.N, 2), 6)
+    if cb > nblk:
+        cb = max(nblk, 2)
+    while cb >= 2:
+        if ((wl.T + 63) // 64) * ((nblk + cb - 1) // cb) >= 256:
+            return False
+        cb -= 1
+    return True
 
 
 def kernel_source_hash(group):
@@ -251,7 +271,8 @@ def _run_oracle(wl, d, n):
         oracle.d8_dense(d["x64"][:n], d["w64"], wl.C_out)
 
 
-STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "d8_kernel", "gemm_rows_kernel")
+STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "cn_split_kernel", "d8_kernel",
+                "gemm_rows_kernel")
 TRAFFIC_WARM = 5   # back-to-back forwards (inputs partly cached from the previous launch)
 TRAFFIC_COLD = 5   # forwards each after a 512 MiB read that evicts the L2s
 TRAFFIC_COPIES = 5

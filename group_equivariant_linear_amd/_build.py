@@ -62,6 +62,14 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # a kernel whose host-side stub was not emitted leaves an undefined symbol
+    # that only shows when the library is loaded: refuse such a link here
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    stubs = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if stubs:
+        os.remove(tmp)
+        raise RuntimeError("kernel stubs missing from the link (host compilation dropped them): "
+                           + ", ".join(stubs[:4]))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")

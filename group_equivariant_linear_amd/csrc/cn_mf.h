@@ -176,7 +176,9 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
     const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
     const int64_t t0 = (int64_t)(tile / n_c_tiles) * C::TT;
     const int o0 = (int)(tile % n_c_tiles) * C::CT;
-    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+    // the wave index is uniform: held in a scalar register, LDS destinations of
+    // the direct loads (M0) are then scalar arithmetic
+    const int lane = (int)threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int kg = lane >> 4, tl = lane & 15;
 
     const uint32_t row_x = (uint32_t)C_in * (N * S), row_y = (uint32_t)C_out * (N * S);
@@ -230,21 +232,44 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
 
     const int nch = (C_in + C::KC - 1) / C::KC;
     const uint32_t chunk_x = (uint32_t)C::KC * (N * S);
+    // Only a last, partial chunk needs per-lane masking of channels past C_in;
+    // full chunks issue their loads with the precomputed offsets alone.
     auto dma_x = [&](int c) {
         if (c >= nch) return;
-        const uint32_t valid = (uint32_t)(C_in - c * C::KC) * (N * S);  // bytes of this chunk's rows
+        if (c * C::KC + C::KC > C_in) {
+            const uint32_t valid = (uint32_t)(C_in - c * C::KC) * (N * S);  // bytes of this chunk's rows
 #pragma unroll
-        for (int j = 0; j < C::XDMA; ++j) {
-            const int sl = 64 * j + lane, pos = sl % C::XPITCH;
-            const int k = C::XROT ? (pos + XP - (sl / C::XPITCH) % XP) % XP : pos;
-            const uint32_t off = (uint32_t)k * 16u < valid ? xoff[j] : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void*)(xex + j * 1024), 16, off, (uint32_t)c * chunk_x, 0, 0);
+            for (int j = 0; j < C::XDMA; ++j) {
+                const int sl = 64 * j + lane, pos = sl % C::XPITCH;
+                const int k = C::XROT ? (pos + XP - (sl / C::XPITCH) % XP) % XP : pos;
+                const uint32_t off = (uint32_t)k * 16u < valid ? xoff[j] : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(xex + j * 1024), 16, off, (uint32_t)c * chunk_x, 0, 0);
+            }
+        } else {
+            // (the offsets pass through locals: an array element given straight
+            // to the builtin makes the host compilation drop the kernel's stub)
+#pragma unroll
+            for (int j = 0; j < C::XDMA; ++j) {
+                const uint32_t off = xoff[j];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(xex + j * 1024), 16, off, (uint32_t)c * chunk_x, 0, 0);
+            }
         }
     };
     auto dma = [&](int c, char* buf) {
-        if (c < nch)
-            fast_dma_w<C>(rw, woff, (uint32_t)(c * C::KC * S), c * C::KC + C::KC > C_in, c * C::KC, C_in, buf);
+        if (c >= nch) return;
+        if (c * C::KC + C::KC > C_in) {
+            fast_dma_w<C>(rw, woff, (uint32_t)(c * C::KC * S), true, c * C::KC, C_in, buf);
+        } else {
+#pragma unroll
+            for (int it = 0; it < C::DMA_ITERS; ++it) {
+                const uint32_t off = woff[it];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (__attribute__((address_space(3))) void*)(buf + (it * C::WAVES + wave) * 1024), 16, off,
+                    (uint32_t)(c * C::KC * S), 0, 0);
+            }
+        }
     };
     const int o_l = lane & 15;
     const int lane_off = (o_l * 4 + (kg ^ ((o_l >> 1) & 3))) * 16;
@@ -402,15 +427,47 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
                     u32x2{pk[2 * q], pk[2 * q + 1]};
             }
         }
-        const uint32_t cols = (uint32_t)(C_out - o0) * (N * S);
-        for (int pc = lane; pc < 16 * C::YP; pc += 64) {
-            const int r = pc / C::YP, k = pc % C::YP;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(yst + xpiece<C::YROT, C::YP, C::YPITCH>(r, k) * 16);
-            const uint32_t off = ((uint32_t)k * 16u < cols)
-                                     ? (uint32_t)(wave * 16 + r) * row_y + (uint32_t)o0 * (N * S) + (uint32_t)k * 16u
-                                     : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
-        }
+        // Lane (r = lane/4, u = lane%4) stores pieces u, u+4, u+8, ... of tile
+        // row r: 64 contiguous bytes of each of the 16 rows per instruction, and
+        // no per-piece index arithmetic beyond the rotation's single wrap.
+        const uint32_t cols = (uint32_t)(C_out - o0) * (N * S);  // valid bytes of a tile row
+        const bool full = cols >= (uint32_t)(C::YP * 16);
+        const int r = lane >> 2, u = lane & 3;
+        const uint32_t gbase = (uint32_t)(wave * 16 + r) * row_y + (uint32_t)o0 * (N * S) + (uint32_t)u * 16u;
+        const char* lrow = yst + r * C::YPITCH * 16;
+        const int rot0 = C::YROT ? (u + r) % C::YP : u;  // rotated position of piece u
+        constexpr int NIT = (C::YP + 3) / 4;
+        constexpr int G = 6;  // LDS reads issued ahead of their stores
+        auto store_rows = [&](auto fullc) {
+            constexpr bool FULL = decltype(fullc)::value;
+#pragma unroll
+            for (int i0 = 0; i0 < NIT; i0 += G) {
+                u32x4 v[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int it = i0 + g;
+                    if (it < NIT) {
+                        int pos = rot0 + 4 * it;
+                        if constexpr (C::YROT) pos = pos >= C::YP ? pos - C::YP : pos;
+                        v[g] = *reinterpret_cast<const u32x4*>(lrow + pos * 16);
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int it = i0 + g;
+                    if (it < NIT) {
+                        const uint32_t k = (uint32_t)(u + 4 * it);
+                        // pieces past the row (YP not a multiple of 4) and
+                        // columns past C_out are dropped by an out-of-range offset
+                        const bool ok = (C::YP % 4 == 0 || it < NIT - 1 || k < (uint32_t)C::YP) &&
+                                        (FULL || k * 16u < cols);
+                        __builtin_amdgcn_raw_buffer_store_b128(v[g], ry, ok ? gbase + 64u * it : kOOB, 0, 0);
+                    }
+                }
+            }
+        };
+        if (full) store_rows(std::true_type{});
+        else store_rows(std::false_type{});
     } else {
         const uint32_t trow = (uint32_t)(wave * 16 + tl);
 #pragma unroll
