@@ -64,6 +64,12 @@ def _load():
         lib.eqref_cn_dense.restype = i
         lib.eqref_cn_direct.argtypes = [i, i, i, i64, d, d, d]
         lib.eqref_cn_direct.restype = None
+        lib.eqref_apply_dense_t.argtypes = [i64, i64, i64, d, d, d]
+        lib.eqref_apply_dense_t.restype = None
+        lib.eqref_cn_backward_data.argtypes = [i, i, i, i64, d, d, d]
+        lib.eqref_cn_backward_data.restype = None
+        lib.eqref_cn_backward_weight.argtypes = [i, i, i, i64, d, d, d]
+        lib.eqref_cn_backward_weight.restype = None
         lib.eqref_cn_weight_dft.argtypes = [i, i, i, d, d]
         lib.eqref_cn_weight_dft.restype = None
         lib.eqref_d8_expand.argtypes = [i, i, d, d]
@@ -127,6 +133,49 @@ def cn_direct(x, w):
     y = np.empty((T, C_out, N), dtype=np.float64)
     _load().eqref_cn_direct(N, C_in, C_out, T, _p(x), _p(w), _p(y))
     return y
+
+
+def apply_dense_t(W, dy2d):
+    """dx[t] = W^T @ dy[t] for dy2d[T][rows]."""
+    W, dy2d = _f64(W), _f64(dy2d)
+    T, rows = dy2d.shape
+    cols = W.shape[1]
+    assert W.shape[0] == rows
+    dx = np.empty((T, cols), dtype=np.float64)
+    _load().eqref_apply_dense_t(T, rows, cols, _p(W), _p(dy2d), _p(dx))
+    return dx
+
+
+def cn_backward_data_dense(dy, w):
+    """Input gradient of the C_N layer as W_dense^T dy; dy[T][C_out][N]."""
+    dy = _f64(dy)
+    T, C_out, N = dy.shape
+    C_in = w.shape[1]
+    assert w.shape == (C_out, C_in, N)
+    dx = apply_dense_t(cn_expand(w), dy.reshape(T, C_out * N))
+    return dx.reshape(T, C_in, N)
+
+
+def cn_backward_data(dy, w):
+    """Input gradient of the C_N layer, direct sum; dy[T][C_out][N] -> dx[T][C_in][N]."""
+    dy, w = _f64(dy), _f64(w)
+    T, C_out, N = dy.shape
+    C_in = w.shape[1]
+    assert w.shape == (C_out, C_in, N)
+    dx = np.empty((T, C_in, N), dtype=np.float64)
+    _load().eqref_cn_backward_data(N, C_in, C_out, T, _p(dy), _p(w), _p(dx))
+    return dx
+
+
+def cn_backward_weight(x, dy):
+    """Weight gradient of the C_N layer; x[T][C_in][N], dy[T][C_out][N] -> dw[C_out][C_in][N]."""
+    x, dy = _f64(x), _f64(dy)
+    T, C_in, N = x.shape
+    C_out = dy.shape[1]
+    assert dy.shape == (T, C_out, N)
+    dw = np.empty((C_out, C_in, N), dtype=np.float64)
+    _load().eqref_cn_backward_weight(N, C_in, C_out, T, _p(x), _p(dy), _p(dw))
+    return dw
 
 
 def cn_weight_dft(w):

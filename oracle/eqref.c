@@ -25,6 +25,17 @@
  *    and packs it into N real planes: plane 0 = Re What[0]; planes 2k-1, 2k =
  *    Re, Im What[k] for 1 <= k < N/2; plane N-1 = Re What[N/2] when N is even.
  *
+ *  - Gradients of the C_N layer.  "Flash EQ-Linear", Implementation: the
+ *    kernels cover the backward pass as well as the forward pass (Experimental
+ *    Results, Operator Level: backward speedups).  The pages give no formula;
+ *    these are the derivatives of the layer's definition above.  For an
+ *    upstream gradient dy = dL/dy,
+ *        dx[t][i][h] = sum_{o,g} w[o][i][(g-h) mod N] * dy[t][o][g]
+ *                    = (W_dense^T dy[t])[i*N+h]
+ *    (eqref_cn_backward_data, and the dense route eqref_apply_dense_t), and
+ *        dw[o][i][m] = sum_{t,g} dy[t][o][g] * x[t][i][(g-m) mod N]
+ *    (eqref_cn_backward_weight).
+ *
  *  - D8 Fourier-domain layer.  "Quick ViTs" (papernotes), key design 2
  *    (Fourier-domain equivariant computation): a width-C map is four square
  *    blocks of size C/8 (irreps A1, A2, B1, B2) and one square block of size
@@ -77,6 +88,21 @@ void eqref_apply_dense(int64_t T, int64_t rows, int64_t cols, const double* W,
     }
 }
 
+/* dx[t][c] = sum_r W[r][c] * dy[t][r]: the transposed matrix applied to every token. */
+void eqref_apply_dense_t(int64_t T, int64_t rows, int64_t cols, const double* W,
+                         const double* dy, double* dx) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double* dyt = dy + t * rows;
+        double* dxt = dx + t * cols;
+        for (int64_t c = 0; c < cols; ++c) {
+            double acc = 0.0;
+            for (int64_t r = 0; r < rows; ++r) acc += W[r * cols + c] * dyt[r];
+            dxt[c] = acc;
+        }
+    }
+}
+
 /* Replicate-and-multiply: the dense definition of the C_N layer.
  * Returns 0 on success, -1 if the dense matrix cannot be allocated. */
 int eqref_cn_dense(int N, int C_in, int C_out, int64_t T, const double* x,
@@ -106,6 +132,41 @@ void eqref_cn_direct(int N, int C_in, int C_out, int64_t T, const double* x,
                                x[(t * C_in + i) * N + h];
                     }
                 y[(t * C_out + o) * N + g] = acc;
+            }
+}
+
+/* Input gradient, directly: dx[t][i][h] = sum_{o,g} w[o][i][(g-h) mod N] dy[t][o][g]. */
+void eqref_cn_backward_data(int N, int C_in, int C_out, int64_t T, const double* dy,
+                            const double* w, double* dx) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int i = 0; i < C_in; ++i)
+            for (int h = 0; h < N; ++h) {
+                double acc = 0.0;
+                for (int o = 0; o < C_out; ++o)
+                    for (int g = 0; g < N; ++g) {
+                        int m = ((g - h) % N + N) % N;
+                        acc += w[((int64_t)o * C_in + i) * N + m] *
+                               dy[(t * C_out + o) * N + g];
+                    }
+                dx[(t * C_in + i) * N + h] = acc;
+            }
+}
+
+/* Weight gradient: dw[o][i][m] = sum_{t,g} dy[t][o][g] x[t][i][(g-m) mod N]. */
+void eqref_cn_backward_weight(int N, int C_in, int C_out, int64_t T, const double* x,
+                              const double* dy, double* dw) {
+#pragma omp parallel for schedule(static)
+    for (int o = 0; o < C_out; ++o)
+        for (int i = 0; i < C_in; ++i)
+            for (int m = 0; m < N; ++m) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    for (int g = 0; g < N; ++g) {
+                        int h = ((g - m) % N + N) % N;
+                        acc += dy[(t * C_out + o) * N + g] * x[(t * C_in + i) * N + h];
+                    }
+                dw[((int64_t)o * C_in + i) * N + m] = acc;
             }
 }
 

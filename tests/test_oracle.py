@@ -152,7 +152,56 @@ def pin_dense_matrix_structure(orc):
             assert np.array_equal(blk, scipy.linalg.circulant(w[o, i])), (o, i)
 
 
-ALL_CN_PINS = [pin_rfft_route, pin_weight_dft, pin_closed_forms, pin_dense_matrix_structure]
+def pin_backward_adjoint(orc):
+    """The gradients are the adjoints of the (pinned) forward map:
+    <dy, y(x, w)> = <dx(dy, w), x> = <dw(x, dy), w> for every x, w, dy, and the
+    direct input gradient equals W_dense^T dy."""
+    for N, C_in, C_out, T in [(3, 2, 4, 5), (4, 3, 2, 3), (7, 2, 3, 4), (8, 1, 2, 2), (1, 3, 2, 4)]:
+        x, w, dy = _rand(T, C_in, N), _rand(C_out, C_in, N), _rand(T, C_out, N)
+        lhs = np.sum(dy * orc.cn_dense(x, w))
+        dx = orc.cn_backward_data(dy, w)
+        dw = orc.cn_backward_weight(x, dy)
+        assert abs(np.sum(dx * x) - lhs) <= 1e-12 * max(1.0, abs(lhs)), (N, C_in, C_out)
+        assert abs(np.sum(dw * w) - lhs) <= 1e-12 * max(1.0, abs(lhs)), (N, C_in, C_out)
+        assert rel(dx, orc.cn_backward_data_dense(dy, w)) < 1e-14
+
+
+def pin_backward_closed_forms(orc):
+    T, C_in, C_out = 5, 3, 2
+    # N = 1: plain matrix products dx = dy w, dw = dy^T x
+    x, w, dy = _rand(T, C_in, 1), _rand(C_out, C_in, 1), _rand(T, C_out, 1)
+    assert rel(orc.cn_backward_data(dy, w)[..., 0], dy[..., 0] @ w[..., 0]) < 1e-15
+    assert rel(orc.cn_backward_weight(x, dy)[..., 0], dy[..., 0].T @ x[..., 0]) < 1e-15
+    # convolution theorem with numpy's FFT: dx = irfft(sum_o conj(W) DY),
+    # dw = irfft(sum_t DY conj(X)) (cross-correlations along the group axis)
+    for N in (3, 4, 6, 7):
+        x, w, dy = _rand(T, C_in, N), _rand(C_out, C_in, N), _rand(T, C_out, N)
+        X, Wf, DY = (np.fft.rfft(a, axis=-1) for a in (x, w, dy))
+        ref_dx = np.fft.irfft(np.einsum("oik,tok->tik", np.conj(Wf), DY), n=N, axis=-1)
+        ref_dw = np.fft.irfft(np.einsum("tok,tik->oik", DY, np.conj(X)), n=N, axis=-1)
+        assert rel(orc.cn_backward_data(dy, w), ref_dx) < 1e-13, N
+        assert rel(orc.cn_backward_weight(x, dy), ref_dw) < 1e-13, N
+    # w = delta_{o,i} delta_{m,s} (a roll by s): dx is dy rolled back by s
+    N = 5
+    dy = _rand(T, C_in, N)
+    for s in range(N):
+        w = np.zeros((C_in, C_in, N))
+        for i in range(C_in):
+            w[i, i, s] = 1.0
+        assert np.array_equal(orc.cn_backward_data(dy, w), np.roll(dy, -s, axis=-1)), s
+
+
+def pin_backward_equivariance(orc):
+    N, C_in, C_out, T = 6, 2, 3, 4
+    x, w, dy = _rand(T, C_in, N), _rand(C_out, C_in, N), _rand(T, C_out, N)
+    dx, dw = orc.cn_backward_data(dy, w), orc.cn_backward_weight(x, dy)
+    for s in (1, 2, 5):
+        assert rel(orc.cn_backward_data(np.roll(dy, s, -1), w), np.roll(dx, s, -1)) < 1e-14
+        assert rel(orc.cn_backward_weight(np.roll(x, s, -1), np.roll(dy, s, -1)), dw) < 1e-14
+
+
+ALL_CN_PINS = [pin_rfft_route, pin_weight_dft, pin_closed_forms, pin_dense_matrix_structure,
+               pin_backward_adjoint, pin_backward_closed_forms, pin_backward_equivariance]
 
 
 # ---------------------------------------------------------------------------
@@ -189,6 +238,18 @@ def test_weight_dft_closed_forms():
 
 def test_closed_forms():
     pin_closed_forms(oracle)
+
+
+def test_backward_adjoint_identities():
+    pin_backward_adjoint(oracle)
+
+
+def test_backward_closed_forms():
+    pin_backward_closed_forms(oracle)
+
+
+def test_backward_equivariance():
+    pin_backward_equivariance(oracle)
 
 
 def test_dense_matrix_structure():
@@ -373,14 +434,24 @@ def test_page_counts(golden_dir):
 # Mutation check: plausible mistakes planted in a copy of the oracle must fail a pin.
 
 MUTANTS = [
-    ("correlation instead of convolution", "int m = ((g - h) % N + N) % N;", "int m = ((h - g) % N + N) % N;"),
-    ("direct sum index sign", "int h = ((g - m) % N + N) % N;", "int h = ((g + m) % N + N) % N;"),
+    ("correlation instead of convolution", "int m = ((g - h) % N + N) % N;\n                    W[",
+     "int m = ((h - g) % N + N) % N;\n                    W["),
+    ("direct sum index sign", "int h = ((g - m) % N + N) % N;\n                        acc += w[",
+     "int h = ((g + m) % N + N) % N;\n                        acc += w["),
     ("transposed channel operand", "W[((int64_t)o * N + g) * cols + (int64_t)i * N + h] =\n                        w[((int64_t)o * C_in + i) * N + m];",
      "W[((int64_t)o * N + g) * cols + (int64_t)i * N + h] =\n                        w[((int64_t)i * C_out + o) * N + m];"),
     ("dropped last term", "for (int64_t c = 0; c < cols; ++c) acc += Wr[c] * xt[c];",
      "for (int64_t c = 0; c + 1 < cols; ++c) acc += Wr[c] * xt[c];"),
     ("imaginary sign", "im -= wm[m] * sin(ang);", "im += wm[m] * sin(ang);"),
     ("Nyquist plane slot", "planes[(int64_t)(N - 1) * plane + oi] = re;", "planes[(int64_t)(N - 2) * plane + oi] = re;"),
+    ("backward data index sign", "int m = ((g - h) % N + N) % N;\n                        acc += w[((int64_t)o * C_in + i) * N + m] *\n                               dy[",
+     "int m = ((h - g) % N + N) % N;\n                        acc += w[((int64_t)o * C_in + i) * N + m] *\n                               dy["),
+    ("backward weight index sign", "int h = ((g - m) % N + N) % N;\n                        acc += dy[",
+     "int h = ((g + m) % N + N) % N;\n                        acc += dy["),
+    ("backward weight transposed channels", "acc += dy[(t * C_out + o) * N + g] * x[(t * C_in + i) * N + h];",
+     "acc += dy[(t * C_out + o) * N + g] * x[(t * C_in + (i % C_out) % C_in) * N + h];"),
+    ("dense transpose drops a row", "for (int64_t r = 0; r < rows; ++r) acc += W[r * cols + c] * dyt[r];",
+     "for (int64_t r = 1; r < rows; ++r) acc += W[r * cols + c] * dyt[r];"),
     ("D8 transposed 1-D block", "blk[(int64_t)r * mi + c];", "blk[(int64_t)c * mi + r];"),
     ("D8 E weight on coordinate 0 only", "4 * mi + 2 * e * mi + c] =", "4 * mi + c] ="),
 ]
@@ -448,6 +519,13 @@ def test_oracle_under_sanitizers(tmp_path):
         "lib.eqref_cn_direct(5, 2, 4, 3, p(x), p(w), p(y))\n"
         "lib.eqref_cn_weight_dft.argtypes = [ctypes.c_int]*3 + [ctypes.c_void_p]*2\n"
         "lib.eqref_cn_weight_dft(5, 4, 2, p(w), p(P))\n"
+        "dx = np.zeros((3, 2, 5)); dw = np.zeros((4, 2, 5))\n"
+        "lib.eqref_cn_backward_data.argtypes = lib.eqref_cn_dense.argtypes\n"
+        "lib.eqref_cn_backward_data(5, 2, 4, 3, p(y), p(w), p(dx))\n"
+        "lib.eqref_cn_backward_weight.argtypes = lib.eqref_cn_dense.argtypes\n"
+        "lib.eqref_cn_backward_weight(5, 2, 4, 3, p(x), p(y), p(dw))\n"
+        "Wd = np.ones((20, 10)); lib.eqref_apply_dense_t.argtypes = [ctypes.c_int64]*3 + [ctypes.c_void_p]*3\n"
+        "lib.eqref_apply_dense_t(3, 20, 10, p(Wd), p(y), p(dx))\n"
         "wb = np.ones(16*16//8); xd = np.ones((2, 16)); yd = np.zeros((2, 16))\n"
         "lib.eqref_d8_dense.argtypes = [ctypes.c_int]*2 + [ctypes.c_int64] + [ctypes.c_void_p]*3\n"
         "assert lib.eqref_d8_dense(16, 16, 2, p(xd), p(wb), p(yd)) == 0\n"
