@@ -27,7 +27,8 @@ ABI_FUNCTIONS = (
     "eqlinear_status_string", "eqlinear_plan", "eqlinear_d8_plan", "eqlinear_plan_destroy",
     "eqlinear_plan_info", "eqlinear_w_hat_elems", "eqlinear_weight_fft", "eqlinear_forward",
     "eqlinear_forward_tiled", "eqlinear_d8_forward", "eqlinear_expand_dense",
-    "eqlinear_dense_forward",
+    "eqlinear_dense_forward", "eqlinear_w_hat_adjoint", "eqlinear_backward_data",
+    "eqlinear_backward_weight_workspace", "eqlinear_backward_weight",
 )
 
 
@@ -80,6 +81,10 @@ def load_library(path: str | None = None):
             "eqlinear_d8_forward": ([vp, vp, vp, vp, i64, vp], st),
             "eqlinear_expand_dense": ([vp, vp, vp, vp], st),
             "eqlinear_dense_forward": ([vp, vp, vp, vp, i64, vp], st),
+            "eqlinear_w_hat_adjoint": ([vp, vp, vp, vp], st),
+            "eqlinear_backward_data": ([vp, vp, vp, vp, i64, vp], st),
+            "eqlinear_backward_weight_workspace": ([vp, i64], ctypes.c_size_t),
+            "eqlinear_backward_weight": ([vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp], st),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -246,6 +251,59 @@ def eqlinear_dense_forward(plan: Plan, x, w_dense, y, T: int | None = None, stre
                                             _ptr(w_dense, plan, K * M, "w_dense"),
                                             _ptr(y, plan, T * M, "y"), T, _stream(stream)),
            "eqlinear_dense_forward")
+
+
+def eqlinear_w_hat_adjoint(plan: Plan, w_hat, w_hat_adj, stream=None):
+    n = eqlinear_w_hat_elems(plan)
+    _check(plan._lib.eqlinear_w_hat_adjoint(plan.handle, _ptr(w_hat, plan, n, "w_hat"),
+                                            _ptr(w_hat_adj, plan, n, "w_hat_adj"), _stream(stream)),
+           "eqlinear_w_hat_adjoint")
+
+
+def eqlinear_backward_data(plan: Plan, dy, w_hat_adj, dx, T: int | None = None, stream=None):
+    K, M = _widths(plan)
+    T = _tokens(dy, T, M)
+    n = eqlinear_w_hat_elems(plan)
+    _check(plan._lib.eqlinear_backward_data(plan.handle, _ptr(dy, plan, T * M, "dy"),
+                                            _ptr(w_hat_adj, plan, n, "w_hat_adj"),
+                                            _ptr(dx, plan, T * K, "dx"), T, _stream(stream)),
+           "eqlinear_backward_data")
+
+
+def eqlinear_backward_weight_workspace(plan: Plan, T: int) -> int:
+    return int(plan._lib.eqlinear_backward_weight_workspace(plan.handle, int(T)))
+
+
+def _raw_ptr(t, name: str, dtype=None, numel: int | None = None):
+    """Device address of a tensor whose dtype does not follow the plan."""
+    if isinstance(t, int):
+        return t
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+def eqlinear_backward_weight(plan: Plan, x, dy, dw, workspace, T: int | None = None, stream=None):
+    """dw (fp32, N*C_in*C_out elements) from x and dy; workspace: a GPU byte
+    tensor of at least eqlinear_backward_weight_workspace(plan, T) bytes."""
+    import torch
+    K, M = _widths(plan)
+    T = _tokens(x, T, K)
+    n = eqlinear_w_hat_elems(plan)
+    if isinstance(workspace, int):
+        raise ValueError("workspace: pass a GPU tensor (its size is checked)")
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(plan._lib.eqlinear_backward_weight(plan.handle, _ptr(x, plan, T * K, "x"), _ptr(dy, plan, T * M, "dy"),
+                                              _raw_ptr(dw, "dw", torch.float32, n),
+                                              T, _raw_ptr(workspace, "workspace"), wbytes, _stream(stream)),
+           "eqlinear_backward_weight")
 
 
 def built() -> bool:

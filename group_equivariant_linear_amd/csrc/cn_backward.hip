@@ -1,0 +1,438 @@
+// cn_backward.hip -- gradients of the C_N layer on gfx950.
+//
+// "Flash EQ-Linear", Implementation: the method's kernels cover the backward
+// pass as well as the forward (Experimental Results, Operator Level: backward
+// speedups, a little below the forward's because of the extra arithmetic and
+// memory traffic of the gradients).  The pages give no formulas; these are the
+// derivatives of the layer y[t][o][g] = sum_{i,m} w[o][i][m] x[t][i][(g-m) mod N].
+//
+// Input gradient.  dx[t][i][h] = sum_{o,g} w[o][i][(g-h) mod N] dy[t][o][g] is
+// the same kind of layer with C_in and C_out exchanged and the weight
+// w'[i][o][m] = w[o][i][(-m) mod N], whose spectrum is conj(What[k])^T.  The
+// library forms that adjoint spectrum once per weight (w_hat_adjoint_kernel)
+// and runs the forward kernels on dy with it.
+//
+// Weight gradient.  dw[o][i][m] = sum_{t,g} dy[t][o][g] x[t][i][(g-m) mod N] is
+// a cross-correlation along the group axis, i.e. in the frequency domain
+//     C_k[o][i] = sum_t DY[t][o][k] conj(X[t][i][k]),   dw = inverse real DFT of C,
+// a contraction over tokens for every kept bin (complex bins: Re C = a c + b d,
+// Im C = b c - a d with DY = a + ib, X = c + id).  Three launches:
+//   1. bw_planes_kernel: real DFT of every record of x and of dy, written as
+//      planes [plane][channel][token] (tokens contiguous, padded to Tp);
+//   2. bw_gemm_kernel: per 64 x 64 (o, i) tile and range of tokens, all bins'
+//      products on the matrix cores with the operand planes streamed through
+//      an LDS ring by direct global->LDS loads; fp32 partial spectra per range;
+//   3. bw_reduce_kernel: partials summed in a fixed order, inverse real DFT
+//      per (o, i), dw written in fp32 [C_out][C_in][N].
+// Every step is deterministic (no atomics).
+#include "eq_device.h"
+#include "eq_launch.h"
+
+namespace eql {
+
+namespace {
+
+constexpr uint32_t kBwOOB = 0x80000000u;  // offset past every resource (extents < 2^31)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bw_rsrc(const void* base, uint32_t bytes) {
+    // word 3 = 0x00020000: raw (untyped) buffer, 32-bit data format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt immediate: vmcnt <= n, lgkmcnt and expcnt unconstrained.
+constexpr int bw_vmcnt(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+template <typename IO>
+__device__ __forceinline__ float to_f32(IO v) {
+    return (float)v;
+}
+
+// plane p of the packed real spectrum holds an imaginary part
+__host__ __device__ constexpr bool imag_plane(int N, int p) {
+    return p > 0 && p % 2 == 0 && !(N % 2 == 0 && p == N - 1);
+}
+
+// --- adjoint spectrum ---------------------------------------------------------------
+// out[p][i][o] = s_p in[p][o][i], s_p = -1 on imaginary planes: the w_hat of
+// the layer with exchanged channels and reversed group axis.
+template <typename IO>
+__global__ __launch_bounds__(256) void w_hat_adjoint_kernel(const IO* __restrict__ in, IO* __restrict__ out,
+                                                            int N, int C_in, int C_out) {
+    __shared__ float tile[32][33];
+    const int p = (int)blockIdx.z;
+    const int o0 = (int)blockIdx.y * 32, i0 = (int)blockIdx.x * 32;
+    const int tx = (int)threadIdx.x & 31, ty = (int)threadIdx.x >> 5;
+    const int64_t plane = (int64_t)C_out * C_in;
+    const IO* src = in + p * plane;
+    for (int r = ty; r < 32; r += 8) {
+        const int o = o0 + r, i = i0 + tx;
+        if (o < C_out && i < C_in) tile[r][tx] = to_f32(src[(int64_t)o * C_in + i]);
+    }
+    __syncthreads();
+    const float s = imag_plane(N, p) ? -1.0f : 1.0f;
+    IO* dst = out + p * plane;
+    for (int r = ty; r < 32; r += 8) {
+        const int i = i0 + r, o = o0 + tx;
+        if (i < C_in && o < C_out) dst[(int64_t)i * C_out + o] = (IO)(s * tile[tx][r]);
+    }
+}
+
+// --- 1. planes ------------------------------------------------------------------------
+// Block: 64 tokens (one per lane) x 16 channels (4 per wave).  Record (t, c) is
+// read, transformed in fp32 and its N planes written at [p][c][t]; tokens
+// T .. Tp-1 get zeros.
+template <int N, typename IO>
+__global__ __launch_bounds__(256) void bw_planes_kernel(const IO* __restrict__ src, IO* __restrict__ planes,
+                                                        int64_t T, int C, int64_t Tp) {
+    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+    const int cbase = (int)blockIdx.y * 16 + wave * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = cbase + j;
+        if (c >= C) break;
+        float xv[N], P[N];
+        if (t < T) {
+            const IO* r = src + (t * C + c) * N;
+#pragma unroll
+            for (int h = 0; h < N; ++h) xv[h] = to_f32(r[h]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < N; ++h) xv[h] = 0.0f;
+        }
+        rdft_forward<N>(xv, P);
+#pragma unroll
+        for (int p = 0; p < N; ++p) planes[((int64_t)p * C + c) * Tp + t] = (IO)P[p];
+    }
+}
+
+// --- 2. per-bin products over tokens --------------------------------------------------
+template <int N_, typename IO_>
+struct BwCfg {
+    static constexpr int N = N_;
+    using IO = IO_;
+    static constexpr int S = (int)sizeof(IO);
+    static constexpr int KC = 64 / S;          // tokens of one chunk: 64 bytes of a plane row
+    static constexpr int TM = 64, TN = 64;     // output rows (o) and columns (i) per workgroup
+    static constexpr int kThreads = 256;       // 2 x 2 waves, 32 x 32 each
+    static constexpr int H = (N - 1) / 2;      // complex bins
+    static constexpr bool NYQ = N % 2 == 0 && N > 1;
+    static constexpr int NB = 1 + H + (NYQ ? 1 : 0);  // bins
+    static constexpr int PBYTES = 64 * 64;     // one plane of one operand: 64 rows x 64 bytes
+    static constexpr int STAGE = 4 * PBYTES;   // two planes of each operand
+    static constexpr int ST = 3;               // ring stages (two in flight)
+    static constexpr int LDS = ST * STAGE;
+    static constexpr int LOADS = 4;            // direct loads per thread and stage
+};
+
+__device__ __forceinline__ void bw_mma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void bw_mma(f32x4& acc, const f32x4& a, const f32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 bw_neg(const bf16x8& v) {
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+    u ^= 0x80008000u;
+    return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ f32x4 bw_neg(const f32x4& v) { return -v; }
+
+template <typename IO>
+struct BwFrag;
+template <>
+struct BwFrag<__bf16> {
+    using T = bf16x8;  // 8 tokens of one row: k-values of one 16x16x32 product
+};
+template <>
+struct BwFrag<float> {
+    using T = f32x4;   // 4 tokens of one row: one value for each of four 16x16x4 products
+};
+
+// Workgroup: (o, i) tile (blockIdx % tiles) and token range (blockIdx / tiles).
+// Stage q = chunk * NB + bin holds, for KC tokens, the bin's planes (one for
+// DC and Nyquist, real and imaginary part otherwise) of the tile's 64 dy rows
+// (A) and 64 x rows (B), each row 64 bytes = 4 parts in LDS order.  The MFMA A
+// operand is a 16-row block of dy planes (rows o, k = tokens), B a block of x
+// planes (k = tokens, columns i): lane l ends with o = 4(l/16)+r, i = l%16.
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::IO* __restrict__ dyp,
+                                                              const typename C::IO* __restrict__ xp,
+                                                              float* __restrict__ part, int C_out, int C_in,
+                                                              int64_t Tp, int n_i, int tiles, int chunks_per_split,
+                                                              int nchunks) {
+    using IO = typename C::IO;
+    using F = typename BwFrag<IO>::T;
+    constexpr int N = C::N, H = C::H, NB = C::NB, ST = C::ST, S = C::S;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+    const int tile = (int)(blockIdx.x % (uint32_t)tiles), split = (int)(blockIdx.x / (uint32_t)tiles);
+    const int o0 = (tile / n_i) * C::TM, i0 = (tile % n_i) * C::TN;
+    const int c_begin = split * chunks_per_split;
+    const int c_end = c_begin + chunks_per_split < nchunks ? c_begin + chunks_per_split : nchunks;
+    const int nq = (c_end - c_begin) * NB;
+
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const uint32_t row_bytes = (uint32_t)(Tp * S);
+    const uint32_t pa = (uint32_t)C_out * row_bytes, pb = (uint32_t)C_in * row_bytes;  // plane strides
+    const __amdgpu_buffer_rsrc_t ra = bw_rsrc(dyp, (uint32_t)N * pa);
+    const __amdgpu_buffer_rsrc_t rb = bw_rsrc(xp, (uint32_t)N * pb);
+
+    // this thread's load: row r = tid / 4, 16-byte part u = tid % 4 of a plane block
+    const int r = tid >> 2, u = tid & 3;
+    const uint32_t offa = o0 + r < C_out ? (uint32_t)(o0 + r) * row_bytes + (uint32_t)u * 16u : kBwOOB;
+    const uint32_t offb = i0 + r < C_in ? (uint32_t)(i0 + r) * row_bytes + (uint32_t)u * 16u : kBwOOB;
+
+    // planes of bin b: first (real part, or the only plane), second (imaginary)
+    auto plane0 = [&](int b) { return b == 0 ? 0 : (b <= H ? 2 * b - 1 : N - 1); };
+    auto dma = [&](int q) {
+        char* st = smem + (q % ST) * C::STAGE;
+        const bool live = q < nq;
+        const int cq = live ? c_begin + q / NB : 0, b = live ? q % NB : 0;
+        const int p0 = plane0(b);
+        const bool cplx = b >= 1 && b <= H;
+        const uint32_t soff = (uint32_t)cq * 64u;  // KC tokens = 64 bytes along a row
+        const uint32_t a0 = live && offa != kBwOOB ? offa + (uint32_t)p0 * pa : kBwOOB;
+        const uint32_t b0 = live && offb != kBwOOB ? offb + (uint32_t)p0 * pb : kBwOOB;
+        const uint32_t a1 = live && cplx && offa != kBwOOB ? a0 + pa : kBwOOB;
+        const uint32_t b1 = live && cplx && offb != kBwOOB ? b0 + pb : kBwOOB;
+        // every thread issues LOADS loads for every stage, so vmcnt counts stages
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(st + wave * 1024), 16,
+                                                 a0, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(st + C::PBYTES + wave * 1024), 16, a1, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(st + 2 * C::PBYTES + wave * 1024), 16, b0, soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(st + 3 * C::PBYTES + wave * 1024), 16, b1, soff, 0, 0);
+    };
+
+    f32x4 acc[2][2][N];
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int p = 0; p < N; ++p) acc[ob][ib][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // fragment of 16-row block blk of a plane region: row blk*16 + lane%16, part lane/16
+    const int frag_off = (lane & 15) * 64 + (lane >> 4) * 16;
+    auto frag = [&](const char* region, int blk) {
+        return *reinterpret_cast<const F*>(region + blk * 1024 + frag_off);
+    };
+
+#pragma unroll
+    for (int q = 0; q < ST - 1; ++q) dma(q);
+    for (int q = 0; q < nq; ++q) {
+        // this thread's loads of stage q are done once at most ST-2 stages remain
+        __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * C::LOADS));
+        asm volatile("s_barrier" ::: "memory");
+        dma(q + ST - 1);
+        const char* st = smem + (q % ST) * C::STAGE;
+        const int b = q % NB;
+        F A0[2], B0[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            A0[k] = frag(st, 2 * wm + k);
+            B0[k] = frag(st + 2 * C::PBYTES, 2 * wn + k);
+        }
+        if (b >= 1 && b <= H) {
+            F A1[2], B1[2], nA0[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                A1[k] = frag(st + C::PBYTES, 2 * wm + k);
+                B1[k] = frag(st + 3 * C::PBYTES, 2 * wn + k);
+                nA0[k] = bw_neg(A0[k]);
+            }
+            // bins are uniform across the workgroup; plane pair chosen at run time
+            static_for<1, H + 1>([&](auto kc) {
+                constexpr int kb = decltype(kc)::value;
+                if (b == kb) {
+                    constexpr int pr = 2 * kb - 1, pi = 2 * kb;
+#pragma unroll
+                    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+                        for (int ib = 0; ib < 2; ++ib) {
+                            bw_mma(acc[ob][ib][pr], A0[ob], B0[ib]);   // a c
+                            bw_mma(acc[ob][ib][pi], A1[ob], B0[ib]);   // b c
+                            bw_mma(acc[ob][ib][pr], A1[ob], B1[ib]);   // + b d
+                            bw_mma(acc[ob][ib][pi], nA0[ob], B1[ib]);  // - a d
+                        }
+                }
+            });
+        } else {
+            const int p = b == 0 ? 0 : N - 1;
+            if (p == 0) {
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) bw_mma(acc[ob][ib][0], A0[ob], B0[ib]);
+            } else if constexpr (C::NYQ) {
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+                    for (int ib = 0; ib < 2; ++ib) bw_mma(acc[ob][ib][N - 1], A0[ob], B0[ib]);
+            }
+        }
+    }
+
+    // partial spectra of this token range: part[split][p][o][i]
+    const int64_t plane = (int64_t)C_out * C_in;
+    float* dst = part + (int64_t)split * N * plane;
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            const int i = i0 + 32 * wn + 16 * ib + (lane & 15);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int o = o0 + 32 * wm + 16 * ob + 4 * (lane >> 4) + rr;
+                if (o < C_out && i < C_in) {
+#pragma unroll
+                    for (int p = 0; p < N; ++p) dst[p * plane + (int64_t)o * C_in + i] = acc[ob][ib][p][rr];
+                }
+            }
+        }
+}
+
+// --- 3. reduction and inverse transform ------------------------------------------------
+// Thread per (o, i): partials summed in split order, then the inverse real DFT
+// of the packed spectrum C gives dw[o][i][0 .. N-1].
+template <int N>
+__global__ __launch_bounds__(256) void bw_reduce_kernel(const float* __restrict__ part, float* __restrict__ dw,
+                                                        int splits, int64_t plane) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= plane) return;
+    float P[N], y[N];
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+        float v = 0.0f;
+        for (int s = 0; s < splits; ++s) v += part[((int64_t)s * N + p) * plane + e];
+        P[p] = v;
+    }
+    rdft_inverse<N>(P, y);
+#pragma unroll
+    for (int m = 0; m < N; ++m) dw[e * N + m] = y[m];
+}
+
+// --- host side ---------------------------------------------------------------------------
+
+struct BwShape {
+    int64_t Tp;
+    int n_o, n_i, tiles, nchunks, splits, chunks_per_split;
+    size_t xp_bytes, dyp_bytes, part_bytes, total;
+};
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
+    BwShape s{};
+    const int S = bf16 ? 2 : 4, KC = 64 / S;
+    s.Tp = (T + 63) / 64 * 64;
+    s.n_o = (C_out + 63) / 64;
+    s.n_i = (C_in + 63) / 64;
+    s.tiles = s.n_o * s.n_i;
+    s.nchunks = (int)(s.Tp / KC);
+    // token ranges: enough workgroups to cover the chip, while the fp32 partials
+    // stay within about an eighth of the operand planes' bytes
+    const int64_t want = (256 + s.tiles - 1) / s.tiles;
+    const int64_t cap = ((int64_t)(C_in + C_out) * s.Tp * S) / ((int64_t)8 * C_out * C_in * 4);
+    int64_t sp = want < cap ? want : cap;
+    sp = sp < 1 ? 1 : (sp > s.nchunks ? s.nchunks : sp);
+    s.chunks_per_split = (int)((s.nchunks + sp - 1) / sp);
+    s.splits = (s.nchunks + s.chunks_per_split - 1) / s.chunks_per_split;
+    s.xp_bytes = round256((size_t)N * C_in * s.Tp * S);
+    s.dyp_bytes = round256((size_t)N * C_out * s.Tp * S);
+    s.part_bytes = round256((size_t)s.splits * N * C_out * C_in * 4);
+    s.total = s.xp_bytes + s.dyp_bytes + s.part_bytes;
+    return s;
+}
+
+template <int N, typename IO>
+hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t T, int C_in, int C_out,
+                               char* ws, const BwShape& s, hipStream_t stream) {
+    using Cfg = BwCfg<N, IO>;
+    IO* xp = reinterpret_cast<IO*>(ws);
+    IO* dyp = reinterpret_cast<IO*>(ws + s.xp_bytes);
+    float* part = reinterpret_cast<float*>(ws + s.xp_bytes + s.dyp_bytes);
+    const dim3 gx((uint32_t)(s.Tp / 64), (uint32_t)((C_in + 15) / 16));
+    const dim3 gy((uint32_t)(s.Tp / 64), (uint32_t)((C_out + 15) / 16));
+    hipLaunchKernelGGL((bw_planes_kernel<N, IO>), gx, dim3(256), 0, stream, (const IO*)x, xp, T, C_in, s.Tp);
+    hipLaunchKernelGGL((bw_planes_kernel<N, IO>), gy, dim3(256), 0, stream, (const IO*)dy, dyp, T, C_out, s.Tp);
+    const int64_t wgs = (int64_t)s.tiles * s.splits;
+    hipLaunchKernelGGL((bw_gemm_kernel<Cfg>), dim3((uint32_t)wgs), dim3(Cfg::kThreads), 0, stream,
+                       (const IO*)dyp, (const IO*)xp, part, C_out, C_in, s.Tp, s.n_i, s.tiles,
+                       s.chunks_per_split, s.nchunks);
+    const int64_t plane = (int64_t)C_out * C_in;
+    hipLaunchKernelGGL((bw_reduce_kernel<N>), dim3((uint32_t)((plane + 255) / 256)), dim3(256), 0, stream,
+                       (const float*)part, dw, s.splits, plane);
+    return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t dispatch_backward_weight(int N, const void* x, const void* dy, float* dw, int64_t T, int C_in,
+                                    int C_out, char* ws, const BwShape& s, hipStream_t stream) {
+    switch (N) {
+#define EQL_BW(n) \
+    case n: return run_backward_weight<n, IO>(x, dy, dw, T, C_in, C_out, ws, s, stream);
+        EQL_BW(1) EQL_BW(2) EQL_BW(3) EQL_BW(4) EQL_BW(5) EQL_BW(6) EQL_BW(7) EQL_BW(8)
+        EQL_BW(9) EQL_BW(10) EQL_BW(11) EQL_BW(12) EQL_BW(13) EQL_BW(14) EQL_BW(15) EQL_BW(16)
+#undef EQL_BW
+        default: return hipErrorInvalidValue;
+    }
+}
+
+__global__ __launch_bounds__(256) void bw_zero_kernel(float* __restrict__ p, int64_t n) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e < n) p[e] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_w_hat_adjoint(int N, int dtype_bf16, const void* w_hat, void* w_hat_adj, int C_in, int C_out,
+                                hipStream_t stream) {
+    const dim3 grid((uint32_t)((C_in + 31) / 32), (uint32_t)((C_out + 31) / 32), (uint32_t)N);
+    if (grid.y > 65535u) return hipErrorInvalidConfiguration;
+    if (dtype_bf16)
+        hipLaunchKernelGGL(w_hat_adjoint_kernel<__bf16>, grid, dim3(256), 0, stream, (const __bf16*)w_hat,
+                           (__bf16*)w_hat_adj, N, C_in, C_out);
+    else
+        hipLaunchKernelGGL(w_hat_adjoint_kernel<float>, grid, dim3(256), 0, stream, (const float*)w_hat,
+                           (float*)w_hat_adj, N, C_in, C_out);
+    return hipGetLastError();
+}
+
+size_t backward_weight_workspace(int N, int dtype_bf16, int64_t T, int C_in, int C_out) {
+    if (T <= 0) return 0;
+    return bw_shape(N, dtype_bf16, T, C_in, C_out).total;
+}
+
+hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const void* dy, float* dw, int64_t T,
+                                     int C_in, int C_out, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+    if (T == 0) {  // no tokens: the gradient is zero (a fill kernel, also fine inside a captured graph)
+        const int64_t n = (int64_t)N * C_in * C_out;
+        hipLaunchKernelGGL(bw_zero_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, dw, n);
+        return hipGetLastError();
+    }
+    const BwShape s = bw_shape(N, dtype_bf16, T, C_in, C_out);
+    if (workspace_bytes < s.total) return hipErrorInvalidValue;
+    // 32-bit buffer offsets over each operand's planes; grid dimensions
+    const int S = dtype_bf16 ? 2 : 4;
+    if ((int64_t)N * C_in * s.Tp * S >= ((int64_t)1 << 31) || (int64_t)N * C_out * s.Tp * S >= ((int64_t)1 << 31))
+        return hipErrorInvalidConfiguration;
+    if (s.Tp / 64 > 0x7fffffff || (C_in + 15) / 16 > 65535 || (C_out + 15) / 16 > 65535 ||
+        (int64_t)s.tiles * s.splits > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    char* ws = static_cast<char*>(workspace);
+    if (dtype_bf16) return dispatch_backward_weight<__bf16>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
+    return dispatch_backward_weight<float>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
+}
+
+}  // namespace eql

@@ -38,6 +38,17 @@ hipError_t launch_gemm_rows(int dtype_bf16, GemmJobs jobs, const void* x, const 
 hipError_t launch_d8_fast(GemmJobs jobs, const void* x, const void* w, void* y, int64_t T, int ldx, int ldy,
                           int64_t w_elems, int cb, hipStream_t stream);
 
+// Adjoint spectrum: w_hat_adj[p][i][o] = +-w_hat[p][o][i] (imaginary planes negated).
+hipError_t launch_w_hat_adjoint(int N, int dtype_bf16, const void* w_hat, void* w_hat_adj, int C_in, int C_out,
+                                hipStream_t stream);
+
+// Weight gradient of the C_N layer into fp32 dw[C_out][C_in][N]; the workspace
+// holds the operand planes and the per-range partial spectra.
+size_t backward_weight_workspace(int N, int dtype_bf16, int64_t T, int C_in, int C_out);
+hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const void* dy, float* dw, int64_t T,
+                                     int C_in, int C_out, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 hipError_t launch_weight_dft(int N, int dtype_bf16, const void* w, void* w_hat, int C_in,
                              int C_out, hipStream_t stream);
 

@@ -159,6 +159,57 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t p, const void* x, const void* w
     return eqlinear_forward_tiled(p, x, w_hat, y, T, stream, -1);
 }
 
+eqlinear_status eqlinear_w_hat_adjoint(eqlinear_plan_t p, const void* w_hat, void* w_hat_adj, void* stream) {
+    if (!p || p->kind != EQL_KIND_CN || !w_hat || !w_hat_adj) return EQL_ERR_INVALID;
+    if (!aligned16(w_hat) || !aligned16(w_hat_adj)) return EQL_ERR_INVALID;
+    const size_t b = eqlinear_w_hat_elems(p) * elem_size(p);
+    if (overlaps(w_hat, b, w_hat_adj, b)) return EQL_ERR_INVALID;
+    return hip_status(eql::launch_w_hat_adjoint(p->N, p->dtype == EQL_BF16, w_hat, w_hat_adj, p->C_in, p->C_out,
+                                                (hipStream_t)stream));
+}
+
+eqlinear_status eqlinear_backward_data(eqlinear_plan_t p, const void* dy, const void* w_hat_adj, void* dx,
+                                       int64_t T, void* stream) {
+    if (!p || p->kind != EQL_KIND_CN) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (T == 0) return EQL_OK;
+    if (!dy || !w_hat_adj || !dx) return EQL_ERR_INVALID;
+    if (!aligned16(dy) || !aligned16(w_hat_adj) || !aligned16(dx)) return EQL_ERR_INVALID;
+    const size_t es = elem_size(p);
+    const size_t dyb = (size_t)T * out_width(p) * es, dxb = (size_t)T * in_width(p) * es;
+    const size_t wb = eqlinear_w_hat_elems(p) * es;
+    if (overlaps(dy, dyb, dx, dxb) || overlaps(w_hat_adj, wb, dx, dxb)) return EQL_ERR_INVALID;
+    // the layer with C_in and C_out exchanged, run by the forward kernels
+    return hip_status(eql::launch_cn_forward(p->N, p->dtype == EQL_BF16, dy, w_hat_adj, dx, T, p->C_out, p->C_in,
+                                             (hipStream_t)stream, -1));
+}
+
+size_t eqlinear_backward_weight_workspace(eqlinear_plan_t p, int64_t T) {
+    if (!p || p->kind != EQL_KIND_CN || T < 0) return 0;
+    return eql::backward_weight_workspace(p->N, p->dtype == EQL_BF16, T, p->C_in, p->C_out);
+}
+
+eqlinear_status eqlinear_backward_weight(eqlinear_plan_t p, const void* x, const void* dy, float* dw, int64_t T,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (!p || p->kind != EQL_KIND_CN || !dw) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (!aligned16(dw)) return EQL_ERR_INVALID;
+    const size_t dwb = eqlinear_w_hat_elems(p) * sizeof(float);
+    if (T > 0) {
+        if (!x || !dy || !workspace) return EQL_ERR_INVALID;
+        if (!aligned16(x) || !aligned16(dy) || ((uintptr_t)workspace & 255u) != 0) return EQL_ERR_INVALID;
+        const size_t need = eql::backward_weight_workspace(p->N, p->dtype == EQL_BF16, T, p->C_in, p->C_out);
+        if (workspace_bytes < need) return EQL_ERR_INVALID;
+        const size_t es = elem_size(p);
+        const size_t xb = (size_t)T * in_width(p) * es, dyb = (size_t)T * out_width(p) * es;
+        if (overlaps(dw, dwb, x, xb) || overlaps(dw, dwb, dy, dyb) || overlaps(dw, dwb, workspace, need) ||
+            overlaps(workspace, need, x, xb) || overlaps(workspace, need, dy, dyb))
+            return EQL_ERR_INVALID;
+    }
+    return hip_status(eql::launch_cn_backward_weight(p->N, p->dtype == EQL_BF16, x, dy, dw, T, p->C_in, p->C_out,
+                                                     workspace, workspace_bytes, (hipStream_t)stream));
+}
+
 eqlinear_status eqlinear_d8_forward(eqlinear_plan_t p, const void* x, const void* wb, void* y,
                                     int64_t T, void* stream) {
     if (!p || p->kind != EQL_KIND_D8) return EQL_ERR_INVALID;

@@ -152,6 +152,51 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
 eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                        void* y, int64_t T, void* stream, int tile);
 
+/* Backward pass ("Flash EQ-Linear", Implementation: the kernels cover forward
+ * and backward; Experimental Results, Operator Level, backward pass).  The
+ * pages give no formulas; these are the derivatives of the layer
+ * y[t][o][g] = sum_{i,m} w[o][i][m] x[t][i][(g-m) mod N] for an upstream
+ * gradient dy = dL/dy [T][C_out][N]:
+ *   dx[t][i][h] = sum_{o,g} w[o][i][(g-h) mod N] dy[t][o][g]
+ *   dw[o][i][m] = sum_{t,g} dy[t][o][g] x[t][i][(g-m) mod N]
+ *
+ * eqlinear_w_hat_adjoint: the spectrum of the adjoint layer, once per weight:
+ *   w_hat_adj[p][i][o] = w_hat[p][o][i] on real planes, -w_hat[p][o][i] on
+ *   imaginary planes (planes 2k, 1 <= k < N/2) -- conj(What[k])^T, the w_hat
+ *   of the layer with C_in and C_out exchanged and the group axis reversed.
+ *   Both device buffers hold N*C_in*C_out plan-dtype elements, 16-byte
+ *   aligned, not overlapping.  Asynchronous on stream; no allocation.
+ *   C_N plans only (EQL_ERR_INVALID otherwise). */
+eqlinear_status eqlinear_w_hat_adjoint(eqlinear_plan_t plan, const void* w_hat, void* w_hat_adj,
+                                       void* stream);
+
+/* Input gradient: dx [T][C_in][N] from dy [T][C_out][N] and w_hat_adj (as
+ * written by eqlinear_w_hat_adjoint), computed by the forward kernels on the
+ * exchanged-channel layer (same precision contract as eqlinear_forward).
+ * Device pointers, plan dtype, 16-byte aligned; dx must not overlap dy or
+ * w_hat_adj.  T == 0: EQL_OK, nothing launched.  Asynchronous on stream. */
+eqlinear_status eqlinear_backward_data(eqlinear_plan_t plan, const void* dy, const void* w_hat_adj,
+                                       void* dx, int64_t T, void* stream);
+
+/* Bytes of device workspace that eqlinear_backward_weight needs for T tokens
+ * (0 for T <= 0 or a non-C_N plan). */
+size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t T);
+
+/* Weight gradient: dw [C_out][C_in][N] in fp32 (overwritten, for either plan
+ * dtype) from x [T][C_in][N] and dy [T][C_out][N] in the plan dtype.  Computed
+ * in the frequency domain: real DFT of every record of x and dy along the
+ * group axis (fp32, stored in the plan dtype in the workspace), per kept bin
+ * the products C_k = sum_t DY[t][o][k] conj(X[t][i][k]) on the matrix cores
+ * with fp32 accumulation over token ranges, the ranges' partials summed in a
+ * fixed order (results are deterministic), then the inverse real DFT.
+ * workspace: device, 256-byte aligned, at least
+ * eqlinear_backward_weight_workspace(plan, T) bytes, owned by the caller and
+ * not overlapping x, dy or dw; its contents are scratch.  x, dy, dw 16-byte
+ * aligned.  T == 0 writes zeros to dw.  Asynchronous on stream; no allocation.
+ * EQL_ERR_INVALID for a D8 plan, bad pointers, overlap or a short workspace. */
+eqlinear_status eqlinear_backward_weight(eqlinear_plan_t plan, const void* x, const void* dy, float* dw,
+                                         int64_t T, void* workspace, size_t workspace_bytes, void* stream);
+
 /* D8 forward: y_rho = W_rho x_rho for rho in A1, A2, B1, B2 and
  * y_Ec = W_E x_Ec for both E coordinates c ("Quick ViTs", key design 2).
  *   x  [T][C_in], y [T][C_out], features laid out [A1|A2|B1|B2|E0|E1] with

@@ -137,6 +137,43 @@ def test_forward_validation_before_any_hip_call(eq):
     assert lib.eqlinear_dense_forward(h, None, None, None, 0, None) == eq.EQL_OK
 
 
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="uses fake device addresses; kept off machines with a GPU")
+def test_backward_validation_before_any_hip_call(eq):
+    lib = eq.load_library()
+    p = eq.eqlinear_plan(8, 32, 16, eq.EQL_BF16)
+    h = p.handle
+    A, B, W, S = 1 << 20, 1 << 30, 1 << 34, 1 << 38  # aligned, disjoint fake addresses
+    d8 = eq.eqlinear_d8_plan(16, 16, eq.EQL_F32)
+    # adjoint spectrum
+    assert lib.eqlinear_w_hat_adjoint(d8.handle, A, W, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_w_hat_adjoint(h, None, W, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_w_hat_adjoint(h, A, A + 16, None) == eq.EQL_ERR_INVALID   # overlap
+    assert lib.eqlinear_w_hat_adjoint(h, A + 2, W, None) == eq.EQL_ERR_INVALID    # misaligned
+    # input gradient
+    assert lib.eqlinear_backward_data(h, A, W, B, -1, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_backward_data(h, None, None, None, 0, None) == eq.EQL_OK
+    assert lib.eqlinear_backward_data(h, A, W, A, 5, None) == eq.EQL_ERR_INVALID  # dx aliases dy
+    assert lib.eqlinear_backward_data(h, A, W, W, 5, None) == eq.EQL_ERR_INVALID  # dx aliases w_hat_adj
+    assert lib.eqlinear_backward_data(d8.handle, A, W, B, 5, None) == eq.EQL_ERR_INVALID
+    # weight gradient
+    need = lib.eqlinear_backward_weight_workspace(h, 100)
+    assert need > 0 and need % 256 == 0
+    assert lib.eqlinear_backward_weight_workspace(h, 0) == 0
+    assert lib.eqlinear_backward_weight_workspace(h, -5) == 0
+    assert lib.eqlinear_backward_weight_workspace(d8.handle, 100) == 0
+    assert lib.eqlinear_backward_weight(h, A, B, W, -1, S, need, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_backward_weight(h, A, B, W, 100, S, need - 1, None) == eq.EQL_ERR_INVALID  # short
+    assert lib.eqlinear_backward_weight(h, A, B, W, 100, S + 16, need, None) == eq.EQL_ERR_INVALID  # 256-aligned
+    assert lib.eqlinear_backward_weight(h, A, B, W, 100, None, need, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_backward_weight(h, A, B, A, 100, S, need, None) == eq.EQL_ERR_INVALID  # dw aliases x
+    assert lib.eqlinear_backward_weight(h, A, B, W, 100, A, need, None) == eq.EQL_ERR_INVALID  # ws over x
+    assert lib.eqlinear_backward_weight(h, A, B, None, 100, S, need, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_backward_weight(d8.handle, A, B, W, 100, S, need, None) == eq.EQL_ERR_INVALID
+    # the workspace grows with T
+    assert lib.eqlinear_backward_weight_workspace(h, 10000) > need
+
+
 def test_binding_checks_tensors_without_gpu(eq):
     import torch
     p = eq.eqlinear_plan(4, 2, 2, eq.EQL_F32)

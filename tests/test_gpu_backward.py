@@ -1,0 +1,191 @@
+"""GPU parity of the backward pass (input and weight gradients) against the fp64 oracle.
+
+Same bars as the forward (tests/gpu_util.py): rel-L2 <= 1e-5 (fp32 plans) or
+<= 2e-2 (bf16 plans) over the whole output, and the largest element error
+relative to the output's RMS under 2e-4 / 1e-1.  The weight gradient is fp32
+for both plan dtypes.  Inputs come from synthetic.py (seeded); expected values
+only from oracle/.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from gpu_util import Guarded, assert_close, rel_l2, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = synthetic.F32, synthetic.BF16
+
+
+@pytest.fixture(scope="module")
+def eq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import group_equivariant_linear_amd as eq
+    eq.load_library()  # raises if the library was not built: no fallback
+    return eq
+
+
+def _eqdt(eq, dt):
+    return eq.EQL_F32 if dt == F32 else eq.EQL_BF16
+
+
+def _inputs(N, C_in, C_out, T, dt, seed):
+    """x [T][C_in][N], w [C_out][C_in][N] and an upstream gradient dy [T][C_out][N]."""
+    d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed)
+    g = synthetic.cn_inputs(N, C_out, C_in, T, dt, seed + 1000)
+    d["dy"], d["dy64"] = g["x"], g["x64"]
+    return d
+
+
+def _w_hat(eq, plan, d, N, C_in, C_out, dt):
+    wh = Guarded(N * C_out * C_in, dt)
+    eq.eqlinear_weight_fft(plan, to_dev(d["w"], dt), wh.t)
+    return wh
+
+
+def run_backward_data(eq, N, C_in, C_out, T, dt, d):
+    import torch
+    plan = eq.eqlinear_plan(N, C_in, C_out, _eqdt(eq, dt))
+    wh = _w_hat(eq, plan, d, N, C_in, C_out, dt)
+    adj = Guarded(N * C_out * C_in, dt)
+    eq.eqlinear_w_hat_adjoint(plan, wh.t, adj.t)
+    dx = Guarded(T * C_in * N, dt, (T, C_in, N))
+    eq.eqlinear_backward_data(plan, to_dev(d["dy"], dt), adj.t, dx.t, T=T)
+    torch.cuda.synchronize()
+    adj.check_guards()
+    dx.check_guards()
+    return to_f64(dx.t), to_f64(adj.t).reshape(N, C_in, C_out)
+
+
+def run_backward_weight(eq, N, C_in, C_out, T, dt, d):
+    import torch
+    plan = eq.eqlinear_plan(N, C_in, C_out, _eqdt(eq, dt))
+    nb = eq.eqlinear_backward_weight_workspace(plan, T)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    dw = Guarded(N * C_out * C_in, F32, (C_out, C_in, N))
+    eq.eqlinear_backward_weight(plan, to_dev(d["x"], dt), to_dev(d["dy"], dt), dw.t, ws, T=T)
+    torch.cuda.synchronize()
+    dw.check_guards()
+    return to_f64(dw.t)
+
+
+# --- adjoint spectrum -----------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 11, 16])
+def test_w_hat_adjoint_is_the_spectrum_of_the_adjoint_weight(eq, N, dt):
+    C_in, C_out = 37, 21  # ragged 32x32 transpose tiles on both axes
+    d = _inputs(N, C_in, C_out, 1, dt, seed=N)
+    _, adj = run_backward_data(eq, N, C_in, C_out, 1, dt, d)
+    # w'[i][o][m] = w[o][i][(-m) mod N]: the weight of the input gradient layer
+    w_adj = np.roll(d["w64"][..., ::-1], 1, axis=-1).transpose(1, 0, 2)
+    ref = oracle.cn_weight_dft(w_adj)
+    bits = 24 if dt == F32 else 8
+    _, e = np.frexp(ref)
+    half_ulp = np.ldexp(0.5, e - bits)
+    noise = 1e-13 * np.abs(d["w64"]).max()
+    assert np.all(np.abs(adj - ref) <= half_ulp * (1 + 1e-9) + noise)
+
+
+# --- input gradient ---------------------------------------------------------------------
+
+SHAPES = [(5, 7, 37), (32, 48, 150), (8, 24, 64), (96, 40, 97), (3, 130, 29)]
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 12, 16])
+def test_backward_data_sweep(eq, N, dt):
+    for C_in, C_out, T in SHAPES:
+        d = _inputs(N, C_in, C_out, T, dt, seed=7 * N + C_in)
+        dx, _ = run_backward_data(eq, N, C_in, C_out, T, dt, d)
+        ref = oracle.cn_backward_data(d["dy64"], d["w64"])
+        assert_close(dx, ref, dt, f"dx N={N} {dt} {C_in}->{C_out} T={T}")
+
+
+# --- weight gradient --------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 12, 16])
+def test_backward_weight_sweep(eq, N, dt):
+    for C_in, C_out, T in SHAPES + [(16, 16, 1), (70, 66, 1000)]:
+        d = _inputs(N, C_in, C_out, T, dt, seed=11 * N + C_out)
+        dw = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
+        ref = oracle.cn_backward_weight(d["x64"], d["dy64"])
+        # fp32 result for either plan dtype; bf16 inputs round their spectra
+        assert_close(dw, ref, dt, f"dw N={N} {dt} {C_in}->{C_out} T={T}")
+
+
+def test_backward_weight_zero_tokens_writes_zeros(eq):
+    import torch
+    N, C_in, C_out = 8, 16, 24
+    plan = eq.eqlinear_plan(N, C_in, C_out, eq.EQL_F32)
+    dw = Guarded(N * C_out * C_in, F32)
+    dw.t.fill_(3.0)
+    eq.eqlinear_backward_weight(plan, 0, 0, dw.t, torch.empty(256, dtype=torch.uint8, device="cuda"), T=0)
+    torch.cuda.synchronize()
+    dw.check_guards()
+    assert torch.count_nonzero(dw.t).item() == 0
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+def test_backward_weight_is_deterministic(eq, dt):
+    N, C_in, C_out, T = 7, 40, 72, 3000
+    d = _inputs(N, C_in, C_out, T, dt, seed=5)
+    a = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
+    b = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
+def test_gradients_satisfy_the_adjoint_identity(eq, dt):
+    """<dy, y(x)> = <dx, x> = <dw, w> with all three computed on the GPU."""
+    import torch
+    N, C_in, C_out, T = 8, 24, 40, 300
+    d = _inputs(N, C_in, C_out, T, dt, seed=9)
+    plan = eq.eqlinear_plan(N, C_in, C_out, _eqdt(eq, dt))
+    wh = _w_hat(eq, plan, d, N, C_in, C_out, dt)
+    y = Guarded(T * C_out * N, dt, (T, C_out, N))
+    eq.eqlinear_forward(plan, to_dev(d["x"], dt), wh.t, y.t, T=T)
+    dx, _ = run_backward_data(eq, N, C_in, C_out, T, dt, d)
+    dw = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
+    torch.cuda.synchronize()
+    lhs = np.sum(d["dy64"] * to_f64(y.t))
+    tol = 1e-5 if dt == F32 else 2e-2
+    scale = np.linalg.norm(d["dy64"]) * np.linalg.norm(to_f64(y.t))
+    assert abs(np.sum(dx * d["x64"]) - lhs) <= tol * scale
+    assert abs(np.sum(dw * d["w64"]) - lhs) <= tol * scale
+
+
+# --- the benchmark workloads at full size ------------------------------------------------
+
+def _sample_rows(T, n=256, seed=0):
+    rng = np.random.default_rng(seed)
+    head = np.arange(min(T, 64))
+    tail = np.arange(max(0, T - 64), T)
+    mid = rng.choice(T, size=min(T, n), replace=False)
+    return np.unique(np.concatenate([head, tail, mid]))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3a", "c3b", "c3c", "c4"])
+def test_backward_workload_full_size(eq, name):
+    wl = synthetic.WORKLOADS[name]
+    N, C_in, C_out, T, dt = wl.N, wl.C_in, wl.C_out, wl.T, wl.dtype
+    d = _inputs(N, C_in, C_out, T, dt, seed=0)
+    # input gradient on sampled token rows (each row is independent)
+    dx, _ = run_backward_data(eq, N, C_in, C_out, T, dt, d)
+    rows = _sample_rows(T)
+    ref = oracle.cn_backward_data(d["dy64"][rows], d["w64"])
+    r, m = assert_close(dx[rows], ref, dt, f"{name} dx")
+    print(f"{name} dx: rel-L2 {r:.3e} max/rms {m:.3e} over {len(rows)} tokens")
+    # weight gradient on sampled (o, i) pairs: each is the gradient of a one-channel slice
+    dw = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
+    rng = np.random.default_rng(1)
+    pairs = [(0, 0), (C_out - 1, C_in - 1)] + [(int(rng.integers(C_out)), int(rng.integers(C_in))) for _ in range(10)]
+    got = np.stack([dw[o, i] for o, i in pairs])
+    ref = np.stack([oracle.cn_backward_weight(d["x64"][:, [i]], d["dy64"][:, [o]])[0, 0] for o, i in pairs])
+    r, m = assert_close(got, ref, dt, f"{name} dw")
+    print(f"{name} dw: rel-L2 {r:.3e} max/rms {m:.3e} over {len(pairs)} (o, i) pairs")
+    assert np.all(np.isfinite(dw))
