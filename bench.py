@@ -28,6 +28,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "EQ-Linear fwd tokens/sec + TFLOP/s and % roofline vs expanded-dense GEMM"
+OP_METRIC = {
+    "forward": METRIC,
+    "backward_data": "EQ-Linear bwd (input gradient) tokens/sec + TFLOP/s and % roofline vs expanded-dense GEMM",
+    "backward_weight": "EQ-Linear bwd (weight gradient) tokens/sec + TFLOP/s and % roofline vs expanded-dense GEMM",
+}
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 KERNEL_SOURCES = {
@@ -36,6 +41,8 @@ KERNEL_SOURCES = {
           "group_equivariant_linear_amd/csrc/cn_split.h",
           "group_equivariant_linear_amd/csrc/cn_dispatch.h",
           "group_equivariant_linear_amd/csrc/eq_device.h"],
+    "BW": ["group_equivariant_linear_amd/csrc/cn_backward.hip",
+           "group_equivariant_linear_amd/csrc/eq_device.h"],
     "D8": ["group_equivariant_linear_amd/csrc/d8_forward.hip",
            "group_equivariant_linear_amd/csrc/gemm_rows.hip",
            "group_equivariant_linear_amd/csrc/eq_device.h"],
@@ -89,6 +96,8 @@ def parse():
                     help="fixed tile configuration of the C_N kernel (eqlinear_forward_tiled); -1 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample (0 disables)")
+    ap.add_argument("--op", default="forward", choices=["forward", "backward_data", "backward_weight"],
+                    help="which pass of a C_N workload to time (the default line is the forward)")
     ap.add_argument("--mode", default="bench", choices=["bench", "traffic"],
                     help="traffic: a few forwards and a copy of known size, for rocprofv3 --pmc")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -100,7 +109,7 @@ def parse():
 class Layer:
     """One layer of a workload: device buffers, plan, and the step callables."""
 
-    def __init__(self, eq, wl, seed=0, tile=-1):
+    def __init__(self, eq, wl, seed=0, tile=-1, op="forward"):
         import numpy as np
         import torch
 
@@ -158,6 +167,51 @@ class Layer:
         self.y_lin = torch.empty_like(self.y)
         # F.linear(x, W) without a bias is x @ W^T: the same GEMM, written into a fixed buffer
         self.dense_torch = lambda: torch.mm(self.x, self.W_dense.t(), out=self.y_lin)
+        self.op = op
+        self.out = self.y
+        if op != "forward":
+            self._backward(eq, wl, d, dev, eqdt, es)
+
+    def _backward(self, eq, wl, d, dev, eqdt, es):
+        """Buffers and step callables of the input- or weight-gradient pass; the
+        upstream gradient dy is a second seeded standard normal tensor."""
+        import numpy as np
+        import torch
+
+        import synthetic
+        assert wl.group == "C", "the backward pass is defined for C_N layers"
+        g = synthetic.cn_inputs(wl.N, wl.C_out, wl.C_in, wl.T, wl.dtype, 1000)
+        self.inputs["dy64"] = g["x64"]
+        self.dy = dev(g["x"]).reshape(wl.T, -1)
+        if self.op == "backward_data":
+            self.w_hat_adj = torch.empty_like(self.w_hat)
+            eq.eqlinear_w_hat_adjoint(self.plan, self.w_hat, self.w_hat_adj)
+            self.dx = torch.empty(wl.T, self.K, dtype=self.tdt, device="cuda")
+            self.step = lambda: eq.eqlinear_backward_data(self.plan, self.dy, self.w_hat_adj, self.dx, T=wl.T)
+            self.out = self.dx
+            # bytes: dy read, dx written, the adjoint spectrum
+            self.bytes_per_launch = wl.T * self.bytes_per_token + self.w_hat_bytes
+            # comparators: dx = dy W_dense, with W_dense^T materialised for the own GEMM
+            plan_t = eq.eqlinear_plan(wl.N, wl.C_out, wl.C_in, eqdt)
+            self._plan_t = plan_t
+            self.W_dense_t = self.W_dense.t().contiguous()
+            self.y_dense = torch.empty_like(self.dx)
+            self.y_lin = torch.empty_like(self.dx)
+            self.dense_own = lambda: eq.eqlinear_dense_forward(plan_t, self.dy, self.W_dense_t, self.y_dense, T=wl.T)
+            self.dense_torch = lambda: torch.mm(self.dy, self.W_dense, out=self.y_lin)
+        else:
+            nb = eq.eqlinear_backward_weight_workspace(self.plan, wl.T)
+            self.ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            self.dw = torch.empty(self.w_hat.numel(), dtype=torch.float32, device="cuda")
+            self.step = lambda: eq.eqlinear_backward_weight(self.plan, self.x, self.dy, self.dw, self.ws, T=wl.T)
+            self.out = self.dw
+            # bytes: x and dy read once, dw written in fp32
+            self.bytes_per_launch = wl.T * self.bytes_per_token + self.dw.numel() * 4
+            # comparator: the dense weight gradient dy^T x (fp32 accumulation)
+            self.y_dense = torch.empty(self.M, self.K, dtype=self.tdt, device="cuda")
+            self.y_lin = self.y_dense
+            self.dense_own = None
+            self.dense_torch = lambda: torch.mm(self.dy.t().contiguous(), self.x, out=self.y_lin)
 
 
 def time_loop(fns, steps, warmup):
@@ -235,7 +289,7 @@ def time_cold(fns, steps):
     return times[len(times) // 2]
 
 
-def cpu_baseline(layers, target_s):
+def cpu_baseline(layers, target_s, op="forward"):
     """The fp64 oracle (replicate-and-multiply) on the host cores, on a bounded
     sample: passes over the first n tokens of the batch, n sized so that a pass
     takes at most about target_s, repeated until target_s has elapsed."""
@@ -244,14 +298,14 @@ def cpu_baseline(layers, target_s):
     for L in layers:
         p = min(L.wl.T, 64)
         ts = time.perf_counter()
-        _run_oracle(L.wl, L.inputs, p)
+        _run_oracle(L.wl, L.inputs, p, op)
         per_token += (time.perf_counter() - ts) / p
     n = max(1, min(layers[0].wl.T, int(target_s / max(per_token, 1e-12))))
     passes = 0
     t0 = time.perf_counter()
     while True:
         for L in layers:
-            _run_oracle(L.wl, L.inputs, n)
+            _run_oracle(L.wl, L.inputs, n, op)
         passes += 1
         el = time.perf_counter() - t0
         if el >= target_s:
@@ -260,12 +314,17 @@ def cpu_baseline(layers, target_s):
     return {"value": passes * n / el, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{names}: {passes} pass(es) over the first {n} of {layers[0].wl.T} tokens, "
-                      f"fp64 replicate-and-multiply, {el:.1f} s"}
+                      f"fp64 {'replicate-and-multiply' if op == 'forward' else op + ' (direct sums)'}, "
+                      f"{el:.1f} s"}
 
 
-def _run_oracle(wl, d, n):
+def _run_oracle(wl, d, n, op="forward"):
     import oracle
-    if wl.group == "C":
+    if op == "backward_data":
+        oracle.cn_backward_data(d["dy64"][:n], d["w64"])
+    elif op == "backward_weight":
+        oracle.cn_backward_weight(d["x64"][:n], d["dy64"][:n])
+    elif wl.group == "C":
         oracle.cn_dense(d["x64"][:n], d["w64"])
     else:
         oracle.d8_dense(d["x64"][:n], d["w64"], wl.C_out)
@@ -311,14 +370,41 @@ def _counter_rows(d, counter):
     return rows
 
 
-def algorithmic_bytes(wl):
-    """x read once, y written once, the weight operand (w_hat, or the D8 blocks) read once."""
+def op_kernel_name(wl, op):
+    """Kernel(s) one step of the pass launches."""
+    if op == "backward_data":
+        from dataclasses import replace
+        return step_kernel_name(replace(wl, C_in=wl.C_out, C_out=wl.C_in))
+    if op == "backward_weight":
+        return "bw_planes_kernel x2 + bw_gemm_kernel + bw_reduce_kernel"
+    return step_kernel_name(wl)
+
+
+def _dense_grad_agreement(L):
+    """rel-L2 between dw and the dense gradient dy^T x folded along its
+    circulant diagonals: dw[o][i][m] = sum_g G[o*N+g][i*N+(g-m) mod N]."""
+    import torch
+    N, C_in, C_out = L.wl.N, L.wl.C_in, L.wl.C_out
+    G = L.y_dense.float().reshape(C_out, N, C_in, N)
+    g = torch.arange(N, device=G.device)
+    # two index tensors split by a slice: the indexed axis comes first
+    folded = torch.stack([G[:, g, :, (g - m) % N].sum(dim=0) for m in range(N)], dim=-1)
+    dw = L.dw.reshape(C_out, C_in, N)
+    return float(torch.linalg.vector_norm(dw - folded) / torch.linalg.vector_norm(folded))
+
+
+def algorithmic_bytes(wl, op="forward"):
+    """Forward: x read once, y written once, the weight operand (w_hat, or the D8
+    blocks) read once.  Input gradient: dy read, dx written, the adjoint
+    spectrum read.  Weight gradient: x and dy read, dw written in fp32."""
     es = 4 if wl.dtype == "f32" else 2
     if wl.group == "C":
         K, M, w = wl.N * wl.C_in, wl.N * wl.C_out, wl.N * wl.C_in * wl.C_out
     else:
         K, M = wl.C_in, wl.C_out
         w = 4 * (wl.C_in // 8) * (wl.C_out // 8) + (wl.C_in // 4) * (wl.C_out // 4)
+    if op == "backward_weight":
+        return es * wl.T * (K + M) + 4 * w
     return es * (wl.T * (K + M) + w)
 
 
@@ -415,10 +501,10 @@ def main():
     eq.load_library()
     torch.cuda.set_device(0)
 
-    layers = [Layer(eq, wl, tile=args.tile) for wl in wls]
+    layers = [Layer(eq, wl, tile=args.tile, op=args.op) for wl in wls]
     torch.cuda.synchronize()
     for L in layers:
-        assert L.bytes_per_launch == algorithmic_bytes(L.wl)
+        assert L.bytes_per_launch == algorithmic_bytes(L.wl, args.op)
     if args.mode == "traffic":
         traffic_run(layers)
         print(json.dumps({"copy_bytes": TRAFFIC_COPY_BYTES, "workload": args.workload}))
@@ -426,12 +512,14 @@ def main():
 
     steps = [L.step for L in layers]
     ms_eager = time_loop(steps, args.steps, args.warmup)
-    ms_graph = time_graph(steps, [L.y for L in layers], args.steps, args.warmup)
+    ms_graph = time_graph(steps, [L.out for L in layers], args.steps, args.warmup)
     ms = ms_graph if ms_graph is not None else ms_eager
     ms_cold = time_cold(steps, args.cold_steps) if args.cold_steps > 0 else None
     dsteps, dwarm = max(args.steps // 4, 50), max(args.warmup // 4, 5)
-    ms_own_eager = time_loop([L.dense_own for L in layers], dsteps, dwarm)
-    ms_own_graph = time_graph([L.dense_own for L in layers], [L.y_dense for L in layers], dsteps, dwarm)
+    has_own = all(L.dense_own is not None for L in layers)
+    ms_own_eager = time_loop([L.dense_own for L in layers], dsteps, dwarm) if has_own else None
+    ms_own_graph = (time_graph([L.dense_own for L in layers], [L.y_dense for L in layers], dsteps, dwarm)
+                    if has_own else None)
     ms_lin_eager = time_loop([L.dense_torch for L in layers], dsteps, dwarm)
     ms_lin_graph = time_graph([L.dense_torch for L in layers], [L.y_lin for L in layers], dsteps, dwarm)
     # a device copy moving the same number of bytes (half read, half written): the
@@ -443,15 +531,20 @@ def main():
     if ms_copy is None:
         ms_copy = time_loop([lambda: cdst.copy_(csrc)], dsteps, dwarm)
     del csrc, cdst
-    ms_own = min(t for t in (ms_own_eager, ms_own_graph) if t is not None)
+    own = [t for t in (ms_own_eager, ms_own_graph) if t is not None]
+    ms_own = min(own) if own else None
     ms_lin = min(t for t in (ms_lin_eager, ms_lin_graph) if t is not None)
     # agreement of the fused path with the dense comparator on this very batch
     for L in layers:
         L.step()
-        L.dense_own()
+        (L.dense_own if has_own else L.dense_torch)()
     torch.cuda.synchronize()
-    agree = max(float(torch.linalg.vector_norm((L.y.float() - L.y_dense.float())) /
-                      torch.linalg.vector_norm(L.y_dense.float())) for L in layers)
+    if args.op == "backward_weight":
+        # the dense gradient summed along its circulant diagonals is dw
+        agree = max(_dense_grad_agreement(L) for L in layers)
+    else:
+        agree = max(float(torch.linalg.vector_norm((L.out.float() - L.y_dense.float())) /
+                          torch.linalg.vector_norm(L.y_dense.float())) for L in layers)
 
     tokens = wls[0].T
     flops = sum(2 * L.macs_per_token * L.wl.T for L in layers)
@@ -459,12 +552,12 @@ def main():
     bytes_launch = sum(L.bytes_per_launch for L in layers)
     dt = wls[0].dtype
     achieved = bytes_launch / (ms * 1e-3) / 1e9
-    best_dense = min(ms_own, ms_lin)
+    best_dense = min(t for t in (ms_own, ms_lin) if t is not None)
     group = wls[0].group
 
-    traffic = load_traffic(args.workload, group)
+    traffic = load_traffic(args.workload, group) if args.op == "forward" else None
     out = {
-        "metric": METRIC,
+        "metric": OP_METRIC[args.op],
         "value": tokens / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -483,6 +576,7 @@ def main():
             "tokens_per_step": tokens,
             "layers_per_step": len(layers),
             "tile": args.tile,
+            "op": args.op,
         },
         "tflops_actual": flops / (ms * 1e-3) / 1e12,
         "tflops_dense_equiv": dense_flops / (ms * 1e-3) / 1e12,
@@ -507,13 +601,13 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": step_kernel_name(wls[0]),
+            "kernel": op_kernel_name(wls[0], args.op),
             "bytes_per_launch": bytes_launch,
-            "kernel_source_sha": kernel_source_hash(group),
+            "kernel_source_sha": kernel_source_hash(group if args.op != "backward_weight" else "BW"),
         },
     }
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_seconds, args.op)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))

@@ -18,7 +18,8 @@
 // a contraction over tokens for every kept bin (complex bins: Re C = a c + b d,
 // Im C = b c - a d with DY = a + ib, X = c + id).  Three launches:
 //   1. bw_planes_kernel: real DFT of every record of x and of dy, written as
-//      planes [plane][channel][token] (tokens contiguous, padded to Tp);
+//      planes [plane][channel][token] (tokens contiguous, padded to Tp) through
+//      an LDS transpose, so that reads and writes are both contiguous runs;
 //   2. bw_gemm_kernel: per 64 x 64 (o, i) tile and range of tokens, all bins'
 //      products on the matrix cores with the operand planes streamed through
 //      an LDS ring by direct global->LDS loads; fp32 partial spectra per range;
@@ -78,21 +79,34 @@ __global__ __launch_bounds__(256) void w_hat_adjoint_kernel(const IO* __restrict
 }
 
 // --- 1. planes ------------------------------------------------------------------------
-// Block: 64 tokens (one per lane) x 16 channels (4 per wave).  Record (t, c) is
-// read, transformed in fp32 and its N planes written at [p][c][t]; tokens
-// T .. Tp-1 get zeros.
+// Block: 64 channels (one per lane) x 32 tokens (8 per wave).  A wave reads the
+// records of 64 consecutive channels of one token (one contiguous run of the
+// token's row), transforms them in fp32 and leaves the N planes in LDS; the
+// block then writes each (plane, channel) row segment of 32 tokens as 16-byte
+// pieces.  Tokens T .. Tp-1 are written as zeros.
+template <int N, typename IO>
+struct PlanesCfg {
+    static constexpr int S = (int)sizeof(IO);
+    static constexpr int TT = 32, TC = 64;
+    static constexpr int PITCH = TT * S + 16;         // bytes of one staged (plane, channel) row
+    static constexpr int PIECES = TT * S / 16;        // 16-byte pieces of a row segment
+    static constexpr int LDS = N * TC * PITCH;
+};
+
 template <int N, typename IO>
 __global__ __launch_bounds__(256) void bw_planes_kernel(const IO* __restrict__ src, IO* __restrict__ planes,
                                                         int64_t T, int C, int64_t Tp) {
+    using P = PlanesCfg<N, IO>;
+    __shared__ __attribute__((aligned(16))) char stage[P::LDS];
     const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
-    const int64_t t = (int64_t)blockIdx.x * 64 + lane;
-    const int cbase = (int)blockIdx.y * 16 + wave * 4;
+    const int64_t t0 = (int64_t)blockIdx.x * P::TT;
+    const int c0 = (int)blockIdx.y * P::TC, c = c0 + lane;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = cbase + j;
-        if (c >= C) break;
-        float xv[N], P[N];
-        if (t < T) {
+    for (int j = 0; j < P::TT / 4; ++j) {
+        const int tl = wave * (P::TT / 4) + j;
+        const int64_t t = t0 + tl;
+        float xv[N], Pv[N];
+        if (t < T && c < C) {
             const IO* r = src + (t * C + c) * N;
 #pragma unroll
             for (int h = 0; h < N; ++h) xv[h] = to_f32(r[h]);
@@ -100,29 +114,42 @@ __global__ __launch_bounds__(256) void bw_planes_kernel(const IO* __restrict__ s
 #pragma unroll
             for (int h = 0; h < N; ++h) xv[h] = 0.0f;
         }
-        rdft_forward<N>(xv, P);
+        rdft_forward<N>(xv, Pv);
 #pragma unroll
-        for (int p = 0; p < N; ++p) planes[((int64_t)p * C + c) * Tp + t] = (IO)P[p];
+        for (int p = 0; p < N; ++p)
+            *reinterpret_cast<IO*>(stage + (p * P::TC + lane) * P::PITCH + tl * P::S) = (IO)Pv[p];
+    }
+    __syncthreads();
+    for (int k = (int)threadIdx.x; k < N * P::TC * P::PIECES; k += 256) {
+        const int row = k / P::PIECES, piece = k % P::PIECES;
+        const int p = row / P::TC, cl = row % P::TC;
+        if (c0 + cl >= C) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * P::PITCH + piece * 16);
+        char* dst = reinterpret_cast<char*>(planes + ((int64_t)p * C + c0 + cl) * Tp + t0);
+        *reinterpret_cast<u32x4*>(dst + piece * 16) = v;
     }
 }
 
 // --- 2. per-bin products over tokens --------------------------------------------------
-template <int N_, typename IO_>
+template <int N_, typename IO_, int WG_>
 struct BwCfg {
     static constexpr int N = N_;
     using IO = IO_;
     static constexpr int S = (int)sizeof(IO);
     static constexpr int KC = 64 / S;          // tokens of one chunk: 64 bytes of a plane row
-    static constexpr int TM = 64, TN = 64;     // output rows (o) and columns (i) per workgroup
-    static constexpr int kThreads = 256;       // 2 x 2 waves, 32 x 32 each
+    static constexpr int WG = WG_;             // waves per side: WG x WG waves of 32 x 32 outputs
+    static constexpr int TM = 32 * WG, TN = 32 * WG;  // output rows (o) and columns (i) per workgroup
+    static constexpr int kThreads = 64 * WG * WG;
     static constexpr int H = (N - 1) / 2;      // complex bins
     static constexpr bool NYQ = N % 2 == 0 && N > 1;
     static constexpr int NB = 1 + H + (NYQ ? 1 : 0);  // bins
-    static constexpr int PBYTES = 64 * 64;     // one plane of one operand: 64 rows x 64 bytes
+    static constexpr int PBYTES = TM * 64;     // one plane of one operand: TM rows x 64 bytes
+    static constexpr int PL = PBYTES / 16 / kThreads;  // direct loads per thread and plane
     static constexpr int STAGE = 4 * PBYTES;   // two planes of each operand
-    static constexpr int ST = 3;               // ring stages (two in flight)
+    static constexpr int ST = 5;               // ring stages (four in flight)
     static constexpr int LDS = ST * STAGE;
-    static constexpr int LOADS = 4;            // direct loads per thread and stage
+    static constexpr int LOADS = 4 * PL;       // direct loads per thread and stage
+    static_assert(PBYTES % (16 * kThreads) == 0, "whole loads per plane");
 };
 
 __device__ __forceinline__ void bw_mma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
@@ -169,7 +196,10 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
     constexpr int N = C::N, H = C::H, NB = C::NB, ST = C::ST, S = C::S;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
-    const int tile = (int)(blockIdx.x % (uint32_t)tiles), split = (int)(blockIdx.x / (uint32_t)tiles);
+    // the tiles of one token range are consecutive logical blocks, kept on one
+    // XCD: they read the same plane rows, which its L2 then serves once
+    const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = (int)(lb % (uint32_t)tiles), split = (int)(lb / (uint32_t)tiles);
     const int o0 = (tile / n_i) * C::TM, i0 = (tile % n_i) * C::TN;
     const int c_begin = split * chunks_per_split;
     const int c_end = c_begin + chunks_per_split < nchunks ? c_begin + chunks_per_split : nchunks;
@@ -177,17 +207,21 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
 
     const int tid = (int)threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WG, wn = wave % C::WG;
 
     const uint32_t row_bytes = (uint32_t)(Tp * S);
     const uint32_t pa = (uint32_t)C_out * row_bytes, pb = (uint32_t)C_in * row_bytes;  // plane strides
     const __amdgpu_buffer_rsrc_t ra = bw_rsrc(dyp, (uint32_t)N * pa);
     const __amdgpu_buffer_rsrc_t rb = bw_rsrc(xp, (uint32_t)N * pb);
 
-    // this thread's load: row r = tid / 4, 16-byte part u = tid % 4 of a plane block
-    const int r = tid >> 2, u = tid & 3;
-    const uint32_t offa = o0 + r < C_out ? (uint32_t)(o0 + r) * row_bytes + (uint32_t)u * 16u : kBwOOB;
-    const uint32_t offb = i0 + r < C_in ? (uint32_t)(i0 + r) * row_bytes + (uint32_t)u * 16u : kBwOOB;
+    // load l of this thread fills slot l*kThreads + tid: row slot/4, 16-byte part slot%4
+    uint32_t offa[C::PL], offb[C::PL];
+#pragma unroll
+    for (int l = 0; l < C::PL; ++l) {
+        const int slot = l * C::kThreads + tid, r = slot >> 2, u = slot & 3;
+        offa[l] = o0 + r < C_out ? (uint32_t)(o0 + r) * row_bytes + (uint32_t)u * 16u : kBwOOB;
+        offb[l] = i0 + r < C_in ? (uint32_t)(i0 + r) * row_bytes + (uint32_t)u * 16u : kBwOOB;
+    }
 
     // planes of bin b: first (real part, or the only plane), second (imaginary)
     auto plane0 = [&](int b) { return b == 0 ? 0 : (b <= H ? 2 * b - 1 : N - 1); };
@@ -198,19 +232,23 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
         const int p0 = plane0(b);
         const bool cplx = b >= 1 && b <= H;
         const uint32_t soff = (uint32_t)cq * 64u;  // KC tokens = 64 bytes along a row
-        const uint32_t a0 = live && offa != kBwOOB ? offa + (uint32_t)p0 * pa : kBwOOB;
-        const uint32_t b0 = live && offb != kBwOOB ? offb + (uint32_t)p0 * pb : kBwOOB;
-        const uint32_t a1 = live && cplx && offa != kBwOOB ? a0 + pa : kBwOOB;
-        const uint32_t b1 = live && cplx && offb != kBwOOB ? b0 + pb : kBwOOB;
         // every thread issues LOADS loads for every stage, so vmcnt counts stages
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(st + wave * 1024), 16,
-                                                 a0, soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(st + C::PBYTES + wave * 1024), 16, a1, soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (__attribute__((address_space(3))) void*)(st + 2 * C::PBYTES + wave * 1024), 16, b0, soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rb, (__attribute__((address_space(3))) void*)(st + 3 * C::PBYTES + wave * 1024), 16, b1, soff, 0, 0);
+#pragma unroll
+        for (int l = 0; l < C::PL; ++l) {
+            const uint32_t a0 = live && offa[l] != kBwOOB ? offa[l] + (uint32_t)p0 * pa : kBwOOB;
+            const uint32_t b0 = live && offb[l] != kBwOOB ? offb[l] + (uint32_t)p0 * pb : kBwOOB;
+            const uint32_t a1 = live && cplx && offa[l] != kBwOOB ? a0 + pa : kBwOOB;
+            const uint32_t b1 = live && cplx && offb[l] != kBwOOB ? b0 + pb : kBwOOB;
+            char* d = st + (l * C::kThreads + wave * 64) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(d), 16, a0,
+                                                     soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(d + C::PBYTES), 16,
+                                                     a1, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (__attribute__((address_space(3))) void*)(d + 2 * C::PBYTES), 16, b0, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (__attribute__((address_space(3))) void*)(d + 3 * C::PBYTES), 16, b1, soff, 0, 0);
+        }
     };
 
     f32x4 acc[2][2][N];
@@ -302,23 +340,40 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
 }
 
 // --- 3. reduction and inverse transform ------------------------------------------------
-// Thread per (o, i): partials summed in split order, then the inverse real DFT
-// of the packed spectrum C gives dw[o][i][0 .. N-1].
+// Block: 32 consecutive (o, i) elements x N planes, one thread each.  Thread
+// (p, e) sums the partials of plane p in split order (loads issued eight at a
+// time, added in order); then one thread per element runs the inverse real DFT
+// of its packed spectrum and writes dw[o][i][0 .. N-1].
 template <int N>
-__global__ __launch_bounds__(256) void bw_reduce_kernel(const float* __restrict__ part, float* __restrict__ dw,
-                                                        int splits, int64_t plane) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= plane) return;
-    float P[N], y[N];
+__global__ __launch_bounds__(32 * N) void bw_reduce_kernel(const float* __restrict__ part, float* __restrict__ dw,
+                                                           int splits, int64_t plane) {
+    __shared__ float red[32][N + 1];
+    const int el = (int)threadIdx.x & 31, p = (int)threadIdx.x >> 5;
+    const int64_t e = (int64_t)blockIdx.x * 32 + el;
+    float v = 0.0f;
+    if (e < plane) {
+        const float* src = part + (int64_t)p * plane + e;
+        const int64_t step = (int64_t)N * plane;
+        int s = 0;
+        for (; s + 8 <= splits; s += 8) {
+            float t[8];
 #pragma unroll
-    for (int p = 0; p < N; ++p) {
-        float v = 0.0f;
-        for (int s = 0; s < splits; ++s) v += part[((int64_t)s * N + p) * plane + e];
-        P[p] = v;
+            for (int j = 0; j < 8; ++j) t[j] = src[(int64_t)(s + j) * step];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v += t[j];
+        }
+        for (; s < splits; ++s) v += src[(int64_t)s * step];
     }
-    rdft_inverse<N>(P, y);
+    red[el][p] = v;
+    __syncthreads();
+    if (p == 0 && e < plane) {
+        float P[N], y[N];
 #pragma unroll
-    for (int m = 0; m < N; ++m) dw[e * N + m] = y[m];
+        for (int q = 0; q < N; ++q) P[q] = red[el][q];
+        rdft_inverse<N>(P, y);
+#pragma unroll
+        for (int m = 0; m < N; ++m) dw[e * N + m] = y[m];
+    }
 }
 
 // --- host side ---------------------------------------------------------------------------
@@ -331,18 +386,25 @@ struct BwShape {
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
+// Layers with at most 32 output and input channels take one-wave 32 x 32
+// tiles (a 64 x 64 tile would be three quarters padding); the others 2 x 2
+// waves over 64 x 64.
+int bw_wg(int C_in, int C_out) { return (C_in <= 32 && C_out <= 32) ? 1 : 2; }
+
 BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     BwShape s{};
     const int S = bf16 ? 2 : 4, KC = 64 / S;
+    const int tm = 32 * bw_wg(C_in, C_out);
     s.Tp = (T + 63) / 64 * 64;
-    s.n_o = (C_out + 63) / 64;
-    s.n_i = (C_in + 63) / 64;
+    s.n_o = (C_out + tm - 1) / tm;
+    s.n_i = (C_in + tm - 1) / tm;
     s.tiles = s.n_o * s.n_i;
     s.nchunks = (int)(s.Tp / KC);
-    // token ranges: enough workgroups to cover the chip, while the fp32 partials
-    // stay within about an eighth of the operand planes' bytes
-    const int64_t want = (256 + s.tiles - 1) / s.tiles;
-    const int64_t cap = ((int64_t)(C_in + C_out) * s.Tp * S) / ((int64_t)8 * C_out * C_in * 4);
+    // token ranges: enough waves to give every SIMD one (one-wave tiles, ranges
+    // down to one chunk) or every CU a workgroup (ranges of four chunks or more)
+    const bool small = bw_wg(C_in, C_out) == 1;
+    const int64_t want = ((small ? 1024 : 256) + s.tiles - 1) / s.tiles;
+    const int64_t cap = small ? s.nchunks : s.nchunks / 4;
     int64_t sp = want < cap ? want : cap;
     sp = sp < 1 ? 1 : (sp > s.nchunks ? s.nchunks : sp);
     s.chunks_per_split = (int)((s.nchunks + sp - 1) / sp);
@@ -354,15 +416,16 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     return s;
 }
 
-template <int N, typename IO>
+template <int N, typename IO, int WG>
 hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t T, int C_in, int C_out,
                                char* ws, const BwShape& s, hipStream_t stream) {
-    using Cfg = BwCfg<N, IO>;
+    using Cfg = BwCfg<N, IO, WG>;
     IO* xp = reinterpret_cast<IO*>(ws);
     IO* dyp = reinterpret_cast<IO*>(ws + s.xp_bytes);
     float* part = reinterpret_cast<float*>(ws + s.xp_bytes + s.dyp_bytes);
-    const dim3 gx((uint32_t)(s.Tp / 64), (uint32_t)((C_in + 15) / 16));
-    const dim3 gy((uint32_t)(s.Tp / 64), (uint32_t)((C_out + 15) / 16));
+    constexpr int PT = PlanesCfg<N, IO>::TT;  // Tp is a multiple of 64, hence of PT
+    const dim3 gx((uint32_t)(s.Tp / PT), (uint32_t)((C_in + 63) / 64));
+    const dim3 gy((uint32_t)(s.Tp / PT), (uint32_t)((C_out + 63) / 64));
     hipLaunchKernelGGL((bw_planes_kernel<N, IO>), gx, dim3(256), 0, stream, (const IO*)x, xp, T, C_in, s.Tp);
     hipLaunchKernelGGL((bw_planes_kernel<N, IO>), gy, dim3(256), 0, stream, (const IO*)dy, dyp, T, C_out, s.Tp);
     const int64_t wgs = (int64_t)s.tiles * s.splits;
@@ -370,7 +433,7 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
                        (const IO*)dyp, (const IO*)xp, part, C_out, C_in, s.Tp, s.n_i, s.tiles,
                        s.chunks_per_split, s.nchunks);
     const int64_t plane = (int64_t)C_out * C_in;
-    hipLaunchKernelGGL((bw_reduce_kernel<N>), dim3((uint32_t)((plane + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bw_reduce_kernel<N>), dim3((uint32_t)((plane + 31) / 32)), dim3(32 * N), 0, stream,
                        (const float*)part, dw, s.splits, plane);
     return hipGetLastError();
 }
@@ -379,8 +442,10 @@ template <typename IO>
 hipError_t dispatch_backward_weight(int N, const void* x, const void* dy, float* dw, int64_t T, int C_in,
                                     int C_out, char* ws, const BwShape& s, hipStream_t stream) {
     switch (N) {
-#define EQL_BW(n) \
-    case n: return run_backward_weight<n, IO>(x, dy, dw, T, C_in, C_out, ws, s, stream);
+#define EQL_BW(n)                                                                           \
+    case n:                                                                                 \
+        return bw_wg(C_in, C_out) == 1 ? run_backward_weight<n, IO, 1>(x, dy, dw, T, C_in, C_out, ws, s, stream) \
+                                        : run_backward_weight<n, IO, 2>(x, dy, dw, T, C_in, C_out, ws, s, stream);
         EQL_BW(1) EQL_BW(2) EQL_BW(3) EQL_BW(4) EQL_BW(5) EQL_BW(6) EQL_BW(7) EQL_BW(8)
         EQL_BW(9) EQL_BW(10) EQL_BW(11) EQL_BW(12) EQL_BW(13) EQL_BW(14) EQL_BW(15) EQL_BW(16)
 #undef EQL_BW
@@ -427,7 +492,7 @@ hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const
     const int S = dtype_bf16 ? 2 : 4;
     if ((int64_t)N * C_in * s.Tp * S >= ((int64_t)1 << 31) || (int64_t)N * C_out * s.Tp * S >= ((int64_t)1 << 31))
         return hipErrorInvalidConfiguration;
-    if (s.Tp / 64 > 0x7fffffff || (C_in + 15) / 16 > 65535 || (C_out + 15) / 16 > 65535 ||
+    if (s.Tp / 32 > 0x7fffffff || (C_in + 63) / 64 > 65535 || (C_out + 63) / 64 > 65535 ||
         (int64_t)s.tiles * s.splits > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     char* ws = static_cast<char*>(workspace);
