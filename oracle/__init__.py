@@ -70,6 +70,8 @@ def _load():
         lib.eqref_cn_backward_data.restype = None
         lib.eqref_cn_backward_weight.argtypes = [i, i, i, i64, d, d, d]
         lib.eqref_cn_backward_weight.restype = None
+        lib.eqref_bias_act.argtypes = [i64, i, i, d, i, d]
+        lib.eqref_bias_act.restype = None
         lib.eqref_cn_weight_dft.argtypes = [i, i, i, d, d]
         lib.eqref_cn_weight_dft.restype = None
         lib.eqref_d8_expand.argtypes = [i, i, d, d]
@@ -176,6 +178,22 @@ def cn_backward_weight(x, dy):
     dw = np.empty((C_out, C_in, N), dtype=np.float64)
     _load().eqref_cn_backward_weight(N, C_in, C_out, T, _p(x), _p(dy), _p(dw))
     return dw
+
+
+def bias_act(y, bias=None, act=0):
+    """act(y + bias[o]) along [T][C_out][N] (act 0: identity, 1: GELU, erf form); returns a copy."""
+    y = np.array(y, dtype=np.float64, copy=True, order="C")
+    T, C_out, N = y.shape
+    b = None if bias is None else _f64(bias)
+    if b is not None:
+        assert b.shape == (C_out,)
+    _load().eqref_bias_act(T, C_out, N, None if b is None else _p(b), int(act), _p(y))
+    return y
+
+
+def cn_dense_bias_act(x, w, bias=None, act=0):
+    """The C_N layer followed by the fused neighbours: act(y + bias)."""
+    return bias_act(cn_dense(x, w), bias, act)
 
 
 def cn_weight_dft(w):

@@ -36,6 +36,15 @@
  *        dw[o][i][m] = sum_{t,g} dy[t][o][g] * x[t][i][(g-m) mod N]
  *    (eqref_cn_backward_weight).
  *
+ *  - Fused neighbours of the layer in an MLP.  "Quick ViTs" (papernotes), key
+ *    design 2: the MLP keeps its expansion, GELU and contraction, and GELU is
+ *    applied where the group acts by permuting coordinates (the regular
+ *    representation), which for C_N is y[t][o][g] itself: the group acts by a
+ *    cyclic shift along g.  A per-channel bias constant along g and a pointwise
+ *    GELU both commute with that shift.  eqref_bias_act applies, in place,
+ *        y[t][o][g] <- act(y[t][o][g] + b[o]),  GELU(v) = v * Phi(v)
+ *    with Phi the standard normal distribution function, 0.5 (1 + erf(v/sqrt 2)).
+ *
  *  - D8 Fourier-domain layer.  "Quick ViTs" (papernotes), key design 2
  *    (Fourier-domain equivariant computation): a width-C map is four square
  *    blocks of size C/8 (irreps A1, A2, B1, B2) and one square block of size
@@ -167,6 +176,21 @@ void eqref_cn_backward_weight(int N, int C_in, int C_out, int64_t T, const doubl
                         acc += dy[(t * C_out + o) * N + g] * x[(t * C_in + i) * N + h];
                     }
                 dw[((int64_t)o * C_in + i) * N + m] = acc;
+            }
+}
+
+/* In place: y[t][o][g] = act(y[t][o][g] + bias[o]); bias may be NULL, act 0 =
+ * identity, 1 = GELU (erf form). */
+void eqref_bias_act(int64_t T, int C_out, int N, const double* bias, int act, double* y) {
+    const double rsqrt2 = 1.0 / sqrt(2.0);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int o = 0; o < C_out; ++o)
+            for (int g = 0; g < N; ++g) {
+                double v = y[(t * C_out + o) * N + g];
+                if (bias) v += bias[o];
+                if (act == 1) v = 0.5 * v * (1.0 + erf(v * rsqrt2));
+                y[(t * C_out + o) * N + g] = v;
             }
 }
 

@@ -200,7 +200,28 @@ def pin_backward_equivariance(orc):
         assert rel(orc.cn_backward_weight(np.roll(x, s, -1), np.roll(dy, s, -1)), dw) < 1e-14
 
 
-ALL_CN_PINS = [pin_rfft_route, pin_weight_dft, pin_closed_forms, pin_dense_matrix_structure,
+def pin_bias_act(orc):
+    """GELU(v) = v Phi(v) with scipy's normal CDF; the odd-part identity
+    GELU(v) - GELU(-v) = v; textbook values at +-1; the bias is per output
+    channel and constant along the group axis; equivariance survives."""
+    import scipy.special
+    v = np.linspace(-6.0, 6.0, 97).reshape(1, 1, 97)
+    g = orc.bias_act(v, None, 1)
+    assert np.max(np.abs(g - v * scipy.special.ndtr(v))) < 1e-15
+    assert np.max(np.abs((g - orc.bias_act(-v, None, 1)) - v)) < 1e-14
+    one = orc.bias_act(np.array([1.0, -1.0, 0.0]).reshape(1, 1, 3), None, 1).ravel()
+    assert abs(one[0] - 0.8413447460685429) < 1e-15 and abs(one[1] + 0.15865525393145707) < 1e-15 and one[2] == 0.0
+    N, C_in, C_out, T = 5, 3, 4, 6
+    x, w, b = _rand(T, C_in, N), _rand(C_out, C_in, N), _rand(C_out)
+    y = orc.cn_dense(x, w)
+    assert np.array_equal(orc.bias_act(y, b, 0), y + b[None, :, None])
+    assert np.array_equal(orc.bias_act(y, None, 0), y)
+    yb = orc.cn_dense_bias_act(x, w, b, 1)
+    for s in (1, 3):
+        assert rel(orc.cn_dense_bias_act(np.roll(x, s, -1), w, b, 1), np.roll(yb, s, -1)) < 1e-14
+
+
+ALL_CN_PINS = [pin_rfft_route, pin_weight_dft, pin_closed_forms, pin_dense_matrix_structure, pin_bias_act,
                pin_backward_adjoint, pin_backward_closed_forms, pin_backward_equivariance]
 
 
@@ -250,6 +271,10 @@ def test_backward_closed_forms():
 
 def test_backward_equivariance():
     pin_backward_equivariance(oracle)
+
+
+def test_bias_and_gelu():
+    pin_bias_act(oracle)
 
 
 def test_dense_matrix_structure():
@@ -452,6 +477,8 @@ MUTANTS = [
      "acc += dy[(t * C_out + o) * N + g] * x[(t * C_in + (i % C_out) % C_in) * N + h];"),
     ("dense transpose drops a row", "for (int64_t r = 0; r < rows; ++r) acc += W[r * cols + c] * dyt[r];",
      "for (int64_t r = 1; r < rows; ++r) acc += W[r * cols + c] * dyt[r];"),
+    ("bias along the group axis", "if (bias) v += bias[o];", "if (bias) v += bias[g % C_out];"),
+    ("GELU without the 1/sqrt(2)", "v = 0.5 * v * (1.0 + erf(v * rsqrt2));", "v = 0.5 * v * (1.0 + erf(v));"),
     ("D8 transposed 1-D block", "blk[(int64_t)r * mi + c];", "blk[(int64_t)c * mi + r];"),
     ("D8 E weight on coordinate 0 only", "4 * mi + 2 * e * mi + c] =", "4 * mi + c] ="),
 ]
@@ -526,6 +553,8 @@ def test_oracle_under_sanitizers(tmp_path):
         "lib.eqref_cn_backward_weight(5, 2, 4, 3, p(x), p(y), p(dw))\n"
         "Wd = np.ones((20, 10)); lib.eqref_apply_dense_t.argtypes = [ctypes.c_int64]*3 + [ctypes.c_void_p]*3\n"
         "lib.eqref_apply_dense_t(3, 20, 10, p(Wd), p(y), p(dx))\n"
+        "bb = np.ones(4); lib.eqref_bias_act.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]\n"
+        "lib.eqref_bias_act(3, 4, 5, p(bb), 1, p(y))\n"
         "wb = np.ones(16*16//8); xd = np.ones((2, 16)); yd = np.zeros((2, 16))\n"
         "lib.eqref_d8_dense.argtypes = [ctypes.c_int]*2 + [ctypes.c_int64] + [ctypes.c_void_p]*3\n"
         "assert lib.eqref_d8_dense(16, 16, 2, p(xd), p(wb), p(yd)) == 0\n"
