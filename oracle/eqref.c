@@ -43,7 +43,9 @@
  *    cyclic shift along g.  A per-channel bias constant along g and a pointwise
  *    GELU both commute with that shift.  eqref_bias_act applies, in place,
  *        y[t][o][g] <- act(y[t][o][g] + b[o]),  GELU(v) = v * Phi(v)
- *    with Phi the standard normal distribution function, 0.5 (1 + erf(v/sqrt 2)).
+ *    with Phi the standard normal distribution function, written as
+ *    erfc(-v/sqrt 2) / 2 (equal to (1 + erf(v/sqrt 2)) / 2, but without the
+ *    cancellation of 1 + erf for negative v, so the tail keeps its digits).
  *
  *  - D8 Fourier-domain layer.  "Quick ViTs" (papernotes), key design 2
  *    (Fourier-domain equivariant computation): a width-C map is four square
@@ -180,7 +182,7 @@ void eqref_cn_backward_weight(int N, int C_in, int C_out, int64_t T, const doubl
 }
 
 /* In place: y[t][o][g] = act(y[t][o][g] + bias[o]); bias may be NULL, act 0 =
- * identity, 1 = GELU (erf form). */
+ * identity, 1 = GELU (erf form, GELU(v) = v Phi(v), Phi(v) = erfc(-v/sqrt 2)/2). */
 void eqref_bias_act(int64_t T, int C_out, int N, const double* bias, int act, double* y) {
     const double rsqrt2 = 1.0 / sqrt(2.0);
 #pragma omp parallel for schedule(static)
@@ -189,7 +191,7 @@ void eqref_bias_act(int64_t T, int C_out, int N, const double* bias, int act, do
             for (int g = 0; g < N; ++g) {
                 double v = y[(t * C_out + o) * N + g];
                 if (bias) v += bias[o];
-                if (act == 1) v = 0.5 * v * (1.0 + erf(v * rsqrt2));
+                if (act == 1) v = 0.5 * v * erfc(-v * rsqrt2);
                 y[(t * C_out + o) * N + g] = v;
             }
 }

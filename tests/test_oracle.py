@@ -209,6 +209,12 @@ def pin_bias_act(orc):
     g = orc.bias_act(v, None, 1)
     assert np.max(np.abs(g - v * scipy.special.ndtr(v))) < 1e-15
     assert np.max(np.abs((g - orc.bias_act(-v, None, 1)) - v)) < 1e-14
+    # relative accuracy in the far negative tail, where 1 + erf would cancel
+    # (scipy's ndtr takes erfc there): GELU(-30) is about -3e-196.  The bound is
+    # the rounding of the argument v/sqrt 2 carried through erfc, about 2 z^2 2^-53.
+    tail = np.linspace(-30.0, -5.0, 51).reshape(1, 1, 51)
+    ref = tail * scipy.special.ndtr(tail)
+    assert np.all(np.abs(orc.bias_act(tail, None, 1) - ref) <= 1e-12 * np.abs(ref))
     one = orc.bias_act(np.array([1.0, -1.0, 0.0]).reshape(1, 1, 3), None, 1).ravel()
     assert abs(one[0] - 0.8413447460685429) < 1e-15 and abs(one[1] + 0.15865525393145707) < 1e-15 and one[2] == 0.0
     N, C_in, C_out, T = 5, 3, 4, 6
@@ -478,7 +484,8 @@ MUTANTS = [
     ("dense transpose drops a row", "for (int64_t r = 0; r < rows; ++r) acc += W[r * cols + c] * dyt[r];",
      "for (int64_t r = 1; r < rows; ++r) acc += W[r * cols + c] * dyt[r];"),
     ("bias along the group axis", "if (bias) v += bias[o];", "if (bias) v += bias[g % C_out];"),
-    ("GELU without the 1/sqrt(2)", "v = 0.5 * v * (1.0 + erf(v * rsqrt2));", "v = 0.5 * v * (1.0 + erf(v));"),
+    ("GELU without the 1/sqrt(2)", "v = 0.5 * v * erfc(-v * rsqrt2);", "v = 0.5 * v * erfc(-v);"),
+    ("GELU with Phi of the wrong sign", "v = 0.5 * v * erfc(-v * rsqrt2);", "v = 0.5 * v * erfc(v * rsqrt2);"),
     ("D8 transposed 1-D block", "blk[(int64_t)r * mi + c];", "blk[(int64_t)c * mi + r];"),
     ("D8 E weight on coordinate 0 only", "4 * mi + 2 * e * mi + c] =", "4 * mi + c] ="),
 ]
