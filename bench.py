@@ -98,6 +98,9 @@ def parse():
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--op", default="forward", choices=["forward", "backward_data", "backward_weight"],
                     help="which pass of a C_N workload to time (the default line is the forward)")
+    ap.add_argument("--epilogue", default="none", choices=["none", "bias", "bias_gelu"],
+                    help="forward of a C_N workload with the fused per-channel bias (and GELU) "
+                         "of eqlinear_forward_bias_act; the comparators add the same in torch")
     ap.add_argument("--mode", default="bench", choices=["bench", "traffic"],
                     help="traffic: a few forwards and a copy of known size, for rocprofv3 --pmc")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -109,7 +112,7 @@ def parse():
 class Layer:
     """One layer of a workload: device buffers, plan, and the step callables."""
 
-    def __init__(self, eq, wl, seed=0, tile=-1, op="forward"):
+    def __init__(self, eq, wl, seed=0, tile=-1, op="forward", epilogue="none"):
         import numpy as np
         import torch
 
@@ -169,8 +172,40 @@ class Layer:
         self.dense_torch = lambda: torch.mm(self.x, self.W_dense.t(), out=self.y_lin)
         self.op = op
         self.out = self.y
+        self.post = None
         if op != "forward":
             self._backward(eq, wl, d, dev, eqdt, es)
+        elif epilogue != "none":
+            self._epilogue(eq, wl, d, dev, es, tile, epilogue)
+
+    def _epilogue(self, eq, wl, d, dev, es, tile, epilogue):
+        """Forward with the fused bias (+ GELU).  The comparators run the dense GEMM
+        with torch's bias add and in-place GELU after it."""
+        import torch
+
+        import synthetic
+        assert wl.group == "C", "the fused bias and activation belong to the C_N forward"
+        bd, d["b64"] = synthetic.channel_bias(wl.C_out, wl.dtype, 500)
+        self.bias = dev(bd)
+        act = eq.EQL_ACT_GELU if epilogue == "bias_gelu" else eq.EQL_ACT_NONE
+        d["act"] = act
+        self.step = lambda: eq.eqlinear_forward_bias_act(self.plan, self.x, self.w_hat, self.bias, act, self.y,
+                                                         T=wl.T, tile=tile)
+        self.bytes_per_launch += wl.C_out * es
+        # y is [t][o][g]: column o*N+g carries b[o]
+        bias_cols = self.bias.repeat_interleave(wl.N)
+        gelu_ = torch._C._nn.gelu_
+
+        def dense_torch():
+            torch.addmm(bias_cols, self.x, self.W_dense.t(), out=self.y_lin)
+            if act == eq.EQL_ACT_GELU:
+                gelu_(self.y_lin)
+        self.dense_torch = dense_torch
+
+        def post(t):  # the same neighbours on the own GEMM's output, for the agreement figure
+            v = t.float() + bias_cols.float()
+            return torch.nn.functional.gelu(v) if act == eq.EQL_ACT_GELU else v
+        self.post = post
 
     def _backward(self, eq, wl, d, dev, eqdt, es):
         """Buffers and step callables of the input- or weight-gradient pass; the
@@ -320,7 +355,9 @@ def cpu_baseline(layers, target_s, op="forward"):
 
 def _run_oracle(wl, d, n, op="forward"):
     import oracle
-    if op == "backward_data":
+    if "b64" in d:
+        oracle.cn_dense_bias_act(d["x64"][:n], d["w64"], d["b64"], d["act"])
+    elif op == "backward_data":
         oracle.cn_backward_data(d["dy64"][:n], d["w64"])
     elif op == "backward_weight":
         oracle.cn_backward_weight(d["x64"][:n], d["dy64"][:n])
@@ -393,9 +430,9 @@ def _dense_grad_agreement(L):
     return float(torch.linalg.vector_norm(dw - folded) / torch.linalg.vector_norm(folded))
 
 
-def algorithmic_bytes(wl, op="forward"):
+def algorithmic_bytes(wl, op="forward", epilogue="none"):
     """Forward: x read once, y written once, the weight operand (w_hat, or the D8
-    blocks) read once.  Input gradient: dy read, dx written, the adjoint
+    blocks) read once, plus the bias when one is fused.  Input gradient: dy read, dx written, the adjoint
     spectrum read.  Weight gradient: x and dy read, dw written in fp32."""
     es = 4 if wl.dtype == "f32" else 2
     if wl.group == "C":
@@ -405,7 +442,8 @@ def algorithmic_bytes(wl, op="forward"):
         w = 4 * (wl.C_in // 8) * (wl.C_out // 8) + (wl.C_in // 4) * (wl.C_out // 4)
     if op == "backward_weight":
         return es * wl.T * (K + M) + 4 * w
-    return es * (wl.T * (K + M) + w)
+    bias = wl.C_out if epilogue != "none" else 0
+    return es * (wl.T * (K + M) + w + bias)
 
 
 def summarize_traffic(args, wls):
@@ -501,10 +539,13 @@ def main():
     eq.load_library()
     torch.cuda.set_device(0)
 
-    layers = [Layer(eq, wl, tile=args.tile, op=args.op) for wl in wls]
+    if args.epilogue != "none" and (args.op != "forward" or any(wl.group != "C" for wl in wls)):
+        print("--epilogue applies to the forward of C_N workloads", file=sys.stderr)
+        sys.exit(2)
+    layers = [Layer(eq, wl, tile=args.tile, op=args.op, epilogue=args.epilogue) for wl in wls]
     torch.cuda.synchronize()
     for L in layers:
-        assert L.bytes_per_launch == algorithmic_bytes(L.wl, args.op)
+        assert L.bytes_per_launch == algorithmic_bytes(L.wl, args.op, args.epilogue)
     if args.mode == "traffic":
         traffic_run(layers)
         print(json.dumps({"copy_bytes": TRAFFIC_COPY_BYTES, "workload": args.workload}))
@@ -543,8 +584,12 @@ def main():
         # the dense gradient summed along its circulant diagonals is dw
         agree = max(_dense_grad_agreement(L) for L in layers)
     else:
-        agree = max(float(torch.linalg.vector_norm((L.out.float() - L.y_dense.float())) /
-                          torch.linalg.vector_norm(L.y_dense.float())) for L in layers)
+        def ref(L):
+            if not has_own:
+                return L.y_lin.float()
+            return L.post(L.y_dense) if L.post is not None else L.y_dense.float()
+        agree = max(float(torch.linalg.vector_norm(L.out.float() - ref(L)) /
+                          torch.linalg.vector_norm(ref(L))) for L in layers)
 
     tokens = wls[0].T
     flops = sum(2 * L.macs_per_token * L.wl.T for L in layers)
@@ -555,7 +600,7 @@ def main():
     best_dense = min(t for t in (ms_own, ms_lin) if t is not None)
     group = wls[0].group
 
-    traffic = load_traffic(args.workload, group) if args.op == "forward" else None
+    traffic = load_traffic(args.workload, group) if args.op == "forward" and args.epilogue == "none" else None
     out = {
         "metric": OP_METRIC[args.op],
         "value": tokens / (ms * 1e-3),
@@ -577,6 +622,7 @@ def main():
             "layers_per_step": len(layers),
             "tile": args.tile,
             "op": args.op,
+            "epilogue": args.epilogue,
         },
         "tflops_actual": flops / (ms * 1e-3) / 1e12,
         "tflops_dense_equiv": dense_flops / (ms * 1e-3) / 1e12,

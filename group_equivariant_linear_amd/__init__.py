@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libeqlinear.so")
 EQL_OK, EQL_ERR_INVALID, EQL_ERR_UNSUPPORTED, EQL_ERR_HIP, EQL_ERR_NOMEM = range(5)
 EQL_F32, EQL_BF16 = 0, 1
 EQL_KIND_CN, EQL_KIND_D8 = 0, 1
+EQL_ACT_NONE, EQL_ACT_GELU = 0, 1
 
 # Every entry point of include/eqlinear.h.
 ABI_FUNCTIONS = (
@@ -28,7 +29,7 @@ ABI_FUNCTIONS = (
     "eqlinear_plan_info", "eqlinear_w_hat_elems", "eqlinear_weight_fft", "eqlinear_forward",
     "eqlinear_forward_tiled", "eqlinear_d8_forward", "eqlinear_expand_dense",
     "eqlinear_dense_forward", "eqlinear_w_hat_adjoint", "eqlinear_backward_data",
-    "eqlinear_backward_weight_workspace", "eqlinear_backward_weight",
+    "eqlinear_backward_weight_workspace", "eqlinear_backward_weight", "eqlinear_forward_bias_act",
 )
 
 
@@ -85,6 +86,7 @@ def load_library(path: str | None = None):
             "eqlinear_backward_data": ([vp, vp, vp, vp, i64, vp], st),
             "eqlinear_backward_weight_workspace": ([vp, i64], ctypes.c_size_t),
             "eqlinear_backward_weight": ([vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp], st),
+            "eqlinear_forward_bias_act": ([vp, vp, vp, vp, i32, vp, i64, vp, i32], st),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -225,6 +227,19 @@ def eqlinear_forward_tiled(plan: Plan, x, w_hat, y, tile: int, T: int | None = N
                                             _ptr(w_hat, plan, n, "w_hat"),
                                             _ptr(y, plan, T * M, "y"), T, _stream(stream),
                                             int(tile)), "eqlinear_forward_tiled")
+
+
+def eqlinear_forward_bias_act(plan: Plan, x, w_hat, bias, act: int, y, T: int | None = None, stream=None,
+                              tile: int = -1):
+    """y = act(layer(x) + bias[o]); bias may be None (no bias), act EQL_ACT_NONE or EQL_ACT_GELU."""
+    K, M = _widths(plan)
+    T = _tokens(x, T, K)
+    n = eqlinear_w_hat_elems(plan)
+    _check(plan._lib.eqlinear_forward_bias_act(plan.handle, _ptr(x, plan, T * K, "x"),
+                                               _ptr(w_hat, plan, n, "w_hat"),
+                                               _ptr(bias, plan, plan.info["C_out"], "bias"), int(act),
+                                               _ptr(y, plan, T * M, "y"), T, _stream(stream), int(tile)),
+           "eqlinear_forward_bias_act")
 
 
 def eqlinear_d8_forward(plan: Plan, x, wb, y, T: int | None = None, stream=None):

@@ -53,13 +53,13 @@ int choose_fused(int64_t T, int C_in, int C_out) {
 
 template <int N, typename IO>
 hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
-                        hipStream_t stream, int tile) {
+                        hipStream_t stream, int tile, Epi epi) {
     int i = tile >= 0 ? tile : choose_fused<N, IO>(T, C_in, C_out);
     if (i >= kSplitFirstTile) {
         if constexpr (std::is_same_v<IO, float> && N <= kSplitMaxN) {
             if (split_ok<N>(C_in, C_out)) {
-                if (i == kSplitFirstTile) return launch_split<N, 2>(x, w_hat, y, T, C_in, C_out, stream);
-                return launch_split<N, 4>(x, w_hat, y, T, C_in, C_out, stream);
+                if (i == kSplitFirstTile) return launch_split<N, 2>(x, w_hat, y, T, C_in, C_out, stream, epi);
+                return launch_split<N, 4>(x, w_hat, y, T, C_in, C_out, stream, epi);
             }
         }
         i = kMfFirstTile + 6;  // one-wave shape of the other kernels
@@ -69,24 +69,24 @@ hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, in
 #define EQL_MF(k)                                                                       \
     case k:                                                                             \
         if constexpr (mf_supported<N, IO>)                                              \
-            return launch_mf_entry<N, k>(x, w_hat, y, T, C_in, C_out, stream);          \
+            return launch_mf_entry<N, k>(x, w_hat, y, T, C_in, C_out, stream, epi);          \
         else                                                                            \
-            return launch_menu_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream);
+            return launch_menu_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream, epi);
             EQL_MF(0) EQL_MF(1) EQL_MF(2) EQL_MF(3) EQL_MF(4) EQL_MF(5)
 #undef EQL_MF
             default:
                 if constexpr (mf_supported<N, IO>)
-                    return launch_mf_entry<N, 6>(x, w_hat, y, T, C_in, C_out, stream);
+                    return launch_mf_entry<N, 6>(x, w_hat, y, T, C_in, C_out, stream, epi);
                 else
-                    return launch_menu_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream);
+                    return launch_menu_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream, epi);
         }
     }
     switch (i) {
 #define EQL_ENTRY(k) \
-    case k: return launch_menu_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream);
+    case k: return launch_menu_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream, epi);
         EQL_ENTRY(0) EQL_ENTRY(1) EQL_ENTRY(2) EQL_ENTRY(3) EQL_ENTRY(4) EQL_ENTRY(5)
 #undef EQL_ENTRY
-        default: return launch_menu_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream);
+        default: return launch_menu_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream, epi);
     }
 }
 

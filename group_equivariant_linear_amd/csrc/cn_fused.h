@@ -32,6 +32,118 @@
 
 namespace eql {
 
+// GELU in its erf form, v * Phi(v), Phi(v) = erfc(-v / sqrt 2) / 2 (Phi: standard
+// normal distribution function).  erfc(z) for z >= 0 is the Chebyshev-fitted form
+// of Numerical Recipes (Press et al., 2nd ed., section 6.2, "erfcc"):
+// erfc(z) = t exp(-z^2 + P(t)), t = 1 / (1 + z/2), P of degree 9, with a fractional
+// error below 1.2e-7 for every z >= 0, so both tails of GELU keep their relative
+// accuracy; erfc(-z) = 2 - erfc(z).  Branch-free: one reciprocal and one exp2 on
+// the transcendental unit and a dozen FMAs, about half the cost of erff.
+__device__ __forceinline__ float gelu_erf(float v) {
+    const float a = fabsf(v);
+    const float z = a * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+    float p = 0.17087277f;
+    p = fmaf(p, t, -0.82215223f);
+    p = fmaf(p, t, 1.48851587f);
+    p = fmaf(p, t, -1.13520398f);
+    p = fmaf(p, t, 0.27886807f);
+    p = fmaf(p, t, -0.18628806f);
+    p = fmaf(p, t, 0.09678418f);
+    p = fmaf(p, t, 0.37409196f);
+    p = fmaf(p, t, 1.00002368f);
+    p = fmaf(p, t, -1.26551223f);
+    // h = erfc(|v| / sqrt 2) / 2 = Phi(-|v|); -z^2 = -|v| (|v|/2) with the product exact
+    // inside the fma, so the rounding of z does not reach the exponent
+    const float h = 0.5f * t * __builtin_amdgcn_exp2f(fmaf(-a, 0.5f * a, p) * 1.44269504088896341f);
+    return v * (v < 0.0f ? h : 1.0f - h);
+}
+
+constexpr uint32_t kOOB = 0x80000000u;  // offset past every resource (extents < 2^31)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // word 3 = 0x00020000: raw (untyped) buffer, 32-bit data format, as on all gfx9 parts
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Fused neighbours of the layer ("Quick ViTs", key design 2: an MLP keeps its
+// GELU, applied where the group permutes coordinates -- for C_N the output y
+// itself, whose group axis a rotation shifts cyclically; a per-channel bias is
+// constant along that axis).  The epilogue runs them when epi_on(epi): the NV
+// values of one output channel become act(v + b).  Off, nothing is touched (an
+// added zero would turn -0 into +0).
+__device__ __forceinline__ bool epi_on(const Epi& epi) { return epi.bias != nullptr || epi.act != 0; }
+
+template <int NV>
+__device__ __forceinline__ void epi_apply(float* v, float b, int act) {
+    if (act == 1) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) v[k] = gelu_erf(v[k] + b);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) v[k] += b;
+    }
+}
+
+// Bias element o of the layer as raw bits, through a buffer resource over the
+// bias alone: o past C_out, and a NULL bias (an empty resource), read 0 without
+// a branch or a memory access.  The register is not touched until the epilogue,
+// so the load's latency hides under the main loop (vector loads complete in
+// issue order, so the main loop's own waits cover it).  A load issued in the
+// store phase would instead wait behind the stores in flight: one counter
+// tracks both.
+template <typename IO>
+__device__ __forceinline__ uint32_t bias_fetch(const Epi& epi, int C_out, int o) {
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(epi.bias, epi.bias ? (uint32_t)C_out * (uint32_t)sizeof(IO) : 0u);
+    const uint32_t off = o < C_out ? (uint32_t)o * (uint32_t)sizeof(IO) : kOOB;
+    if constexpr (sizeof(IO) == 4) return __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0);
+    else return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, off, 0, 0);
+}
+template <typename IO>
+__device__ __forceinline__ float bias_value(uint32_t bits) {
+    return __uint_as_float(sizeof(IO) == 4 ? bits : bits << 16);
+}
+
+// Workgroups per CU that an LDS allocation of b bytes allows (512-byte granules).
+constexpr int lds_groups(int b) { return 163840 / ((b + 511) / 512 * 512); }
+
+// The bias of a workgroup's CT output channels [o0, o0 + CT) (thread t holds
+// channels t, t + NT, ...), published to LDS and read back per channel in the
+// epilogue.  OWN: a slice of its own after the kernel's LDS bytes, fetched and
+// published just before the main loop, so the load's latency overlaps the first
+// stage's and no register carries it through the loop; taken only when the extra
+// bytes keep as many workgroups per CU.  Otherwise the bytes from FREE_OFF, which
+// the epilogue does not use but the main loop does: fetched and published after
+// the epilogue's first barrier, read after a second (those kernels run two or
+// more workgroups per CU, which hide the load).  FITS is false when neither
+// exists (the epilogue's staging fills the CU's LDS); such kernels keep each
+// lane's bias values in registers instead.
+template <typename IO, int CT, int NT, int LDS, int FREE_OFF>
+struct BiasTile {
+    static constexpr int NR = (CT + NT - 1) / NT;
+    static constexpr int BYTES = (CT * 4 + 15) / 16 * 16;
+    static constexpr bool OWN = LDS + BYTES <= 163840 && lds_groups(LDS + BYTES) == lds_groups(LDS);
+    static constexpr bool FITS = OWN || FREE_OFF + BYTES <= LDS;
+    static constexpr int OFF = OWN ? LDS : FREE_OFF;
+    static constexpr int SMEM = OWN ? LDS + BYTES : LDS;  // the kernel's LDS allocation
+    uint32_t r[NR];
+    __device__ __forceinline__ void fetch(const Epi& epi, int o0, int C_out) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int c = (int)threadIdx.x + k * NT;
+            r[k] = bias_fetch<IO>(epi, C_out, c < CT ? o0 + c : C_out);
+        }
+    }
+    // call before a barrier that precedes every read of the slice
+    __device__ __forceinline__ void publish(float* lds) const {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int c = (int)threadIdx.x + k * NT;
+            if (c < CT) lds[c] = bias_value<IO>(r[k]);
+        }
+    }
+};
+
 template <typename IO>
 struct IoTraits;
 template <>
@@ -268,7 +380,8 @@ __device__ __forceinline__ void chunk_products(const typename AFrag<typename C::
 
 template <class C>
 __device__ __forceinline__ void store_y(const f32x4 (&acc)[C::N][C::CB], typename C::IO* __restrict__ y,
-                                        int64_t T, int C_out, int64_t tw0, int o0) {
+                                        int64_t T, int C_out, int64_t tw0, int o0, const Epi& epi,
+                                        const float* lbias) {
     using IO = typename C::IO;
     constexpr int N = C::N;
     const int lane = (int)threadIdx.x & 63;
@@ -282,6 +395,7 @@ __device__ __forceinline__ void store_y(const f32x4 (&acc)[C::N][C::CB], typenam
 #pragma unroll
             for (int p = 0; p < N; ++p) P[p] = acc[p][b][r];
             rdft_inverse<N>(P, yv);
+            if (epi_on(epi)) epi_apply<N>(yv, epi.bias != nullptr ? lbias[o - o0] : 0.0f, epi.act);
             if (t >= T || o >= C_out) continue;
             IO* dst = y + (t * C_out + o) * N;
             if constexpr (sizeof(IO) == 4) {
@@ -314,14 +428,18 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) void cn_fused_kernel(
     const typename C::IO* __restrict__ x, const typename C::IO* __restrict__ w_hat,
     typename C::IO* __restrict__ y, int64_t T, int C_in, int C_out, int n_c_tiles,
-    uint32_t total_tiles, int vec_ok, int w_dma_ok) {
+    uint32_t total_tiles, int vec_ok, int w_dma_ok, Epi epi) {
     using IO = typename C::IO;
     using F = typename AFrag<IO>::T;
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF_BYTES];
+    using BiasT = BiasTile<IO, C::CT, C::kThreads, 2 * C::BUF_BYTES, 0>;
+    static_assert(BiasT::FITS, "the chunk buffers are free in the epilogue");
+    __shared__ __attribute__((aligned(16))) char smem[BiasT::SMEM];
+    float* lbias = reinterpret_cast<float*>(smem + BiasT::OFF);
 
     const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
     const int64_t t0 = (int64_t)(tile / n_c_tiles) * C::TT;
     const int o0 = (int)(tile % n_c_tiles) * C::CT;
+    BiasT bias;
     const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
     const int64_t tw0 = t0 + wave * 16;          // this wave's first token
     const int64_t t_lane = tw0 + (lane & 15);    // token of this lane's A row
@@ -338,6 +456,14 @@ __global__ __launch_bounds__(C::kThreads) void cn_fused_kernel(
     if (w_dma_ok) dma_w_chunk<C>(w_hat, C_in, C_out, o0, 0, smem);
     else copy_w_chunk<C>(w_hat, C_in, C_out, o0, 0, smem);
     load_x<C>(x, T, C_in, t_lane, q * C::R, vec_ok != 0, xr);
+    // the bias slice is its own: fetch and publish it now, after the first
+    // stage's loads (the wait for the bias load then overlaps the wait for that
+    // stage, which the loop does first); the loop's barriers order it before
+    // the epilogue's reads, and no register carries it through the loop
+    if (BiasT::OWN && epi.bias != nullptr) {
+        bias.fetch(epi, o0, C_out);
+        bias.publish(lbias);
+    }
     for (int c = 0; c < nch; ++c) {
         char* cur = smem + (c & 1) * C::BUF_BYTES;
         char* nxt = smem + ((c + 1) & 1) * C::BUF_BYTES;
@@ -352,7 +478,13 @@ __global__ __launch_bounds__(C::kThreads) void cn_fused_kernel(
         if (c + 1 < nch) load_x<C>(x, T, C_in, t_lane, (c + 1) * C::KC + q * C::R, vec_ok != 0, xr);
         chunk_products<C>(A, cur, acc);
     }
-    store_y<C>(acc, y, T, C_out, tw0, o0);
+    if (!BiasT::OWN && epi.bias != nullptr) {
+        __syncthreads();  // every wave is done with the chunk buffers
+        bias.fetch(epi, o0, C_out);
+        bias.publish(lbias);
+        __syncthreads();
+    }
+    store_y<C>(acc, y, T, C_out, tw0, o0, epi, lbias);
 }
 
 // --- fast path: buffer-resource traffic, coalesced through LDS -----------------
@@ -372,12 +504,6 @@ __global__ __launch_bounds__(C::kThreads) void cn_fused_kernel(
 // pitches that are multiples of 8 pieces rotate each row by its index, other
 // pitches are made odd.
 
-constexpr uint32_t kOOB = 0x80000000u;  // offset past every resource (extents < 2^31)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    // word 3 = 0x00020000: raw (untyped) buffer, 32-bit data format, as on all gfx9 parts
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 template <int N_, typename IO_, int WAVES_, int CB_>
 struct FastCfg : FusedCfg<N_, IO_, WAVES_, CB_> {
@@ -477,17 +603,34 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
     const typename C::IO* __restrict__ x, const typename C::IO* __restrict__ w_hat,
     typename C::IO* __restrict__ y, int64_t T, int C_in, int C_out, int n_c_tiles,
-    uint32_t total_tiles, uint32_t w_bytes, int y_coalesced) {
+    uint32_t total_tiles, uint32_t w_bytes, int y_coalesced, Epi epi) {
     using IO = typename C::IO;
     using F = typename AFrag<IO>::T;
     constexpr int N = C::N, S = C::S, XP = C::XP;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+    using BiasT = BiasTile<IO, C::CT, C::kThreads, C::LDS_BYTES, C::WAVES * C::YST_BYTES>;
+    constexpr bool kLdsBias = BiasT::FITS;
+    __shared__ __attribute__((aligned(16))) char smem[BiasT::SMEM];
+    float* lbias = reinterpret_cast<float*>(smem + BiasT::OFF);
 
     const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
     const int64_t t0 = (int64_t)(tile / n_c_tiles) * C::TT;
     const int o0 = (int)(tile % n_c_tiles) * C::CT;
     const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
     const int q = lane >> 4;
+    // the epilogue's lane holds output channels o0 + 16 b + lane % 16
+    BiasT bias;
+    uint32_t breg[kLdsBias ? 1 : C::CB];
+    if constexpr (!kLdsBias) {
+#pragma unroll
+        for (int b = 0; b < C::CB; ++b) {
+            breg[b] = 0u;
+            if (epi.bias != nullptr) breg[b] = bias_fetch<IO>(epi, C_out, o0 + b * 16 + (lane & 15));
+        }
+    }
+    auto bias_of = [&](int b) -> float {
+        if constexpr (kLdsBias) return epi.bias != nullptr ? lbias[b * 16 + (lane & 15)] : 0.0f;
+        else return bias_value<IO>(breg[b]);
+    };
 
     const uint32_t row_x = (uint32_t)C_in * (N * S), row_y = (uint32_t)C_out * (N * S);
     const int64_t rem = T - t0;
@@ -570,6 +713,10 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
     uint32_t xr[C::XW];
     dma(0, wbuf);
     load_x(0, xr);
+    if (kLdsBias && BiasT::OWN && epi.bias != nullptr) {  // as in the generic kernel
+        bias.fetch(epi, o0, C_out);
+        bias.publish(lbias);
+    }
     for (int c = 0; c < nch; ++c) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -587,6 +734,11 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
     // Epilogue: inverse DFT of each (token, channel) record, then y written once.
     if (y_coalesced) {
         __syncthreads();  // the staging area overlaps the tile and exchange buffers
+        if (kLdsBias && !BiasT::OWN && epi.bias != nullptr) {
+            bias.fetch(epi, o0, C_out);
+            bias.publish(lbias);
+            __syncthreads();
+        }
         char* yst = smem + wave * C::YST_BYTES;
 #pragma unroll
         for (int b = 0; b < C::CB; ++b)
@@ -597,6 +749,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
 #pragma unroll
                 for (int p = 0; p < N; ++p) P[p] = acc[p][b][r];
                 rdft_inverse<N>(P, yv);
+                if (epi_on(epi)) epi_apply<N>(yv, bias_of(b), epi.act);
                 // record bytes [ol*N*S, ol*N*S + N*S) of row tl, piece-rotated like x
                 const int byte0 = ol * N * S;
                 if constexpr ((N * S) % 16 == 0) {
@@ -633,6 +786,12 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
             __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
         }
     } else {
+        if (kLdsBias && !BiasT::OWN && epi.bias != nullptr) {
+            __syncthreads();
+            bias.fetch(epi, o0, C_out);
+            bias.publish(lbias);
+            __syncthreads();
+        }
 #pragma unroll
         for (int b = 0; b < C::CB; ++b)
 #pragma unroll
@@ -644,6 +803,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
 #pragma unroll
                 for (int p = 0; p < N; ++p) P[p] = acc[p][b][r];
                 rdft_inverse<N>(P, yv);
+                if (epi_on(epi)) epi_apply<N>(yv, bias_of(b), epi.act);
 #pragma unroll
                 for (int e = 0; e < N; ++e) {
                     if constexpr (sizeof(IO) == 4)
@@ -660,7 +820,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
 
 template <class C>
 hipError_t launch_fused_cfg(const void* x, const void* w_hat, void* y, int64_t T, int C_in,
-                            int C_out, hipStream_t stream) {
+                            int C_out, hipStream_t stream, Epi epi) {
     using IO = typename C::IO;
     const int64_t n_t = (T + C::TT - 1) / C::TT;
     const int n_c = (C_out + C::CT - 1) / C::CT;
@@ -671,13 +831,13 @@ hipError_t launch_fused_cfg(const void* x, const void* w_hat, void* y, int64_t T
     const int w_dma_ok = ((int64_t)C_in * S) % 16 == 0;
     hipLaunchKernelGGL((cn_fused_kernel<C>), dim3((uint32_t)total), dim3(C::kThreads), 0, stream,
                        (const IO*)x, (const IO*)w_hat, (IO*)y, T, C_in, C_out, n_c, (uint32_t)total,
-                       vec_ok, w_dma_ok);
+                       vec_ok, w_dma_ok, epi);
     return hipGetLastError();
 }
 
 template <class C>
 hipError_t launch_fast_cfg(const void* x, const void* w_hat, void* y, int64_t T, int C_in,
-                           int C_out, hipStream_t stream) {
+                           int C_out, hipStream_t stream, Epi epi) {
     using IO = typename C::IO;
     const int64_t n_t = (T + C::TT - 1) / C::TT;
     const int n_c = (C_out + C::CT - 1) / C::CT;
@@ -688,7 +848,7 @@ hipError_t launch_fast_cfg(const void* x, const void* w_hat, void* y, int64_t T,
     const int y_coalesced = ((int64_t)C_out * C::N * (int64_t)sizeof(IO)) % 16 == 0;
     hipLaunchKernelGGL((cn_fast_kernel<C>), dim3((uint32_t)total), dim3(C::kThreads), 0, stream,
                        (const IO*)x, (const IO*)w_hat, (IO*)y, T, C_in, C_out, n_c, (uint32_t)total,
-                       (uint32_t)w_bytes, y_coalesced);
+                       (uint32_t)w_bytes, y_coalesced, epi);
     return hipGetLastError();
 }
 
@@ -714,7 +874,7 @@ struct FusedMenu {
 
 template <int N, typename IO, int I>
 hipError_t launch_menu_entry(const void* x, const void* w_hat, void* y, int64_t T, int C_in,
-                             int C_out, hipStream_t stream) {
+                             int C_out, hipStream_t stream, Epi epi) {
     constexpr int W = FusedMenu<N, IO>::waves[I];
     constexpr int CBr = FusedMenu<N, IO>::cb[I];
     // keep the accumulators within 192 registers per lane and the LDS tiles
@@ -728,10 +888,10 @@ hipError_t launch_menu_entry(const void* x, const void* w_hat, void* y, int64_t 
     constexpr int CB = CBr < cap ? CBr : cap;
     using Cfg = FastCfg<N, IO, W, CB>;
     if (fast_ok<N, IO>(C_in, C_out, Cfg::TT))
-        return launch_fast_cfg<Cfg>(x, w_hat, y, T, C_in, C_out, stream);
+        return launch_fast_cfg<Cfg>(x, w_hat, y, T, C_in, C_out, stream, epi);
     // generic path (ragged channel groups): two shapes only
-    if constexpr (W == 4) return launch_fused_cfg<FusedCfg<N, IO, 4, (N <= 8 ? 2 : 1)>>(x, w_hat, y, T, C_in, C_out, stream);
-    else return launch_fused_cfg<FusedCfg<N, IO, 1, 1>>(x, w_hat, y, T, C_in, C_out, stream);
+    if constexpr (W == 4) return launch_fused_cfg<FusedCfg<N, IO, 4, (N <= 8 ? 2 : 1)>>(x, w_hat, y, T, C_in, C_out, stream, epi);
+    else return launch_fused_cfg<FusedCfg<N, IO, 1, 1>>(x, w_hat, y, T, C_in, C_out, stream, epi);
 }
 
 }  // namespace eql

@@ -4,12 +4,12 @@
 namespace eql {
 
 template hipError_t launch_fused<1, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<2, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<3, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<4, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 
 }  // namespace eql

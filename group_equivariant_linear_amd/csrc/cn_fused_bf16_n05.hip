@@ -4,12 +4,12 @@
 namespace eql {
 
 template hipError_t launch_fused<5, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<6, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<7, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<8, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 
 }  // namespace eql

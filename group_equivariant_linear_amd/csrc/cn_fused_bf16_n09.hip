@@ -4,12 +4,12 @@
 namespace eql {
 
 template hipError_t launch_fused<9, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<10, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<11, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<12, __bf16>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 
 }  // namespace eql

@@ -4,12 +4,12 @@
 namespace eql {
 
 template hipError_t launch_fused<1, float>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<2, float>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<3, float>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<4, float>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 
 }  // namespace eql

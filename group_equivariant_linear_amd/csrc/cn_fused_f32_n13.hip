@@ -4,12 +4,12 @@
 namespace eql {
 
 template hipError_t launch_fused<13, float>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<14, float>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<15, float>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 template hipError_t launch_fused<16, float>(const void*, const void*, void*, int64_t, int, int,
-                                            hipStream_t, int);
+                                            hipStream_t, int, Epi);
 
 }  // namespace eql

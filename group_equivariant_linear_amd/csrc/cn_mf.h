@@ -168,14 +168,18 @@ template <class C>
 __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ w_hat, __bf16* __restrict__ y,
     int64_t T, int C_in, int C_out, int n_c_tiles, uint32_t total_tiles, uint32_t w_bytes,
-    int y_coalesced) {
+    int y_coalesced, Epi epi) {
     constexpr int N = C::N, XP = C::XP, MQ = C::MQ, CB = C::CB;
     constexpr int S = 2;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+    using BiasT = BiasTile<__bf16, C::CT, C::kThreads, C::LDS_BYTES, C::WAVES * C::YST_BYTES>;
+    static_assert(BiasT::FITS, "room in LDS for the bias of the tile");
+    __shared__ __attribute__((aligned(16))) char smem[BiasT::SMEM];
+    float* lbias = reinterpret_cast<float*>(smem + BiasT::OFF);
 
     const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
     const int64_t t0 = (int64_t)(tile / n_c_tiles) * C::TT;
     const int o0 = (int)(tile % n_c_tiles) * C::CT;
+    BiasT bias;
     // the wave index is uniform: held in a scalar register, LDS destinations of
     // the direct loads (M0) are then scalar arithmetic
     const int lane = (int)threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -306,6 +310,14 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
         for (int b = 0; b < CB; ++b) acc[p][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     dma(0, wbuf);
     dma_x(0);
+    // the bias slice is its own: fetch and publish it now, after the first
+    // stage's loads (the wait for the bias load then overlaps the wait for that
+    // stage, which the loop does first); the loop's barriers order it before
+    // the epilogue's reads, and no register carries it through the loop
+    if (BiasT::OWN && epi.bias != nullptr) {
+        bias.fetch(epi, o0, C_out);
+        bias.publish(lbias);
+    }
     for (int c = 0; c < nch; ++c) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -385,6 +397,11 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
     // Epilogue.  Lane (tl, kg) holds token tl and output channels 16b + 4kg + i.
     if (y_coalesced) {
         __syncthreads();  // the staging area overlaps the tile and exchange buffers
+        if (!BiasT::OWN && epi.bias != nullptr) {
+            bias.fetch(epi, o0, C_out);
+            bias.publish(lbias);
+            __syncthreads();
+        }
         char* yst = smem + wave * C::YST_BYTES;
         bf16x8 Ga[MQ];
         make_frags<C, true>(Ga);
@@ -413,6 +430,11 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
                     for (int r = 0; r < 4; ++r)
                         if (4 * m + r < N) flat[i * N + 4 * m + r] = d[r];
                 }
+            }
+            if (epi_on(epi)) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    epi_apply<N>(flat + i * N, epi.bias != nullptr ? lbias[16 * b + 4 * kg + i] : 0.0f, epi.act);
             }
             uint32_t pk[2 * N];
 #pragma unroll
@@ -469,6 +491,12 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
         if (full) store_rows(std::true_type{});
         else store_rows(std::false_type{});
     } else {
+        if (!BiasT::OWN && epi.bias != nullptr) {
+            __syncthreads();
+            bias.fetch(epi, o0, C_out);
+            bias.publish(lbias);
+            __syncthreads();
+        }
         const uint32_t trow = (uint32_t)(wave * 16 + tl);
 #pragma unroll
         for (int b = 0; b < CB; ++b)
@@ -480,6 +508,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
 #pragma unroll
                 for (int p = 0; p < N; ++p) P[p] = acc[p][b][i];
                 rdft_inverse<N>(P, yv);
+                if (epi_on(epi)) epi_apply<N>(yv, epi.bias != nullptr ? lbias[o - o0] : 0.0f, epi.act);
 #pragma unroll
                 for (int e = 0; e < N; ++e)
                     __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(yv[e], 0.f) & 0xffffu), ry,
@@ -492,7 +521,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
 
 template <class C>
 hipError_t launch_mf_cfg(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
-                         hipStream_t stream) {
+                         hipStream_t stream, Epi epi) {
     const int64_t n_t = (T + C::TT - 1) / C::TT;
     const int n_c = (C_out + C::CT - 1) / C::CT;
     const int64_t total = n_t * n_c;
@@ -501,7 +530,7 @@ hipError_t launch_mf_cfg(const void* x, const void* w_hat, void* y, int64_t T, i
     const int y_coalesced = ((int64_t)C_out * C::N * 2) % 16 == 0;
     hipLaunchKernelGGL((cn_mf_kernel<C>), dim3((uint32_t)total), dim3(C::kThreads), 0, stream,
                        (const __bf16*)x, (const __bf16*)w_hat, (__bf16*)y, T, C_in, C_out, n_c,
-                       (uint32_t)total, (uint32_t)w_bytes, y_coalesced);
+                       (uint32_t)total, (uint32_t)w_bytes, y_coalesced, epi);
     return hipGetLastError();
 }
 
@@ -521,13 +550,13 @@ constexpr int mf_cap() {
 // shapes it cannot take (ragged C_in, huge rows) go to the fused kernel.
 template <int N, int I>
 hipError_t launch_mf_entry(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
-                           hipStream_t stream) {
+                           hipStream_t stream, Epi epi) {
     constexpr int W = FusedMenu<N, __bf16>::waves[I];
     constexpr int CB = mf_cap<N, W, FusedMenu<N, __bf16>::cb[I]>();
     using Cfg = MfCfg<N, W, CB>;
     if (fast_ok<N, __bf16>(C_in, C_out, Cfg::TT))
-        return launch_mf_cfg<Cfg>(x, w_hat, y, T, C_in, C_out, stream);
-    return launch_menu_entry<N, __bf16, I>(x, w_hat, y, T, C_in, C_out, stream);
+        return launch_mf_cfg<Cfg>(x, w_hat, y, T, C_in, C_out, stream, epi);
+    return launch_menu_entry<N, __bf16, I>(x, w_hat, y, T, C_in, C_out, stream, epi);
 }
 
 }  // namespace eql

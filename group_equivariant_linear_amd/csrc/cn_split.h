@@ -51,7 +51,13 @@ struct SplitCfg {
     static constexpr int YST = 16 * YPITCH * 16;
     // the y staging overlaps the x tiles (both at offset 0); the partials follow
     static constexpr int PART_OFF = 2 * XBUF > YST ? 2 * XBUF : YST;
-    static constexpr int LDS = PART_OFF + kWaves * RED;
+    // the tile's bias (fp32) has a slice of its own when that keeps as many
+    // workgroups per CU; otherwise each lane fetches its one value in the epilogue
+    static constexpr int BIAS_OFF = PART_OFF + kWaves * RED;
+    static constexpr int BIAS_BYTES = (CT * 4 + 15) / 16 * 16;
+    static constexpr bool BIAS_OWN = lds_groups(BIAS_OFF + BIAS_BYTES) == lds_groups(BIAS_OFF);
+    static constexpr int LDS = BIAS_OFF + (BIAS_OWN ? BIAS_BYTES : 0);
+    static_assert(LDS <= 163840, "the CU's LDS");
     static_assert(4 % KS == 0, "KS divides the 4 accumulator rows");
     static_assert(R == 2 || R == 4, "two or four channels per lane");
     static_assert(YROW % 16 == 0, "tile rows are whole pieces");
@@ -66,7 +72,8 @@ __device__ __forceinline__ void lds_barrier() {
 template <class C>
 __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
     const float* __restrict__ x, const float* __restrict__ w_hat, float* __restrict__ y, int64_t T,
-    int C_in, int C_out, int n_c_tiles, uint32_t total_tiles, uint32_t w_bytes, int y_coalesced) {
+    int C_in, int C_out, int n_c_tiles, uint32_t total_tiles, uint32_t w_bytes, int y_coalesced,
+    Epi epi) {
     constexpr int N = C::N, R = C::R, H = C::H, XP = C::XP;
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
@@ -141,6 +148,12 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
     load_x(0, xr);
     __builtin_amdgcn_sched_barrier(0);  // x first: it is needed first
     load_w(0, B0);
+    // The tile's bias to its LDS slice, fetched after the first step's loads (the
+    // wait for it overlaps theirs); the loop's barriers order it before the
+    // epilogue's reads, and no register carries it through the loop.
+    float* lbias = reinterpret_cast<float*>(smem + C::BIAS_OFF);
+    if (C::BIAS_OWN && epi.bias != nullptr && tid < C::CT)
+        lbias[tid] = bias_value<float>(bias_fetch<float>(epi, C_out, o0 + tid));
 
     // One step with weights B; the next step's weights load into Bnext.  VALU
     // work placed between fp32 MFMAs stretches each of them by about half, so
@@ -263,6 +276,12 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
             for (int p = 0; p < N; ++p) mine[(i * N + p) * 64 + lane] = acc[p][i];
     }
     __syncthreads();
+    // this lane's bias: from the slice, or fetched now (its latency overlaps the sums)
+    float bias_v = 0.0f;
+    if (epi.bias != nullptr) {
+        if constexpr (C::BIAS_OWN) bias_v = lbias[orow - o0];
+        else bias_v = bias_value<float>(bias_fetch<float>(epi, C_out, orow));
+    }
     const float* red =
         reinterpret_cast<const float*>(smem + C::PART_OFF) + ob * (C::RED / 4) + kh * C::ROWS * N * 64 + lane;
     float P[C::ROWS][N];
@@ -284,6 +303,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
             const int tl = q * 4 + kh * C::ROWS + ii, ol = ob * 16 + l16;
             float yv[N];
             rdft_inverse<N>(P[ii], yv);
+            if (epi_on(epi)) epi_apply<N>(yv, bias_v, epi.act);
             const int byte0 = ol * N * 4;
             if constexpr (N % 4 == 0) {
 #pragma unroll
@@ -318,6 +338,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
             const uint32_t off = orow < C_out ? tl * row_y + (uint32_t)orow * (N * 4) : kOOB;
             float yv[N];
             rdft_inverse<N>(P[ii], yv);
+            if (epi_on(epi)) epi_apply<N>(yv, bias_v, epi.act);
 #pragma unroll
             for (int e = 0; e < N; ++e)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[e]), ry, off + 4u * e, 0, 0);
@@ -335,7 +356,7 @@ bool split_ok(int C_in, int C_out) {
 
 template <class C>
 hipError_t launch_split_cfg(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
-                            hipStream_t stream) {
+                            hipStream_t stream, Epi epi) {
     const int64_t n_t = (T + C::TT - 1) / C::TT;
     const int n_c = (C_out + C::CT - 1) / C::CT;
     const int64_t total = n_t * n_c;
@@ -344,7 +365,7 @@ hipError_t launch_split_cfg(const void* x, const void* w_hat, void* y, int64_t T
     const int y_coalesced = ((int64_t)C_out * C::N * 4) % 16 == 0;
     hipLaunchKernelGGL((cn_split_kernel<C>), dim3((uint32_t)total), dim3(C::kThreads), 0, stream,
                        (const float*)x, (const float*)w_hat, (float*)y, T, C_in, C_out, n_c, (uint32_t)total,
-                       (uint32_t)w_bytes, y_coalesced);
+                       (uint32_t)w_bytes, y_coalesced, epi);
     return hipGetLastError();
 }
 
@@ -353,10 +374,10 @@ hipError_t launch_split_cfg(const void* x, const void* w_hat, void* y, int64_t T
 // channels, else two.
 template <int N, int KS>
 hipError_t launch_split(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
-                        hipStream_t stream) {
+                        hipStream_t stream, Epi epi) {
     constexpr int R = (KS == 2 && N <= 8) ? 4 : 2;
-    if (C_out <= 16) return launch_split_cfg<SplitCfg<N, 1, KS, R>>(x, w_hat, y, T, C_in, C_out, stream);
-    return launch_split_cfg<SplitCfg<N, 2, KS, R>>(x, w_hat, y, T, C_in, C_out, stream);
+    if (C_out <= 16) return launch_split_cfg<SplitCfg<N, 1, KS, R>>(x, w_hat, y, T, C_in, C_out, stream, epi);
+    return launch_split_cfg<SplitCfg<N, 2, KS, R>>(x, w_hat, y, T, C_in, C_out, stream, epi);
 }
 
 }  // namespace eql

@@ -8,6 +8,13 @@ namespace eql {
 
 constexpr int kMaxGemmJobs = 6;
 
+// Fused neighbours of the C_N forward: y = act(y + bias[o]) in the epilogue.
+// bias: device, plan dtype, C_out elements, or null; act: 0 identity, 1 GELU.
+struct Epi {
+    const void* bias;
+    int act;
+};
+
 // One independent product y[t][y_col+n] = sum_k W[n][k] x[t][x_col+k],
 // n < Nn, k < K, W = w + w_off with row stride ldw (elements).
 struct GemmJob {
@@ -27,7 +34,7 @@ struct GemmJobs {
 
 // tile: -1 = automatic choice, else a fixed tile configuration (tests, tuning).
 hipError_t launch_cn_forward(int N, int dtype_bf16, const void* x, const void* w_hat, void* y,
-                             int64_t T, int C_in, int C_out, hipStream_t stream, int tile);
+                             int64_t T, int C_in, int C_out, hipStream_t stream, int tile, Epi epi = Epi{nullptr, 0});
 
 hipError_t launch_gemm_rows(int dtype_bf16, GemmJobs jobs, const void* x, const void* w, void* y,
                             int64_t T, int ldx, int ldy, hipStream_t stream);

@@ -159,6 +159,24 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t p, const void* x, const void* w
     return eqlinear_forward_tiled(p, x, w_hat, y, T, stream, -1);
 }
 
+eqlinear_status eqlinear_forward_bias_act(eqlinear_plan_t p, const void* x, const void* w_hat, const void* bias,
+                                          int act, void* y, int64_t T, void* stream, int tile) {
+    if (!p || p->kind != EQL_KIND_CN) return EQL_ERR_INVALID;
+    if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (T == 0) return EQL_OK;
+    if (!x || !w_hat || !y) return EQL_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(w_hat) || !aligned16(y)) return EQL_ERR_INVALID;
+    const size_t es = elem_size(p);
+    const size_t xb = (size_t)T * in_width(p) * es, yb = (size_t)T * out_width(p) * es;
+    const size_t wb = eqlinear_w_hat_elems(p) * es, bb = (size_t)p->C_out * es;
+    if (overlaps(x, xb, y, yb) || overlaps(w_hat, wb, y, yb)) return EQL_ERR_INVALID;
+    if (bias && (((uintptr_t)bias % es) != 0 || overlaps(bias, bb, y, yb))) return EQL_ERR_INVALID;
+    if (tile < -1 || tile > 15) return EQL_ERR_INVALID;
+    return hip_status(eql::launch_cn_forward(p->N, p->dtype == EQL_BF16, x, w_hat, y, T, p->C_in, p->C_out,
+                                             (hipStream_t)stream, tile, eql::Epi{bias, act}));
+}
+
 eqlinear_status eqlinear_w_hat_adjoint(eqlinear_plan_t p, const void* w_hat, void* w_hat_adj, void* stream) {
     if (!p || p->kind != EQL_KIND_CN || !w_hat || !w_hat_adj) return EQL_ERR_INVALID;
     if (!aligned16(w_hat) || !aligned16(w_hat_adj)) return EQL_ERR_INVALID;

@@ -152,6 +152,31 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
 eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                        void* y, int64_t T, void* stream, int tile);
 
+/* Activations that eqlinear_forward_bias_act can apply. */
+typedef enum {
+    EQL_ACT_NONE = 0, /* y = layer(x) + bias                                   */
+    EQL_ACT_GELU = 1  /* y = GELU(layer(x) + bias), GELU(v) = v * Phi(v) =
+                         v/2 * (1 + erf(v / sqrt 2)), the exact (erf) form     */
+} eqlinear_act;
+
+/* C_N forward with the layer's neighbours fused into the store: a per-channel
+ * bias and an optional GELU ("Quick ViTs", key design 2: an MLP keeps its
+ * pointwise nonlinearity, applied to the regular-representation (group-axis)
+ * values, which a group element only permutes, so the block stays equivariant).
+ *   y[t][o][g] = act(sum_{i,m} w[o][i][m] x[t][i][(g-m) mod N] + bias[o])
+ * bias is constant along the group axis, as an equivariant bias must be.
+ *   bias  [C_out] device, plan dtype, aligned to its element size, must not
+ *         overlap y; NULL means no bias
+ *   act   EQL_ACT_NONE or EQL_ACT_GELU (others -> EQL_ERR_INVALID)
+ *   tile  as for eqlinear_forward_tiled (-1: automatic)
+ * The bias add and the activation run in fp32 on the fp32 layer output
+ * before its one rounding to the plan dtype; everything else (arguments,
+ * layouts, precision, T == 0, asynchrony) is as for eqlinear_forward.
+ * With bias == NULL and act == EQL_ACT_NONE it equals eqlinear_forward_tiled. */
+eqlinear_status eqlinear_forward_bias_act(eqlinear_plan_t plan, const void* x, const void* w_hat,
+                                          const void* bias, int act, void* y, int64_t T, void* stream,
+                                          int tile);
+
 /* Backward pass ("Flash EQ-Linear", Implementation: the kernels cover forward
  * and backward; Experimental Results, Operator Level, backward pass).  The
  * pages give no formulas; these are the derivatives of the layer

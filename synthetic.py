@@ -116,6 +116,14 @@ def cn_inputs(N: int, C_in: int, C_out: int, T: int, dtype: str, seed: int = 0):
     return {"x": xd, "x64": x64, "w": wd, "w64": w64}
 
 
+def channel_bias(C_out: int, dtype: str, seed: int = 0):
+    """A per-output-channel bias b[C_out] ~ N(0, 0.5^2): ('b', 'b64') like quantize().
+
+    Its spread keeps layer output + bias on both sides of 0, where GELU bends."""
+    rng = np.random.default_rng(seed)
+    return quantize(_normal(rng, (C_out,), 0.5), dtype)
+
+
 def d8_block_shapes(C_in: int, C_out: int):
     """Shapes of the five D8 weight blocks, in packing order A1, A2, B1, B2, E."""
     mi, mo = C_in // 8, C_out // 8

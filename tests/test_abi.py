@@ -174,6 +174,32 @@ def test_backward_validation_before_any_hip_call(eq):
     assert lib.eqlinear_backward_weight_workspace(h, 10000) > need
 
 
+def test_bias_act_validation_before_any_hip_call(eq):
+    lib = eq.load_library()
+    p = eq.eqlinear_plan(8, 32, 16, eq.EQL_BF16)  # bias: 16 bf16 = 32 bytes
+    h = p.handle
+    X, W, Y, Bz = 1 << 20, 1 << 30, 1 << 34, 1 << 38  # aligned, disjoint fake addresses
+    f = lib.eqlinear_forward_bias_act
+    G, NONE = eq.EQL_ACT_GELU, eq.EQL_ACT_NONE
+    assert f(h, X, W, Bz, 2, Y, 5, None, -1) == eq.EQL_ERR_INVALID       # unknown activation
+    assert f(h, X, W, Bz, -1, Y, 5, None, -1) == eq.EQL_ERR_INVALID
+    assert f(h, X, W, Bz, G, Y, -1, None, -1) == eq.EQL_ERR_INVALID      # negative T
+    assert f(h, None, None, None, G, None, 0, None, -1) == eq.EQL_OK     # T == 0: nothing to do
+    assert f(h, X, W, Bz + 1, G, Y, 5, None, -1) == eq.EQL_ERR_INVALID   # bias misaligned for bf16
+    assert f(h, X, W, Y + 30, G, Y, 5, None, -1) == eq.EQL_ERR_INVALID   # bias inside y
+    assert f(h, X, W, Y - 30, G, Y, 5, None, -1) == eq.EQL_ERR_INVALID   # bias runs into y
+    assert f(h, X, W, Bz, G, X, 5, None, -1) == eq.EQL_ERR_INVALID       # y aliases x
+    assert f(h, X, W, Bz, G, W, 5, None, -1) == eq.EQL_ERR_INVALID       # y aliases w_hat
+    assert f(h, X + 2, W, Bz, G, Y, 5, None, -1) == eq.EQL_ERR_INVALID   # x misaligned
+    assert f(h, X, W, Bz, NONE, Y, 5, None, 16) == eq.EQL_ERR_INVALID    # tile out of range
+    assert f(h, X, W, Bz, NONE, Y, 5, None, -2) == eq.EQL_ERR_INVALID
+    assert f(h, None, W, Bz, G, Y, 5, None, -1) == eq.EQL_ERR_INVALID
+    d8 = eq.eqlinear_d8_plan(16, 16, eq.EQL_F32)
+    assert f(d8.handle, X, W, Bz, G, Y, 5, None, -1) == eq.EQL_ERR_INVALID
+    pf = eq.eqlinear_plan(8, 32, 16, eq.EQL_F32)
+    assert f(pf.handle, X, W, Bz + 2, G, Y, 5, None, -1) == eq.EQL_ERR_INVALID  # fp32 bias needs 4 bytes
+
+
 def test_binding_checks_tensors_without_gpu(eq):
     import torch
     p = eq.eqlinear_plan(4, 2, 2, eq.EQL_F32)
