@@ -72,6 +72,14 @@ def _load():
         lib.eqref_cn_backward_weight.restype = None
         lib.eqref_bias_act.argtypes = [i64, i, i, d, i, d]
         lib.eqref_bias_act.restype = None
+        lib.eqref_d8_fourier_matrix.argtypes = [d]
+        lib.eqref_d8_fourier_matrix.restype = None
+        lib.eqref_d8_to_regular.argtypes = [i64, i, d, d]
+        lib.eqref_d8_to_regular.restype = None
+        lib.eqref_d8_to_fourier.argtypes = [i64, i, d, d]
+        lib.eqref_d8_to_fourier.restype = None
+        lib.eqref_d8_bias_act.argtypes = [i64, i, d, i, d]
+        lib.eqref_d8_bias_act.restype = None
         lib.eqref_cn_weight_dft.argtypes = [i, i, i, d, d]
         lib.eqref_cn_weight_dft.restype = None
         lib.eqref_d8_expand.argtypes = [i, i, d, d]
@@ -203,6 +211,50 @@ def cn_weight_dft(w):
     P = np.empty((N, C_out, C_in), dtype=np.float64)
     _load().eqref_cn_weight_dft(N, C_out, C_in, _p(w), _p(P))
     return P
+
+
+def d8_fourier_matrix():
+    """The orthonormal D8 Fourier matrix F[p][q] (coefficient p, group element q = a + 4b)."""
+    F = np.empty((8, 8), dtype=np.float64)
+    _load().eqref_d8_fourier_matrix(_p(F))
+    return F
+
+
+def d8_to_regular(v):
+    """Fourier layout [T][8m] -> regular layout [T][m][8]."""
+    v = _f64(v)
+    T, C = v.shape
+    assert C % 8 == 0
+    f = np.empty((T, C // 8, 8), dtype=np.float64)
+    _load().eqref_d8_to_regular(T, C // 8, _p(v), _p(f))
+    return f
+
+
+def d8_to_fourier(f):
+    """Regular layout [T][m][8] -> Fourier layout [T][8m]."""
+    f = _f64(f)
+    T, m, e = f.shape
+    assert e == 8
+    v = np.empty((T, 8 * m), dtype=np.float64)
+    _load().eqref_d8_to_fourier(T, m, _p(f), _p(v))
+    return v
+
+
+def d8_bias_act(y, bias=None, act=0):
+    """The D8 round trip on Fourier features y[T][8m]: regular domain, act(f + bias[j]), back; a copy."""
+    y = np.array(y, dtype=np.float64, copy=True, order="C")
+    T, C = y.shape
+    assert C % 8 == 0
+    b = None if bias is None else _f64(bias)
+    if b is not None:
+        assert b.shape == (C // 8,)
+    _load().eqref_d8_bias_act(T, C // 8, None if b is None else _p(b), int(act), _p(y))
+    return y
+
+
+def d8_dense_bias_act(x, wb, C_out, bias=None, act=0):
+    """The D8 layer followed by its fused neighbours in the regular domain."""
+    return d8_bias_act(d8_dense(x, wb, C_out), bias, act)
 
 
 def d8_expand(wb, C_in, C_out):

@@ -53,6 +53,17 @@
  *    C/4 that is applied to both coordinates of the 2-D irrep E.  With the
  *    feature layout [A1 | A2 | B1 | B2 | E coord 0 | E coord 1] the layer is a
  *    block-diagonal matrix (eqref_d8_expand) times x.
+ *
+ *  - D8 round trip around GELU.  "Quick ViTs", key design 2: GELU does not
+ *    commute with a general representation, so the features go back to the
+ *    regular representation (where the group only permutes the 8 values of a
+ *    channel), GELU is applied there, and they return to the Fourier domain;
+ *    the page fuses the round trip and GELU into one kernel.  The transform is
+ *    the group's orthonormal Fourier matrix (eqref_d8_fourier_matrix, built
+ *    from the irreps' generator matrices), one regular channel j of m = C/8
+ *    gathering A1..B2 at j and E copies 2j, 2j+1 (eqref_d8_to_regular,
+ *    eqref_d8_to_fourier, eqref_d8_bias_act).  A bias that keeps the block
+ *    equivariant is constant over the group elements: one value per channel j.
  */
 #include <math.h>
 #include <stdint.h>
@@ -239,6 +250,111 @@ void eqref_d8_expand(int C_in, int C_out, const double* wb, double* W) {
             for (int c = 0; c < 2 * mi; ++c)
                 W[(int64_t)(4 * mo + 2 * e * mo + r) * C_in + 4 * mi + 2 * e * mi + c] =
                     blk[(int64_t)r * (2 * mi) + c];
+}
+
+/* The D8 group Fourier transform on one regular-representation channel.
+ * D8 = <r, s | r^4 = s^2 = 1, s r s = r^-1>; element q = a + 4b (0 <= a < 4,
+ * b in {0, 1}) is r^a s^b.  Its real irreps, with the generators the layer's
+ * feature action uses: A1 (r, s) -> (1, 1), A2 (1, -1), B1 (-1, 1), B2 (-1, -1),
+ * and E: r -> [[0, -1], [1, 0]], s -> diag(1, -1), so E(r^a s^b) = E(r)^a E(s)^b.
+ * F[p][q] (8 x 8, row-major): rows 0..3 are the 1-D irreps' values at element q
+ * times sqrt(1/8); row 4 + 2k + c is entry (k, c) of E(q) times sqrt(2/8).  By
+ * Schur orthogonality the rows are orthonormal: F^-1 = F^T.  The coefficients of
+ * a function f on the group are F f; under a left translation of f the 2 x 2
+ * matrix of E coefficients is multiplied by E(g) on the left, so each of its
+ * columns c is one copy of E (coordinates k = 0, 1). */
+void eqref_d8_fourier_matrix(double* F) {
+    const double Er[2][2] = {{0.0, -1.0}, {1.0, 0.0}}, Es[2][2] = {{1.0, 0.0}, {0.0, -1.0}};
+    const double chi_r[4] = {1.0, 1.0, -1.0, -1.0}, chi_s[4] = {1.0, -1.0, 1.0, -1.0};
+    const double n1 = sqrt(1.0 / 8.0), n2 = sqrt(2.0 / 8.0);
+    for (int q = 0; q < 8; ++q) {
+        const int a = q % 4, b = q / 4;
+        double M[2][2] = {{1.0, 0.0}, {0.0, 1.0}};
+        for (int i = 0; i < a; ++i) { /* M <- E(r) M */
+            double T2[2][2];
+            for (int k = 0; k < 2; ++k)
+                for (int c = 0; c < 2; ++c) T2[k][c] = Er[k][0] * M[0][c] + Er[k][1] * M[1][c];
+            memcpy(M, T2, sizeof M);
+        }
+        if (b) { /* M <- M E(s) */
+            double T2[2][2];
+            for (int k = 0; k < 2; ++k)
+                for (int c = 0; c < 2; ++c) T2[k][c] = M[k][0] * Es[0][c] + M[k][1] * Es[1][c];
+            memcpy(M, T2, sizeof M);
+        }
+        for (int p = 0; p < 4; ++p) {
+            double v = 1.0;
+            for (int i = 0; i < a; ++i) v *= chi_r[p];
+            if (b) v *= chi_s[p];
+            F[p * 8 + q] = n1 * v;
+        }
+        for (int k = 0; k < 2; ++k)
+            for (int c = 0; c < 2; ++c) F[(4 + 2 * k + c) * 8 + q] = n2 * M[k][c];
+    }
+}
+
+/* Fourier features of regular channel j (of m) in one token row of width 8m,
+ * laid out [A1 | A2 | B1 | B2 | E coord 0 | E coord 1]: A1..B2 at j, the E
+ * copies of channel j are 2j + c (column c of its E coefficient matrix), each
+ * with coordinates k = 0, 1 in the two E slabs.  Index p as in F. */
+static int64_t d8_slot(int m, int j, int p) {
+    if (p < 4) return (int64_t)p * m + j;
+    const int k = (p - 4) / 2, c = (p - 4) % 2;
+    return 4 * (int64_t)m + 2 * (int64_t)m * k + 2 * j + c;
+}
+
+/* Fourier layout [T][8m] -> regular layout [T][m][8]: f = F^T v per channel. */
+void eqref_d8_to_regular(int64_t T, int m, const double* v, double* f) {
+    double F[64];
+    eqref_d8_fourier_matrix(F);
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < m; ++j)
+            for (int q = 0; q < 8; ++q) {
+                double acc = 0.0;
+                for (int p = 0; p < 8; ++p) acc += F[p * 8 + q] * v[t * 8 * m + d8_slot(m, j, p)];
+                f[(t * m + j) * 8 + q] = acc;
+            }
+}
+
+/* Regular layout [T][m][8] -> Fourier layout [T][8m]: v = F f per channel. */
+void eqref_d8_to_fourier(int64_t T, int m, const double* f, double* v) {
+    double F[64];
+    eqref_d8_fourier_matrix(F);
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < m; ++j)
+            for (int p = 0; p < 8; ++p) {
+                double acc = 0.0;
+                for (int q = 0; q < 8; ++q) acc += F[p * 8 + q] * f[(t * m + j) * 8 + q];
+                v[t * 8 * m + d8_slot(m, j, p)] = acc;
+            }
+}
+
+/* In place on D8 Fourier features y[T][8m]: the pointwise neighbours of the
+ * layer applied where the group only permutes coordinates ("Quick ViTs", key
+ * design 2: back to the regular representation, GELU, forward again).  Per
+ * token and regular channel j: f = F^T v_j; f <- act(f + bias[j]) (bias may be
+ * NULL: a constant over the group elements, act as eqref_bias_act); v_j = F f. */
+void eqref_d8_bias_act(int64_t T, int m, const double* bias, int act, double* y) {
+    double F[64];
+    eqref_d8_fourier_matrix(F);
+    const double rsqrt2 = 1.0 / sqrt(2.0);
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < m; ++j) {
+            double v[8], f[8];
+            for (int p = 0; p < 8; ++p) v[p] = y[t * 8 * m + d8_slot(m, j, p)];
+            for (int q = 0; q < 8; ++q) {
+                double acc = 0.0;
+                for (int p = 0; p < 8; ++p) acc += F[p * 8 + q] * v[p];
+                if (bias) acc += bias[j];
+                if (act == 1) acc = 0.5 * acc * erfc(-acc * rsqrt2);
+                f[q] = acc;
+            }
+            for (int p = 0; p < 8; ++p) {
+                double acc = 0.0;
+                for (int q = 0; q < 8; ++q) acc += F[p * 8 + q] * f[q];
+                y[t * 8 * m + d8_slot(m, j, p)] = acc;
+            }
+        }
 }
 
 int eqref_d8_dense(int C_in, int C_out, int64_t T, const double* x, const double* wb,

@@ -227,6 +227,81 @@ def pin_bias_act(orc):
         assert rel(orc.cn_dense_bias_act(np.roll(x, s, -1), w, b, 1), np.roll(yb, s, -1)) < 1e-14
 
 
+def _d4_elements():
+    """D8 as the square's symmetries, 2 x 2 integer matrices: element q = a + 4b is R^a S^b
+    (R a quarter turn, S the mirror y -> -y)."""
+    R = np.array([[0, -1], [1, 0]])
+    S = np.array([[1, 0], [0, -1]])
+    return [np.linalg.matrix_power(R, q % 4) @ (S if q // 4 else np.eye(2, dtype=int)) for q in range(8)]
+
+
+def _left_regular(g):
+    """The left-regular action of g on functions of the group: f -> f(g^-1 .), i.e.
+    P[q', q] = 1 where h_q' = g h_q (the group law from the matrices)."""
+    E = _d4_elements()
+    P = np.zeros((8, 8))
+    for q in range(8):
+        gq = g @ E[q]
+        P[next(i for i in range(8) if np.array_equal(E[i], gq)), q] = 1.0
+    return P
+
+
+def _d8_slots(m, j):
+    """Fourier-layout columns of regular channel j (the reading of the layout: A1..B2
+    at j, E copies 2j + c in the coordinate-0 and coordinate-1 slabs)."""
+    return [j, m + j, 2 * m + j, 3 * m + j, 4 * m + 2 * j, 4 * m + 2 * j + 1, 6 * m + 2 * j, 6 * m + 2 * j + 1]
+
+
+def pin_d8_fourier(orc):
+    """The D8 Fourier matrix: orthonormal rows (Schur orthogonality); the
+    identity's column by hand; it intertwines the left-regular action (built
+    from the group law) with the layer's feature action on one channel, for both
+    generators; the transforms invert each other and follow the layout."""
+    F = orc.d8_fourier_matrix()
+    assert np.max(np.abs(F @ F.T - np.eye(8))) < 1e-15
+    assert np.max(np.abs(F[:, 0] - np.array([8 ** -0.5] * 4 + [0.5, 0.0, 0.0, 0.5]))) < 1e-16
+    r, s = d8_action(8)
+    E = _d4_elements()
+    for g, A in ((E[1], r), (E[4], s)):
+        assert np.max(np.abs(F @ _left_regular(g) - A @ F)) < 1e-15
+    m = 5
+    f = _rand(3, m, 8)
+    v = orc.d8_to_fourier(f)
+    assert rel(orc.d8_to_regular(v), f) < 1e-15
+    for j in (0, 3):
+        assert rel(v[:, _d8_slots(m, j)], f[:, j] @ F.T) < 1e-15
+
+
+def pin_d8_bias_act(orc):
+    """The D8 round trip: the identity when no bias and no activation; a bias
+    constant over the group elements lands on A1 alone, times sqrt(8); a delta
+    at the identity comes back times Phi(1); GELU acts on the regular-domain
+    values (scipy's ndtr); the layer followed by the round trip is equivariant."""
+    import scipy.special
+    m, T = 3, 4
+    y = _rand(T, 8 * m)
+    assert rel(orc.d8_bias_act(y, None, 0), y) < 1e-15
+    b = _rand(m)
+    expect = np.zeros_like(y)
+    expect[:, :m] = np.sqrt(8.0) * b
+    assert np.max(np.abs(orc.d8_bias_act(y, b, 0) - y - expect)) < 1e-14
+    v = np.zeros((1, 8 * m))
+    col = np.array([8 ** -0.5] * 4 + [0.5, 0.0, 0.0, 0.5])
+    v[0, _d8_slots(m, 1)] = col
+    expect = np.zeros_like(v)
+    expect[0, _d8_slots(m, 1)] = 0.8413447460685429 * col
+    assert np.max(np.abs(orc.d8_bias_act(v, None, 1) - expect)) < 1e-15
+    fr = orc.d8_to_regular(y) + b[None, :, None]
+    assert rel(orc.d8_bias_act(y, b, 1), orc.d8_to_fourier(fr * scipy.special.ndtr(fr))) < 1e-14
+    C_in, C_out = 16, 24
+    x, wb, bb = _rand(T, C_in), _rand(C_in * C_out // 8), _rand(C_out // 8)
+    rin, sin_ = d8_action(C_in)
+    rout, sout = d8_action(C_out)
+    yb = orc.d8_dense_bias_act(x, wb, C_out, bb, 1)
+    assert rel(orc.d8_dense_bias_act(x @ rin.T, wb, C_out, bb, 1), yb @ rout.T) < 1e-13
+    assert rel(orc.d8_dense_bias_act(x @ sin_.T, wb, C_out, bb, 1), yb @ sout.T) < 1e-13
+
+
 ALL_CN_PINS = [pin_rfft_route, pin_weight_dft, pin_closed_forms, pin_dense_matrix_structure, pin_bias_act,
                pin_backward_adjoint, pin_backward_closed_forms, pin_backward_equivariance]
 
@@ -281,6 +356,14 @@ def test_backward_equivariance():
 
 def test_bias_and_gelu():
     pin_bias_act(oracle)
+
+
+def test_d8_fourier_transform():
+    pin_d8_fourier(oracle)
+
+
+def test_d8_round_trip_bias_and_gelu():
+    pin_d8_bias_act(oracle)
 
 
 def test_dense_matrix_structure():
@@ -488,6 +571,12 @@ MUTANTS = [
     ("GELU with Phi of the wrong sign", "v = 0.5 * v * erfc(-v * rsqrt2);", "v = 0.5 * v * erfc(v * rsqrt2);"),
     ("D8 transposed 1-D block", "blk[(int64_t)r * mi + c];", "blk[(int64_t)c * mi + r];"),
     ("D8 E weight on coordinate 0 only", "4 * mi + 2 * e * mi + c] =", "4 * mi + c] ="),
+    ("D8 Fourier: E copies taken as rows", "return 4 * (int64_t)m + 2 * (int64_t)m * k + 2 * j + c;",
+     "return 4 * (int64_t)m + 2 * (int64_t)m * c + 2 * j + k;"),
+    ("D8 Fourier: E rows unnormalised", "n2 = sqrt(2.0 / 8.0);", "n2 = sqrt(1.0 / 8.0);"),
+    ("D8 Fourier: quarter turn the other way", "Er[2][2] = {{0.0, -1.0}, {1.0, 0.0}}",
+     "Er[2][2] = {{0.0, 1.0}, {-1.0, 0.0}}"),
+    ("D8 round trip: bias on one group element", "if (bias) acc += bias[j];", "if (bias && q == 0) acc += bias[j];"),
 ]
 
 
@@ -514,7 +603,8 @@ def test_mutants_are_caught(tmp_path, golden_dir, name, old, new):
         oracle.build = lambda *a, **k: path
         caught = []
         checks = [lambda: pin_hand_examples(oracle, golden_dir),
-                  lambda: pin_d8_blockdiag(oracle, golden_dir)] + [
+                  lambda: pin_d8_blockdiag(oracle, golden_dir),
+                  lambda: pin_d8_fourier(oracle), lambda: pin_d8_bias_act(oracle)] + [
             (lambda f=f: f(oracle)) for f in ALL_CN_PINS]
         for chk in checks:
             try:
@@ -565,6 +655,12 @@ def test_oracle_under_sanitizers(tmp_path):
         "wb = np.ones(16*16//8); xd = np.ones((2, 16)); yd = np.zeros((2, 16))\n"
         "lib.eqref_d8_dense.argtypes = [ctypes.c_int]*2 + [ctypes.c_int64] + [ctypes.c_void_p]*3\n"
         "assert lib.eqref_d8_dense(16, 16, 2, p(xd), p(wb), p(yd)) == 0\n"
+        "F = np.zeros(64); lib.eqref_d8_fourier_matrix.argtypes = [ctypes.c_void_p]; lib.eqref_d8_fourier_matrix(p(F))\n"
+        "fr = np.zeros((2, 2, 8)); lib.eqref_d8_to_regular.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]\n"
+        "lib.eqref_d8_to_regular(2, 2, p(yd), p(fr))\n"
+        "lib.eqref_d8_to_fourier.argtypes = lib.eqref_d8_to_regular.argtypes; lib.eqref_d8_to_fourier(2, 2, p(fr), p(yd))\n"
+        "b2 = np.ones(2); lib.eqref_d8_bias_act.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]\n"
+        "lib.eqref_d8_bias_act(2, 2, p(b2), 1, p(yd))\n"
         "print('SAN-OK')\n"
     )
     asan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
