@@ -99,8 +99,10 @@ def parse():
     ap.add_argument("--op", default="forward", choices=["forward", "backward_data", "backward_weight"],
                     help="which pass of a C_N workload to time (the default line is the forward)")
     ap.add_argument("--epilogue", default="none", choices=["none", "bias", "bias_gelu"],
-                    help="forward of a C_N workload with the fused per-channel bias (and GELU) "
-                         "of eqlinear_forward_bias_act; the comparators add the same in torch")
+                    help="forward with its pointwise neighbours: C_N workloads through "
+                         "eqlinear_forward_bias_act (bias and GELU fused into the store), D8 through "
+                         "eqlinear_d8_forward + the fused regular-domain round trip eqlinear_d8_bias_act; "
+                         "the comparators add the same in torch")
     ap.add_argument("--mode", default="bench", choices=["bench", "traffic"],
                     help="traffic: a few forwards and a copy of known size, for rocprofv3 --pmc")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -184,7 +186,8 @@ class Layer:
         import torch
 
         import synthetic
-        assert wl.group == "C", "the fused bias and activation belong to the C_N forward"
+        if wl.group != "C":
+            return self._d8_epilogue(eq, wl, d, dev, es, epilogue)
         bd, d["b64"] = synthetic.channel_bias(wl.C_out, wl.dtype, 500)
         self.bias = dev(bd)
         act = eq.EQL_ACT_GELU if epilogue == "bias_gelu" else eq.EQL_ACT_NONE
@@ -205,6 +208,51 @@ class Layer:
         def post(t):  # the same neighbours on the own GEMM's output, for the agreement figure
             v = t.float() + bias_cols.float()
             return torch.nn.functional.gelu(v) if act == eq.EQL_ACT_GELU else v
+        self.post = post
+
+    def _d8_epilogue(self, eq, wl, d, dev, es, epilogue):
+        """D8 layer, then the fused regular-domain round trip in place (bias per
+        regular channel, GELU).  The torch comparator: dense GEMM, then gather to
+        the regular layout, the 8 x 8 transform, bias, in-place GELU, transform
+        back and scatter."""
+        import numpy as np
+        import torch
+
+        import synthetic
+        m = wl.C_out // 8
+        bd, d["b64"] = synthetic.channel_bias(m, wl.dtype, 500)
+        self.bias = dev(bd)
+        act = eq.EQL_ACT_GELU if epilogue == "bias_gelu" else eq.EQL_ACT_NONE
+        d["act"] = act
+
+        def step():
+            eq.eqlinear_d8_forward(self.plan, self.x, self.w_hat, self.y, T=wl.T)
+            eq.eqlinear_d8_bias_act(self.plan, self.y, self.bias, act, self.y, T=wl.T)
+        self.step = step
+        self.bytes_per_launch += m * es
+        F = torch.tensor(_d8_fourier_matrix(), dtype=torch.float32, device="cuda").to(self.tdt)
+        j = np.arange(m)[:, None]
+        cols = np.concatenate([j, m + j, 2 * m + j, 3 * m + j, 4 * m + 2 * j, 4 * m + 2 * j + 1,
+                               6 * m + 2 * j, 6 * m + 2 * j + 1], axis=1)  # [m][8] Fourier columns
+        idx = torch.tensor(cols.reshape(-1), device="cuda")
+        gelu_ = torch._C._nn.gelu_
+        bias_j = self.bias[:, None]
+
+        def round_trip(t):
+            f = torch.matmul(t[:, idx].view(wl.T, m, 8), F) + bias_j  # regular values: v F
+            if act == eq.EQL_ACT_GELU:
+                gelu_(f)
+            t[:, idx] = torch.matmul(f, F.t().contiguous()).view(wl.T, -1)
+
+        def dense_torch():
+            torch.mm(self.x, self.W_dense.t(), out=self.y_lin)
+            round_trip(self.y_lin)
+        self.dense_torch = dense_torch
+
+        def post(t):
+            u = t.clone()
+            round_trip(u)
+            return u.float()
         self.post = post
 
     def _backward(self, eq, wl, d, dev, eqdt, es):
@@ -247,6 +295,23 @@ class Layer:
             self.y_lin = self.y_dense
             self.dense_own = None
             self.dense_torch = lambda: torch.mm(self.dy.t().contiguous(), self.x, out=self.y_lin)
+
+
+def _d8_fourier_matrix():
+    """The orthonormal D8 Fourier matrix F[p][q] for the torch comparator, from the
+    irreps: rows sqrt(1/8) chi(q) for A1, A2, B1, B2 and (1/2) E(q)[k][c] for E,
+    element q = a + 4b being r^a s^b, E(r) = [[0,-1],[1,0]], E(s) = diag(1,-1)."""
+    import numpy as np
+    Er, Es = np.array([[0.0, -1.0], [1.0, 0.0]]), np.diag([1.0, -1.0])
+    chars = [(1, 1), (1, -1), (-1, 1), (-1, -1)]
+    F = np.zeros((8, 8))
+    for q in range(8):
+        a, b = q % 4, q // 4
+        M = np.linalg.matrix_power(Er, a) @ (Es if b else np.eye(2))
+        for p, (cr, cs) in enumerate(chars):
+            F[p, q] = cr ** a * cs ** b / np.sqrt(8.0)
+        F[4:, q] = 0.5 * M.reshape(-1)
+    return F
 
 
 def time_loop(fns, steps, warmup):
@@ -355,7 +420,9 @@ def cpu_baseline(layers, target_s, op="forward"):
 
 def _run_oracle(wl, d, n, op="forward"):
     import oracle
-    if "b64" in d:
+    if "b64" in d and wl.group != "C":
+        oracle.d8_dense_bias_act(d["x64"][:n], d["w64"], wl.C_out, d["b64"], d["act"])
+    elif "b64" in d:
         oracle.cn_dense_bias_act(d["x64"][:n], d["w64"], d["b64"], d["act"])
     elif op == "backward_data":
         oracle.cn_backward_data(d["dy64"][:n], d["w64"])
@@ -442,7 +509,7 @@ def algorithmic_bytes(wl, op="forward", epilogue="none"):
         w = 4 * (wl.C_in // 8) * (wl.C_out // 8) + (wl.C_in // 4) * (wl.C_out // 4)
     if op == "backward_weight":
         return es * wl.T * (K + M) + 4 * w
-    bias = wl.C_out if epilogue != "none" else 0
+    bias = 0 if epilogue == "none" else (wl.C_out if wl.group == "C" else wl.C_out // 8)
     return es * (wl.T * (K + M) + w + bias)
 
 
@@ -539,8 +606,8 @@ def main():
     eq.load_library()
     torch.cuda.set_device(0)
 
-    if args.epilogue != "none" and (args.op != "forward" or any(wl.group != "C" for wl in wls)):
-        print("--epilogue applies to the forward of C_N workloads", file=sys.stderr)
+    if args.epilogue != "none" and args.op != "forward":
+        print("--epilogue applies to the forward pass", file=sys.stderr)
         sys.exit(2)
     layers = [Layer(eq, wl, tile=args.tile, op=args.op, epilogue=args.epilogue) for wl in wls]
     torch.cuda.synchronize()
@@ -647,7 +714,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": op_kernel_name(wls[0], args.op),
+            "kernel": op_kernel_name(wls[0], args.op) + (" + d8_pass_kernel" if group != "C" and args.epilogue != "none" else ""),
             "bytes_per_launch": bytes_launch,
             "kernel_source_sha": kernel_source_hash(group if args.op != "backward_weight" else "BW"),
         },

@@ -30,6 +30,7 @@ ABI_FUNCTIONS = (
     "eqlinear_forward_tiled", "eqlinear_d8_forward", "eqlinear_expand_dense",
     "eqlinear_dense_forward", "eqlinear_w_hat_adjoint", "eqlinear_backward_data",
     "eqlinear_backward_weight_workspace", "eqlinear_backward_weight", "eqlinear_forward_bias_act",
+    "eqlinear_d8_bias_act", "eqlinear_d8_to_fourier", "eqlinear_d8_to_regular",
 )
 
 
@@ -87,6 +88,9 @@ def load_library(path: str | None = None):
             "eqlinear_backward_weight_workspace": ([vp, i64], ctypes.c_size_t),
             "eqlinear_backward_weight": ([vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp], st),
             "eqlinear_forward_bias_act": ([vp, vp, vp, vp, i32, vp, i64, vp, i32], st),
+            "eqlinear_d8_bias_act": ([vp, vp, vp, i32, vp, i64, vp], st),
+            "eqlinear_d8_to_fourier": ([vp, vp, vp, i64, vp], st),
+            "eqlinear_d8_to_regular": ([vp, vp, vp, i64, vp], st),
         }
         for name, (args, res) in sig.items():
             f = getattr(lib, name)
@@ -249,6 +253,32 @@ def eqlinear_d8_forward(plan: Plan, x, wb, y, T: int | None = None, stream=None)
     _check(plan._lib.eqlinear_d8_forward(plan.handle, _ptr(x, plan, T * K, "x"),
                                          _ptr(wb, plan, n, "wb"), _ptr(y, plan, T * M, "y"),
                                          T, _stream(stream)), "eqlinear_d8_forward")
+
+
+def eqlinear_d8_bias_act(plan: Plan, y_in, bias, act: int, y_out, T: int | None = None, stream=None):
+    """y_out = F act(F^T y_in + bias[j]) per regular channel (y_out may be y_in); bias None or [C_out/8]."""
+    _, M = _widths(plan)
+    T = _tokens(y_in, T, M)
+    _check(plan._lib.eqlinear_d8_bias_act(plan.handle, _ptr(y_in, plan, T * M, "y_in"),
+                                          _ptr(bias, plan, plan.info["C_out"] // 8, "bias"), int(act),
+                                          _ptr(y_out, plan, T * M, "y_out"), T, _stream(stream)),
+           "eqlinear_d8_bias_act")
+
+
+def eqlinear_d8_to_fourier(plan: Plan, x_reg, x_four, T: int | None = None, stream=None):
+    K, _ = _widths(plan)
+    T = _tokens(x_reg, T, K)
+    _check(plan._lib.eqlinear_d8_to_fourier(plan.handle, _ptr(x_reg, plan, T * K, "x_reg"),
+                                            _ptr(x_four, plan, T * K, "x_four"), T, _stream(stream)),
+           "eqlinear_d8_to_fourier")
+
+
+def eqlinear_d8_to_regular(plan: Plan, y_four, y_reg, T: int | None = None, stream=None):
+    _, M = _widths(plan)
+    T = _tokens(y_four, T, M)
+    _check(plan._lib.eqlinear_d8_to_regular(plan.handle, _ptr(y_four, plan, T * M, "y_four"),
+                                            _ptr(y_reg, plan, T * M, "y_reg"), T, _stream(stream)),
+           "eqlinear_d8_to_regular")
 
 
 def eqlinear_expand_dense(plan: Plan, w, w_dense, stream=None):

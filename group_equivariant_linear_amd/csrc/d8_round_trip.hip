@@ -1,0 +1,250 @@
+// d8_round_trip.hip -- the D8 layer's regular-representation passes ("Quick
+// ViTs", key design 2).  GELU does not commute with a general representation,
+// so the MLP takes the layer's Fourier features back to the regular
+// representation -- where the group only permutes the 8 values of a channel --
+// applies GELU there and returns to the Fourier domain; the page fuses that
+// round trip into one kernel.  This file does the same in one pass over y, and
+// also runs either half alone (regular inputs into the Fourier layout, Fourier
+// outputs back to the regular layout).
+//
+// Layouts: Fourier [T][8m] = [A1 | A2 | B1 | B2 | E coord 0 | E coord 1] with
+// widths (m, m, m, m, 2m, 2m); regular [T][m][8], element q = a + 4b of the
+// group being r^a s^b (r the quarter turn, s the mirror).  Regular channel j
+// owns A1..B2 at j and the E copies 2j, 2j+1 (the two columns c of its E
+// coefficient matrix M, coordinates k = 0, 1 its rows).  The transform is the
+// group's orthonormal Fourier matrix: rows sqrt(1/8) chi(q) for the 1-D irreps
+// and (1/2) E(q)[k][c] for E, E(r) = [[0,-1],[1,0]], E(s) = diag(1,-1); its
+// entries are 0, +-1/2 and +-1/sqrt 8, so both directions are butterflies.
+//
+// One thread owns G consecutive regular channels of one token (G = 4 when m is
+// a multiple of 4: 8- and 16-byte vector accesses for bf16, 16- and 32-byte
+// for fp32; else, and for regular-layout outputs, G = 1), reads their
+// features, transforms and writes them in one pass.  The identity passes run at about 1.5x the time of a device copy of
+// the same bytes; the GELU round trip adds about 25 VALU operations per value
+// (cn_fused.h: gelu_erf), which at one pass per element do not hide under the
+// memory time.  (Tiles staged in LDS, with or without a register prefetch of
+// the next tile, measured no faster.)
+#include "cn_fused.h"
+
+namespace eql {
+
+namespace {
+
+constexpr float kC8 = 0.35355339059327376f;  // 1/sqrt(8)
+
+// f = F^T v: the 8 regular values of one channel from its Fourier features
+// v = (a1, a2, b1, b2, M00, M01, M10, M11).
+__device__ __forceinline__ void to_regular8(const float (&v)[8], float (&f)[8]) {
+    const float s1 = (v[0] + v[1]) * kC8, s2 = (v[0] - v[1]) * kC8;  // a1 +- a2
+    const float d1 = (v[2] + v[3]) * kC8, d2 = (v[2] - v[3]) * kC8;  // b1 +- b2
+    const float p = 0.5f * (v[4] + v[7]), pm = 0.5f * (v[4] - v[7]);  // M00 +- M11
+    const float n = 0.5f * (v[6] - v[5]), np = 0.5f * (v[5] + v[6]);  // M10 -+ M01
+    const float u0 = s1 + d1, u1 = s1 - d1, u4 = s2 + d2, u5 = s2 - d2;
+    f[0] = u0 + p;
+    f[2] = u0 - p;
+    f[1] = u1 + n;
+    f[3] = u1 - n;
+    f[4] = u4 + pm;
+    f[6] = u4 - pm;
+    f[5] = u5 + np;
+    f[7] = u5 - np;
+}
+
+// v = F f: the Fourier features of one channel from its 8 regular values.
+__device__ __forceinline__ void to_fourier8(const float (&f)[8], float (&v)[8]) {
+    const float e0 = f[0] + f[2], o0 = f[0] - f[2], e1 = f[1] + f[3], o1 = f[1] - f[3];
+    const float e4 = f[4] + f[6], o4 = f[4] - f[6], e5 = f[5] + f[7], o5 = f[5] - f[7];
+    const float g0 = e0 + e1, g1 = e0 - e1, g4 = e4 + e5, g5 = e4 - e5;
+    v[0] = (g0 + g4) * kC8;   // A1
+    v[1] = (g0 - g4) * kC8;   // A2
+    v[2] = (g1 + g5) * kC8;   // B1
+    v[3] = (g1 - g5) * kC8;   // B2
+    v[4] = 0.5f * (o0 + o4);  // M00
+    v[5] = 0.5f * (o5 - o1);  // M01
+    v[6] = 0.5f * (o1 + o5);  // M10
+    v[7] = 0.5f * (o0 - o4);  // M11
+}
+
+// K consecutive elements <-> fp32, with vector accesses (K*sizeof(IO) is a
+// multiple of 4 here except K = 1, 2 bf16, which take element accesses).
+template <typename IO, int K>
+__device__ __forceinline__ void load_k(const IO* p, float (&o)[K]) {
+    if constexpr (sizeof(IO) == 4 && K % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < K / 4; ++i) {
+            const u32x4 w = reinterpret_cast<const u32x4*>(p)[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[4 * i + e] = __uint_as_float(w[e]);
+        }
+    } else if constexpr (sizeof(IO) == 2 && K % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < K / 8; ++i) {
+            const u32x4 w = reinterpret_cast<const u32x4*>(p)[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
+                o[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            }
+        }
+    } else if constexpr (sizeof(IO) == 2 && K == 4) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            o[2 * e] = __uint_as_float(w[e] << 16);
+            o[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < K; ++e) o[e] = (float)p[e];
+    }
+}
+
+template <typename IO, int K>
+__device__ __forceinline__ void store_k(IO* p, const float (&v)[K]) {
+    if constexpr (sizeof(IO) == 4 && K % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < K / 4; ++i)
+            reinterpret_cast<u32x4*>(p)[i] = u32x4{__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                                                   __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3])};
+    } else if constexpr (sizeof(IO) == 2 && K % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < K / 8; ++i)
+            reinterpret_cast<u32x4*>(p)[i] =
+                u32x4{pack_bf16x2(v[8 * i], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
+                      pack_bf16x2(v[8 * i + 4], v[8 * i + 5]), pack_bf16x2(v[8 * i + 6], v[8 * i + 7])};
+    } else if constexpr (sizeof(IO) == 2 && K == 4) {
+        *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    } else {
+#pragma unroll
+        for (int e = 0; e < K; ++e) {
+            if constexpr (sizeof(IO) == 4) p[e] = v[e];
+            else reinterpret_cast<uint16_t*>(p)[e] = (uint16_t)(pack_bf16x2(v[e], 0.f) & 0xffffu);
+        }
+    }
+}
+
+enum D8Pass { kRoundTrip = 0, kToFourier = 1, kToRegular = 2 };
+
+// MODE kRoundTrip: Fourier in, act(F^T v + b) back through F, Fourier out
+// (in == out allowed: a thread reads every element it writes before writing).
+// kToFourier: regular in, Fourier out.  kToRegular: Fourier in, regular out.
+template <typename IO, int G, int MODE>
+__global__ __launch_bounds__(256) void d8_pass_kernel(const IO* in, IO* out, const IO* bias, int act, int m,
+                                                      uint32_t groups, uint32_t total) {
+    const uint32_t idx = blockIdx.x * 256u + threadIdx.x;  // total < 2^31 (host-checked)
+    if (idx >= total) return;
+    const uint32_t t = idx / groups;
+    const int j0 = (int)(idx - t * groups) * G;
+    const int64_t row = (int64_t)t * 8 * (int64_t)m;  // first element of this token (either layout)
+
+    float v[G][8];  // Fourier features of the G channels
+    float f[G][8];  // their regular values
+    if constexpr (MODE == kToFourier) {
+        float r[8 * G];
+        load_k<IO, 8 * G>(in + row + 8 * (int64_t)j0, r);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) f[g][q] = r[8 * g + q];
+    } else {
+        float a[4][G], e[2][2 * G];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) load_k<IO, G>(in + row + (int64_t)p * m + j0, a[p]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) load_k<IO, 2 * G>(in + row + 4 * (int64_t)m + 2 * (int64_t)m * k + 2 * j0, e[k]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) v[g][p] = a[p][g];
+            v[g][4] = e[0][2 * g];
+            v[g][5] = e[0][2 * g + 1];
+            v[g][6] = e[1][2 * g];
+            v[g][7] = e[1][2 * g + 1];
+            to_regular8(v[g], f[g]);
+        }
+    }
+
+    if constexpr (MODE == kRoundTrip) {
+        float b[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) b[g] = bias != nullptr ? (float)bias[j0 + g] : 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (act == 1) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[g][q] = gelu_erf(f[g][q] + b[g]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[g][q] += b[g];
+            }
+        }
+    }
+
+    if constexpr (MODE == kToRegular) {
+        float r[8 * G];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) r[8 * g + q] = f[g][q];
+        store_k<IO, 8 * G>(out + row + 8 * (int64_t)j0, r);
+    } else {
+        float a[4][G], e[2][2 * G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            to_fourier8(f[g], v[g]);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) a[p][g] = v[g][p];
+            e[0][2 * g] = v[g][4];
+            e[0][2 * g + 1] = v[g][5];
+            e[1][2 * g] = v[g][6];
+            e[1][2 * g + 1] = v[g][7];
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) store_k<IO, G>(out + row + (int64_t)p * m + j0, a[p]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) store_k<IO, 2 * G>(out + row + 4 * (int64_t)m + 2 * (int64_t)m * k + 2 * j0, e[k]);
+    }
+}
+
+template <typename IO, int MODE>
+hipError_t launch_pass(const void* in, void* out, const void* bias, int act, int m, int64_t T, hipStream_t stream) {
+    // regular-layout output: one channel per thread, so a wave's stores are
+    // consecutive 8-value records (with four, they would stride 4 records)
+    const int G = (MODE != kToRegular && m % 4 == 0) ? 4 : 1;
+    const int64_t groups = m / G, total = T * groups;
+    if (total > 0x7fffffff) return hipErrorInvalidConfiguration;  // 32-bit thread indices
+    const uint32_t blocks = (uint32_t)((total + 255) / 256);
+    if (G == 4)
+        hipLaunchKernelGGL((d8_pass_kernel<IO, 4, MODE>), dim3(blocks), dim3(256), 0, stream, (const IO*)in,
+                           (IO*)out, (const IO*)bias, act, m, (uint32_t)groups, (uint32_t)total);
+    else
+        hipLaunchKernelGGL((d8_pass_kernel<IO, 1, MODE>), dim3(blocks), dim3(256), 0, stream, (const IO*)in,
+                           (IO*)out, (const IO*)bias, act, m, (uint32_t)groups, (uint32_t)total);
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_pass_dt(int dtype_bf16, const void* in, void* out, const void* bias, int act, int m, int64_t T,
+                          hipStream_t stream) {
+    if (dtype_bf16) return launch_pass<__bf16, MODE>(in, out, bias, act, m, T, stream);
+    return launch_pass<float, MODE>(in, out, bias, act, m, T, stream);
+}
+
+}  // namespace
+
+hipError_t launch_d8_round_trip(int dtype_bf16, const void* y_in, void* y_out, const void* bias, int act, int m,
+                                int64_t T, hipStream_t stream) {
+    return launch_pass_dt<kRoundTrip>(dtype_bf16, y_in, y_out, bias, act, m, T, stream);
+}
+
+hipError_t launch_d8_to_fourier(int dtype_bf16, const void* x_reg, void* x_four, int m, int64_t T,
+                                hipStream_t stream) {
+    return launch_pass_dt<kToFourier>(dtype_bf16, x_reg, x_four, nullptr, 0, m, T, stream);
+}
+
+hipError_t launch_d8_to_regular(int dtype_bf16, const void* y_four, void* y_reg, int m, int64_t T,
+                                hipStream_t stream) {
+    return launch_pass_dt<kToRegular>(dtype_bf16, y_four, y_reg, nullptr, 0, m, T, stream);
+}
+
+}  // namespace eql

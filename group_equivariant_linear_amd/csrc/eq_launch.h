@@ -65,4 +65,12 @@ hipError_t launch_cn_expand(int N, int dtype_bf16, const void* w, void* w_dense,
 hipError_t launch_d8_expand(int dtype_bf16, const void* wb, void* w_dense, int C_in, int C_out,
                             hipStream_t stream);
 
+// d8_round_trip.hip: m = C/8 regular channels per token
+hipError_t launch_d8_round_trip(int dtype_bf16, const void* y_in, void* y_out, const void* bias, int act, int m,
+                                int64_t T, hipStream_t stream);
+hipError_t launch_d8_to_fourier(int dtype_bf16, const void* x_reg, void* x_four, int m, int64_t T,
+                                hipStream_t stream);
+hipError_t launch_d8_to_regular(int dtype_bf16, const void* y_four, void* y_reg, int m, int64_t T,
+                                hipStream_t stream);
+
 }  // namespace eql

@@ -177,6 +177,45 @@ eqlinear_status eqlinear_forward_bias_act(eqlinear_plan_t p, const void* x, cons
                                              (hipStream_t)stream, tile, eql::Epi{bias, act}));
 }
 
+eqlinear_status eqlinear_d8_bias_act(eqlinear_plan_t p, const void* y_in, const void* bias, int act, void* y_out,
+                                     int64_t T, void* stream) {
+    if (!p || p->kind != EQL_KIND_D8) return EQL_ERR_INVALID;
+    if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (T == 0) return EQL_OK;
+    if (!y_in || !y_out || !aligned16(y_in) || !aligned16(y_out)) return EQL_ERR_INVALID;
+    const size_t es = elem_size(p);
+    const size_t yb = (size_t)T * p->C_out * es, bb = (size_t)(p->C_out / 8) * es;
+    if (y_in != y_out && overlaps(y_in, yb, y_out, yb)) return EQL_ERR_INVALID;  // in place, or apart
+    if (bias && (((uintptr_t)bias % es) != 0 || overlaps(bias, bb, y_out, yb))) return EQL_ERR_INVALID;
+    return hip_status(eql::launch_d8_round_trip(p->dtype == EQL_BF16, y_in, y_out, bias, act, p->C_out / 8, T,
+                                                (hipStream_t)stream));
+}
+
+eqlinear_status eqlinear_d8_to_fourier(eqlinear_plan_t p, const void* x_reg, void* x_four, int64_t T,
+                                       void* stream) {
+    if (!p || p->kind != EQL_KIND_D8) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (T == 0) return EQL_OK;
+    if (!x_reg || !x_four || !aligned16(x_reg) || !aligned16(x_four)) return EQL_ERR_INVALID;
+    const size_t b = (size_t)T * p->C_in * elem_size(p);
+    if (overlaps(x_reg, b, x_four, b)) return EQL_ERR_INVALID;
+    return hip_status(eql::launch_d8_to_fourier(p->dtype == EQL_BF16, x_reg, x_four, p->C_in / 8, T,
+                                                (hipStream_t)stream));
+}
+
+eqlinear_status eqlinear_d8_to_regular(eqlinear_plan_t p, const void* y_four, void* y_reg, int64_t T,
+                                       void* stream) {
+    if (!p || p->kind != EQL_KIND_D8) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (T == 0) return EQL_OK;
+    if (!y_four || !y_reg || !aligned16(y_four) || !aligned16(y_reg)) return EQL_ERR_INVALID;
+    const size_t b = (size_t)T * p->C_out * elem_size(p);
+    if (overlaps(y_four, b, y_reg, b)) return EQL_ERR_INVALID;
+    return hip_status(eql::launch_d8_to_regular(p->dtype == EQL_BF16, y_four, y_reg, p->C_out / 8, T,
+                                                (hipStream_t)stream));
+}
+
 eqlinear_status eqlinear_w_hat_adjoint(eqlinear_plan_t p, const void* w_hat, void* w_hat_adj, void* stream) {
     if (!p || p->kind != EQL_KIND_CN || !w_hat || !w_hat_adj) return EQL_ERR_INVALID;
     if (!aligned16(w_hat) || !aligned16(w_hat_adj)) return EQL_ERR_INVALID;

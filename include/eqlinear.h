@@ -177,6 +177,41 @@ eqlinear_status eqlinear_forward_bias_act(eqlinear_plan_t plan, const void* x, c
                                           const void* bias, int act, void* y, int64_t T, void* stream,
                                           int tile);
 
+/* D8 layer's pointwise neighbours in the regular representation ("Quick ViTs",
+ * key design 2: GELU does not commute with a general representation, so the
+ * features go back to the regular representation, where the group only
+ * permutes coordinates, GELU acts there, and they return to the Fourier
+ * domain; the page fuses this round trip into one kernel).
+ *   y_in, y_out [T][C_out] D8 Fourier layout (as eqlinear_d8_forward writes),
+ *         plan dtype, 16-byte aligned; y_out == y_in (in place) or apart
+ *   bias  [C_out/8] plan dtype, one value per regular channel (constant over
+ *         the 8 group elements, as an equivariant bias must be), aligned to
+ *         its element size, not overlapping y_out; NULL means no bias
+ *   act   EQL_ACT_NONE or EQL_ACT_GELU (others -> EQL_ERR_INVALID)
+ * Per token and regular channel j (m = C_out/8): its 8 Fourier features
+ * (A1, A2, B1, B2 at j; E copies 2j and 2j+1 -- the columns of its E
+ * coefficient matrix -- in the coordinate-0 and coordinate-1 slabs) go to its
+ * values at the 8 group elements by the group's orthonormal Fourier matrix
+ * F^T, become act(f + bias[j]) in fp32, and return through F; one rounding to
+ * the plan dtype.  Element q = a + 4b is r^a s^b with the layer's generators
+ * (E(r) = [[0,-1],[1,0]], E(s) = diag(1,-1)).  With no bias and no activation
+ * the pass is the identity up to that rounding.  D8 plans only; T == 0:
+ * EQL_OK, nothing launched.  Asynchronous on stream; no allocation. */
+eqlinear_status eqlinear_d8_bias_act(eqlinear_plan_t plan, const void* y_in, const void* bias, int act,
+                                     void* y_out, int64_t T, void* stream);
+
+/* The two halves of that round trip alone, for D8 layers between regular-
+ * representation features: eqlinear_d8_to_fourier takes x_reg [T][C_in/8][8]
+ * (regular channel j's values at the 8 group elements) to the Fourier layout
+ * x_four [T][C_in] that eqlinear_d8_forward consumes; eqlinear_d8_to_regular
+ * takes the layer's output y_four [T][C_out] to y_reg [T][C_out/8][8].  Same
+ * transform, layouts and rules as eqlinear_d8_bias_act (fp32 arithmetic, one
+ * rounding), except that input and output must not overlap. */
+eqlinear_status eqlinear_d8_to_fourier(eqlinear_plan_t plan, const void* x_reg, void* x_four, int64_t T,
+                                       void* stream);
+eqlinear_status eqlinear_d8_to_regular(eqlinear_plan_t plan, const void* y_four, void* y_reg, int64_t T,
+                                       void* stream);
+
 /* Backward pass ("Flash EQ-Linear", Implementation: the kernels cover forward
  * and backward; Experimental Results, Operator Level, backward pass).  The
  * pages give no formulas; these are the derivatives of the layer

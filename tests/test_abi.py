@@ -200,6 +200,32 @@ def test_bias_act_validation_before_any_hip_call(eq):
     assert f(pf.handle, X, W, Bz + 2, G, Y, 5, None, -1) == eq.EQL_ERR_INVALID  # fp32 bias needs 4 bytes
 
 
+def test_d8_passes_validation_before_any_hip_call(eq):
+    lib = eq.load_library()
+    d8 = eq.eqlinear_d8_plan(32, 64, eq.EQL_BF16)  # y rows: 64 bf16 = 128 bytes; bias: 8 bf16
+    h = d8.handle
+    A, B, Bz = 1 << 20, 1 << 30, 1 << 38
+    G, NONE = eq.EQL_ACT_GELU, eq.EQL_ACT_NONE
+    f = lib.eqlinear_d8_bias_act
+    assert f(h, A, Bz, 2, B, 5, None) == eq.EQL_ERR_INVALID          # unknown activation
+    assert f(h, A, Bz, G, B, -1, None) == eq.EQL_ERR_INVALID         # negative T
+    assert f(h, None, None, G, None, 0, None) == eq.EQL_OK           # T == 0
+    assert f(h, A, Bz, G, A + 128, 5, None) == eq.EQL_ERR_INVALID    # partial overlap of in and out
+    assert f(h, A + 2, Bz, G, B, 5, None) == eq.EQL_ERR_INVALID      # misaligned
+    assert f(h, A, Bz + 1, G, B, 5, None) == eq.EQL_ERR_INVALID      # bias misaligned for bf16
+    assert f(h, A, B + 8, G, B, 5, None) == eq.EQL_ERR_INVALID       # bias inside y_out
+    assert f(h, None, Bz, NONE, B, 5, None) == eq.EQL_ERR_INVALID
+    cn = eq.eqlinear_plan(8, 4, 8, eq.EQL_BF16)
+    assert f(cn.handle, A, Bz, G, B, 5, None) == eq.EQL_ERR_INVALID  # C_N plan
+    for g in (lib.eqlinear_d8_to_fourier, lib.eqlinear_d8_to_regular):
+        assert g(h, A, B, -1, None) == eq.EQL_ERR_INVALID
+        assert g(h, None, None, 0, None) == eq.EQL_OK
+        assert g(h, A, A, 5, None) == eq.EQL_ERR_INVALID             # no in-place transform
+        assert g(h, A, A + 64, 5, None) == eq.EQL_ERR_INVALID
+        assert g(h, A + 8, B, 5, None) == eq.EQL_ERR_INVALID
+        assert g(cn.handle, A, B, 5, None) == eq.EQL_ERR_INVALID
+
+
 def test_binding_checks_tensors_without_gpu(eq):
     import torch
     p = eq.eqlinear_plan(4, 2, 2, eq.EQL_F32)
