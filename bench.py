@@ -34,7 +34,7 @@ OP_METRIC = {
     "backward_weight": "EQ-Linear bwd (weight gradient) tokens/sec + TFLOP/s and % roofline vs expanded-dense GEMM",
 }
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}
 KERNEL_SOURCES = {
     "C": ["group_equivariant_linear_amd/csrc/cn_fused.h",
           "group_equivariant_linear_amd/csrc/cn_mf.h",
@@ -54,9 +54,9 @@ def step_kernel_name(wl):
     if wl.group != "C":
         whole = (wl.C_in // 8) % 8 == 0 and (wl.C_out // 8) % 8 == 0  # block columns in 16-byte pieces
         return "d8_kernel" if wl.dtype == "bf16" and whole else "gemm_rows_kernel"
-    if wl.dtype == "bf16" and 2 <= wl.N <= 8:
+    if wl.dtype in ("bf16", "f16") and 2 <= wl.N <= 8:
         return "cn_mf_kernel"
-    if wl.dtype != "bf16" and wl.N <= 10 and wl.C_in % 4 == 0 and _one_wave_shape(wl):
+    if wl.dtype == "f32" and wl.N <= 10 and wl.C_in % 4 == 0 and _one_wave_shape(wl):
         return "cn_split_kernel"
     return "cn_fast_kernel"
 
@@ -92,6 +92,8 @@ def parse():
     ap.add_argument("--workload", default="c2",
                     help="c1, c2, c3a, c3b, c3c, c3 (the three MLP layers), c4, c5")
     ap.add_argument("--cold-steps", type=int, default=100)
+    ap.add_argument("--dtype", default="workload", choices=["workload", "f32", "bf16", "f16"],
+                    help="element type of a C_N workload (default: the workload's own)")
     ap.add_argument("--tile", type=int, default=-1,
                     help="fixed tile configuration of the C_N kernel (eqlinear_forward_tiled); -1 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -121,15 +123,16 @@ class Layer:
         import synthetic
         self.wl = wl
         self.dt = wl.dtype
-        self.tdt = torch.float32 if wl.dtype == synthetic.F32 else torch.bfloat16
-        eqdt = eq.EQL_F32 if wl.dtype == synthetic.F32 else eq.EQL_BF16
+        self.tdt = {synthetic.F32: torch.float32, synthetic.BF16: torch.bfloat16,
+                    synthetic.F16: torch.float16}[wl.dtype]
+        eqdt = {synthetic.F32: eq.EQL_F32, synthetic.BF16: eq.EQL_BF16, synthetic.F16: eq.EQL_F16}[wl.dtype]
         d = synthetic.workload_inputs(wl, seed=seed)
         self.inputs = d
 
         def dev(a):
             if wl.dtype == synthetic.F32:
                 return torch.from_numpy(a).cuda()
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(a.view(np.int16)).view(self.tdt).cuda()
 
         self.x = dev(d["x"]).reshape(wl.T, -1)
         w = dev(d["w"])
@@ -593,6 +596,12 @@ def main():
     import synthetic
     names = ["c3a", "c3b", "c3c"] if args.workload == "c3" else [args.workload]
     wls = [synthetic.WORKLOADS[n] for n in names]
+    if args.dtype != "workload":
+        from dataclasses import replace
+        if any(wl.group != "C" for wl in wls) and args.dtype == "f16":
+            print("--dtype f16 applies to C_N workloads (the D8 kernels are fp32 and bf16)", file=sys.stderr)
+            sys.exit(2)
+        wls = [replace(wl, dtype=args.dtype) for wl in wls]
     if args.traffic_from:
         summarize_traffic(args, wls)
         return
@@ -667,7 +676,8 @@ def main():
     best_dense = min(t for t in (ms_own, ms_lin) if t is not None)
     group = wls[0].group
 
-    traffic = load_traffic(args.workload, group) if args.op == "forward" and args.epilogue == "none" else None
+    same = args.op == "forward" and args.epilogue == "none" and args.dtype == "workload"
+    traffic = load_traffic(args.workload, group) if same else None
     out = {
         "metric": OP_METRIC[args.op],
         "value": tokens / (ms * 1e-3),

@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libeqlinear.so")
 
 EQL_OK, EQL_ERR_INVALID, EQL_ERR_UNSUPPORTED, EQL_ERR_HIP, EQL_ERR_NOMEM = range(5)
-EQL_F32, EQL_BF16 = 0, 1
+EQL_F32, EQL_BF16, EQL_F16 = 0, 1, 2
 EQL_KIND_CN, EQL_KIND_D8 = 0, 1
 EQL_ACT_NONE, EQL_ACT_GELU = 0, 1
 
@@ -162,7 +162,7 @@ def eqlinear_w_hat_elems(plan: Plan) -> int:
 
 def _torch_dtype(plan: Plan):
     import torch
-    return torch.bfloat16 if plan.dtype == EQL_BF16 else torch.float32
+    return {EQL_F32: torch.float32, EQL_BF16: torch.bfloat16, EQL_F16: torch.float16}[plan.dtype]
 
 
 def _ptr(t, plan: Plan, numel: int | None, name: str):

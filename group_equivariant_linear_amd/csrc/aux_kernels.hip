@@ -44,6 +44,10 @@ template <>
 __device__ __forceinline__ __bf16 round_out<__bf16>(double d) {
     return (__bf16)f64_to_f32_odd(d);
 }
+template <>
+__device__ __forceinline__ _Float16 round_out<_Float16>(double d) {
+    return (_Float16)f64_to_f32_odd(d);  // fp32 carries 13 more bits than fp16
+}
 
 // One thread per (o, i): the N-point real DFT of w[o][i][:], in fp64, packed
 // into planes [N][C_out][C_in] (plane 0 = Re X0, 2k-1/2k = Re/Im Xk, N-1 = Re X_{N/2}).
@@ -76,7 +80,7 @@ __global__ void weight_dft_kernel(const IO* __restrict__ w, IO* __restrict__ w_h
     }
 }
 
-hipError_t launch_weight_dft(int N, int dtype_bf16, const void* w, void* w_hat, int C_in,
+hipError_t launch_weight_dft(int N, int io, const void* w, void* w_hat, int C_in,
                              int C_out, hipStream_t stream) {
     TwArg tw{};
     for (int j = 0; j < N; ++j) {
@@ -87,9 +91,12 @@ hipError_t launch_weight_dft(int N, int dtype_bf16, const void* w, void* w_hat, 
     const int threads = 256;
     const int64_t blocks = (plane + threads - 1) / threads;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (dtype_bf16)
+    if (io == kIoBF16)
         hipLaunchKernelGGL(weight_dft_kernel<__bf16>, dim3((uint32_t)blocks), dim3(threads), 0,
                            stream, (const __bf16*)w, (__bf16*)w_hat, N, plane, tw);
+    else if (io == kIoF16)
+        hipLaunchKernelGGL(weight_dft_kernel<_Float16>, dim3((uint32_t)blocks), dim3(threads), 0,
+                           stream, (const _Float16*)w, (_Float16*)w_hat, N, plane, tw);
     else
         hipLaunchKernelGGL(weight_dft_kernel<float>, dim3((uint32_t)blocks), dim3(threads), 0,
                            stream, (const float*)w, (float*)w_hat, N, plane, tw);
@@ -139,12 +146,15 @@ static uint32_t grid_for(int64_t total, int threads) {
     return (uint32_t)(b > 65536 ? 65536 : (b < 1 ? 1 : b));
 }
 
-hipError_t launch_cn_expand(int N, int dtype_bf16, const void* w, void* w_dense, int C_in,
+hipError_t launch_cn_expand(int N, int io, const void* w, void* w_dense, int C_in,
                             int C_out, hipStream_t stream) {
     const int64_t total = (int64_t)N * C_out * N * C_in;
-    if (dtype_bf16)
+    if (io == kIoBF16)
         hipLaunchKernelGGL(cn_expand_kernel<__bf16>, dim3(grid_for(total, 256)), dim3(256), 0,
                            stream, (const __bf16*)w, (__bf16*)w_dense, N, C_in, total);
+    else if (io == kIoF16)
+        hipLaunchKernelGGL(cn_expand_kernel<_Float16>, dim3(grid_for(total, 256)), dim3(256), 0,
+                           stream, (const _Float16*)w, (_Float16*)w_dense, N, C_in, total);
     else
         hipLaunchKernelGGL(cn_expand_kernel<float>, dim3(grid_for(total, 256)), dim3(256), 0,
                            stream, (const float*)w, (float*)w_dense, N, C_in, total);

@@ -460,11 +460,14 @@ __global__ __launch_bounds__(256) void bw_zero_kernel(float* __restrict__ p, int
 
 }  // namespace
 
-hipError_t launch_w_hat_adjoint(int N, int dtype_bf16, const void* w_hat, void* w_hat_adj, int C_in, int C_out,
+hipError_t launch_w_hat_adjoint(int N, int io, const void* w_hat, void* w_hat_adj, int C_in, int C_out,
                                 hipStream_t stream) {
     const dim3 grid((uint32_t)((C_in + 31) / 32), (uint32_t)((C_out + 31) / 32), (uint32_t)N);
     if (grid.y > 65535u) return hipErrorInvalidConfiguration;
-    if (dtype_bf16)
+    if (io == kIoF16)
+        hipLaunchKernelGGL(w_hat_adjoint_kernel<_Float16>, grid, dim3(256), 0, stream, (const _Float16*)w_hat,
+                           (_Float16*)w_hat_adj, N, C_in, C_out);
+    else if (io == kIoBF16)
         hipLaunchKernelGGL(w_hat_adjoint_kernel<__bf16>, grid, dim3(256), 0, stream, (const __bf16*)w_hat,
                            (__bf16*)w_hat_adj, N, C_in, C_out);
     else

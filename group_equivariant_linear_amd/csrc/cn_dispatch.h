@@ -38,7 +38,7 @@ int choose_shape(int64_t T, int C_in, int C_out) {
 
 template <int N, typename IO>
 int choose_fused(int64_t T, int C_in, int C_out) {
-    // bf16 orders up to 8 take the matrix-core transform kernel, same shapes
+    // 16-bit orders up to 8 take the matrix-core transform kernel, same shapes
     if constexpr (mf_supported<N, IO>) {
         return kMfFirstTile + choose_shape<N>(T, C_in, C_out);
     } else {
@@ -69,14 +69,14 @@ hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, in
 #define EQL_MF(k)                                                                       \
     case k:                                                                             \
         if constexpr (mf_supported<N, IO>)                                              \
-            return launch_mf_entry<N, k>(x, w_hat, y, T, C_in, C_out, stream, epi);          \
+            return launch_mf_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream, epi);          \
         else                                                                            \
             return launch_menu_entry<N, IO, k>(x, w_hat, y, T, C_in, C_out, stream, epi);
             EQL_MF(0) EQL_MF(1) EQL_MF(2) EQL_MF(3) EQL_MF(4) EQL_MF(5)
 #undef EQL_MF
             default:
                 if constexpr (mf_supported<N, IO>)
-                    return launch_mf_entry<N, 6>(x, w_hat, y, T, C_in, C_out, stream, epi);
+                    return launch_mf_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream, epi);
                 else
                     return launch_menu_entry<N, IO, 6>(x, w_hat, y, T, C_in, C_out, stream, epi);
         }

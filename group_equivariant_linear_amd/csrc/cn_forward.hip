@@ -1,5 +1,5 @@
 // cn_forward.hip -- dispatch of the fused C_N forward over group order and dtype.
-// The kernel (cn_fused.h) is instantiated in cn_fused_{f32,bf16}_nXX.hip so the
+// The kernel (cn_fused.h) is instantiated in cn_fused_{f32,bf16,f16}_nXX.hip so the
 // instantiations build in parallel.
 #include "eq_launch.h"
 
@@ -23,10 +23,14 @@ static hipError_t launch_dt(int N, const void* x, const void* w_hat, void* y, in
     }
 }
 
-hipError_t launch_cn_forward(int N, int dtype_bf16, const void* x, const void* w_hat, void* y,
+hipError_t launch_cn_forward(int N, int io, const void* x, const void* w_hat, void* y,
                              int64_t T, int C_in, int C_out, hipStream_t stream, int tile, Epi epi) {
-    if (dtype_bf16) return launch_dt<__bf16>(N, x, w_hat, y, T, C_in, C_out, stream, tile, epi);
-    return launch_dt<float>(N, x, w_hat, y, T, C_in, C_out, stream, tile, epi);
+    switch (io) {
+        case kIoBF16: return launch_dt<__bf16>(N, x, w_hat, y, T, C_in, C_out, stream, tile, epi);
+        case kIoF16: return launch_dt<_Float16>(N, x, w_hat, y, T, C_in, C_out, stream, tile, epi);
+        case kIoF32: return launch_dt<float>(N, x, w_hat, y, T, C_in, C_out, stream, tile, epi);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace eql

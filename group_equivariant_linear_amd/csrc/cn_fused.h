@@ -101,7 +101,8 @@ __device__ __forceinline__ uint32_t bias_fetch(const Epi& epi, int C_out, int o)
 }
 template <typename IO>
 __device__ __forceinline__ float bias_value(uint32_t bits) {
-    return __uint_as_float(sizeof(IO) == 4 ? bits : bits << 16);
+    if constexpr (sizeof(IO) == 4) return __uint_as_float(bits);
+    else return Half<IO>::lo(bits);
 }
 
 // Workgroups per CU that an LDS allocation of b bytes allows (512-byte granules).
@@ -156,6 +157,11 @@ struct IoTraits<__bf16> {
     static constexpr int KC = 32;  // one MFMA 16x16x32 step
     static constexpr int R = 8;
 };
+template <>
+struct IoTraits<_Float16> {
+    static constexpr int KC = 32;  // one MFMA 16x16x32 step
+    static constexpr int R = 8;
+};
 
 template <int N_, typename IO_, int WAVES_, int CB_>
 struct FusedCfg {
@@ -180,7 +186,7 @@ __device__ __forceinline__ int wslot(int o, int q) { return o * 4 + (q ^ ((o >> 
 template <typename IO>
 __device__ __forceinline__ float elem_f32(const uint32_t* w, int e) {
     if constexpr (sizeof(IO) == 4) return __uint_as_float(w[e]);
-    else return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
+    else return (e & 1) ? Half<IO>::hi(w[e >> 1]) : Half<IO>::lo(w[e >> 1]);
 }
 
 template <typename IO>
@@ -233,6 +239,10 @@ struct AFrag<__bf16> {
     using T = bf16x8;
 };
 template <>
+struct AFrag<_Float16> {
+    using T = f16x8;
+};
+template <>
 struct AFrag<float> {
     using T = f32x4;
 };
@@ -266,12 +276,12 @@ __device__ __forceinline__ void x_to_planes(const uint32_t (&xr)[C::XW],
             rdft_forward<N>(xa, Pa);
             rdft_forward<N>(xb, Pb);
 #pragma unroll
-            for (int p = 0; p < N; ++p) pk[p][r / 2] = pack_bf16x2(Pa[p], Pb[p]);
+            for (int p = 0; p < N; ++p) pk[p][r / 2] = Half<IO>::pack2(Pa[p], Pb[p]);
         }
 #pragma unroll
         for (int p = 0; p < N; ++p) {
             const u32x4 v = {pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
-            A[p] = __builtin_bit_cast(bf16x8, v);
+            A[p] = __builtin_bit_cast(typename AFrag<IO>::T, v);
         }
     }
 }
@@ -327,6 +337,9 @@ __device__ __forceinline__ void copy_w_chunk(const typename C::IO* __restrict__ 
 __device__ __forceinline__ void mma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
+__device__ __forceinline__ void mma(f32x4& acc, const f16x8& a, const f16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
 __device__ __forceinline__ void mma(f32x4& acc, const f32x4& a, const f32x4& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
@@ -338,6 +351,11 @@ __device__ __forceinline__ bf16x8 neg(const bf16x8& v) {
     u32x4 u = __builtin_bit_cast(u32x4, v);
     u ^= 0x80008000u;
     return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ f16x8 neg(const f16x8& v) {
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+    u ^= 0x80008000u;
+    return __builtin_bit_cast(f16x8, u);
 }
 __device__ __forceinline__ f32x4 neg(const f32x4& v) { return -v; }
 
@@ -412,13 +430,13 @@ __device__ __forceinline__ void store_y(const f32x4 (&acc)[C::N][C::CB], typenam
                 if constexpr (N % 8 == 0) {
 #pragma unroll
                     for (int j = 0; j < N / 8; ++j) {
-                        const u32x4 v = {pack_bf16x2(yv[8 * j], yv[8 * j + 1]), pack_bf16x2(yv[8 * j + 2], yv[8 * j + 3]),
-                                         pack_bf16x2(yv[8 * j + 4], yv[8 * j + 5]), pack_bf16x2(yv[8 * j + 6], yv[8 * j + 7])};
+                        const u32x4 v = {Half<IO>::pack2(yv[8 * j], yv[8 * j + 1]), Half<IO>::pack2(yv[8 * j + 2], yv[8 * j + 3]),
+                                         Half<IO>::pack2(yv[8 * j + 4], yv[8 * j + 5]), Half<IO>::pack2(yv[8 * j + 6], yv[8 * j + 7])};
                         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst) + j);
                     }
                 } else {
 #pragma unroll
-                    for (int j = 0; j < N; ++j) dst[j] = (__bf16)yv[j];
+                    for (int j = 0; j < N; ++j) dst[j] = (IO)yv[j];
                 }
             }
         }
@@ -760,8 +778,8 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
                             v = u32x4{__float_as_uint(yv[4 * j]), __float_as_uint(yv[4 * j + 1]),
                                       __float_as_uint(yv[4 * j + 2]), __float_as_uint(yv[4 * j + 3])};
                         } else {
-                            v = u32x4{pack_bf16x2(yv[8 * j], yv[8 * j + 1]), pack_bf16x2(yv[8 * j + 2], yv[8 * j + 3]),
-                                      pack_bf16x2(yv[8 * j + 4], yv[8 * j + 5]), pack_bf16x2(yv[8 * j + 6], yv[8 * j + 7])};
+                            v = u32x4{Half<IO>::pack2(yv[8 * j], yv[8 * j + 1]), Half<IO>::pack2(yv[8 * j + 2], yv[8 * j + 3]),
+                                      Half<IO>::pack2(yv[8 * j + 4], yv[8 * j + 5]), Half<IO>::pack2(yv[8 * j + 6], yv[8 * j + 7])};
                         }
                         *reinterpret_cast<u32x4*>(yst + xpiece<C::YROT, C::YP, C::YPITCH>(tl, byte0 / 16 + j) * 16) = v;
                     }
@@ -771,7 +789,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
                         const int by = byte0 + e * S;
                         char* dst = yst + xpiece<C::YROT, C::YP, C::YPITCH>(tl, by / 16) * 16 + (by % 16);
                         if constexpr (sizeof(IO) == 4) *reinterpret_cast<float*>(dst) = yv[e];
-                        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16x2(yv[e], 0.f) & 0xffffu);
+                        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(Half<IO>::pack2(yv[e], 0.f) & 0xffffu);
                     }
                 }
             }
@@ -809,7 +827,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
                     if constexpr (sizeof(IO) == 4)
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv[e]), ry, off + 4u * e, 0, 0);
                     else
-                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(yv[e], 0.f) & 0xffffu), ry,
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(Half<IO>::pack2(yv[e], 0.f) & 0xffffu), ry,
                                                              off + 2u * e, 0, 0);
                 }
             }

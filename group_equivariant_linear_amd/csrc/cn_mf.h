@@ -1,4 +1,5 @@
-// cn_mf.h -- bf16 C_N forward with the group transform on the matrix cores.
+// cn_mf.h -- 16-bit (bf16 or fp16) C_N forward with the group transform on
+// the matrix cores.
 //
 // Same dataflow as the fused kernel ("Flash EQ-Linear", Algorithmic Approach
 // and Implementation: DFT along the group axis, per-frequency channel products
@@ -29,12 +30,14 @@
 // channels) returns y in fp32, which leaves through an LDS staging area as
 // contiguous 16-byte pieces.
 //
-// Supported: bf16, 2 <= N <= 8 (one channel record per 8 k-values), C_in a
-// multiple of 8.  The transform coefficients enter the matrix cores in bf16:
-// exact for 0, +-1, +-1/2^j and the quarter turns; other twiddles carry a
-// rounding of at most 2^-9 relative, and the Fourier-domain outputs one more
-// bf16 rounding before the inverse -- both of the order of the bf16 rounding
-// of Xhat and of y that the fused kernel already makes.
+// Supported: bf16 and fp16, 2 <= N <= 8 (one channel record per 8 k-values),
+// C_in a multiple of 8.  The transform coefficients enter the matrix cores in
+// the I/O type: exact for 0, +-1, +-1/2^j and the quarter turns; other
+// twiddles carry a rounding of at most 2^-9 (bf16) or 2^-12 (fp16) relative,
+// and the Fourier-domain outputs one more rounding to that type before the
+// inverse -- both of the order of the rounding of Xhat and of y that the fused
+// kernel already makes.  (In fp16 the Fourier-domain values must also stay
+// within its range, 65504: a bin can reach N times the largest |y|.)
 #pragma once
 
 #include "cn_fused.h"
@@ -60,9 +63,10 @@ constexpr double inv_coef(int g, int p) {
     return (p % 2) ? 2.0 / N * turn_trig((long)g * k, N, false) : -2.0 / N * turn_trig((long)g * k, N, true);
 }
 
-template <int N_, int WAVES_, int CB_>
-struct MfCfg : FastCfg<N_, __bf16, WAVES_, CB_> {
-    using Base = FastCfg<N_, __bf16, WAVES_, CB_>;
+template <int N_, int WAVES_, int CB_, typename IO_ = __bf16>
+struct MfCfg : FastCfg<N_, IO_, WAVES_, CB_> {
+    using Base = FastCfg<N_, IO_, WAVES_, CB_>;
+    using F8 = typename Half<IO_>::x8;  // 16-bit MFMA fragment (bf16 or fp16)
     static constexpr int N = N_, CB = CB_, CT = 16 * CB_;
     static constexpr int MQ = (N_ + 3) / 4;  // transform products per four channels
     static constexpr int XP = 4 * N_;        // 16-byte pieces of a token row of one chunk
@@ -90,7 +94,7 @@ struct MfCfg : FastCfg<N_, __bf16, WAVES_, CB_> {
 // row (gr, ir) of fragment m, k-values (kg, e): coef(4m + ir, e) if kg == gr.
 // INV selects the inverse transform (rows = group elements, k = planes).
 template <class C, bool INV>
-__device__ __forceinline__ void make_frags(bf16x8 (&Fa)[C::MQ]) {
+__device__ __forceinline__ void make_frags(typename C::F8 (&Fa)[C::MQ]) {
     constexpr int N = C::N;
     const int lane = (int)threadIdx.x & 63;
     const int r = lane & 15, kg = lane >> 4;
@@ -114,15 +118,15 @@ __device__ __forceinline__ void make_frags(bf16x8 (&Fa)[C::MQ]) {
         });
         u32x4 u;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) u[q] = diag ? pack_bf16x2(v[2 * q], v[2 * q + 1]) : 0u;
-        Fa[m] = __builtin_bit_cast(bf16x8, u);
+        for (int q = 0; q < 4; ++q) u[q] = diag ? Half<typename C::IO>::pack2(v[2 * q], v[2 * q + 1]) : 0u;
+        Fa[m] = __builtin_bit_cast(typename C::F8, u);
     });
 }
 
 // Record of channel 8*kg + J of token row t (this lane's k-values of transform
 // product J): elements 0..N-1 of the record, zeros after.
 template <class C, int J>
-__device__ __forceinline__ bf16x8 read_record(const char* xex, int t, int kg) {
+__device__ __forceinline__ typename C::F8 read_record(const char* xex, int t, int kg) {
     constexpr int N = C::N;
     u32x4 e = {0u, 0u, 0u, 0u};
     if constexpr (N == 8) {
@@ -157,21 +161,26 @@ __device__ __forceinline__ bf16x8 read_record(const char* xex, int t, int kg) {
             }
         }
     }
-    return __builtin_bit_cast(bf16x8, e);
+    return __builtin_bit_cast(typename C::F8, e);
 }
 
 __device__ __forceinline__ void mma_ab(f32x4& acc, const bf16x8& a, const bf16x8& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
+__device__ __forceinline__ void mma_ab(f32x4& acc, const f16x8& a, const f16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
 
 template <class C>
 __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
-    const __bf16* __restrict__ x, const __bf16* __restrict__ w_hat, __bf16* __restrict__ y,
+    const typename C::IO* __restrict__ x, const typename C::IO* __restrict__ w_hat, typename C::IO* __restrict__ y,
     int64_t T, int C_in, int C_out, int n_c_tiles, uint32_t total_tiles, uint32_t w_bytes,
     int y_coalesced, Epi epi) {
     constexpr int N = C::N, XP = C::XP, MQ = C::MQ, CB = C::CB;
     constexpr int S = 2;
-    using BiasT = BiasTile<__bf16, C::CT, C::kThreads, C::LDS_BYTES, C::WAVES * C::YST_BYTES>;
+    using IO = typename C::IO;
+    using F8 = typename C::F8;
+    using BiasT = BiasTile<IO, C::CT, C::kThreads, C::LDS_BYTES, C::WAVES * C::YST_BYTES>;
     static_assert(BiasT::FITS, "room in LDS for the bias of the tile");
     __shared__ __attribute__((aligned(16))) char smem[BiasT::SMEM];
     float* lbias = reinterpret_cast<float*>(smem + BiasT::OFF);
@@ -229,7 +238,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
         __syncthreads();
     }
 
-    bf16x8 Fa[MQ];
+    F8 Fa[MQ];
     make_frags<C, false>(Fa);
 
     f32x4 acc[N][CB];
@@ -278,14 +287,14 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
     const int o_l = lane & 15;
     const int lane_off = (o_l * 4 + (kg ^ ((o_l >> 1) & 3))) * 16;
     auto ldW = [&](const char* buf, int p, int b) {
-        return *reinterpret_cast<const bf16x8*>(buf + p * C::CT * 64 + b * 1024 + lane_off);
+        return *reinterpret_cast<const F8*>(buf + p * C::CT * 64 + b * 1024 + lane_off);
     };
 
     // Frequency bins in product order: 0 (DC), 1..H (complex), Nyquist (even N).
     constexpr int H = (N - 1) / 2;
     constexpr int NB = 1 + H + (N % 2 == 0 ? 1 : 0);
     // w_hat fragments of bin s (re part; im part for complex bins), one bin ahead
-    auto load_bin = [&](auto sc, const char* buf, bf16x8(&Wr)[CB], bf16x8(&Wi)[CB]) {
+    auto load_bin = [&](auto sc, const char* buf, F8(&Wr)[CB], F8(&Wi)[CB]) {
         constexpr int sb = decltype(sc)::value;
 #pragma unroll
         for (int b = 0; b < CB; ++b) {
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
         const char* buf = wbuf + (c & 1) * C::BUF_BYTES;
 
         // records of channels 8kg + j (j = 0..7) of token tl
-        bf16x8 rec[8];
+        F8 rec[8];
         static_for<0, 8>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             rec[j] = read_record<C, j>(xex, tl, kg);
@@ -335,10 +344,10 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
             const int left = C_in - c * C::KC;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (8 * kg + j >= left) rec[j] = bf16x8{};
+                if (8 * kg + j >= left) rec[j] = F8{};
         }
         // transform: Xh[p] = planes p of channels 8kg .. 8kg+7, token tl
-        bf16x8 Xh[N];
+        F8 Xh[N];
         {
             uint32_t pk[N][4];
 #pragma unroll
@@ -352,18 +361,18 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
                     mma_ab(d1[m], Fa[m], rec[2 * jj + 1]);
                 }
 #pragma unroll
-                for (int p = 0; p < N; ++p) pk[p][jj] = pack_bf16x2(d0[p / 4][p % 4], d1[p / 4][p % 4]);
+                for (int p = 0; p < N; ++p) pk[p][jj] = Half<IO>::pack2(d0[p / 4][p % 4], d1[p / 4][p % 4]);
             }
 #pragma unroll
             for (int p = 0; p < N; ++p) {
                 const u32x4 v = {pk[p][0], pk[p][1], pk[p][2], pk[p][3]};
-                Xh[p] = __builtin_bit_cast(bf16x8, v);
+                Xh[p] = __builtin_bit_cast(F8, v);
             }
         }
         // the records are consumed: the exchange rows may be refilled
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         dma_x(c + 1);
-        bf16x8 Wr[2][CB], Wi[2][CB];
+        F8 Wr[2][CB], Wi[2][CB];
         load_bin(std::integral_constant<int, 0>{}, buf, Wr[0], Wi[0]);
         __builtin_amdgcn_sched_barrier(0);
 
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
                 for (int b = 0; b < CB; ++b) mma_ab(acc[0][b], Wr[cur][b], Xh[0]);
             } else if constexpr (sb <= H) {
                 constexpr int pr = 2 * sb - 1, pi = 2 * sb;
-                const bf16x8 nXi = neg(Xh[pi]);
+                const F8 nXi = neg(Xh[pi]);
 #pragma unroll
                 for (int b = 0; b < CB; ++b) mma_ab(acc[pr][b], Wr[cur][b], Xh[pr]);
 #pragma unroll
@@ -403,7 +412,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
             __syncthreads();
         }
         char* yst = smem + wave * C::YST_BYTES;
-        bf16x8 Ga[MQ];
+        F8 Ga[MQ];
         make_frags<C, true>(Ga);
 #pragma unroll
         for (int b = 0; b < CB; ++b) {
@@ -419,9 +428,9 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const float lo = 2 * q < N ? acc[2 * q < N ? 2 * q : 0][b][i] : 0.f;
                     const float hi = 2 * q + 1 < N ? acc[2 * q + 1 < N ? 2 * q + 1 : 0][b][i] : 0.f;
-                    bu[q] = pack_bf16x2(lo, hi);
+                    bu[q] = Half<IO>::pack2(lo, hi);
                 }
-                const bf16x8 Bv = __builtin_bit_cast(bf16x8, bu);
+                const F8 Bv = __builtin_bit_cast(F8, bu);
 #pragma unroll
                 for (int m = 0; m < MQ; ++m) {
                     f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -438,7 +447,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
             }
             uint32_t pk[2 * N];
 #pragma unroll
-            for (int q = 0; q < 2 * N; ++q) pk[q] = pack_bf16x2(flat[2 * q], flat[2 * q + 1]);
+            for (int q = 0; q < 2 * N; ++q) pk[q] = Half<IO>::pack2(flat[2 * q], flat[2 * q + 1]);
             // 8N bytes at byte (16b + 4kg) * 2N of row tl: N dword pairs, each
             // inside one 16-byte piece
             const int byte0 = (16 * b + 4 * kg) * 2 * N;
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
                 if (epi_on(epi)) epi_apply<N>(yv, epi.bias != nullptr ? lbias[o - o0] : 0.0f, epi.act);
 #pragma unroll
                 for (int e = 0; e < N; ++e)
-                    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(yv[e], 0.f) & 0xffffu), ry,
+                    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(Half<IO>::pack2(yv[e], 0.f) & 0xffffu), ry,
                                                          off + 2u * e, 0, 0);
             }
     }
@@ -529,13 +538,13 @@ hipError_t launch_mf_cfg(const void* x, const void* w_hat, void* y, int64_t T, i
     const int64_t w_bytes = (int64_t)C::N * C_out * C_in * 2;
     const int y_coalesced = ((int64_t)C_out * C::N * 2) % 16 == 0;
     hipLaunchKernelGGL((cn_mf_kernel<C>), dim3((uint32_t)total), dim3(C::kThreads), 0, stream,
-                       (const __bf16*)x, (const __bf16*)w_hat, (__bf16*)y, T, C_in, C_out, n_c,
+                       (const typename C::IO*)x, (const typename C::IO*)w_hat, (typename C::IO*)y, T, C_in, C_out, n_c,
                        (uint32_t)total, (uint32_t)w_bytes, y_coalesced, epi);
     return hipGetLastError();
 }
 
 template <int N, typename IO>
-constexpr bool mf_supported = std::is_same_v<IO, __bf16> && N >= 2 && N <= 8;
+constexpr bool mf_supported = (std::is_same_v<IO, __bf16> || std::is_same_v<IO, _Float16>) && N >= 2 && N <= 8;
 
 // Largest output-block count <= CB whose LDS fits the CU and whose
 // accumulators stay within 192 registers per lane.
@@ -544,19 +553,19 @@ constexpr int mf_cap() {
     if constexpr (CB <= 1) return 1;
     else if constexpr (MfCfg<N, W, CB>::LDS_BYTES <= 163840 && 4 * N * CB <= 192) return CB;
     else return mf_cap<N, W, CB - 1>();
-}
+}  // (the LDS layout is the same for both 16-bit types)
 
 // Menu entry I (same shapes as FusedMenu) on the matrix-core transform kernel;
 // shapes it cannot take (ragged C_in, huge rows) go to the fused kernel.
-template <int N, int I>
+template <int N, typename IO, int I>
 hipError_t launch_mf_entry(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
                            hipStream_t stream, Epi epi) {
-    constexpr int W = FusedMenu<N, __bf16>::waves[I];
-    constexpr int CB = mf_cap<N, W, FusedMenu<N, __bf16>::cb[I]>();
-    using Cfg = MfCfg<N, W, CB>;
-    if (fast_ok<N, __bf16>(C_in, C_out, Cfg::TT))
+    constexpr int W = FusedMenu<N, IO>::waves[I];
+    constexpr int CB = mf_cap<N, W, FusedMenu<N, IO>::cb[I]>();
+    using Cfg = MfCfg<N, W, CB, IO>;
+    if (fast_ok<N, IO>(C_in, C_out, Cfg::TT))
         return launch_mf_cfg<Cfg>(x, w_hat, y, T, C_in, C_out, stream, epi);
-    return launch_menu_entry<N, __bf16, I>(x, w_hat, y, T, C_in, C_out, stream, epi);
+    return launch_menu_entry<N, IO, I>(x, w_hat, y, T, C_in, C_out, stream, epi);
 }
 
 }  // namespace eql

@@ -284,6 +284,40 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// fp16 (IEEE binary16) helpers.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> fp16 (overflow to infinity), two values packed
+// in one dword.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// The two 16-bit storage types behind one interface: an 8-element MFMA
+// fragment, packing two fp32 values (RNE) and reading either half of a dword.
+template <typename IO>
+struct Half;
+template <>
+struct Half<__bf16> {
+    using x8 = bf16x8;
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+    static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+};
+template <>
+struct Half<_Float16> {
+    using x8 = f16x8;
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_f16x2(lo, hi); }
+    static __device__ __forceinline__ float lo(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    }
+    static __device__ __forceinline__ float hi(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Workgroup ids are handed to the 8 XCDs round-robin.  Remap them so that a
 // run of consecutive logical tiles executes on one XCD and shares its L2.

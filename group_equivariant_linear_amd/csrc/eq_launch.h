@@ -8,6 +8,11 @@ namespace eql {
 
 constexpr int kMaxGemmJobs = 6;
 
+// Element type of a launch's tensors ("io" arguments), the codes of the C ABI's
+// eqlinear_dtype.  Launchers that take a plain "dtype_bf16" flag have no fp16
+// form; the C ABI turns fp16 plans away before it reaches them.
+enum : int { kIoF32 = 0, kIoBF16 = 1, kIoF16 = 2 };
+
 // Fused neighbours of the C_N forward: y = act(y + bias[o]) in the epilogue.
 // bias: device, plan dtype, C_out elements, or null; act: 0 identity, 1 GELU.
 struct Epi {
@@ -33,10 +38,10 @@ struct GemmJobs {
 };
 
 // tile: -1 = automatic choice, else a fixed tile configuration (tests, tuning).
-hipError_t launch_cn_forward(int N, int dtype_bf16, const void* x, const void* w_hat, void* y,
+hipError_t launch_cn_forward(int N, int io, const void* x, const void* w_hat, void* y,
                              int64_t T, int C_in, int C_out, hipStream_t stream, int tile, Epi epi = Epi{nullptr, 0});
 
-hipError_t launch_gemm_rows(int dtype_bf16, GemmJobs jobs, const void* x, const void* w, void* y,
+hipError_t launch_gemm_rows(int io, GemmJobs jobs, const void* x, const void* w, void* y,
                             int64_t T, int ldx, int ldy, hipStream_t stream);
 
 // bf16 D8 jobs on the dedicated kernel (16*cb output channels per workgroup);
@@ -46,7 +51,7 @@ hipError_t launch_d8_fast(GemmJobs jobs, const void* x, const void* w, void* y, 
                           int64_t w_elems, int cb, hipStream_t stream);
 
 // Adjoint spectrum: w_hat_adj[p][i][o] = +-w_hat[p][o][i] (imaginary planes negated).
-hipError_t launch_w_hat_adjoint(int N, int dtype_bf16, const void* w_hat, void* w_hat_adj, int C_in, int C_out,
+hipError_t launch_w_hat_adjoint(int N, int io, const void* w_hat, void* w_hat_adj, int C_in, int C_out,
                                 hipStream_t stream);
 
 // Weight gradient of the C_N layer into fp32 dw[C_out][C_in][N]; the workspace
@@ -56,10 +61,10 @@ hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const
                                      int C_in, int C_out, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
-hipError_t launch_weight_dft(int N, int dtype_bf16, const void* w, void* w_hat, int C_in,
+hipError_t launch_weight_dft(int N, int io, const void* w, void* w_hat, int C_in,
                              int C_out, hipStream_t stream);
 
-hipError_t launch_cn_expand(int N, int dtype_bf16, const void* w, void* w_dense, int C_in,
+hipError_t launch_cn_expand(int N, int io, const void* w, void* w_dense, int C_in,
                             int C_out, hipStream_t stream);
 
 hipError_t launch_d8_expand(int dtype_bf16, const void* wb, void* w_dense, int C_in, int C_out,

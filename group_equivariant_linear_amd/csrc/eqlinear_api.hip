@@ -16,9 +16,12 @@ struct eqlinear_plan_s {
 namespace {
 
 
-bool dtype_ok(int dt) { return dt == EQL_F32 || dt == EQL_BF16; }
+bool dtype_ok(int dt) { return dt == EQL_F32 || dt == EQL_BF16 || dt == EQL_F16; }
 
-size_t elem_size(const eqlinear_plan_s* p) { return p->dtype == EQL_BF16 ? 2 : 4; }
+// The plan dtype is the launchers' element-type code (eql::kIo*).
+static_assert(EQL_F32 == eql::kIoF32 && EQL_BF16 == eql::kIoBF16 && EQL_F16 == eql::kIoF16, "type codes");
+
+size_t elem_size(const eqlinear_plan_s* p) { return p->dtype == EQL_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -71,6 +74,7 @@ eqlinear_status eqlinear_d8_plan(eqlinear_plan_t* out, int C_in, int C_out, eqli
     *out = nullptr;
     if (C_in < 8 || C_out < 8 || C_in % 8 || C_out % 8 || !dtype_ok((int)dt))
         return EQL_ERR_INVALID;
+    if (dt == EQL_F16) return EQL_ERR_UNSUPPORTED;  // the D8 kernels are fp32 and bf16
     if (C_in > kMaxWidth || C_out > kMaxWidth) return EQL_ERR_INVALID;
     eqlinear_plan_s* p = new (std::nothrow) eqlinear_plan_s{EQL_KIND_D8, (int)dt, 8, C_in, C_out};
     if (!p) return EQL_ERR_NOMEM;
@@ -132,7 +136,7 @@ eqlinear_status eqlinear_weight_fft(eqlinear_plan_t p, const void* w, void* w_ha
     if (!aligned16(w) || !aligned16(w_hat)) return EQL_ERR_INVALID;
     const size_t bytes = eqlinear_w_hat_elems(p) * elem_size(p);
     if (overlaps(w, bytes, w_hat, bytes)) return EQL_ERR_INVALID;
-    hipError_t e = eql::launch_weight_dft(p->N, p->dtype == EQL_BF16, w, w_hat, p->C_in,
+    hipError_t e = eql::launch_weight_dft(p->N, p->dtype, w, w_hat, p->C_in,
                                           p->C_out, nullptr);
     if (e != hipSuccess) return EQL_ERR_HIP;
     return hip_status(hipStreamSynchronize(nullptr));
@@ -150,7 +154,7 @@ eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t p, const void* x, const v
     const size_t wb = eqlinear_w_hat_elems(p) * es;
     if (overlaps(x, xb, y, yb) || overlaps(w_hat, wb, y, yb)) return EQL_ERR_INVALID;
     if (tile < -1 || tile > 15) return EQL_ERR_INVALID;
-    return hip_status(eql::launch_cn_forward(p->N, p->dtype == EQL_BF16, x, w_hat, y, T, p->C_in,
+    return hip_status(eql::launch_cn_forward(p->N, p->dtype, x, w_hat, y, T, p->C_in,
                                              p->C_out, (hipStream_t)stream, tile));
 }
 
@@ -173,7 +177,7 @@ eqlinear_status eqlinear_forward_bias_act(eqlinear_plan_t p, const void* x, cons
     if (overlaps(x, xb, y, yb) || overlaps(w_hat, wb, y, yb)) return EQL_ERR_INVALID;
     if (bias && (((uintptr_t)bias % es) != 0 || overlaps(bias, bb, y, yb))) return EQL_ERR_INVALID;
     if (tile < -1 || tile > 15) return EQL_ERR_INVALID;
-    return hip_status(eql::launch_cn_forward(p->N, p->dtype == EQL_BF16, x, w_hat, y, T, p->C_in, p->C_out,
+    return hip_status(eql::launch_cn_forward(p->N, p->dtype, x, w_hat, y, T, p->C_in, p->C_out,
                                              (hipStream_t)stream, tile, eql::Epi{bias, act}));
 }
 
@@ -221,7 +225,7 @@ eqlinear_status eqlinear_w_hat_adjoint(eqlinear_plan_t p, const void* w_hat, voi
     if (!aligned16(w_hat) || !aligned16(w_hat_adj)) return EQL_ERR_INVALID;
     const size_t b = eqlinear_w_hat_elems(p) * elem_size(p);
     if (overlaps(w_hat, b, w_hat_adj, b)) return EQL_ERR_INVALID;
-    return hip_status(eql::launch_w_hat_adjoint(p->N, p->dtype == EQL_BF16, w_hat, w_hat_adj, p->C_in, p->C_out,
+    return hip_status(eql::launch_w_hat_adjoint(p->N, p->dtype, w_hat, w_hat_adj, p->C_in, p->C_out,
                                                 (hipStream_t)stream));
 }
 
@@ -237,12 +241,12 @@ eqlinear_status eqlinear_backward_data(eqlinear_plan_t p, const void* dy, const 
     const size_t wb = eqlinear_w_hat_elems(p) * es;
     if (overlaps(dy, dyb, dx, dxb) || overlaps(w_hat_adj, wb, dx, dxb)) return EQL_ERR_INVALID;
     // the layer with C_in and C_out exchanged, run by the forward kernels
-    return hip_status(eql::launch_cn_forward(p->N, p->dtype == EQL_BF16, dy, w_hat_adj, dx, T, p->C_out, p->C_in,
+    return hip_status(eql::launch_cn_forward(p->N, p->dtype, dy, w_hat_adj, dx, T, p->C_out, p->C_in,
                                              (hipStream_t)stream, -1));
 }
 
 size_t eqlinear_backward_weight_workspace(eqlinear_plan_t p, int64_t T) {
-    if (!p || p->kind != EQL_KIND_CN || T < 0) return 0;
+    if (!p || p->kind != EQL_KIND_CN || T < 0 || p->dtype == EQL_F16) return 0;
     return eql::backward_weight_workspace(p->N, p->dtype == EQL_BF16, T, p->C_in, p->C_out);
 }
 
@@ -250,6 +254,7 @@ eqlinear_status eqlinear_backward_weight(eqlinear_plan_t p, const void* x, const
                                          void* workspace, size_t workspace_bytes, void* stream) {
     if (!p || p->kind != EQL_KIND_CN || !dw) return EQL_ERR_INVALID;
     if (T < 0) return EQL_ERR_INVALID;
+    if (p->dtype == EQL_F16) return EQL_ERR_UNSUPPORTED;  // the weight-gradient kernels are fp32 and bf16
     if (!aligned16(dw)) return EQL_ERR_INVALID;
     const size_t dwb = eqlinear_w_hat_elems(p) * sizeof(float);
     if (T > 0) {
@@ -294,7 +299,7 @@ eqlinear_status eqlinear_d8_forward(eqlinear_plan_t p, const void* x, const void
                                                  (int64_t)eqlinear_w_hat_elems(p), cb, (hipStream_t)stream);
         if (e != hipErrorNotSupported) return hip_status(e);
     }
-    return hip_status(eql::launch_gemm_rows(p->dtype == EQL_BF16, jobs, x, wb, y, T, p->C_in,
+    return hip_status(eql::launch_gemm_rows(p->dtype, jobs, x, wb, y, T, p->C_in,
                                             p->C_out, (hipStream_t)stream));
 }
 
@@ -308,7 +313,7 @@ eqlinear_status eqlinear_expand_dense(eqlinear_plan_t p, const void* w, void* w_
     if (overlaps(w, wb, w_dense, db)) return EQL_ERR_INVALID;
     hipError_t e;
     if (p->kind == EQL_KIND_CN)
-        e = eql::launch_cn_expand(p->N, p->dtype == EQL_BF16, w, w_dense, p->C_in, p->C_out,
+        e = eql::launch_cn_expand(p->N, p->dtype, w, w_dense, p->C_in, p->C_out,
                                   (hipStream_t)stream);
     else
         e = eql::launch_d8_expand(p->dtype == EQL_BF16, w, w_dense, p->C_in, p->C_out,
@@ -330,7 +335,7 @@ eqlinear_status eqlinear_dense_forward(eqlinear_plan_t p, const void* x, const v
     eql::GemmJobs jobs{};
     jobs.njobs = 1;
     jobs.j[0] = eql::GemmJob{0, 0, (int)K, (int)M, 0, (int)K, 0, 0, 0, 0};
-    return hip_status(eql::launch_gemm_rows(p->dtype == EQL_BF16, jobs, x, w_dense, y, T, (int)K,
+    return hip_status(eql::launch_gemm_rows(p->dtype, jobs, x, w_dense, y, T, (int)K,
                                             (int)M, (hipStream_t)stream));
 }
 

@@ -28,6 +28,11 @@ struct GemmTraits<__bf16> {
     static constexpr int KC = 32;
     static constexpr int R = 8;
 };
+template <>
+struct GemmTraits<_Float16> {
+    static constexpr int KC = 32;
+    static constexpr int R = 8;
+};
 
 template <typename IO_, int NPW_, int TPW_>
 struct GemmCfg {
@@ -59,6 +64,10 @@ __device__ __forceinline__ void set_half<__bf16>(uint32_t* w, int e, uint32_t bi
     if (e & 1) w[e >> 1] = (w[e >> 1] & 0x0000ffffu) | (bits << 16);
     else w[e >> 1] = (w[e >> 1] & 0xffff0000u) | bits;
 }
+template <>
+__device__ __forceinline__ void set_half<_Float16>(uint32_t* w, int e, uint32_t bits) {
+    set_half<__bf16>(w, e, bits);  // the same 16-bit placement
+}
 
 template <typename IO>
 __device__ __forceinline__ uint32_t bits_of(const IO* p) {
@@ -82,6 +91,9 @@ __device__ __forceinline__ uint4 load_row_vec(const IO* src, bool row_ok, int av
 __device__ __forceinline__ void mma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
+__device__ __forceinline__ void mma16(f32x4& acc, const f16x8& a, const f16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
 __device__ __forceinline__ void mma16(f32x4& acc, const f32x4& a, const f32x4& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
@@ -94,7 +106,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_rows_kernel(
     GemmJobs jobs, const typename C::IO* __restrict__ x, const typename C::IO* __restrict__ w,
     typename C::IO* __restrict__ y, int64_t T, int ldx, int ldy, uint32_t total_tiles) {
     using IO = typename C::IO;
-    using F = std::conditional_t<std::is_same<IO, float>::value, f32x4, bf16x8>;
+    using F = std::conditional_t<std::is_same<IO, float>::value, f32x4,
+                                 std::conditional_t<std::is_same<IO, _Float16>::value, f16x8, bf16x8>>;
     __shared__ __attribute__((aligned(16))) IO sW[C::NT * C::PITCH];
     __shared__ __attribute__((aligned(16))) IO sX[C::TT * C::PITCH];
 
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_rows_kernel(
                 if constexpr (std::is_same<IO, float>::value) {
                     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
                 } else {
-                    u32x2 u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    u32x2 u = {Half<IO>::pack2(v[0], v[1]), Half<IO>::pack2(v[2], v[3])};
                     __builtin_nontemporal_store(u, reinterpret_cast<u32x2*>(dst));
                 }
             } else {
@@ -244,9 +257,10 @@ static hipError_t launch_gemm_dt(GemmJobs jobs, const void* x, const void* w, vo
     return launch_gemm_cfg<GemmCfg<IO, 2, 2>>(jobs, x, w, y, T, ldx, ldy, stream);
 }
 
-hipError_t launch_gemm_rows(int dtype_bf16, GemmJobs jobs, const void* x, const void* w, void* y,
+hipError_t launch_gemm_rows(int io, GemmJobs jobs, const void* x, const void* w, void* y,
                             int64_t T, int ldx, int ldy, hipStream_t stream) {
-    if (dtype_bf16) return launch_gemm_dt<__bf16>(jobs, x, w, y, T, ldx, ldy, stream);
+    if (io == kIoBF16) return launch_gemm_dt<__bf16>(jobs, x, w, y, T, ldx, ldy, stream);
+    if (io == kIoF16) return launch_gemm_dt<_Float16>(jobs, x, w, y, T, ldx, ldy, stream);
     return launch_gemm_dt<float>(jobs, x, w, y, T, ldx, ldy, stream);
 }
 

@@ -20,8 +20,15 @@
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
  *    never allocates, frees or keeps them.  Base pointers must be 16-byte aligned.
- *  - Element type is the plan dtype: EQL_F32 = IEEE fp32, EQL_BF16 = bfloat16
- *    (accumulation is always fp32).
+ *  - Element type is the plan dtype: EQL_F32 = IEEE fp32, EQL_BF16 = bfloat16,
+ *    EQL_F16 = IEEE binary16 (accumulation is always fp32).  fp16 ("Flash
+ *    EQ-Linear", Implementation: FP32 and FP16 kernels; "Quick ViTs", key
+ *    findings, Table 2 in fp16) is taken by the C_N plans' weight spectrum,
+ *    forward (every tile; with fused bias/GELU), adjoint spectrum, input
+ *    gradient and expanded-dense comparator; the weight gradient and D8 plans
+ *    return EQL_ERR_UNSUPPORTED for it.  fp16 holds values up to 65504: inputs,
+ *    outputs and (in the matrix-core transform kernel) the Fourier-domain
+ *    intermediates must stay within that range.
  *  - Layouts are row-major with the last index contiguous:
  *      x [T][C_in][N], y [T][C_out][N], w [C_out][C_in][N]           (C_N)
  *      x [T][C_in], y [T][C_out] with features [A1|A2|B1|B2|E0|E1]  (D8)
@@ -53,7 +60,7 @@ typedef enum {
     EQL_ERR_NOMEM = 4        /* host allocation failed */
 } eqlinear_status;
 
-typedef enum { EQL_F32 = 0, EQL_BF16 = 1 } eqlinear_dtype;
+typedef enum { EQL_F32 = 0, EQL_BF16 = 1, EQL_F16 = 2 } eqlinear_dtype;
 
 typedef enum { EQL_KIND_CN = 0, EQL_KIND_D8 = 1 } eqlinear_kind;
 
@@ -81,13 +88,14 @@ typedef struct {
 const char* eqlinear_status_string(eqlinear_status s);
 
 /* Create a C_N plan.  1 <= N <= 16, C_in >= 1, C_out >= 1, dt in {EQL_F32,
- * EQL_BF16}; otherwise EQL_ERR_INVALID and *out is left NULL.  Host metadata
- * only: needs no GPU.  Release with eqlinear_plan_destroy. */
+ * EQL_BF16, EQL_F16}; otherwise EQL_ERR_INVALID and *out is left NULL.  Host
+ * metadata only: needs no GPU.  Release with eqlinear_plan_destroy. */
 eqlinear_status eqlinear_plan(eqlinear_plan_t* out, int N, int C_in, int C_out,
                               eqlinear_dtype dt);
 
 /* Create a D8 plan ("Quick ViTs", key design 2).  C_in and C_out are full
- * widths, multiples of 8 (C/8 channels per 1-D irrep, C/4 copies of E). */
+ * widths, multiples of 8 (C/8 channels per 1-D irrep, C/4 copies of E); dt in
+ * {EQL_F32, EQL_BF16} (EQL_F16: EQL_ERR_UNSUPPORTED). */
 eqlinear_status eqlinear_d8_plan(eqlinear_plan_t* out, int C_in, int C_out,
                                  eqlinear_dtype dt);
 
@@ -122,10 +130,11 @@ eqlinear_status eqlinear_weight_fft(eqlinear_plan_t plan, const void* w, void* w
  *   w_hat [N][C_out][C_in] device, as written by eqlinear_weight_fft
  *   y     [T][C_out][N] device, plan dtype; must not overlap x or w_hat
  *   T >= 0 tokens (T == 0: returns EQL_OK, launches nothing)
- * bf16 plans round the frequency-domain inputs to bf16 before the matrix
- * cores and round y once from fp32; for 2 <= N <= 8 the transforms run on the
- * matrix cores too, with bf16 coefficients, and the frequency-domain outputs
- * are rounded to bf16 before the inverse transform. */
+ * 16-bit plans (bf16, fp16) round the frequency-domain inputs to the plan
+ * dtype before the matrix cores and round y once from fp32; for 2 <= N <= 8
+ * the transforms run on the matrix cores too, with coefficients in the plan
+ * dtype, and the frequency-domain outputs are rounded to it before the inverse
+ * transform. */
 eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                  void* y, int64_t T, void* stream);
 
@@ -136,11 +145,11 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
  *   tile 0: W=4 B=6   1: W=4 B=5   2: W=4 B=4   3: W=4 B=3   4: W=4 B=2
  *   tile 5: W=1 B=2   6: W=1 B=1   -1: automatic (same as eqlinear_forward).
  * Tiles 7..13 are the shapes of tiles 0..6 on the kernel that runs the group
- * DFT and its inverse as block-diagonal matrix-core products (bf16 plans with
- * 2 <= N <= 8; other plans run tile - 7).  It rounds the transform
- * coefficients and the Fourier-domain outputs to bf16, so its results differ
- * from the other tiles by bf16 rounding; the automatic choice uses it where
- * it applies.  Tiles 14 and 15 (fp32 plans with N <= 10, C_in a multiple of
+ * DFT and its inverse as block-diagonal matrix-core products (bf16 and fp16
+ * plans with 2 <= N <= 8; other plans run tile - 7).  It rounds the transform
+ * coefficients and the Fourier-domain outputs to the plan dtype, so its
+ * results differ from the other tiles by that rounding; the automatic choice
+ * uses it where it applies.  Tiles 14 and 15 (fp32 plans with N <= 10, C_in a multiple of
  * 4; other plans and shapes run tile 13) cover 16 tokens and 32 output channels (16
  * when C_out <= 16) with the input channels of every step split over 2 or 4
  * waves per output block, whose partial spectra are summed in a fixed order;
@@ -239,7 +248,7 @@ eqlinear_status eqlinear_backward_data(eqlinear_plan_t plan, const void* dy, con
                                        void* dx, int64_t T, void* stream);
 
 /* Bytes of device workspace that eqlinear_backward_weight needs for T tokens
- * (0 for T <= 0 or a non-C_N plan). */
+ * (0 for T <= 0, a non-C_N plan or an fp16 plan). */
 size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t T);
 
 /* Weight gradient: dw [C_out][C_in][N] in fp32 (overwritten, for either plan
@@ -253,7 +262,8 @@ size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t T);
  * eqlinear_backward_weight_workspace(plan, T) bytes, owned by the caller and
  * not overlapping x, dy or dw; its contents are scratch.  x, dy, dw 16-byte
  * aligned.  T == 0 writes zeros to dw.  Asynchronous on stream; no allocation.
- * EQL_ERR_INVALID for a D8 plan, bad pointers, overlap or a short workspace. */
+ * EQL_ERR_INVALID for a D8 plan, bad pointers, overlap or a short workspace;
+ * EQL_ERR_UNSUPPORTED for an fp16 plan. */
 eqlinear_status eqlinear_backward_weight(eqlinear_plan_t plan, const void* x, const void* dy, float* dw,
                                          int64_t T, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -25,6 +25,7 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"
 
 
 @dataclass(frozen=True)
@@ -86,8 +87,9 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 def quantize(a64: np.ndarray, dtype: str):
     """Return (device_array, exact_fp64) for the workload dtype.
 
-    device_array is float32 (f32) or uint16 bf16 bit patterns (bf16).
-    exact_fp64 holds the same values exactly in fp64.
+    device_array is float32 (f32), or uint16 bit patterns (bf16, f16).
+    exact_fp64 holds the same values exactly in fp64.  fp16 takes numpy's
+    fp64 -> float16 conversion (round-to-nearest-even, correctly rounded).
     """
     if dtype == F32:
         d = round_f32(a64)
@@ -95,6 +97,9 @@ def quantize(a64: np.ndarray, dtype: str):
     if dtype == BF16:
         b = round_bf16_bits(a64)
         return b, bf16_bits_to_f64(b)
+    if dtype == F16:
+        h = np.ascontiguousarray(a64, dtype=np.float64).astype(np.float16)
+        return h.view(np.uint16), h.astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

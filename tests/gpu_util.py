@@ -10,14 +10,14 @@ SENTINEL_BF16_BITS = np.int16(0x7F7F)  # a large finite bf16
 
 def torch_dtype(dt):
     import torch
-    return torch.float32 if dt == synthetic.F32 else torch.bfloat16
+    return {synthetic.F32: torch.float32, synthetic.BF16: torch.bfloat16, synthetic.F16: torch.float16}[dt]
 
 
 def to_dev(a, dt):
     import torch
     if dt == synthetic.F32:
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch_dtype(dt)).cuda()
 
 
 def to_f64(t):
@@ -60,7 +60,8 @@ def max_err_over_rms(a, b):
 
 # rel-L2 bars for the whole output; the max-error bar (relative to the output's
 # RMS) catches a localised mistake that a whole-tensor norm would dilute.
-BARS = {synthetic.F32: (1e-5, 2e-4), synthetic.BF16: (2e-2, 1e-1)}
+# fp16: the bf16 bars scaled by the ratio of the unit roundoffs, 2^-11 / 2^-8
+BARS = {synthetic.F32: (1e-5, 2e-4), synthetic.BF16: (2e-2, 1e-1), synthetic.F16: (2.5e-3, 1.25e-2)}
 
 
 def assert_close(y, ref, dt, what=""):

@@ -54,7 +54,7 @@ def test_status_strings(eq):
 
 
 @pytest.mark.parametrize("args", [(0, 4, 4, 0), (17, 4, 4, 0), (4, 0, 4, 0), (4, 4, 0, 0),
-                                  (4, 4, 4, 2), (4, 4, 4, -1), (2, 1 << 20, 2, 0)])
+                                  (4, 4, 4, 3), (4, 4, 4, -1), (2, 1 << 20, 2, 0)])
 def test_plan_rejects_invalid(eq, args):
     with pytest.raises(eq.EqlError) as e:
         eq.eqlinear_plan(*args)
@@ -65,6 +65,23 @@ def test_plan_rejects_invalid(eq, args):
 def test_d8_plan_rejects_invalid(eq, args):
     with pytest.raises(eq.EqlError):
         eq.eqlinear_d8_plan(*args)
+
+
+def test_fp16_plans(eq):
+    """fp16 C_N plans exist (weight spectrum, forward, input gradient, comparator);
+    the weight gradient and D8 plans turn fp16 away before any HIP call."""
+    lib = eq.load_library()
+    p = eq.eqlinear_plan(8, 16, 24, eq.EQL_F16)
+    assert p.info["dtype"] == eq.EQL_F16 and p.info["w_hat_elems"] == 8 * 16 * 24
+    with pytest.raises(eq.EqlError) as e:
+        eq.eqlinear_d8_plan(16, 16, eq.EQL_F16)
+    assert e.value.status == eq.EQL_ERR_UNSUPPORTED
+    A, B, W, S = 1 << 20, 1 << 30, 1 << 34, 1 << 38
+    assert lib.eqlinear_backward_weight_workspace(p.handle, 100) == 0
+    assert lib.eqlinear_backward_weight(p.handle, A, B, W, 100, S, 1 << 20, None) == eq.EQL_ERR_UNSUPPORTED
+    # the forward's checks size fp16 tensors at 2 bytes: y one element into x's last row overlaps
+    x_bytes = 5 * 16 * 8 * 2
+    assert lib.eqlinear_forward(p.handle, A, W, A + x_bytes - 16, 5, None) == eq.EQL_ERR_INVALID
 
 
 def test_null_out_and_null_plan(eq):

@@ -15,7 +15,7 @@ from gpu_util import Guarded, assert_close, rel_l2, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
-F32, BF16 = synthetic.F32, synthetic.BF16
+F32, BF16, F16 = synthetic.F32, synthetic.BF16, synthetic.F16
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,7 @@ def eq():
 
 
 def _eqdt(eq, dt):
-    return eq.EQL_F32 if dt == F32 else eq.EQL_BF16
+    return {F32: eq.EQL_F32, BF16: eq.EQL_BF16, F16: eq.EQL_F16}[dt]
 
 
 def _inputs(N, C_in, C_out, T, dt, seed):
@@ -74,7 +74,7 @@ def run_backward_weight(eq, N, C_in, C_out, T, dt, d):
 
 # --- adjoint spectrum -----------------------------------------------------------------
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 11, 16])
 def test_w_hat_adjoint_is_the_spectrum_of_the_adjoint_weight(eq, N, dt):
     C_in, C_out = 37, 21  # ragged 32x32 transpose tiles on both axes
@@ -83,9 +83,11 @@ def test_w_hat_adjoint_is_the_spectrum_of_the_adjoint_weight(eq, N, dt):
     # w'[i][o][m] = w[o][i][(-m) mod N]: the weight of the input gradient layer
     w_adj = np.roll(d["w64"][..., ::-1], 1, axis=-1).transpose(1, 0, 2)
     ref = oracle.cn_weight_dft(w_adj)
-    bits = 24 if dt == F32 else 8
+    bits = {F32: 24, BF16: 8, F16: 11}[dt]
     _, e = np.frexp(ref)
     half_ulp = np.ldexp(0.5, e - bits)
+    if dt == F16:  # fp16 subnormals below 2^-14
+        half_ulp = np.maximum(half_ulp, 2.0 ** -25)
     noise = 1e-13 * np.abs(d["w64"]).max()
     assert np.all(np.abs(adj - ref) <= half_ulp * (1 + 1e-9) + noise)
 
@@ -95,7 +97,7 @@ def test_w_hat_adjoint_is_the_spectrum_of_the_adjoint_weight(eq, N, dt):
 SHAPES = [(5, 7, 37), (32, 48, 150), (8, 24, 64), (96, 40, 97), (3, 130, 29)]
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 12, 16])
 def test_backward_data_sweep(eq, N, dt):
     for C_in, C_out, T in SHAPES:

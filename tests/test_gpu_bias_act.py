@@ -16,7 +16,7 @@ from gpu_util import Guarded, assert_close, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
-F32, BF16 = synthetic.F32, synthetic.BF16
+F32, BF16, F16 = synthetic.F32, synthetic.BF16, synthetic.F16
 TILES = range(-1, 16)
 # (C_in, C_out, T): ragged C_out blocks and token tail; C_in % 4 == 0 for the split
 # kernel; 7 -> 5 takes the generic path (rows not a multiple of 16 bytes)
@@ -34,7 +34,7 @@ def eq():
 
 
 def _eqdt(eq, dt):
-    return eq.EQL_F32 if dt == F32 else eq.EQL_BF16
+    return {F32: eq.EQL_F32, BF16: eq.EQL_BF16, F16: eq.EQL_F16}[dt]
 
 
 class Layer:
@@ -68,7 +68,7 @@ class Layer:
 MODES = [(True, 1), (False, 1), (True, 0)]  # (bias?, act)
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 10, 12, 16])
 def test_bias_act_every_tile(eq, N, dt):
     for C_in, C_out, T in SHAPES:

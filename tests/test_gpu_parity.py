@@ -16,7 +16,7 @@ from gpu_util import Guarded, assert_close, rel_l2, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
-F32, BF16 = synthetic.F32, synthetic.BF16
+F32, BF16, F16 = synthetic.F32, synthetic.BF16, synthetic.F16
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +30,7 @@ def eq():
 
 
 def _eqdt(eq, dt):
-    return eq.EQL_F32 if dt == F32 else eq.EQL_BF16
+    return {F32: eq.EQL_F32, BF16: eq.EQL_BF16, F16: eq.EQL_F16}[dt]
 
 
 def run_cn(eq, N, C_in, C_out, T, dt, seed=0, tile=-1, inputs=None):
@@ -53,7 +53,7 @@ def run_cn(eq, N, C_in, C_out, T, dt, seed=0, tile=-1, inputs=None):
 
 # --- weight spectrum ---------------------------------------------------------------
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N", range(1, 17))
 def test_weight_fft_matches_oracle(eq, N, dt):
     import torch
@@ -70,12 +70,14 @@ def test_weight_fft_matches_oracle(eq, N, dt):
     # value is a correctly rounded neighbour of the exact DFT, which the oracle
     # gives up to fp64 noise (libm's cos(pi/2) is 6e-17, not 0, so exact ties
     # of sums of fp32 values may fall either way in the oracle).
-    bits = 24 if dt == F32 else 8
+    bits = {F32: 24, BF16: 8, F16: 11}[dt]
     _, e = np.frexp(ref)
     half_ulp = np.ldexp(0.5, e - bits)
+    if dt == F16:  # below 2^-14 fp16 is subnormal: spacing 2^-24
+        half_ulp = np.maximum(half_ulp, 2.0 ** -25)
     noise = 1e-13 * np.abs(d["w64"]).max()
     assert np.all(np.abs(got - ref) <= half_ulp * (1 + 1e-9) + noise)
-    assert rel_l2(got, ref) <= (1e-6 if dt == F32 else 4e-3)
+    assert rel_l2(got, ref) <= {F32: 1e-6, BF16: 4e-3, F16: 5e-4}[dt]
 
 
 # --- fused forward: sweeps over group order, shapes, tails and tile configurations ----
@@ -83,7 +85,7 @@ def test_weight_fft_matches_oracle(eq, N, dt):
 SHAPES = [(1, 1, 1), (3, 5, 17), (33, 17, 65), (40, 72, 130)]
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N", range(1, 17))
 def test_forward_sweep(eq, N, dt):
     for (C_in, C_out, T) in SHAPES:
@@ -94,7 +96,7 @@ def test_forward_sweep(eq, N, dt):
             assert_close(y, ref, dt, f"N={N} {dt} C_in={C_in} C_out={C_out} T={T} tile={tile}")
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N,C_in,C_out,T", [
     (8, 96, 96, 1000), (7, 160, 160, 777), (8, 96, 384, 300), (8, 384, 96, 300),
     (4, 8, 8, 64), (8, 32, 32, 4096), (5, 64, 64, 129), (16, 48, 80, 97), (12, 20, 36, 200),
@@ -136,7 +138,20 @@ def test_workload_full_size(eq, name):
 
 # --- invariants on the GPU --------------------------------------------------------------
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("name", ["c2", "c3b", "c4"])
+def test_fp16_workload_full_size(eq, name):
+    """The benchmark layers with fp16 I/O at full size, checked on sampled tokens."""
+    from dataclasses import replace
+    wl = replace(synthetic.WORKLOADS[name], dtype=F16)
+    d = synthetic.cn_inputs(wl.N, wl.C_in, wl.C_out, wl.T, F16, seed=0)
+    y, _ = run_cn(eq, wl.N, wl.C_in, wl.C_out, wl.T, F16, inputs=d)
+    rows = _sample_rows(wl.T)
+    ref = oracle.cn_dense(d["x64"][rows], d["w64"])
+    r, m = assert_close(y[rows], ref, F16, f"{name} fp16")
+    print(f"{name} fp16: rel-L2 {r:.3e} max/rms {m:.3e} over {len(rows)} tokens")
+
+
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N", [3, 4, 7, 8])
 def test_equivariance_on_gpu(eq, N, dt):
     C_in, C_out, T = 24, 40, 70
@@ -227,7 +242,7 @@ def test_d8_workload_full_size(eq):
 
 # --- expanded-dense comparator ------------------------------------------------------------
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N,C_in,C_out,T", [(4, 8, 8, 64), (7, 20, 12, 33), (8, 32, 48, 300)])
 def test_dense_comparator(eq, N, C_in, C_out, T, dt):
     import torch
