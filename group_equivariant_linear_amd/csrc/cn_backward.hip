@@ -339,37 +339,225 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
         }
 }
 
-// --- 3. reduction and inverse transform ------------------------------------------------
-// Block: 32 consecutive (o, i) elements x N planes, one thread each.  Thread
-// (p, e) sums the partials of plane p in split order (loads issued eight at a
-// time, added in order); then one thread per element runs the inverse real DFT
-// of its packed spectrum and writes dw[o][i][0 .. N-1].
+// --- small layers: transforms and products in one launch ---------------------------------
+// For C_in, C_out <= 32 the plane round trip through HBM and the launches around
+// it dominate, so a workgroup (4 waves) does both steps for its token chunks
+// [c_begin, c_end) of 16 tokens.  Per chunk, 256 threads load the (token,
+// channel) records of x and dy (zeros past T and past the channel counts, padded
+// to 32), transform them in fp32 and leave the N planes in LDS ([plane][token]
+// [channel], a pitch of 48 floats so that the two token rows of a 16-lane half
+// sit in different banks); the next chunk's records load while wave w runs the
+// products of the bins it owns, accumulating the 32 x 32 (o, i) tile of each of
+// its planes.  Bins go to waves greedily by cost (a complex bin is four real
+// products, a real bin one), so no plane is shared between waves and nothing is
+// summed across them.  The planes stay in fp32 for both I/O types.  The partial
+// spectrum of the range goes to part[split][p][o][i] for the reduction.
 template <int N>
-__global__ __launch_bounds__(32 * N) void bw_reduce_kernel(const float* __restrict__ part, float* __restrict__ dw,
-                                                           int splits, int64_t plane) {
-    __shared__ float red[32][N + 1];
-    const int el = (int)threadIdx.x & 31, p = (int)threadIdx.x >> 5;
+constexpr int bw_small_wave(int bin) {
+    int load[4] = {0, 0, 0, 0};
+    int owner = 0;
+    for (int pass = 0; pass < 2; ++pass)  // complex bins first, then the real ones
+        for (int k = 0; k <= N / 2; ++k) {
+            const bool cplx = k > 0 && 2 * k != N;
+            if ((pass == 0) != cplx) continue;
+            int w = 0;
+            for (int j = 1; j < 4; ++j)
+                if (load[j] < load[w]) w = j;
+            load[w] += cplx ? 4 : 1;
+            if (k == bin) owner = w;
+        }
+    return owner;
+}
+
+template <int N, typename IO>
+struct BwSmallCfg {
+    static constexpr int TT = 16, CH = 32, PITCH = 48;
+    static constexpr int PLANE = TT * PITCH;            // floats of one plane in LDS
+    static constexpr int RECS = 2 * TT * CH / 256;      // records per thread per chunk (x and dy)
+};
+
+template <int N, typename IO>
+__global__ __launch_bounds__(256) void bw_small_kernel(const IO* __restrict__ x, const IO* __restrict__ dy,
+                                                       float* __restrict__ part, int64_t T, int C_in, int C_out,
+                                                       int chunks_per_split, int nchunks) {
+    using C = BwSmallCfg<N, IO>;
+    __shared__ __attribute__((aligned(16))) float xs[N * C::PLANE];
+    __shared__ __attribute__((aligned(16))) float ds[N * C::PLANE];
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int split = (int)blockIdx.x;
+    const int c_begin = split * chunks_per_split;
+    const int c_end = c_begin + chunks_per_split < nchunks ? c_begin + chunks_per_split : nchunks;
+
+    // a record is whole 16-byte pieces when N * sizeof(IO) is a multiple of 16
+    // (records then start 16-byte aligned: the base pointers are)
+    constexpr int RB = N * (int)sizeof(IO);
+    constexpr int VP = RB % 16 == 0 ? RB / 16 : 0;
+    float rec[C::RECS][N];
+    auto load = [&](int c) {
+#pragma unroll
+        for (int j = 0; j < C::RECS; ++j) {
+            const int r = tid + 256 * j, rr = r % (C::TT * C::CH);
+            const bool is_dy = r >= C::TT * C::CH;
+            const int t = rr / C::CH, ch = rr % C::CH;
+            const int64_t tok = (int64_t)c * C::TT + t;
+            const int Cn = is_dy ? C_out : C_in;
+            const IO* src = (is_dy ? dy : x) + (tok * Cn + ch) * N;
+            const bool ok = tok < T && ch < Cn;
+            if constexpr (VP > 0) {
+                uint32_t w[4 * VP];
+#pragma unroll
+                for (int v = 0; v < VP; ++v) {
+                    const u32x4 q = ok ? reinterpret_cast<const u32x4*>(src)[v] : u32x4{0u, 0u, 0u, 0u};
+                    w[4 * v] = q[0];
+                    w[4 * v + 1] = q[1];
+                    w[4 * v + 2] = q[2];
+                    w[4 * v + 3] = q[3];
+                }
+#pragma unroll
+                for (int h = 0; h < N; ++h) {
+                    if constexpr (sizeof(IO) == 4) rec[j][h] = __uint_as_float(w[h]);
+                    else rec[j][h] = (h & 1) ? Half<IO>::hi(w[h >> 1]) : Half<IO>::lo(w[h >> 1]);
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < N; ++h) rec[j][h] = ok ? (float)src[h] : 0.0f;
+            }
+        }
+    };
+
+    // accumulators of this wave's planes: bin k -> planes (2k-1, 2k) or one real plane
+    f32x4 acc[N][2][2];
+#pragma unroll
+    for (int p = 0; p < N; ++p)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc[p][a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (c_begin < c_end) load(c_begin);
+    for (int c = c_begin; c < c_end; ++c) {
+#pragma unroll
+        for (int j = 0; j < C::RECS; ++j) {
+            const int r = tid + 256 * j, rr = r % (C::TT * C::CH);
+            float* dstp = (r >= C::TT * C::CH ? ds : xs) + (rr / C::CH) * C::PITCH + rr % C::CH;
+            float P[N];
+            rdft_forward<N>(rec[j], P);
+#pragma unroll
+            for (int p = 0; p < N; ++p) dstp[p * C::PLANE] = P[p];
+        }
+        __syncthreads();
+        if (c + 1 < c_end) load(c + 1);  // in flight during the products
+        const int row = lane >> 4, col = lane & 15;
+        static_for<0, N / 2 + 1>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            constexpr bool cplx = k > 0 && 2 * k != N;
+            constexpr int pr = k == 0 ? 0 : (cplx ? 2 * k - 1 : N - 1);
+            constexpr int pi = cplx ? 2 * k : pr;
+            if (wave != bw_small_wave<N>(k)) return;
+#pragma unroll
+            for (int ks = 0; ks < C::TT / 4; ++ks) {
+                const int off = (4 * ks + row) * C::PITCH + col;
+                float a[2], b[2], cc[2], d[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    a[h] = ds[pr * C::PLANE + off + 16 * h];
+                    cc[h] = xs[pr * C::PLANE + off + 16 * h];
+                    if constexpr (cplx) {
+                        b[h] = ds[pi * C::PLANE + off + 16 * h];
+                        d[h] = xs[pi * C::PLANE + off + 16 * h];
+                    }
+                }
+#pragma unroll
+                for (int to = 0; to < 2; ++to)
+#pragma unroll
+                    for (int ti = 0; ti < 2; ++ti) {
+                        // Re C += a c + b d, Im C += b c - a d (DY = a + ib, X = c + id)
+                        acc[pr][to][ti] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[to], cc[ti], acc[pr][to][ti], 0, 0, 0);
+                        if constexpr (cplx) {
+                            acc[pr][to][ti] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[to], d[ti], acc[pr][to][ti], 0, 0, 0);
+                            acc[pi][to][ti] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[to], cc[ti], acc[pi][to][ti], 0, 0, 0);
+                            acc[pi][to][ti] = __builtin_amdgcn_mfma_f32_16x16x4f32(-a[to], d[ti], acc[pi][to][ti], 0, 0, 0);
+                        }
+                    }
+            }
+        });
+        __syncthreads();  // the next chunk's planes overwrite these
+    }
+
+    const int64_t plane = (int64_t)C_out * C_in;
+    float* dst = part + (int64_t)split * N * plane;
+    static_for<0, N / 2 + 1>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        constexpr bool cplx = k > 0 && 2 * k != N;
+        constexpr int pr = k == 0 ? 0 : (cplx ? 2 * k - 1 : N - 1);
+        if (wave != bw_small_wave<N>(k)) return;
+#pragma unroll
+        for (int h = 0; h < (cplx ? 2 : 1); ++h) {
+            const int p = pr + h;
+#pragma unroll
+            for (int to = 0; to < 2; ++to)
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti) {
+                    const int i = 16 * ti + (lane & 15);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int o = 16 * to + 4 * (lane >> 4) + rr;
+                        if (o < C_out && i < C_in) dst[p * plane + (int64_t)o * C_in + i] = acc[p][to][ti][rr];
+                    }
+                }
+        }
+    });
+}
+
+// --- 3. reduction and inverse transform ------------------------------------------------
+// Block: 32 consecutive (o, i) elements x N planes x R lanes (R = 1024 / 32N, at
+// most 8).  Lane r of (p, e) sums the r-th contiguous sub-range of the splits in
+// order, sixteen loads in flight; the R sub-sums are added in lane order.  The
+// order is fixed, so the result is deterministic.  Then one thread per element
+// runs the inverse real DFT of its packed spectrum and writes dw[o][i][0 .. N-1].
+template <int N>
+struct BwReduceCfg {
+    static constexpr int R0 = 1024 / (32 * N);
+    static constexpr int R = R0 > 8 ? 8 : R0;
+    static constexpr int kThreads = 32 * N * R;
+};
+
+template <int N>
+__global__ __launch_bounds__(BwReduceCfg<N>::kThreads) void bw_reduce_kernel(const float* __restrict__ part,
+                                                                             float* __restrict__ dw, int splits,
+                                                                             int64_t plane) {
+    constexpr int R = BwReduceCfg<N>::R;
+    __shared__ float red[R][32][N + 1];
+    const int el = (int)threadIdx.x & 31, p = ((int)threadIdx.x >> 5) % N, r = (int)threadIdx.x / (32 * N);
     const int64_t e = (int64_t)blockIdx.x * 32 + el;
+    const int len = (splits + R - 1) / R;
+    const int s0 = r * len, s1 = s0 + len < splits ? s0 + len : splits;
     float v = 0.0f;
     if (e < plane) {
         const float* src = part + (int64_t)p * plane + e;
         const int64_t step = (int64_t)N * plane;
-        int s = 0;
-        for (; s + 8 <= splits; s += 8) {
-            float t[8];
+        int s = s0;
+        for (; s + 16 <= s1; s += 16) {
+            float t[16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) t[j] = src[(int64_t)(s + j) * step];
+            for (int j = 0; j < 16; ++j) t[j] = src[(int64_t)(s + j) * step];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v += t[j];
+            for (int j = 0; j < 16; ++j) v += t[j];
         }
-        for (; s < splits; ++s) v += src[(int64_t)s * step];
+        for (; s < s1; ++s) v += src[(int64_t)s * step];
     }
-    red[el][p] = v;
+    red[r][el][p] = v;
     __syncthreads();
-    if (p == 0 && e < plane) {
+    if (r == 0 && p == 0 && e < plane) {
         float P[N], y[N];
 #pragma unroll
-        for (int q = 0; q < N; ++q) P[q] = red[el][q];
+        for (int q = 0; q < N; ++q) {
+            float sum = red[0][el][q];
+#pragma unroll
+            for (int rr = 1; rr < R; ++rr) sum += red[rr][el][q];
+            P[q] = sum;
+        }
         rdft_inverse<N>(P, y);
 #pragma unroll
         for (int m = 0; m < N; ++m) dw[e * N + m] = y[m];
@@ -381,6 +569,7 @@ __global__ __launch_bounds__(32 * N) void bw_reduce_kernel(const float* __restri
 struct BwShape {
     int64_t Tp;
     int n_o, n_i, tiles, nchunks, splits, chunks_per_split;
+    bool fused;  // small layers: transforms and products in one launch, no planes
     size_t xp_bytes, dyp_bytes, part_bytes, total;
 };
 
@@ -393,6 +582,23 @@ int bw_wg(int C_in, int C_out) { return (C_in <= 32 && C_out <= 32) ? 1 : 2; }
 
 BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     BwShape s{};
+    if (C_in <= 32 && C_out <= 32) {
+        // one fused launch: token chunks of 16 over at most 256 workgroups, two
+        // chunks or more each where the tokens allow (the second chunk's loads
+        // then overlap the first one's products; c2: 13.0 us at 128 ranges, 15.0
+        // at 256 or 64)
+        s.fused = true;
+        s.Tp = (T + 15) / 16 * 16;
+        s.tiles = 1;
+        s.nchunks = (int)(s.Tp / 16);
+        int sp = s.nchunks / 2;
+        sp = sp < 1 ? 1 : (sp > 256 ? 256 : sp);
+        s.chunks_per_split = (s.nchunks + sp - 1) / sp;
+        s.splits = (s.nchunks + s.chunks_per_split - 1) / s.chunks_per_split;
+        s.part_bytes = round256((size_t)s.splits * N * C_out * C_in * 4);
+        s.total = s.part_bytes;
+        return s;
+    }
     const int S = bf16 ? 2 : 4, KC = 64 / S;
     const int tm = 32 * bw_wg(C_in, C_out);
     s.Tp = (T + 63) / 64 * 64;
@@ -420,6 +626,15 @@ template <int N, typename IO, int WG>
 hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t T, int C_in, int C_out,
                                char* ws, const BwShape& s, hipStream_t stream) {
     using Cfg = BwCfg<N, IO, WG>;
+    const int64_t plane = (int64_t)C_out * C_in;
+    if (s.fused) {
+        float* part = reinterpret_cast<float*>(ws);
+        hipLaunchKernelGGL((bw_small_kernel<N, IO>), dim3((uint32_t)s.splits), dim3(256), 0, stream, (const IO*)x,
+                           (const IO*)dy, part, T, C_in, C_out, s.chunks_per_split, s.nchunks);
+        hipLaunchKernelGGL((bw_reduce_kernel<N>), dim3((uint32_t)((plane + 31) / 32)),
+                           dim3(BwReduceCfg<N>::kThreads), 0, stream, (const float*)part, dw, s.splits, plane);
+        return hipGetLastError();
+    }
     IO* xp = reinterpret_cast<IO*>(ws);
     IO* dyp = reinterpret_cast<IO*>(ws + s.xp_bytes);
     float* part = reinterpret_cast<float*>(ws + s.xp_bytes + s.dyp_bytes);
@@ -432,9 +647,8 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
     hipLaunchKernelGGL((bw_gemm_kernel<Cfg>), dim3((uint32_t)wgs), dim3(Cfg::kThreads), 0, stream,
                        (const IO*)dyp, (const IO*)xp, part, C_out, C_in, s.Tp, s.n_i, s.tiles,
                        s.chunks_per_split, s.nchunks);
-    const int64_t plane = (int64_t)C_out * C_in;
-    hipLaunchKernelGGL((bw_reduce_kernel<N>), dim3((uint32_t)((plane + 31) / 32)), dim3(32 * N), 0, stream,
-                       (const float*)part, dw, s.splits, plane);
+    hipLaunchKernelGGL((bw_reduce_kernel<N>), dim3((uint32_t)((plane + 31) / 32)),
+                       dim3(BwReduceCfg<N>::kThreads), 0, stream, (const float*)part, dw, s.splits, plane);
     return hipGetLastError();
 }
 

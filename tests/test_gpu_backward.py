@@ -142,6 +142,20 @@ def test_backward_weight_is_deterministic(eq, dt):
 
 
 @pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("N,C_in,C_out", [(5, 24, 32), (8, 32, 32), (16, 32, 9)])
+def test_backward_weight_small_layers_many_chunks(eq, N, C_in, C_out, dt):
+    """Layers with at most 32 channels each way take the one-launch path; at
+    T = 20000 every workgroup runs several 16-token chunks (loads of the next
+    chunk in flight during the products).  Also deterministic."""
+    T = 20000
+    d = _inputs(N, C_in, C_out, T, dt, seed=N + C_out)
+    dw = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
+    ref = oracle.cn_backward_weight(d["x64"], d["dy64"])
+    assert_close(dw, ref, dt, f"dw N={N} {dt} {C_in}->{C_out} T={T}")
+    assert np.array_equal(dw, run_backward_weight(eq, N, C_in, C_out, T, dt, d))
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
 def test_gradients_satisfy_the_adjoint_identity(eq, dt):
     """<dy, y(x)> = <dx, x> = <dw, w> with all three computed on the GPU."""
     import torch
