@@ -80,6 +80,18 @@ def _load():
         lib.eqref_d8_to_fourier.restype = None
         lib.eqref_d8_bias_act.argtypes = [i64, i, d, i, d]
         lib.eqref_d8_bias_act.restype = None
+        lib.eqref_dn_expand.argtypes = [i, i, i, d, d]
+        lib.eqref_dn_expand.restype = None
+        lib.eqref_dn_dense.argtypes = [i, i, i, i64, d, d, d]
+        lib.eqref_dn_dense.restype = i
+        lib.eqref_dn_fourier_matrix.argtypes = [i, d]
+        lib.eqref_dn_fourier_matrix.restype = None
+        lib.eqref_dn_to_regular.argtypes = [i, i64, i, d, d]
+        lib.eqref_dn_to_regular.restype = None
+        lib.eqref_dn_to_fourier.argtypes = [i, i64, i, d, d]
+        lib.eqref_dn_to_fourier.restype = None
+        lib.eqref_dn_bias_act.argtypes = [i, i64, i, d, i, d]
+        lib.eqref_dn_bias_act.restype = None
         lib.eqref_cn_weight_dft.argtypes = [i, i, i, d, d]
         lib.eqref_cn_weight_dft.restype = None
         lib.eqref_d8_expand.argtypes = [i, i, d, d]
@@ -255,6 +267,78 @@ def d8_bias_act(y, bias=None, act=0):
 def d8_dense_bias_act(x, wb, C_out, bias=None, act=0):
     """The D8 layer followed by its fused neighbours in the regular domain."""
     return d8_bias_act(d8_dense(x, wb, C_out), bias, act)
+
+
+def dn_one_dim(n: int) -> int:
+    return 4 if n % 2 == 0 else 2
+
+
+def dn_two_dim(n: int) -> int:
+    return n // 2 - 1 if n % 2 == 0 else (n - 1) // 2
+
+
+def dn_params(n: int, C_in: int, C_out: int) -> int:
+    """Parameters of the D_n layer: one square block per 1-D irrep, one 2m x 2m per E_k."""
+    mi, mo = C_in // (2 * n), C_out // (2 * n)
+    return dn_one_dim(n) * mi * mo + dn_two_dim(n) * (2 * mi) * (2 * mo)
+
+
+def dn_expand(n, wb, C_in, C_out):
+    wb = _f64(wb)
+    assert C_in % (2 * n) == 0 and C_out % (2 * n) == 0 and wb.size == dn_params(n, C_in, C_out)
+    W = np.empty((C_out, C_in), dtype=np.float64)
+    _load().eqref_dn_expand(n, C_in, C_out, _p(wb), _p(W))
+    return W
+
+
+def dn_dense(n, x, wb, C_out):
+    """D_n Fourier-domain layer on x[T][C_in] (the D8 layout generalised)."""
+    x, wb = _f64(x), _f64(wb)
+    T, C_in = x.shape
+    assert wb.size == dn_params(n, C_in, C_out)
+    y = np.empty((T, C_out), dtype=np.float64)
+    if _load().eqref_dn_dense(n, C_in, C_out, T, _p(x), _p(wb), _p(y)) != 0:
+        raise MemoryError("oracle: cannot allocate the dense matrix")
+    return y
+
+
+def dn_fourier_matrix(n):
+    F = np.empty((2 * n, 2 * n), dtype=np.float64)
+    _load().eqref_dn_fourier_matrix(n, _p(F))
+    return F
+
+
+def dn_to_regular(n, v):
+    v = _f64(v)
+    T, C = v.shape
+    assert C % (2 * n) == 0
+    f = np.empty((T, C // (2 * n), 2 * n), dtype=np.float64)
+    _load().eqref_dn_to_regular(n, T, C // (2 * n), _p(v), _p(f))
+    return f
+
+
+def dn_to_fourier(n, f):
+    f = _f64(f)
+    T, m, g = f.shape
+    assert g == 2 * n
+    v = np.empty((T, g * m), dtype=np.float64)
+    _load().eqref_dn_to_fourier(n, T, m, _p(f), _p(v))
+    return v
+
+
+def dn_bias_act(n, y, bias=None, act=0):
+    y = np.array(y, dtype=np.float64, copy=True, order="C")
+    T, C = y.shape
+    assert C % (2 * n) == 0
+    b = None if bias is None else _f64(bias)
+    if b is not None:
+        assert b.shape == (C // (2 * n),)
+    _load().eqref_dn_bias_act(n, T, C // (2 * n), None if b is None else _p(b), int(act), _p(y))
+    return y
+
+
+def dn_dense_bias_act(n, x, wb, C_out, bias=None, act=0):
+    return dn_bias_act(n, dn_dense(n, x, wb, C_out), bias, act)
 
 
 def d8_expand(wb, C_in, C_out):

@@ -64,6 +64,21 @@
  *    gathering A1..B2 at j and E copies 2j, 2j+1 (eqref_d8_to_regular,
  *    eqref_d8_to_fourier, eqref_d8_bias_act).  A bias that keeps the block
  *    equivariant is constant over the group elements: one value per channel j.
+ *
+ *  - Dihedral groups beyond D8.  "Flash EQ-Linear" (Dutch summary, closing
+ *    paragraph) names other shapes and motions as the extension of the 90-degree
+ *    case; the reflection groups of the regular n-gon are the direct one.
+ *    D_n = <r, s | r^n = s^2 = 1, s r s = r^-1> has order 2n and real irreps
+ *    A1 (r, s) -> (1, 1), A2 (1, -1), for even n also B1 (-1, 1), B2 (-1, -1),
+ *    and E_k (k = 1 .. n/2 - 1 for even n, .. (n-1)/2 for odd n): r -> rotation
+ *    by 2 pi k / n, s -> diag(1, -1).  The layer keeps the D8 layout: per token,
+ *    the 1-D irreps' slabs of m = C/2n channels, then for each E_k its
+ *    coordinate-0 and coordinate-1 slabs of 2m copies; a square block per 1-D
+ *    irrep and one 2m x 2m block per E_k, shared by its two coordinates
+ *    (eqref_dn_expand).  The Fourier matrix, transforms and round trip follow
+ *    the D8 ones with rows sqrt(d / 2n) times the irreps' entries
+ *    (eqref_dn_fourier_matrix, eqref_dn_to_regular, eqref_dn_to_fourier,
+ *    eqref_dn_bias_act).  For n = 4 every one of them is the D8 routine.
  */
 #include <math.h>
 #include <stdint.h>
@@ -355,6 +370,157 @@ void eqref_d8_bias_act(int64_t T, int m, const double* bias, int act, double* y)
                 y[t * 8 * m + d8_slot(m, j, p)] = acc;
             }
         }
+}
+
+/* ---- dihedral groups D_n (order 2n) ---- */
+
+/* Number of 1-D irreps (2 or 4) and of 2-D irreps of D_n. */
+static int dn_one_dim(int n) { return n % 2 == 0 ? 4 : 2; }
+static int dn_two_dim(int n) { return n % 2 == 0 ? n / 2 - 1 : (n - 1) / 2; }
+
+/* Block-diagonal matrix [C_out][C_in] of the D_n layer from the packed blocks
+ * wb = [W of each 1-D irrep (C_out/2n x C_in/2n) | W of each E_k (C_out/n x C_in/n)]. */
+void eqref_dn_expand(int n, int C_in, int C_out, const double* wb, double* W) {
+    const int mi = C_in / (2 * n), mo = C_out / (2 * n), n1 = dn_one_dim(n), n2 = dn_two_dim(n);
+    memset(W, 0, sizeof(double) * (size_t)C_in * (size_t)C_out);
+    const double* blk = wb;
+    for (int b = 0; b < n1; ++b) {
+        for (int r = 0; r < mo; ++r)
+            for (int c = 0; c < mi; ++c)
+                W[(int64_t)(b * mo + r) * C_in + b * mi + c] = blk[(int64_t)r * mi + c];
+        blk += (int64_t)mo * mi;
+    }
+    for (int k = 0; k < n2; ++k) {
+        for (int e = 0; e < 2; ++e) /* coordinate e of E_{k+1} */
+            for (int r = 0; r < 2 * mo; ++r)
+                for (int c = 0; c < 2 * mi; ++c)
+                    W[(int64_t)(n1 * mo + 4 * k * mo + 2 * e * mo + r) * C_in + n1 * mi + 4 * k * mi + 2 * e * mi + c] =
+                        blk[(int64_t)r * (2 * mi) + c];
+        blk += (int64_t)(2 * mo) * (2 * mi);
+    }
+}
+
+int eqref_dn_dense(int n, int C_in, int C_out, int64_t T, const double* x, const double* wb, double* y) {
+    double* W = (double*)malloc(sizeof(double) * (size_t)C_in * (size_t)C_out);
+    if (!W) return -1;
+    eqref_dn_expand(n, C_in, C_out, wb, W);
+    eqref_apply_dense(T, C_out, C_in, W, x, y);
+    free(W);
+    return 0;
+}
+
+/* Orthonormal Fourier matrix F[p][q] of D_n, 2n x 2n, element q = a + n b being
+ * r^a s^b.  Rows: the 1-D irreps' values times sqrt(1/2n); then for each E_k
+ * (k = 1, 2, ...) entry (kk, c) of E_k(q) times sqrt(2/2n), row index
+ * n1 + 4(k-1) + 2 kk + c. */
+void eqref_dn_fourier_matrix(int n, double* F) {
+    const int n1 = dn_one_dim(n), n2 = dn_two_dim(n), G = 2 * n;
+    const double chi_r[4] = {1.0, 1.0, -1.0, -1.0}, chi_s[4] = {1.0, -1.0, 1.0, -1.0};
+    const double two_pi = 2.0 * acos(-1.0);
+    for (int q = 0; q < G; ++q) {
+        const int a = q % n, b = q / n;
+        for (int p = 0; p < n1; ++p) {
+            double v = 1.0;
+            for (int i = 0; i < a; ++i) v *= chi_r[p];
+            if (b) v *= chi_s[p];
+            F[p * G + q] = sqrt(1.0 / G) * v;
+        }
+        for (int k = 1; k <= n2; ++k) {
+            /* E_k(r)^a E_k(s)^b, E_k(r) = rotation by 2 pi k / n */
+            const double c1 = cos(two_pi * k / n), s1 = sin(two_pi * k / n);
+            double M[2][2] = {{1.0, 0.0}, {0.0, 1.0}};
+            for (int i = 0; i < a; ++i) {
+                double T2[2][2];
+                for (int kk = 0; kk < 2; ++kk) {
+                    T2[0][kk] = c1 * M[0][kk] - s1 * M[1][kk];
+                    T2[1][kk] = s1 * M[0][kk] + c1 * M[1][kk];
+                }
+                memcpy(M, T2, sizeof M);
+            }
+            if (b) { /* right factor diag(1, -1): negate column 1 */
+                M[0][1] = -M[0][1];
+                M[1][1] = -M[1][1];
+            }
+            for (int kk = 0; kk < 2; ++kk)
+                for (int c = 0; c < 2; ++c) F[(n1 + 4 * (k - 1) + 2 * kk + c) * G + q] = sqrt(2.0 / G) * M[kk][c];
+        }
+    }
+}
+
+/* Fourier-layout column of coefficient p of regular channel j (of m), D_n layout. */
+static int64_t dn_slot(int n, int m, int j, int p) {
+    const int n1 = dn_one_dim(n);
+    if (p < n1) return (int64_t)p * m + j;
+    const int e = p - n1, k = e / 4, kk = (e % 4) / 2, c = e % 2;
+    return (int64_t)n1 * m + 4 * (int64_t)m * k + 2 * (int64_t)m * kk + 2 * j + c;
+}
+
+/* Fourier layout [T][2n m] -> regular layout [T][m][2n]: f = F^T v per channel. */
+void eqref_dn_to_regular(int n, int64_t T, int m, const double* v, double* f) {
+    const int G = 2 * n;
+    double* F = (double*)malloc(sizeof(double) * G * G);
+    if (!F) return;
+    eqref_dn_fourier_matrix(n, F);
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < m; ++j)
+            for (int q = 0; q < G; ++q) {
+                double acc = 0.0;
+                for (int p = 0; p < G; ++p) acc += F[p * G + q] * v[t * G * m + dn_slot(n, m, j, p)];
+                f[(t * m + j) * G + q] = acc;
+            }
+    free(F);
+}
+
+/* Regular layout [T][m][2n] -> Fourier layout [T][2n m]: v = F f per channel. */
+void eqref_dn_to_fourier(int n, int64_t T, int m, const double* f, double* v) {
+    const int G = 2 * n;
+    double* F = (double*)malloc(sizeof(double) * G * G);
+    if (!F) return;
+    eqref_dn_fourier_matrix(n, F);
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < m; ++j)
+            for (int p = 0; p < G; ++p) {
+                double acc = 0.0;
+                for (int q = 0; q < G; ++q) acc += F[p * G + q] * f[(t * m + j) * G + q];
+                v[t * G * m + dn_slot(n, m, j, p)] = acc;
+            }
+    free(F);
+}
+
+/* In place on D_n Fourier features y[T][2n m]: per token and regular channel j,
+ * f = F^T v_j, f <- act(f + bias[j]), v_j = F f (as eqref_d8_bias_act). */
+void eqref_dn_bias_act(int n, int64_t T, int m, const double* bias, int act, double* y) {
+    const int G = 2 * n;
+    double* F = (double*)malloc(sizeof(double) * G * G);
+    double* v = (double*)malloc(sizeof(double) * G);
+    double* f = (double*)malloc(sizeof(double) * G);
+    if (!F || !v || !f) {
+        free(F);
+        free(v);
+        free(f);
+        return;
+    }
+    eqref_dn_fourier_matrix(n, F);
+    const double rsqrt2 = 1.0 / sqrt(2.0);
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < m; ++j) {
+            for (int p = 0; p < G; ++p) v[p] = y[t * G * m + dn_slot(n, m, j, p)];
+            for (int q = 0; q < G; ++q) {
+                double acc = 0.0;
+                for (int p = 0; p < G; ++p) acc += F[p * G + q] * v[p];
+                if (bias) acc += bias[j];
+                if (act == 1) acc = 0.5 * acc * erfc(-acc * rsqrt2);
+                f[q] = acc;
+            }
+            for (int p = 0; p < G; ++p) {
+                double acc = 0.0;
+                for (int q = 0; q < G; ++q) acc += F[p * G + q] * f[q];
+                y[t * G * m + dn_slot(n, m, j, p)] = acc;
+            }
+        }
+    free(F);
+    free(v);
+    free(f);
 }
 
 int eqref_d8_dense(int C_in, int C_out, int64_t T, const double* x, const double* wb,

@@ -302,6 +302,128 @@ def pin_d8_bias_act(orc):
     assert rel(orc.d8_dense_bias_act(x @ sin_.T, wb, C_out, bb, 1), yb @ sout.T) < 1e-13
 
 
+def _dn_elements(n):
+    """D_n as the regular n-gon's symmetries, 2 x 2 matrices: element q = a + n b is
+    R^a S^b (R the turn by 2 pi / n, S the mirror y -> -y)."""
+    c, s_ = np.cos(2 * np.pi / n), np.sin(2 * np.pi / n)
+    R = np.array([[c, -s_], [s_, c]])
+    S = np.diag([1.0, -1.0])
+    return [np.linalg.matrix_power(R, q % n) @ (S if q // n else np.eye(2)) for q in range(2 * n)]
+
+
+def _dn_left_regular(n, g):
+    E = _dn_elements(n)
+    P = np.zeros((2 * n, 2 * n))
+    for q in range(2 * n):
+        gq = g @ E[q]
+        P[next(i for i in range(2 * n) if np.allclose(E[i], gq, atol=1e-12)), q] = 1.0
+    return P
+
+
+def dn_action(n, C):
+    """Generators r, s of D_n acting on Fourier features of width C laid out as the
+    layer's: m = C/2n channels per 1-D irrep (A1, A2, and B1, B2 for even n), then
+    per E_k (k = 1, 2, ...) a coordinate-0 and a coordinate-1 slab of 2m copies,
+    r turning each copy by 2 pi k / n and s = diag(1, -1)."""
+    m = C // (2 * n)
+    chars = [(1, 1), (1, -1)] + ([(-1, 1), (-1, -1)] if n % 2 == 0 else [])
+    n2 = n // 2 - 1 if n % 2 == 0 else (n - 1) // 2
+    r, s_ = np.zeros((C, C)), np.zeros((C, C))
+    for b, (rv, sv) in enumerate(chars):
+        for j in range(m):
+            r[b * m + j, b * m + j] = rv
+            s_[b * m + j, b * m + j] = sv
+    base = len(chars) * m
+    for k in range(1, n2 + 1):
+        c, sn = np.cos(2 * np.pi * k / n), np.sin(2 * np.pi * k / n)
+        e0 = base + 4 * m * (k - 1)
+        for cp in range(2 * m):
+            a, b = e0 + cp, e0 + 2 * m + cp
+            r[a, a], r[a, b], r[b, a], r[b, b] = c, -sn, sn, c
+            s_[a, a], s_[b, b] = 1.0, -1.0
+    return r, s_
+
+
+def _dn_slots(n, m, j):
+    """Fourier columns of regular channel j (the layout reading: 1-D irreps at j, E_k
+    copies 2j + c in its coordinate slabs)."""
+    n1 = 4 if n % 2 == 0 else 2
+    n2 = n // 2 - 1 if n % 2 == 0 else (n - 1) // 2
+    cols = [b * m + j for b in range(n1)]
+    for k in range(n2):
+        for kk in range(2):
+            for c in range(2):
+                cols.append(n1 * m + 4 * m * k + 2 * m * kk + 2 * j + c)
+    return cols
+
+
+def pin_dn_fourier(orc):
+    """Dihedral groups of the regular n-gon: the feature action is a representation
+    with the regular character; the Fourier matrix is orthonormal and intertwines
+    the left-regular action (group law of the symmetry matrices) with it; the
+    transforms invert each other and follow the layout; n = 4 is the D8 matrix."""
+    for n in (2, 3, 5, 6):
+        r, s_ = dn_action(n, 2 * n)
+        G = 2 * n
+        assert np.allclose(np.linalg.matrix_power(r, n), np.eye(G), atol=1e-12)
+        assert np.allclose(s_ @ s_, np.eye(G)) and np.allclose(s_ @ r @ s_, np.linalg.matrix_power(r, n - 1), atol=1e-12)
+        tr = [np.trace(np.linalg.matrix_power(r, a) @ (s_ if b else np.eye(G))) for b in (0, 1) for a in range(n)]
+        assert abs(tr[0] - G) < 1e-12 and max(abs(t) for t in tr[1:]) < 1e-12
+        F = orc.dn_fourier_matrix(n)
+        assert np.max(np.abs(F @ F.T - np.eye(G))) < 1e-14
+        E = _dn_elements(n)
+        for g, A in ((E[1], r), (E[n], s_)):
+            assert np.max(np.abs(F @ _dn_left_regular(n, g) - A @ F)) < 1e-14
+        m = 3
+        f = _rand(2, m, G)
+        v = orc.dn_to_fourier(n, f)
+        assert rel(orc.dn_to_regular(n, v), f) < 1e-14
+        assert rel(v[:, _dn_slots(n, m, 1)], f[:, 1] @ F.T) < 1e-14
+    assert np.max(np.abs(orc.dn_fourier_matrix(4) - orc.d8_fourier_matrix())) < 1e-15
+
+
+def pin_dn_layer(orc):
+    """The D_n layer: the equivariant maps of its features have dimension C^2/2n and
+    the oracle's expansion spans them; n = 4 is the D8 layer; the round trip is the
+    identity without bias or activation, puts a bias on A1 times sqrt(2n), and the
+    layer followed by the GELU round trip is equivariant."""
+    for n in (3, 6):
+        C = 2 * n * 2
+        r, s_ = dn_action(n, C)
+        dim = _commutant_dim([r, s_], [r, s_])
+        assert dim == C * C // (2 * n) == orc.dn_params(n, C, C)
+        basis = []
+        for idx in range(dim):
+            e = np.zeros(dim)
+            e[idx] = 1.0
+            W = orc.dn_expand(n, e, C, C)
+            assert np.allclose(r @ W, W @ r, atol=1e-12) and np.allclose(s_ @ W, W @ s_, atol=1e-12)
+            basis.append(W.ravel())
+        assert np.linalg.matrix_rank(np.array(basis)) == dim
+    C_in, C_out, T = 16, 24, 4
+    wb = _rand(orc.d8_params(C_in, C_out))
+    x = _rand(T, C_in)
+    assert np.array_equal(orc.dn_expand(4, wb, C_in, C_out), orc.d8_expand(wb, C_in, C_out))
+    y = _rand(T, 24)
+    b = _rand(3)
+    assert rel(orc.dn_bias_act(4, y, b, 1), orc.d8_bias_act(y, b, 1)) < 1e-14
+    for n in (3, 6):
+        C_in, C_out = 2 * n * 2, 2 * n * 3
+        wb, bb = _rand(orc.dn_params(n, C_in, C_out)), _rand(C_out // (2 * n))
+        x = _rand(T, C_in)
+        y = orc.dn_dense(n, x, wb, C_out)
+        assert rel(orc.dn_bias_act(n, y, None, 0), y) < 1e-14
+        d = orc.dn_bias_act(n, y, bb, 0) - y
+        expect = np.zeros_like(y)
+        expect[:, :C_out // (2 * n)] = np.sqrt(2.0 * n) * bb
+        assert np.max(np.abs(d - expect)) < 1e-13
+        rin, sin_ = dn_action(n, C_in)
+        rout, sout = dn_action(n, C_out)
+        yb = orc.dn_dense_bias_act(n, x, wb, C_out, bb, 1)
+        assert rel(orc.dn_dense_bias_act(n, x @ rin.T, wb, C_out, bb, 1), yb @ rout.T) < 1e-13
+        assert rel(orc.dn_dense_bias_act(n, x @ sin_.T, wb, C_out, bb, 1), yb @ sout.T) < 1e-13
+
+
 ALL_CN_PINS = [pin_rfft_route, pin_weight_dft, pin_closed_forms, pin_dense_matrix_structure, pin_bias_act,
                pin_backward_adjoint, pin_backward_closed_forms, pin_backward_equivariance]
 
@@ -364,6 +486,14 @@ def test_d8_fourier_transform():
 
 def test_d8_round_trip_bias_and_gelu():
     pin_d8_bias_act(oracle)
+
+
+def test_dihedral_fourier_transform():
+    pin_dn_fourier(oracle)
+
+
+def test_dihedral_layer_and_round_trip():
+    pin_dn_layer(oracle)
 
 
 def test_dense_matrix_structure():
@@ -569,14 +699,27 @@ MUTANTS = [
     ("bias along the group axis", "if (bias) v += bias[o];", "if (bias) v += bias[g % C_out];"),
     ("GELU without the 1/sqrt(2)", "v = 0.5 * v * erfc(-v * rsqrt2);", "v = 0.5 * v * erfc(-v);"),
     ("GELU with Phi of the wrong sign", "v = 0.5 * v * erfc(-v * rsqrt2);", "v = 0.5 * v * erfc(v * rsqrt2);"),
-    ("D8 transposed 1-D block", "blk[(int64_t)r * mi + c];", "blk[(int64_t)c * mi + r];"),
+    ("D8 transposed 1-D block", "blk[(int64_t)r * mi + c];\n        blk += (int64_t)mo * mi;\n    }\n    for (int e = 0;",
+     "blk[(int64_t)c * mi + r];\n        blk += (int64_t)mo * mi;\n    }\n    for (int e = 0;"),
+    ("D_n transposed 1-D block", "blk[(int64_t)r * mi + c];\n        blk += (int64_t)mo * mi;\n    }\n    for (int k = 0;",
+     "blk[(int64_t)c * mi + r];\n        blk += (int64_t)mo * mi;\n    }\n    for (int k = 0;"),
     ("D8 E weight on coordinate 0 only", "4 * mi + 2 * e * mi + c] =", "4 * mi + c] ="),
     ("D8 Fourier: E copies taken as rows", "return 4 * (int64_t)m + 2 * (int64_t)m * k + 2 * j + c;",
      "return 4 * (int64_t)m + 2 * (int64_t)m * c + 2 * j + k;"),
     ("D8 Fourier: E rows unnormalised", "n2 = sqrt(2.0 / 8.0);", "n2 = sqrt(1.0 / 8.0);"),
     ("D8 Fourier: quarter turn the other way", "Er[2][2] = {{0.0, -1.0}, {1.0, 0.0}}",
      "Er[2][2] = {{0.0, 1.0}, {-1.0, 0.0}}"),
-    ("D8 round trip: bias on one group element", "if (bias) acc += bias[j];", "if (bias && q == 0) acc += bias[j];"),
+    ("D8 round trip: bias on one group element", "acc += F[p * 8 + q] * v[p];\n                if (bias) acc += bias[j];",
+     "acc += F[p * 8 + q] * v[p];\n                if (bias && q == 0) acc += bias[j];"),
+    ("D_n round trip: bias on one group element", "acc += F[p * G + q] * v[p];\n                if (bias) acc += bias[j];",
+     "acc += F[p * G + q] * v[p];\n                if (bias && q == 0) acc += bias[j];"),
+    ("D_n: E_k turning at the next frequency", "const double c1 = cos(two_pi * k / n), s1 = sin(two_pi * k / n);",
+     "const double c1 = cos(two_pi * (k + 1) / n), s1 = sin(two_pi * (k + 1) / n);"),
+    ("D_n: E rows unnormalised", "F[(n1 + 4 * (k - 1) + 2 * kk + c) * G + q] = sqrt(2.0 / G) * M[kk][c];",
+     "F[(n1 + 4 * (k - 1) + 2 * kk + c) * G + q] = sqrt(1.0 / G) * M[kk][c];"),
+    ("D_n: E weight on coordinate 0 only", "n1 * mi + 4 * k * mi + 2 * e * mi + c] =", "n1 * mi + 4 * k * mi + c] ="),
+    ("D_n: mirror negates row 1", "M[0][1] = -M[0][1];\n                M[1][1] = -M[1][1];",
+     "M[1][0] = -M[1][0];\n                M[1][1] = -M[1][1];"),
 ]
 
 
@@ -604,7 +747,8 @@ def test_mutants_are_caught(tmp_path, golden_dir, name, old, new):
         caught = []
         checks = [lambda: pin_hand_examples(oracle, golden_dir),
                   lambda: pin_d8_blockdiag(oracle, golden_dir),
-                  lambda: pin_d8_fourier(oracle), lambda: pin_d8_bias_act(oracle)] + [
+                  lambda: pin_d8_fourier(oracle), lambda: pin_d8_bias_act(oracle),
+                  lambda: pin_dn_fourier(oracle), lambda: pin_dn_layer(oracle)] + [
             (lambda f=f: f(oracle)) for f in ALL_CN_PINS]
         for chk in checks:
             try:
@@ -661,6 +805,15 @@ def test_oracle_under_sanitizers(tmp_path):
         "lib.eqref_d8_to_fourier.argtypes = lib.eqref_d8_to_regular.argtypes; lib.eqref_d8_to_fourier(2, 2, p(fr), p(yd))\n"
         "b2 = np.ones(2); lib.eqref_d8_bias_act.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]\n"
         "lib.eqref_d8_bias_act(2, 2, p(b2), 1, p(yd))\n"
+        "wn = np.ones(12); xn = np.ones((2, 12)); yn = np.zeros((2, 12))  # D_6, width 12: 4 + 2 * 4 weights\n"
+        "lib.eqref_dn_dense.argtypes = [ctypes.c_int]*3 + [ctypes.c_int64] + [ctypes.c_void_p]*3\n"
+        "assert lib.eqref_dn_dense(6, 12, 12, 2, p(xn), p(wn), p(yn)) == 0\n"
+        "Fn = np.zeros(144); lib.eqref_dn_fourier_matrix.argtypes = [ctypes.c_int, ctypes.c_void_p]; lib.eqref_dn_fourier_matrix(6, p(Fn))\n"
+        "fn = np.zeros((2, 1, 12)); lib.eqref_dn_to_regular.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]\n"
+        "lib.eqref_dn_to_regular(6, 2, 1, p(yn), p(fn)); lib.eqref_dn_to_fourier.argtypes = lib.eqref_dn_to_regular.argtypes\n"
+        "lib.eqref_dn_to_fourier(6, 2, 1, p(fn), p(yn))\n"
+        "bn = np.ones(1); lib.eqref_dn_bias_act.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]\n"
+        "lib.eqref_dn_bias_act(6, 2, 1, p(bn), 1, p(yn))\n"
         "print('SAN-OK')\n"
     )
     asan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
