@@ -47,12 +47,14 @@ KERNEL_SOURCES = {
            "group_equivariant_linear_amd/csrc/gemm_rows.hip",
            "group_equivariant_linear_amd/csrc/eq_device.h"],
 }
+KERNEL_SOURCES["D"] = KERNEL_SOURCES["D8"]  # the dihedral layers of other orders: same kernels
 
 
 def step_kernel_name(wl):
     """The kernel one forward of this workload launches (automatic tile choice)."""
     if wl.group != "C":
-        whole = (wl.C_in // 8) % 8 == 0 and (wl.C_out // 8) % 8 == 0  # block columns in 16-byte pieces
+        # dihedral (D8 or D_n, N = group order): block columns in whole 16-byte pieces
+        whole = (wl.C_in // wl.N) % 8 == 0 and (wl.C_out // wl.N) % 8 == 0
         return "d8_kernel" if wl.dtype == "bf16" and whole else "gemm_rows_kernel"
     if wl.dtype in ("bf16", "f16") and 2 <= wl.N <= 8:
         return "cn_mf_kernel"
@@ -149,7 +151,7 @@ class Layer:
             else:
                 self.step = lambda: eq.eqlinear_forward_tiled(self.plan, self.x, self.w_hat, self.y, tile, T=wl.T)
         else:
-            self.plan = eq.eqlinear_d8_plan(wl.C_in, wl.C_out, eqdt)
+            self.plan = eq.eqlinear_dihedral_plan(wl.N // 2, wl.C_in, wl.C_out, eqdt)
             self.w_hat = w
             self.weight_fft_ms = None
             self.K, self.M = wl.C_in, wl.C_out
@@ -214,15 +216,16 @@ class Layer:
         self.post = post
 
     def _d8_epilogue(self, eq, wl, d, dev, es, epilogue):
-        """D8 layer, then the fused regular-domain round trip in place (bias per
-        regular channel, GELU).  The torch comparator: dense GEMM, then gather to
-        the regular layout, the 8 x 8 transform, bias, in-place GELU, transform
-        back and scatter."""
+        """Dihedral layer (D8, or D_n with N = 2n), then the fused regular-domain
+        round trip in place (bias per regular channel, GELU).  The torch
+        comparator: dense GEMM, then gather to the regular layout, the N x N
+        transform, bias, in-place GELU, transform back and scatter."""
         import numpy as np
         import torch
 
         import synthetic
-        m = wl.C_out // 8
+        G, n = wl.N, wl.N // 2
+        m = wl.C_out // G
         bd, d["b64"] = synthetic.channel_bias(m, wl.dtype, 500)
         self.bias = dev(bd)
         act = eq.EQL_ACT_GELU if epilogue == "bias_gelu" else eq.EQL_ACT_NONE
@@ -233,16 +236,19 @@ class Layer:
             eq.eqlinear_d8_bias_act(self.plan, self.y, self.bias, act, self.y, T=wl.T)
         self.step = step
         self.bytes_per_launch += m * es
-        F = torch.tensor(_d8_fourier_matrix(), dtype=torch.float32, device="cuda").to(self.tdt)
+        Fm, n1, n2 = _dihedral_fourier_matrix(n)
+        F = torch.tensor(Fm, dtype=torch.float32, device="cuda").to(self.tdt)
         j = np.arange(m)[:, None]
-        cols = np.concatenate([j, m + j, 2 * m + j, 3 * m + j, 4 * m + 2 * j, 4 * m + 2 * j + 1,
-                               6 * m + 2 * j, 6 * m + 2 * j + 1], axis=1)  # [m][8] Fourier columns
-        idx = torch.tensor(cols.reshape(-1), device="cuda")
+        cols = [b * m + j for b in range(n1)]
+        for k in range(n2):  # E_k copies 2j, 2j+1 in its coordinate-0 and -1 slabs
+            base = n1 * m + 4 * m * k
+            cols += [base + 2 * j, base + 2 * j + 1, base + 2 * m + 2 * j, base + 2 * m + 2 * j + 1]
+        idx = torch.tensor(np.concatenate(cols, axis=1).reshape(-1), device="cuda")  # [m][G] Fourier columns
         gelu_ = torch._C._nn.gelu_
         bias_j = self.bias[:, None]
 
         def round_trip(t):
-            f = torch.matmul(t[:, idx].view(wl.T, m, 8), F) + bias_j  # regular values: v F
+            f = torch.matmul(t[:, idx].view(wl.T, m, G), F) + bias_j  # regular values: v F
             if act == eq.EQL_ACT_GELU:
                 gelu_(f)
             t[:, idx] = torch.matmul(f, F.t().contiguous()).view(wl.T, -1)
@@ -300,21 +306,27 @@ class Layer:
             self.dense_torch = lambda: torch.mm(self.dy.t().contiguous(), self.x, out=self.y_lin)
 
 
-def _d8_fourier_matrix():
-    """The orthonormal D8 Fourier matrix F[p][q] for the torch comparator, from the
-    irreps: rows sqrt(1/8) chi(q) for A1, A2, B1, B2 and (1/2) E(q)[k][c] for E,
-    element q = a + 4b being r^a s^b, E(r) = [[0,-1],[1,0]], E(s) = diag(1,-1)."""
+def _dihedral_fourier_matrix(n):
+    """The orthonormal Fourier matrix F[p][q] of D_n (order G = 2n; n = 4: D8) for
+    the torch comparator, from the irreps: rows sqrt(1/G) chi(q) for A1, A2 (and
+    B1, B2 for even n), then sqrt(2/G) E_k(q)[kk][c] for each E_k; element
+    q = a + n b is r^a s^b, E_k(r) the turn by 2 pi k / n, E_k(s) = diag(1,-1).
+    Returns (F, number of 1-D irreps, number of 2-D irreps)."""
     import numpy as np
-    Er, Es = np.array([[0.0, -1.0], [1.0, 0.0]]), np.diag([1.0, -1.0])
-    chars = [(1, 1), (1, -1), (-1, 1), (-1, -1)]
-    F = np.zeros((8, 8))
-    for q in range(8):
-        a, b = q % 4, q // 4
-        M = np.linalg.matrix_power(Er, a) @ (Es if b else np.eye(2))
+    G = 2 * n
+    chars = [(1, 1), (1, -1)] + ([(-1, 1), (-1, -1)] if n % 2 == 0 else [])
+    n2 = n // 2 - 1 if n % 2 == 0 else (n - 1) // 2
+    F = np.zeros((G, G))
+    for q in range(G):
+        a, b = q % n, q // n
         for p, (cr, cs) in enumerate(chars):
-            F[p, q] = cr ** a * cs ** b / np.sqrt(8.0)
-        F[4:, q] = 0.5 * M.reshape(-1)
-    return F
+            F[p, q] = cr ** a * cs ** b / np.sqrt(G)
+        for k in range(1, n2 + 1):
+            th = 2 * np.pi * k / n
+            R = np.array([[np.cos(th), -np.sin(th)], [np.sin(th), np.cos(th)]])
+            M = np.linalg.matrix_power(R, a) @ (np.diag([1.0, -1.0]) if b else np.eye(2))
+            F[len(chars) + 4 * (k - 1):len(chars) + 4 * k, q] = np.sqrt(2.0 / G) * M.reshape(-1)
+    return F, len(chars), n2
 
 
 def time_loop(fns, steps, warmup):
@@ -424,7 +436,7 @@ def cpu_baseline(layers, target_s, op="forward"):
 def _run_oracle(wl, d, n, op="forward"):
     import oracle
     if "b64" in d and wl.group != "C":
-        oracle.d8_dense_bias_act(d["x64"][:n], d["w64"], wl.C_out, d["b64"], d["act"])
+        oracle.dn_dense_bias_act(wl.N // 2, d["x64"][:n], d["w64"], wl.C_out, d["b64"], d["act"])
     elif "b64" in d:
         oracle.cn_dense_bias_act(d["x64"][:n], d["w64"], d["b64"], d["act"])
     elif op == "backward_data":
@@ -434,7 +446,7 @@ def _run_oracle(wl, d, n, op="forward"):
     elif wl.group == "C":
         oracle.cn_dense(d["x64"][:n], d["w64"])
     else:
-        oracle.d8_dense(d["x64"][:n], d["w64"], wl.C_out)
+        oracle.dn_dense(wl.N // 2, d["x64"][:n], d["w64"], wl.C_out)
 
 
 STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "cn_split_kernel", "d8_kernel",
@@ -509,10 +521,12 @@ def algorithmic_bytes(wl, op="forward", epilogue="none"):
         K, M, w = wl.N * wl.C_in, wl.N * wl.C_out, wl.N * wl.C_in * wl.C_out
     else:
         K, M = wl.C_in, wl.C_out
-        w = 4 * (wl.C_in // 8) * (wl.C_out // 8) + (wl.C_in // 4) * (wl.C_out // 4)
+        nd = wl.N // 2  # dihedral D_n, N = 2n
+        mi, mo = wl.C_in // wl.N, wl.C_out // wl.N
+        w = (4 if nd % 2 == 0 else 2) * mi * mo + (nd // 2 - 1 if nd % 2 == 0 else (nd - 1) // 2) * 4 * mi * mo
     if op == "backward_weight":
         return es * wl.T * (K + M) + 4 * w
-    bias = 0 if epilogue == "none" else (wl.C_out if wl.group == "C" else wl.C_out // 8)
+    bias = 0 if epilogue == "none" else (wl.C_out if wl.group == "C" else wl.C_out // wl.N)
     return es * (wl.T * (K + M) + w + bias)
 
 
@@ -693,7 +707,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "; ".join(f"{wl.name}: {wl.note}, {'C' if wl.group == 'C' else ''}"
-                                  f"{wl.N if wl.group == 'C' else 'D8'} T={wl.T} "
+                                  f"{wl.N if wl.group == 'C' else 'D%d' % (wl.N // 2)} T={wl.T} "
                                   f"C_in={wl.C_in} C_out={wl.C_out} {wl.dtype}" for wl in wls),
             "tokens_per_step": tokens,
             "layers_per_step": len(layers),

@@ -30,7 +30,7 @@ ABI_FUNCTIONS = (
     "eqlinear_forward_tiled", "eqlinear_d8_forward", "eqlinear_expand_dense",
     "eqlinear_dense_forward", "eqlinear_w_hat_adjoint", "eqlinear_backward_data",
     "eqlinear_backward_weight_workspace", "eqlinear_backward_weight", "eqlinear_forward_bias_act",
-    "eqlinear_d8_bias_act", "eqlinear_d8_to_fourier", "eqlinear_d8_to_regular",
+    "eqlinear_d8_bias_act", "eqlinear_d8_to_fourier", "eqlinear_d8_to_regular", "eqlinear_dihedral_plan",
 )
 
 
@@ -89,6 +89,7 @@ def load_library(path: str | None = None):
             "eqlinear_backward_weight": ([vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp], st),
             "eqlinear_forward_bias_act": ([vp, vp, vp, vp, i32, vp, i64, vp, i32], st),
             "eqlinear_d8_bias_act": ([vp, vp, vp, i32, vp, i64, vp], st),
+            "eqlinear_dihedral_plan": ([ctypes.POINTER(ctypes.c_void_p), i32, i32, i32, i32], st),
             "eqlinear_d8_to_fourier": ([vp, vp, vp, i64, vp], st),
             "eqlinear_d8_to_regular": ([vp, vp, vp, i64, vp], st),
         }
@@ -118,10 +119,13 @@ class Plan:
         self.info = eqlinear_plan_info(self)
 
     def __del__(self):
+        # may run during interpreter shutdown, when module globals (ctypes among
+        # them) are already gone: touch only what the instance holds
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
-            self._lib.eqlinear_plan_destroy(h)
-            self.handle = ctypes.c_void_p(0)
+        lib = getattr(self, "_lib", None)
+        if h is not None and lib is not None and h.value:
+            lib.eqlinear_plan_destroy(h)
+            h.value = None
 
     @property
     def dtype(self):
@@ -139,6 +143,14 @@ def eqlinear_d8_plan(C_in: int, C_out: int, dtype: int) -> Plan:
     lib = load_library()
     h = ctypes.c_void_p()
     _check(lib.eqlinear_d8_plan(ctypes.byref(h), C_in, C_out, int(dtype)), "eqlinear_d8_plan")
+    return Plan(h.value, lib)
+
+
+def eqlinear_dihedral_plan(n: int, C_in: int, C_out: int, dtype: int) -> Plan:
+    """Plan of the D_n layer (dihedral group of the regular n-gon, order 2n; n = 4 is D8)."""
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.eqlinear_dihedral_plan(ctypes.byref(h), n, C_in, C_out, int(dtype)), "eqlinear_dihedral_plan")
     return Plan(h.value, lib)
 
 
@@ -256,11 +268,12 @@ def eqlinear_d8_forward(plan: Plan, x, wb, y, T: int | None = None, stream=None)
 
 
 def eqlinear_d8_bias_act(plan: Plan, y_in, bias, act: int, y_out, T: int | None = None, stream=None):
-    """y_out = F act(F^T y_in + bias[j]) per regular channel (y_out may be y_in); bias None or [C_out/8]."""
+    """y_out = F act(F^T y_in + bias[j]) per regular channel (y_out may be y_in); bias None or
+    [C_out / group order]."""
     _, M = _widths(plan)
     T = _tokens(y_in, T, M)
     _check(plan._lib.eqlinear_d8_bias_act(plan.handle, _ptr(y_in, plan, T * M, "y_in"),
-                                          _ptr(bias, plan, plan.info["C_out"] // 8, "bias"), int(act),
+                                          _ptr(bias, plan, plan.info["C_out"] // plan.info["N"], "bias"), int(act),
                                           _ptr(y_out, plan, T * M, "y_out"), T, _stream(stream)),
            "eqlinear_d8_bias_act")
 

@@ -118,24 +118,27 @@ __global__ void cn_expand_kernel(const IO* __restrict__ w, IO* __restrict__ W, i
 }
 
 // Block-diagonal D8 matrix [C_out][C_in] from [W_A1|W_A2|W_B1|W_B2|W_E].
+// Dihedral block matrix W[C_out][C_in] from the packed blocks: a square block per
+// 1-D irrep (n1 of them, m x m), then per 2-D irrep E_k one (2m x 2m) block on
+// both of its coordinates (D8: n = 4, n1 = 4, one E).
 template <typename IO>
-__global__ void d8_expand_kernel(const IO* __restrict__ wb, IO* __restrict__ W, int C_in,
-                                 int C_out, int64_t total) {
-    const int mi = C_in / 8, mo = C_out / 8;
+__global__ void dn_expand_kernel(const IO* __restrict__ wb, IO* __restrict__ W, int n, int C_in, int C_out,
+                                 int64_t total) {
+    const int mi = C_in / (2 * n), mo = C_out / (2 * n), n1 = n % 2 == 0 ? 4 : 2;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * blockDim.x) {
         const int r = (int)(e / C_in), c = (int)(e % C_in);
         IO v = (IO)0.0f;
-        if (r < 4 * mo) {
+        if (r < n1 * mo) {
             const int b = r / mo;
             if (c >= b * mi && c < (b + 1) * mi)
                 v = wb[(int64_t)b * mo * mi + (int64_t)(r - b * mo) * mi + (c - b * mi)];
         } else {
-            const int ce = (r - 4 * mo) / (2 * mo);
-            const int rr = r - 4 * mo - 2 * ce * mo;
-            const int c_lo = 4 * mi + 2 * ce * mi;
+            const int er = r - n1 * mo, k = er / (4 * mo);
+            const int ce = (er % (4 * mo)) / (2 * mo), rr = er % (2 * mo);
+            const int c_lo = n1 * mi + 4 * k * mi + 2 * ce * mi;
             if (c >= c_lo && c < c_lo + 2 * mi)
-                v = wb[(int64_t)4 * mo * mi + (int64_t)rr * (2 * mi) + (c - c_lo)];
+                v = wb[(int64_t)n1 * mo * mi + (int64_t)k * 4 * mo * mi + (int64_t)rr * (2 * mi) + (c - c_lo)];
         }
         W[e] = v;
     }
@@ -161,15 +164,15 @@ hipError_t launch_cn_expand(int N, int io, const void* w, void* w_dense, int C_i
     return hipGetLastError();
 }
 
-hipError_t launch_d8_expand(int dtype_bf16, const void* wb, void* w_dense, int C_in, int C_out,
+hipError_t launch_dn_expand(int n, int dtype_bf16, const void* wb, void* w_dense, int C_in, int C_out,
                             hipStream_t stream) {
     const int64_t total = (int64_t)C_out * C_in;
     if (dtype_bf16)
-        hipLaunchKernelGGL(d8_expand_kernel<__bf16>, dim3(grid_for(total, 256)), dim3(256), 0,
-                           stream, (const __bf16*)wb, (__bf16*)w_dense, C_in, C_out, total);
+        hipLaunchKernelGGL(dn_expand_kernel<__bf16>, dim3(grid_for(total, 256)), dim3(256), 0,
+                           stream, (const __bf16*)wb, (__bf16*)w_dense, n, C_in, C_out, total);
     else
-        hipLaunchKernelGGL(d8_expand_kernel<float>, dim3(grid_for(total, 256)), dim3(256), 0,
-                           stream, (const float*)wb, (float*)w_dense, C_in, C_out, total);
+        hipLaunchKernelGGL(dn_expand_kernel<float>, dim3(grid_for(total, 256)), dim3(256), 0,
+                           stream, (const float*)wb, (float*)w_dense, n, C_in, C_out, total);
     return hipGetLastError();
 }
 

@@ -230,7 +230,146 @@ hipError_t launch_pass_dt(int dtype_bf16, const void* in, void* out, const void*
     return launch_pass<float, MODE>(in, out, bias, act, m, T, stream);
 }
 
+// --- other dihedral orders ------------------------------------------------------------
+// D_n of the regular n-gon (order G = 2n): 1-D irreps A1, A2 (and B1, B2 for even
+// n), 2-D irreps E_k turning by 2 pi k / n, the layer's layout generalised (1-D
+// slabs of m channels, then per E_k a coordinate-0 and a coordinate-1 slab of 2m
+// copies; regular channel j owns column j of each 1-D slab and copies 2j, 2j+1).
+// The Fourier matrix is a compile-time table (exact twiddles), so each channel's
+// transforms are unrolled multiply-adds with the zero entries gone; one thread
+// per channel.
+constexpr double csqrt(double x) {
+    double r = x > 1.0 ? x : 1.0;
+    for (int i = 0; i < 60; ++i) r = 0.5 * (r + x / r);
+    return r;
+}
+
+template <int n>
+struct DnGroup {
+    static constexpr int G = 2 * n;
+    static constexpr int N1 = n % 2 == 0 ? 4 : 2;
+    static constexpr int N2 = n % 2 == 0 ? n / 2 - 1 : (n - 1) / 2;
+    // F[p][q], element q = a + n b = r^a s^b
+    static constexpr double entry(int p, int q) {
+        const int a = q % n, b = q / n;
+        if (p < N1) {
+            const double cr = (p >= 2) ? -1.0 : 1.0, cs = (p % 2) ? -1.0 : 1.0;
+            double v = 1.0;
+            for (int i = 0; i < a; ++i) v *= cr;
+            if (b) v *= cs;
+            return v / csqrt((double)G);
+        }
+        const int e = p - N1, k = e / 4 + 1, kk = (e % 4) / 2, c = e % 2;
+        const double co = turn_trig((long)k * a, n, false), si = turn_trig((long)k * a, n, true);
+        // E_k(r^a) = rotation by 2 pi k a / n; E_k(s) = diag(1, -1) negates column 1
+        const double m = c == 0 ? (kk == 0 ? co : si) : (kk == 0 ? -si : co) * (b ? -1.0 : 1.0);
+        return m * csqrt(2.0 / (double)G);
+    }
+    static constexpr int64_t slot(int m, int j, int p) {  // Fourier column of (channel j, coefficient p)
+        if (p < N1) return (int64_t)p * m + j;
+        const int e = p - N1, k = e / 4, kk = (e % 4) / 2, c = e % 2;
+        return (int64_t)N1 * m + 4 * (int64_t)m * k + 2 * (int64_t)m * kk + 2 * j + c;
+    }
+};
+
+template <typename IO, int n, int MODE>
+__global__ __launch_bounds__(256) void dn_pass_kernel(const IO* in, IO* out, const IO* bias, int act, int m,
+                                                      uint32_t total) {
+    using D = DnGroup<n>;
+    constexpr int G = D::G;
+    const uint32_t idx = blockIdx.x * 256u + threadIdx.x;  // total < 2^31 (host-checked)
+    if (idx >= total) return;
+    const uint32_t t = idx / (uint32_t)m;
+    const int j = (int)(idx - t * (uint32_t)m);
+    const int64_t row = (int64_t)t * G * m;
+    float v[G], f[G];
+    if constexpr (MODE == kToFourier) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) f[q] = (float)in[row + (int64_t)G * j + q];
+    } else {
+#pragma unroll
+        for (int p = 0; p < G; ++p) v[p] = (float)in[row + D::slot(m, j, p)];
+        static_for<0, G>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            float acc = 0.0f;
+            static_for<0, G>([&](auto pc) {
+                constexpr int p = decltype(pc)::value;
+                constexpr float c = (float)D::entry(p, q);
+                if constexpr (c != 0.0f) acc = fmaf(c, v[p], acc);
+            });
+            f[q] = acc;
+        });
+    }
+    if constexpr (MODE == kRoundTrip) {
+        const float b = bias != nullptr ? (float)bias[j] : 0.0f;
+        if (act == 1) {
+#pragma unroll
+            for (int q = 0; q < G; ++q) f[q] = gelu_erf(f[q] + b);
+        } else {
+#pragma unroll
+            for (int q = 0; q < G; ++q) f[q] += b;
+        }
+    }
+    if constexpr (MODE == kToRegular) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) out[row + (int64_t)G * j + q] = (IO)f[q];
+    } else {
+        static_for<0, G>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            float acc = 0.0f;
+            static_for<0, G>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                constexpr float c = (float)D::entry(p, q);
+                if constexpr (c != 0.0f) acc = fmaf(c, f[q], acc);
+            });
+            out[row + D::slot(m, j, p)] = (IO)acc;
+        });
+    }
+}
+
+template <typename IO, int MODE>
+hipError_t launch_dn_pass(int n, const void* in, void* out, const void* bias, int act, int m, int64_t T,
+                          hipStream_t stream) {
+    const int64_t total = T * m;
+    if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const uint32_t blocks = (uint32_t)((total + 255) / 256);
+    switch (n) {
+#define EQL_DN(k)                                                                                       \
+    case k:                                                                                             \
+        hipLaunchKernelGGL((dn_pass_kernel<IO, k, MODE>), dim3(blocks), dim3(256), 0, stream, (const IO*)in, \
+                           (IO*)out, (const IO*)bias, act, m, (uint32_t)total);                         \
+        return hipGetLastError();
+        EQL_DN(2) EQL_DN(3) EQL_DN(5) EQL_DN(6) EQL_DN(7) EQL_DN(8) EQL_DN(9) EQL_DN(10) EQL_DN(11) EQL_DN(12)
+#undef EQL_DN
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// n == 4 (D8) takes the butterfly kernel above; other orders the table kernel
+template <int MODE>
+hipError_t launch_dihedral_pass(int n, int dtype_bf16, const void* in, void* out, const void* bias, int act, int m,
+                                int64_t T, hipStream_t stream) {
+    if (n == 4) return launch_pass_dt<MODE>(dtype_bf16, in, out, bias, act, m, T, stream);
+    if (dtype_bf16) return launch_dn_pass<__bf16, MODE>(n, in, out, bias, act, m, T, stream);
+    return launch_dn_pass<float, MODE>(n, in, out, bias, act, m, T, stream);
+}
+
 }  // namespace
+
+hipError_t launch_dn_round_trip(int n, int dtype_bf16, const void* y_in, void* y_out, const void* bias, int act,
+                                int m, int64_t T, hipStream_t stream) {
+    return launch_dihedral_pass<kRoundTrip>(n, dtype_bf16, y_in, y_out, bias, act, m, T, stream);
+}
+
+hipError_t launch_dn_to_fourier(int n, int dtype_bf16, const void* x_reg, void* x_four, int m, int64_t T,
+                                hipStream_t stream) {
+    return launch_dihedral_pass<kToFourier>(n, dtype_bf16, x_reg, x_four, nullptr, 0, m, T, stream);
+}
+
+hipError_t launch_dn_to_regular(int n, int dtype_bf16, const void* y_four, void* y_reg, int m, int64_t T,
+                                hipStream_t stream) {
+    return launch_dihedral_pass<kToRegular>(n, dtype_bf16, y_four, y_reg, nullptr, 0, m, T, stream);
+}
 
 hipError_t launch_d8_round_trip(int dtype_bf16, const void* y_in, void* y_out, const void* bias, int act, int m,
                                 int64_t T, hipStream_t stream) {

@@ -6,7 +6,7 @@
 
 namespace eql {
 
-constexpr int kMaxGemmJobs = 6;
+constexpr int kMaxGemmJobs = 16;  // D8: 6 jobs; D_n: n + 1 (odd n) or n + 2 (even n), n <= 12
 
 // Element type of a launch's tensors ("io" arguments), the codes of the C ABI's
 // eqlinear_dtype.  Launchers that take a plain "dtype_bf16" flag have no fp16
@@ -67,7 +67,8 @@ hipError_t launch_weight_dft(int N, int io, const void* w, void* w_hat, int C_in
 hipError_t launch_cn_expand(int N, int io, const void* w, void* w_dense, int C_in,
                             int C_out, hipStream_t stream);
 
-hipError_t launch_d8_expand(int dtype_bf16, const void* wb, void* w_dense, int C_in, int C_out,
+// dihedral D_n block matrix (n = 4: D8)
+hipError_t launch_dn_expand(int n, int dtype_bf16, const void* wb, void* w_dense, int C_in, int C_out,
                             hipStream_t stream);
 
 // d8_round_trip.hip: m = C/8 regular channels per token
@@ -76,6 +77,13 @@ hipError_t launch_d8_round_trip(int dtype_bf16, const void* y_in, void* y_out, c
 hipError_t launch_d8_to_fourier(int dtype_bf16, const void* x_reg, void* x_four, int m, int64_t T,
                                 hipStream_t stream);
 hipError_t launch_d8_to_regular(int dtype_bf16, const void* y_four, void* y_reg, int m, int64_t T,
+                                hipStream_t stream);
+// the same passes for D_n, m = C/2n regular channels (n = 4 takes the D8 kernels)
+hipError_t launch_dn_round_trip(int n, int dtype_bf16, const void* y_in, void* y_out, const void* bias, int act,
+                                int m, int64_t T, hipStream_t stream);
+hipError_t launch_dn_to_fourier(int n, int dtype_bf16, const void* x_reg, void* x_four, int m, int64_t T,
+                                hipStream_t stream);
+hipError_t launch_dn_to_regular(int n, int dtype_bf16, const void* y_four, void* y_reg, int m, int64_t T,
                                 hipStream_t stream);
 
 }  // namespace eql

@@ -42,6 +42,11 @@ int64_t out_width(const eqlinear_plan_s* p) {
 // Widths are capped so every per-row offset fits an int in the kernels.
 constexpr int64_t kMaxWidth = 1 << 20;
 
+// Irreps of the dihedral group of the regular n-gon: 1-D ones (A1, A2, and B1,
+// B2 for even n) and 2-D ones E_k.
+int dihedral_one_dim(int n) { return n % 2 == 0 ? 4 : 2; }
+int dihedral_two_dim(int n) { return n % 2 == 0 ? n / 2 - 1 : (n - 1) / 2; }
+
 }  // namespace
 
 extern "C" {
@@ -69,17 +74,22 @@ eqlinear_status eqlinear_plan(eqlinear_plan_t* out, int N, int C_in, int C_out,
     return EQL_OK;
 }
 
-eqlinear_status eqlinear_d8_plan(eqlinear_plan_t* out, int C_in, int C_out, eqlinear_dtype dt) {
+eqlinear_status eqlinear_dihedral_plan(eqlinear_plan_t* out, int n, int C_in, int C_out, eqlinear_dtype dt) {
     if (!out) return EQL_ERR_INVALID;
     *out = nullptr;
-    if (C_in < 8 || C_out < 8 || C_in % 8 || C_out % 8 || !dtype_ok((int)dt))
-        return EQL_ERR_INVALID;
-    if (dt == EQL_F16) return EQL_ERR_UNSUPPORTED;  // the D8 kernels are fp32 and bf16
+    if (n < 2 || n > 12) return EQL_ERR_INVALID;
+    const int G = 2 * n;  // group order: the plan's N
+    if (C_in < G || C_out < G || C_in % G || C_out % G || !dtype_ok((int)dt)) return EQL_ERR_INVALID;
+    if (dt == EQL_F16) return EQL_ERR_UNSUPPORTED;  // the dihedral kernels are fp32 and bf16
     if (C_in > kMaxWidth || C_out > kMaxWidth) return EQL_ERR_INVALID;
-    eqlinear_plan_s* p = new (std::nothrow) eqlinear_plan_s{EQL_KIND_D8, (int)dt, 8, C_in, C_out};
+    eqlinear_plan_s* p = new (std::nothrow) eqlinear_plan_s{EQL_KIND_D8, (int)dt, G, C_in, C_out};
     if (!p) return EQL_ERR_NOMEM;
     *out = p;
     return EQL_OK;
+}
+
+eqlinear_status eqlinear_d8_plan(eqlinear_plan_t* out, int C_in, int C_out, eqlinear_dtype dt) {
+    return eqlinear_dihedral_plan(out, 4, C_in, C_out, dt);
 }
 
 eqlinear_status eqlinear_plan_destroy(eqlinear_plan_t plan) {
@@ -110,14 +120,16 @@ eqlinear_status eqlinear_plan_info(eqlinear_plan_t p, eqlinear_info* out) {
         in.macs_per_token = in.real_gemms * ci * co;
         in.dense_macs_per_token = (int64_t)N * N * ci * co;
     } else {
-        const int64_t mi = ci / 8, mo = co / 8;
-        in.bins = 5;
+        const int n = p->N / 2;
+        const int64_t mi = ci / p->N, mo = co / p->N;
+        const int n1 = dihedral_one_dim(n), n2 = dihedral_two_dim(n);
+        in.bins = n1 + n2;  // irrep blocks
         in.planes = 0;
         in.has_nyquist = 0;
-        in.params = 4 * mi * mo + (2 * mi) * (2 * mo);
+        in.params = n1 * mi * mo + n2 * (2 * mi) * (2 * mo);
         in.w_hat_elems = in.params;
         in.real_gemms = 0;
-        in.macs_per_token = 4 * mi * mo + 2 * (2 * mi) * (2 * mo);
+        in.macs_per_token = n1 * mi * mo + 2 * n2 * (2 * mi) * (2 * mo);
         in.dense_macs_per_token = ci * co;
     }
     *out = in;
@@ -189,11 +201,11 @@ eqlinear_status eqlinear_d8_bias_act(eqlinear_plan_t p, const void* y_in, const 
     if (T == 0) return EQL_OK;
     if (!y_in || !y_out || !aligned16(y_in) || !aligned16(y_out)) return EQL_ERR_INVALID;
     const size_t es = elem_size(p);
-    const size_t yb = (size_t)T * p->C_out * es, bb = (size_t)(p->C_out / 8) * es;
+    const size_t yb = (size_t)T * p->C_out * es, bb = (size_t)(p->C_out / p->N) * es;
     if (y_in != y_out && overlaps(y_in, yb, y_out, yb)) return EQL_ERR_INVALID;  // in place, or apart
     if (bias && (((uintptr_t)bias % es) != 0 || overlaps(bias, bb, y_out, yb))) return EQL_ERR_INVALID;
-    return hip_status(eql::launch_d8_round_trip(p->dtype == EQL_BF16, y_in, y_out, bias, act, p->C_out / 8, T,
-                                                (hipStream_t)stream));
+    return hip_status(eql::launch_dn_round_trip(p->N / 2, p->dtype == EQL_BF16, y_in, y_out, bias, act,
+                                                p->C_out / p->N, T, (hipStream_t)stream));
 }
 
 eqlinear_status eqlinear_d8_to_fourier(eqlinear_plan_t p, const void* x_reg, void* x_four, int64_t T,
@@ -204,8 +216,8 @@ eqlinear_status eqlinear_d8_to_fourier(eqlinear_plan_t p, const void* x_reg, voi
     if (!x_reg || !x_four || !aligned16(x_reg) || !aligned16(x_four)) return EQL_ERR_INVALID;
     const size_t b = (size_t)T * p->C_in * elem_size(p);
     if (overlaps(x_reg, b, x_four, b)) return EQL_ERR_INVALID;
-    return hip_status(eql::launch_d8_to_fourier(p->dtype == EQL_BF16, x_reg, x_four, p->C_in / 8, T,
-                                                (hipStream_t)stream));
+    return hip_status(eql::launch_dn_to_fourier(p->N / 2, p->dtype == EQL_BF16, x_reg, x_four, p->C_in / p->N,
+                                                T, (hipStream_t)stream));
 }
 
 eqlinear_status eqlinear_d8_to_regular(eqlinear_plan_t p, const void* y_four, void* y_reg, int64_t T,
@@ -216,8 +228,8 @@ eqlinear_status eqlinear_d8_to_regular(eqlinear_plan_t p, const void* y_four, vo
     if (!y_four || !y_reg || !aligned16(y_four) || !aligned16(y_reg)) return EQL_ERR_INVALID;
     const size_t b = (size_t)T * p->C_out * elem_size(p);
     if (overlaps(y_four, b, y_reg, b)) return EQL_ERR_INVALID;
-    return hip_status(eql::launch_d8_to_regular(p->dtype == EQL_BF16, y_four, y_reg, p->C_out / 8, T,
-                                                (hipStream_t)stream));
+    return hip_status(eql::launch_dn_to_regular(p->N / 2, p->dtype == EQL_BF16, y_four, y_reg, p->C_out / p->N,
+                                                T, (hipStream_t)stream));
 }
 
 eqlinear_status eqlinear_w_hat_adjoint(eqlinear_plan_t p, const void* w_hat, void* w_hat_adj, void* stream) {
@@ -283,15 +295,17 @@ eqlinear_status eqlinear_d8_forward(eqlinear_plan_t p, const void* x, const void
     const size_t xb = (size_t)T * p->C_in * es, yb = (size_t)T * p->C_out * es;
     const size_t wbb = eqlinear_w_hat_elems(p) * es;
     if (overlaps(x, xb, y, yb) || overlaps(wb, wbb, y, yb)) return EQL_ERR_INVALID;
-    const int mi = p->C_in / 8, mo = p->C_out / 8;
+    const int n = p->N / 2, mi = p->C_in / p->N, mo = p->C_out / p->N;
+    const int n1 = dihedral_one_dim(n), n2 = dihedral_two_dim(n);
     eql::GemmJobs jobs{};
-    jobs.njobs = 6;
-    const int64_t e_off = 4LL * mo * mi;
-    for (int b = 0; b < 4; ++b)  // A1, A2, B1, B2
+    jobs.njobs = n1 + 2 * n2;  // <= kMaxGemmJobs for n <= 12
+    for (int b = 0; b < n1; ++b)  // A1, A2 (, B1, B2)
         jobs.j[b] = eql::GemmJob{b * mi, b * mo, mi, mo, (int64_t)b * mo * mi, mi, 0, 0, 0, 0};
-    for (int c = 0; c < 2; ++c)  // W_E on E coordinate 0 and 1
-        jobs.j[4 + c] = eql::GemmJob{4 * mi + 2 * c * mi, 4 * mo + 2 * c * mo, 2 * mi, 2 * mo,
-                                     e_off, 2 * mi, 0, 0, 0, 0};
+    for (int k = 0; k < n2; ++k)  // W of E_{k+1} on its coordinate 0 and 1
+        for (int c = 0; c < 2; ++c)
+            jobs.j[n1 + 2 * k + c] =
+                eql::GemmJob{n1 * mi + 4 * k * mi + 2 * c * mi, n1 * mo + 4 * k * mo + 2 * c * mo, 2 * mi, 2 * mo,
+                             (int64_t)n1 * mo * mi + (int64_t)k * 4 * mo * mi, 2 * mi, 0, 0, 0, 0};
     if (p->dtype == EQL_BF16) {
         // widest output tile that the 1-D blocks fill: 160, 80 or 32 channels
         const int cb = mo % 160 == 0 ? 10 : (mo % 80 == 0 ? 5 : 2);
@@ -316,7 +330,7 @@ eqlinear_status eqlinear_expand_dense(eqlinear_plan_t p, const void* w, void* w_
         e = eql::launch_cn_expand(p->N, p->dtype, w, w_dense, p->C_in, p->C_out,
                                   (hipStream_t)stream);
     else
-        e = eql::launch_d8_expand(p->dtype == EQL_BF16, w, w_dense, p->C_in, p->C_out,
+        e = eql::launch_dn_expand(p->N / 2, p->dtype == EQL_BF16, w, w_dense, p->C_in, p->C_out,
                                   (hipStream_t)stream);
     return hip_status(e);
 }

@@ -95,9 +95,25 @@ eqlinear_status eqlinear_plan(eqlinear_plan_t* out, int N, int C_in, int C_out,
 
 /* Create a D8 plan ("Quick ViTs", key design 2).  C_in and C_out are full
  * widths, multiples of 8 (C/8 channels per 1-D irrep, C/4 copies of E); dt in
- * {EQL_F32, EQL_BF16} (EQL_F16: EQL_ERR_UNSUPPORTED). */
+ * {EQL_F32, EQL_BF16} (EQL_F16: EQL_ERR_UNSUPPORTED).  Same as
+ * eqlinear_dihedral_plan(out, 4, C_in, C_out, dt). */
 eqlinear_status eqlinear_d8_plan(eqlinear_plan_t* out, int C_in, int C_out,
                                  eqlinear_dtype dt);
+
+/* Create a plan for the dihedral group D_n of the regular n-gon (order 2n,
+ * 2 <= n <= 12; n = 4 is D8): the extension to other shapes that "Flash
+ * EQ-Linear" (Dutch summary, closing paragraph) names, in the Fourier-domain
+ * form of "Quick ViTs" key design 2.  D_n has 1-D irreps A1, A2 (and B1, B2 for
+ * even n) and 2-D irreps E_k (k = 1 .. n/2 - 1 for even n, .. (n-1)/2 for odd
+ * n; r turns by 2 pi k / n, s = diag(1, -1)).  C_in, C_out multiples of 2n;
+ * m = C/2n.  Layout per token: the 1-D irreps' slabs of m, then for each E_k
+ * a coordinate-0 and a coordinate-1 slab of 2m copies.  Weights packed
+ * [W per 1-D irrep (m_out x m_in) | W per E_k (2m_out x 2m_in)], each [out][in];
+ * a block of E_k acts on both of its coordinates.  Every eqlinear_d8_* call
+ * and the comparator take these plans (kind EQL_KIND_D8, info.N = 2n,
+ * info.bins = number of irrep blocks); dt as for eqlinear_d8_plan. */
+eqlinear_status eqlinear_dihedral_plan(eqlinear_plan_t* out, int n, int C_in, int C_out,
+                                       eqlinear_dtype dt);
 
 /* Free a plan.  NULL -> EQL_ERR_INVALID. */
 eqlinear_status eqlinear_plan_destroy(eqlinear_plan_t plan);
@@ -204,8 +220,12 @@ eqlinear_status eqlinear_forward_bias_act(eqlinear_plan_t plan, const void* x, c
  * F^T, become act(f + bias[j]) in fp32, and return through F; one rounding to
  * the plan dtype.  Element q = a + 4b is r^a s^b with the layer's generators
  * (E(r) = [[0,-1],[1,0]], E(s) = diag(1,-1)).  With no bias and no activation
- * the pass is the identity up to that rounding.  D8 plans only; T == 0:
- * EQL_OK, nothing launched.  Asynchronous on stream; no allocation. */
+ * the pass is the identity up to that rounding.  Dihedral plans of other orders
+ * (eqlinear_dihedral_plan) take the same pass with their own Fourier matrix:
+ * 2n values per channel, rows sqrt(1/2n) times the 1-D irreps and sqrt(2/2n)
+ * times the entries (k, c) of E_k, element q = a + n b; bias [C_out/2n].  C_N
+ * plans -> EQL_ERR_INVALID; T == 0: EQL_OK, nothing launched.  Asynchronous on
+ * stream; no allocation. */
 eqlinear_status eqlinear_d8_bias_act(eqlinear_plan_t plan, const void* y_in, const void* bias, int act,
                                      void* y_out, int64_t T, void* stream);
 

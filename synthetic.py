@@ -30,11 +30,12 @@ F16 = "f16"
 
 @dataclass(frozen=True)
 class Workload:
-    """One layer workload: a cyclic-group layer (group='C') or the D8 variant."""
+    """One layer workload: a cyclic-group layer (group='C'), the D8 variant
+    (group='D8', N = 8) or another dihedral group D_n (group='D', N = 2n)."""
 
     name: str
-    group: str  # "C" (cyclic C_N) or "D8"
-    N: int  # group order (8 for D8)
+    group: str  # "C" (cyclic C_N), "D8", or "D" (dihedral D_n)
+    N: int  # group order (8 for D8, 2n for D_n)
     C_in: int  # C: channels per group element; D8: full width
     C_out: int
     T: int  # tokens
@@ -64,6 +65,8 @@ WORKLOADS = {
     "c3c": Workload("c3c", "C", 8, 384, 96, 64 * 197, BF16, "C8 ViT-B MLP 3072->768"),
     "c4": Workload("c4", "C", 7, 160, 160, 32768, BF16, "C7 odd order, width 1120"),
     "c5": Workload("c5", "D8", 8, 1280, 1280, 16 * 257, BF16, "D8 Fourier-domain, width 1280"),
+    # the extension to other shapes: the hexagon's symmetries (order 12), c5's batch
+    "d6": Workload("d6", "D", 12, 1152, 1152, 16 * 257, BF16, "D6 (hexagon) Fourier-domain, width 1152"),
 }
 
 
@@ -135,6 +138,27 @@ def d8_block_shapes(C_in: int, C_out: int):
     return [(mo, mi)] * 4 + [(2 * mo, 2 * mi)]
 
 
+def dn_block_shapes(n: int, C_in: int, C_out: int):
+    """Shapes of the D_n weight blocks in packing order: one (C_out/2n, C_in/2n)
+    per 1-D irrep (4 for even n, 2 for odd), then one (C_out/n, C_in/n) per E_k."""
+    mi, mo = C_in // (2 * n), C_out // (2 * n)
+    n1 = 4 if n % 2 == 0 else 2
+    n2 = n // 2 - 1 if n % 2 == 0 else (n - 1) // 2
+    return [(mo, mi)] * n1 + [(2 * mo, 2 * mi)] * n2
+
+
+def dn_inputs(n: int, C_in: int, C_out: int, T: int, dtype: str, seed: int = 0):
+    """x[T][C_in] ~ N(0,1) and the D_n blocks ~ N(0, 1/fan_in), packed flat ('wb')."""
+    if C_in % (2 * n) or C_out % (2 * n):
+        raise ValueError("D_n widths must be multiples of 2n")
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (T, C_in), 1.0)
+    wb = np.concatenate([_normal(rng, shp, 1.0 / np.sqrt(shp[1])).ravel() for shp in dn_block_shapes(n, C_in, C_out)])
+    xd, x64 = quantize(x, dtype)
+    wd, w64 = quantize(wb, dtype)
+    return {"x": xd, "x64": x64, "w": wd, "w64": w64}
+
+
 def d8_inputs(C_in: int, C_out: int, T: int, dtype: str, seed: int = 0):
     """x[T][C_in] ~ N(0,1); blocks W_A1, W_A2, W_B1, W_B2 (std 1/sqrt(C_in/8))
     and W_E (std 1/sqrt(C_in/4)), packed flat in that order ('wb')."""
@@ -155,7 +179,9 @@ def workload_inputs(wl: Workload, seed: int = 0, T: int | None = None):
     T = wl.T if T is None else T
     if wl.group == "C":
         return cn_inputs(wl.N, wl.C_in, wl.C_out, T, wl.dtype, seed)
-    return d8_inputs(wl.C_in, wl.C_out, T, wl.dtype, seed)
+    if wl.group == "D8":
+        return d8_inputs(wl.C_in, wl.C_out, T, wl.dtype, seed)
+    return dn_inputs(wl.N // 2, wl.C_in, wl.C_out, T, wl.dtype, seed)
 
 
 def sha256(a: np.ndarray) -> str:

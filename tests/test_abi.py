@@ -67,6 +67,28 @@ def test_d8_plan_rejects_invalid(eq, args):
         eq.eqlinear_d8_plan(*args)
 
 
+def test_dihedral_plans(eq):
+    """D_n plans: n = 4 is the D8 plan; widths must be multiples of 2n; counts."""
+    lib = eq.load_library()
+    d8 = eq.eqlinear_d8_plan(32, 64, eq.EQL_BF16).info
+    d4 = eq.eqlinear_dihedral_plan(4, 32, 64, eq.EQL_BF16).info
+    assert d8 == d4 and d8["N"] == 8 and d8["bins"] == 5
+    for n in (2, 3, 5, 6, 12):
+        C = 2 * n * 4
+        info = eq.eqlinear_dihedral_plan(n, C, 2 * C, eq.EQL_F32).info
+        n1 = 4 if n % 2 == 0 else 2
+        n2 = n // 2 - 1 if n % 2 == 0 else (n - 1) // 2
+        mi, mo = 4, 8
+        assert info["N"] == 2 * n and info["bins"] == n1 + n2
+        assert info["params"] == n1 * mi * mo + n2 * 4 * mi * mo == C * 2 * C // (2 * n)
+        assert info["dense_macs_per_token"] == C * 2 * C
+    h = ctypes.c_void_p()
+    for bad in ((1, 8, 8), (13, 26, 26), (3, 8, 12), (3, 12, 8), (6, 12, 18)):
+        assert lib.eqlinear_dihedral_plan(ctypes.byref(h), *bad, eq.EQL_F32) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_dihedral_plan(ctypes.byref(h), 3, 12, 12, eq.EQL_F16) == eq.EQL_ERR_UNSUPPORTED
+    assert lib.eqlinear_dihedral_plan(None, 3, 12, 12, eq.EQL_F32) == eq.EQL_ERR_INVALID
+
+
 def test_fp16_plans(eq):
     """fp16 C_N plans exist (weight spectrum, forward, input gradient, comparator);
     the weight gradient and D8 plans turn fp16 away before any HIP call."""
