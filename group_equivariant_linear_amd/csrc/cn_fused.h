@@ -38,24 +38,32 @@ namespace eql {
 // erfc(z) = t exp(-z^2 + P(t)), t = 1 / (1 + z/2), P of degree 9, with a fractional
 // error below 1.2e-7 for every z >= 0, so both tails of GELU keep their relative
 // accuracy; erfc(-z) = 2 - erfc(z).  Branch-free: one reciprocal and one exp2 on
-// the transcendental unit and a dozen FMAs, about half the cost of erff.
+// the transcendental unit and a dozen FMAs, about half the cost of erff.  The
+// constants are folded at compile time: z/2 = |v| / (2 sqrt 2); P is scaled by
+// log2(e) (exp -> exp2) with the halving of erfc/2 as -1 in its constant term;
+// -z^2 log2(e) = -|v| (|v| log2(e) / 2), the product exact inside the fma.
+struct GeluCoef {
+    static constexpr double kLog2e = 1.44269504088896340736;
+    static constexpr double c[10] = {0.17087277, -0.82215223, 1.48851587, -1.13520398, 0.27886807,
+                                     -0.18628806, 0.09678418, 0.37409196, 1.00002368, -1.26551223};
+    static constexpr float scaled(int i) { return (float)(c[i] * kLog2e - (i == 9 ? 1.0 : 0.0)); }
+};
+
 __device__ __forceinline__ float gelu_erf(float v) {
     const float a = fabsf(v);
-    const float z = a * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
-    float p = 0.17087277f;
-    p = fmaf(p, t, -0.82215223f);
-    p = fmaf(p, t, 1.48851587f);
-    p = fmaf(p, t, -1.13520398f);
-    p = fmaf(p, t, 0.27886807f);
-    p = fmaf(p, t, -0.18628806f);
-    p = fmaf(p, t, 0.09678418f);
-    p = fmaf(p, t, 0.37409196f);
-    p = fmaf(p, t, 1.00002368f);
-    p = fmaf(p, t, -1.26551223f);
-    // h = erfc(|v| / sqrt 2) / 2 = Phi(-|v|); -z^2 = -|v| (|v|/2) with the product exact
-    // inside the fma, so the rounding of z does not reach the exponent
-    const float h = 0.5f * t * __builtin_amdgcn_exp2f(fmaf(-a, 0.5f * a, p) * 1.44269504088896341f);
+    const float t = __builtin_amdgcn_rcpf(fmaf(a, 0.35355339059327376f, 1.0f));
+    float p = GeluCoef::scaled(0);
+    p = fmaf(p, t, GeluCoef::scaled(1));
+    p = fmaf(p, t, GeluCoef::scaled(2));
+    p = fmaf(p, t, GeluCoef::scaled(3));
+    p = fmaf(p, t, GeluCoef::scaled(4));
+    p = fmaf(p, t, GeluCoef::scaled(5));
+    p = fmaf(p, t, GeluCoef::scaled(6));
+    p = fmaf(p, t, GeluCoef::scaled(7));
+    p = fmaf(p, t, GeluCoef::scaled(8));
+    p = fmaf(p, t, GeluCoef::scaled(9));
+    // h = erfc(|v| / sqrt 2) / 2 = Phi(-|v|)
+    const float h = t * __builtin_amdgcn_exp2f(fmaf(-a, a * (float)(0.5 * GeluCoef::kLog2e), p));
     return v * (v < 0.0f ? h : 1.0f - h);
 }
 
