@@ -79,52 +79,91 @@ __global__ __launch_bounds__(256) void w_hat_adjoint_kernel(const IO* __restrict
 }
 
 // --- 1. planes ------------------------------------------------------------------------
-// Block: 64 channels (one per lane) x 32 tokens (8 per wave).  A wave reads the
-// records of 64 consecutive channels of one token (one contiguous run of the
-// token's row), transforms them in fp32 and leaves the N planes in LDS; the
-// block then writes each (plane, channel) row segment of 32 tokens as 16-byte
-// pieces.  Tokens T .. Tp-1 are written as zeros.
+// Block: 64 tokens (one per lane) x TC = 4R channels (R per wave, R = 16/S, so a
+// lane's R records are 16N contiguous bytes: N 16-byte loads when every token
+// row, C N S bytes, is a whole number of 16-byte pieces, else one load per
+// element).  The lane transforms its records in fp32 and writes each plane
+// value to LDS rows [plane][channel][token], where the 64 lanes fill one
+// contiguous row (no bank conflicts); the block then writes each (plane,
+// channel) row segment of 64 tokens as 16-byte pieces, a 16-lane group reading
+// two or more whole rows.  Tokens T .. Tp-1 lie past the input's buffer range
+// and come out as zeros.  x and dy go through the same launch (blockIdx.z).
+// Channels past C belong to the next token's row (or to nothing) and are
+// transformed but never written.
 template <int N, typename IO>
 struct PlanesCfg {
     static constexpr int S = (int)sizeof(IO);
-    static constexpr int TT = 32, TC = 64;
-    static constexpr int PITCH = TT * S + 16;         // bytes of one staged (plane, channel) row
-    static constexpr int PIECES = TT * S / 16;        // 16-byte pieces of a row segment
-    static constexpr int LDS = N * TC * PITCH;
+    static constexpr int R = 16 / S;           // channels per lane
+    static constexpr int TT = 64, TC = 4 * R;  // tokens and channels per block
+    static constexpr int ROW = TT * S;         // bytes of one (plane, channel) row segment
+    static constexpr int LDS = N * TC * ROW;
+    static constexpr int PIECES = LDS / 16;
 };
 
+template <typename IO>
+__device__ __forceinline__ float plane_elem(const uint32_t* w, int v) {
+    if constexpr (sizeof(IO) == 4) return __uint_as_float(w[v]);
+    else return (v & 1) ? Half<IO>::hi(w[v >> 1]) : Half<IO>::lo(w[v >> 1]);
+}
+
 template <int N, typename IO>
-__global__ __launch_bounds__(256) void bw_planes_kernel(const IO* __restrict__ src, IO* __restrict__ planes,
-                                                        int64_t T, int C, int64_t Tp) {
+__global__ __launch_bounds__(256) void bw_planes_kernel(const IO* __restrict__ x, IO* __restrict__ xp, int C_in,
+                                                        const IO* __restrict__ dy, IO* __restrict__ dyp, int C_out,
+                                                        int64_t T, int64_t Tp) {
     using P = PlanesCfg<N, IO>;
+    constexpr int S = P::S, R = P::R;
     __shared__ __attribute__((aligned(16))) char stage[P::LDS];
+    const bool is_dy = blockIdx.z != 0;
+    const IO* src = is_dy ? dy : x;
+    IO* planes = is_dy ? dyp : xp;
+    const int C = is_dy ? C_out : C_in;
+    const int c0 = (int)blockIdx.y * P::TC;
+    if (c0 >= C) return;  // uniform over the block: the grid spans the wider operand
     const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
-    const int64_t t0 = (int64_t)blockIdx.x * P::TT;
-    const int c0 = (int)blockIdx.y * P::TC, c = c0 + lane;
+    const int64_t t0 = (int64_t)blockIdx.x * P::TT, t = t0 + lane;
+    const int cw = c0 + wave * R;
+    const uint32_t row_bytes = (uint32_t)C * N * S;
+    const __amdgpu_buffer_rsrc_t rs = bw_rsrc(src, (uint32_t)(T * row_bytes));
+    const uint32_t off = t < T ? (uint32_t)t * row_bytes + (uint32_t)cw * N * S : kBwOOB;
+
+    uint32_t w[4 * N];  // R records: 16N bytes
+    if ((row_bytes & 15u) == 0) {
 #pragma unroll
-    for (int j = 0; j < P::TT / 4; ++j) {
-        const int tl = wave * (P::TT / 4) + j;
-        const int64_t t = t0 + tl;
-        float xv[N], Pv[N];
-        if (t < T && c < C) {
-            const IO* r = src + (t * C + c) * N;
-#pragma unroll
-            for (int h = 0; h < N; ++h) xv[h] = to_f32(r[h]);
-        } else {
-#pragma unroll
-            for (int h = 0; h < N; ++h) xv[h] = 0.0f;
+        for (int j = 0; j < N; ++j) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 16u * j, 0);
+            w[4 * j] = v[0]; w[4 * j + 1] = v[1]; w[4 * j + 2] = v[2]; w[4 * j + 3] = v[3];
         }
+    } else {
+#pragma unroll
+        for (int v = 0; v < R * N; ++v) {
+            uint32_t e;
+            if constexpr (S == 4) e = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 4u * v, 0);
+            else e = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 2u * v, 0);
+            if constexpr (S == 4) w[v] = e;
+            else if (v & 1) w[v >> 1] |= e << 16;
+            else w[v >> 1] = e;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float xv[N], Pv[N];
+#pragma unroll
+        for (int h = 0; h < N; ++h) xv[h] = plane_elem<IO>(w, r * N + h);
         rdft_forward<N>(xv, Pv);
 #pragma unroll
         for (int p = 0; p < N; ++p)
-            *reinterpret_cast<IO*>(stage + (p * P::TC + lane) * P::PITCH + tl * P::S) = (IO)Pv[p];
+            *reinterpret_cast<IO*>(stage + (p * P::TC + wave * R + r) * P::ROW + lane * S) = (IO)Pv[p];
     }
     __syncthreads();
-    for (int k = (int)threadIdx.x; k < N * P::TC * P::PIECES; k += 256) {
-        const int row = k / P::PIECES, piece = k % P::PIECES;
+    constexpr int RP = P::ROW / 16;  // pieces per row
+#pragma unroll
+    for (int k0 = 0; k0 < P::PIECES; k0 += 256) {
+        const int k = k0 + (int)threadIdx.x;
+        if (P::PIECES % 256 != 0 && k >= P::PIECES) break;
+        const int row = k / RP, piece = k % RP;
         const int p = row / P::TC, cl = row % P::TC;
         if (c0 + cl >= C) continue;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * P::PITCH + piece * 16);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * P::ROW + piece * 16);
         char* dst = reinterpret_cast<char*>(planes + ((int64_t)p * C + c0 + cl) * Tp + t0);
         *reinterpret_cast<u32x4*>(dst + piece * 16) = v;
     }
@@ -601,15 +640,27 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     }
     const int S = bf16 ? 2 : 4, KC = 64 / S;
     const int tm = 32 * bw_wg(C_in, C_out);
-    s.Tp = (T + 63) / 64 * 64;
+    // plane rows: a whole number of 64-token blocks whose byte length is an odd
+    // multiple of 256.  Rows of a power-of-two length (64 KiB at T = 32768 in
+    // bf16) all start at the same offset modulo the memory interleave, so the 64
+    // rows a workgroup streams would queue on the same channels.
+    const int64_t unit = 256 / S;  // tokens per 256 bytes
+    int64_t m = (T + unit - 1) / unit;
+    if (m % 2 == 0) ++m;
+    s.Tp = m * unit;
     s.n_o = (C_out + tm - 1) / tm;
     s.n_i = (C_in + tm - 1) / tm;
     s.tiles = s.n_o * s.n_i;
     s.nchunks = (int)(s.Tp / KC);
     // token ranges: enough waves to give every SIMD one (one-wave tiles, ranges
-    // down to one chunk) or every CU a workgroup (ranges of four chunks or more)
+    // down to one chunk) or every CU two workgroups (ranges of four chunks or
+    // more).  The product loop waits on its ring once per stage, and a second
+    // workgroup on the CU fills those waits: on MI355X 512 workgroups ran c4
+    // (C7, 160 -> 160, T = 32768) in 132 us against 174 at 256 and 149 at 1024
+    // (more ranges, more partial spectra to write and sum); a deeper ring at one
+    // workgroup per CU instead was slower still (252 us at nine stages).
     const bool small = bw_wg(C_in, C_out) == 1;
-    const int64_t want = ((small ? 1024 : 256) + s.tiles - 1) / s.tiles;
+    const int64_t want = ((small ? 1024 : 512) + s.tiles - 1) / s.tiles;
     const int64_t cap = small ? s.nchunks : s.nchunks / 4;
     int64_t sp = want < cap ? want : cap;
     sp = sp < 1 ? 1 : (sp > s.nchunks ? s.nchunks : sp);
@@ -638,11 +689,11 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
     IO* xp = reinterpret_cast<IO*>(ws);
     IO* dyp = reinterpret_cast<IO*>(ws + s.xp_bytes);
     float* part = reinterpret_cast<float*>(ws + s.xp_bytes + s.dyp_bytes);
-    constexpr int PT = PlanesCfg<N, IO>::TT;  // Tp is a multiple of 64, hence of PT
-    const dim3 gx((uint32_t)(s.Tp / PT), (uint32_t)((C_in + 63) / 64));
-    const dim3 gy((uint32_t)(s.Tp / PT), (uint32_t)((C_out + 63) / 64));
-    hipLaunchKernelGGL((bw_planes_kernel<N, IO>), gx, dim3(256), 0, stream, (const IO*)x, xp, T, C_in, s.Tp);
-    hipLaunchKernelGGL((bw_planes_kernel<N, IO>), gy, dim3(256), 0, stream, (const IO*)dy, dyp, T, C_out, s.Tp);
+    using PC = PlanesCfg<N, IO>;  // Tp is a multiple of 64 = PC::TT
+    const int cmax = C_in > C_out ? C_in : C_out;
+    const dim3 gp((uint32_t)(s.Tp / PC::TT), (uint32_t)((cmax + PC::TC - 1) / PC::TC), 2);
+    hipLaunchKernelGGL((bw_planes_kernel<N, IO>), gp, dim3(256), 0, stream, (const IO*)x, xp, C_in, (const IO*)dy,
+                       dyp, C_out, T, s.Tp);
     const int64_t wgs = (int64_t)s.tiles * s.splits;
     hipLaunchKernelGGL((bw_gemm_kernel<Cfg>), dim3((uint32_t)wgs), dim3(Cfg::kThreads), 0, stream,
                        (const IO*)dyp, (const IO*)xp, part, C_out, C_in, s.Tp, s.n_i, s.tiles,
@@ -709,7 +760,7 @@ hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const
     const int S = dtype_bf16 ? 2 : 4;
     if ((int64_t)N * C_in * s.Tp * S >= ((int64_t)1 << 31) || (int64_t)N * C_out * s.Tp * S >= ((int64_t)1 << 31))
         return hipErrorInvalidConfiguration;
-    if (s.Tp / 32 > 0x7fffffff || (C_in + 63) / 64 > 65535 || (C_out + 63) / 64 > 65535 ||
+    if (s.Tp / 64 > 0x7fffffff || (C_in + 7) / 8 > 65535 || (C_out + 7) / 8 > 65535 ||
         (int64_t)s.tiles * s.splits > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     char* ws = static_cast<char*>(workspace);
