@@ -80,24 +80,33 @@ __global__ __launch_bounds__(256) void w_hat_adjoint_kernel(const IO* __restrict
 
 // --- 1. planes ------------------------------------------------------------------------
 // Block: 64 tokens (one per lane) x TC = 4R channels (R per wave, R = 16/S, so a
-// lane's R records are 16N contiguous bytes: N 16-byte loads when every token
-// row, C N S bytes, is a whole number of 16-byte pieces, else one load per
-// element).  The lane transforms its records in fp32 and writes each plane
-// value to LDS rows [plane][channel][token], where the 64 lanes fill one
-// contiguous row (no bank conflicts); the block then writes each (plane,
-// channel) row segment of 64 tokens as 16-byte pieces, a 16-lane group reading
-// two or more whole rows.  Tokens T .. Tp-1 lie past the input's buffer range
-// and come out as zeros.  x and dy go through the same launch (blockIdx.z).
-// Channels past C belong to the next token's row (or to nothing) and are
-// transformed but never written.
+// lane's R records are 16N contiguous bytes).  When every token row (C N S
+// bytes) is a whole number of 16-byte pieces, the block first copies its 64
+// token segments of TC records (4N pieces each) into LDS with consecutive
+// lanes on consecutive pieces (coalesced), at a row pitch of an odd number of
+// pieces so that the lanes' reads of their own token's records do not collide;
+// otherwise each lane loads its elements one by one.  The lane transforms its
+// records in fp32 and writes each plane value to LDS rows [plane][channel]
+// [token] (the raw tile's space, after a barrier), where the 64 lanes fill one
+// contiguous row; the block then writes each (plane, channel) row segment of
+// 64 tokens as 16-byte pieces.  Tokens T .. Tp-1 lie past the input's buffer
+// range and come out as zeros.  x and dy go through the same launch
+// (blockIdx.z).  Channels past C belong to the next token's row (or to
+// nothing) and are transformed but never written.  (Measured on MI355X: blocks
+// of 128 or 256 tokens, for longer store segments, were no faster.)
 template <int N, typename IO>
 struct PlanesCfg {
     static constexpr int S = (int)sizeof(IO);
     static constexpr int R = 16 / S;           // channels per lane
     static constexpr int TT = 64, TC = 4 * R;  // tokens and channels per block
     static constexpr int ROW = TT * S;         // bytes of one (plane, channel) row segment
-    static constexpr int LDS = N * TC * ROW;
-    static constexpr int PIECES = LDS / 16;
+    static constexpr int PLANES = N * TC * ROW;
+    static constexpr int PPT = 4 * N;              // 16-byte pieces of a token's TC records
+    static constexpr int RAW_PITCH = (PPT + 1) * 16;
+    static constexpr int RAW = TT * RAW_PITCH;
+    static constexpr int LDS = PLANES > RAW ? PLANES : RAW;
+    static constexpr int PIECES = PLANES / 16;
+    static_assert(TC * N * S == PPT * 16, "a token's TC records are 4N pieces");
 };
 
 template <typename IO>
@@ -128,11 +137,26 @@ __global__ __launch_bounds__(256) void bw_planes_kernel(const IO* __restrict__ x
 
     uint32_t w[4 * N];  // R records: 16N bytes
     if ((row_bytes & 15u) == 0) {
+        u32x4 v[N];
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 16u * j, 0);
-            w[4 * j] = v[0]; w[4 * j + 1] = v[1]; w[4 * j + 2] = v[2]; w[4 * j + 3] = v[3];
+            const int k = j * 256 + (int)threadIdx.x, tok = k / P::PPT, pc = k % P::PPT;
+            const uint32_t o = t0 + tok < T ? (uint32_t)(t0 + tok) * row_bytes + (uint32_t)(c0 * N * S + pc * 16)
+                                            : kBwOOB;
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0);
         }
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int k = j * 256 + (int)threadIdx.x, tok = k / P::PPT, pc = k % P::PPT;
+            *reinterpret_cast<u32x4*>(stage + tok * P::RAW_PITCH + pc * 16) = v[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const u32x4 e = *reinterpret_cast<const u32x4*>(stage + lane * P::RAW_PITCH + (wave * N + j) * 16);
+            w[4 * j] = e[0]; w[4 * j + 1] = e[1]; w[4 * j + 2] = e[2]; w[4 * j + 3] = e[3];
+        }
+        __syncthreads();  // the planes reuse the raw tile's space
     } else {
 #pragma unroll
         for (int v = 0; v < R * N; ++v) {
