@@ -40,6 +40,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bw_rsrc(const void* base, uint
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Stride of one plane of the partial spectra [split][plane][o][i]: C_out C_in
+// rounded up to a multiple of four, so that the reduction reads 16-byte groups.
+__host__ __device__ constexpr int64_t bw_pstride(int C_in, int C_out) {
+    return ((int64_t)C_out * C_in + 3) / 4 * 4;
+}
+
 // s_waitcnt immediate: vmcnt <= n, lgkmcnt and expcnt unconstrained.
 constexpr int bw_vmcnt(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
@@ -384,7 +390,7 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
     }
 
     // partial spectra of this token range: part[split][p][o][i]
-    const int64_t plane = (int64_t)C_out * C_in;
+    const int64_t plane = bw_pstride(C_in, C_out);  // partial planes padded to whole 16-byte groups
     float* dst = part + (int64_t)split * N * plane;
 #pragma unroll
     for (int ob = 0; ob < 2; ++ob)
@@ -548,7 +554,7 @@ __global__ __launch_bounds__(256) void bw_small_kernel(const IO* __restrict__ x,
         __syncthreads();  // the next chunk's planes overwrite these
     }
 
-    const int64_t plane = (int64_t)C_out * C_in;
+    const int64_t plane = bw_pstride(C_in, C_out);  // partial planes padded to whole 16-byte groups
     float* dst = part + (int64_t)split * N * plane;
     static_for<0, N / 2 + 1>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
@@ -574,35 +580,44 @@ __global__ __launch_bounds__(256) void bw_small_kernel(const IO* __restrict__ x,
 }
 
 // --- 3. reduction and inverse transform ------------------------------------------------
-// Block: 32 consecutive (o, i) elements x N planes x R lanes (R = 1024 / 32N, at
-// most 8).  Lane r of (p, e) sums the r-th contiguous sub-range of the splits in
-// order, sixteen loads in flight; the R sub-sums are added in lane order.  The
-// order is fixed, so the result is deterministic.  Then one thread per element
-// runs the inverse real DFT of its packed spectrum and writes dw[o][i][0 .. N-1].
-template <int N>
+// Block: 32 G consecutive (o, i) elements (G per lane: 16-byte loads for G = 4,
+// taken where the plane gives at least 64 such blocks; G = 1 for small planes,
+// whose few blocks would otherwise leave most CUs idle) x N planes x R lanes
+// (R = 1024 / 32N, at most 8).  Lane r of (p, group) sums the r-th contiguous
+// sub-range of the splits in order, sixteen loads in flight; the R sub-sums
+// are added in lane order.  The order is fixed, so the result is
+// deterministic.  Then one thread per element runs the inverse real DFT of its
+// packed spectrum and writes dw[o][i][0 .. N-1].
+template <int N, int G>
 struct BwReduceCfg {
     static constexpr int R0 = 1024 / (32 * N);
     static constexpr int R = R0 > 8 ? 8 : R0;
     static constexpr int kThreads = 32 * N * R;
+    static constexpr int EL = 32 * G;  // elements per block
+    using V = std::conditional_t<G == 4, f32x4, float>;
+    static_assert(G == 1 || G == 4, "one element or a 16-byte group per lane");
+    static_assert(kThreads >= EL, "a thread per element for the inverse transform");
 };
 
-template <int N>
-__global__ __launch_bounds__(BwReduceCfg<N>::kThreads) void bw_reduce_kernel(const float* __restrict__ part,
-                                                                             float* __restrict__ dw, int splits,
-                                                                             int64_t plane) {
-    constexpr int R = BwReduceCfg<N>::R;
-    __shared__ float red[R][32][N + 1];
-    const int el = (int)threadIdx.x & 31, p = ((int)threadIdx.x >> 5) % N, r = (int)threadIdx.x / (32 * N);
-    const int64_t e = (int64_t)blockIdx.x * 32 + el;
+template <int N, int G>
+__global__ __launch_bounds__((BwReduceCfg<N, G>::kThreads)) void bw_reduce_kernel(const float* __restrict__ part,
+                                                                                float* __restrict__ dw, int splits,
+                                                                                int64_t plane, int64_t pstride) {
+    using RC = BwReduceCfg<N, G>;
+    using V = typename RC::V;
+    constexpr int R = RC::R;
+    __shared__ V red[R][32][N];
+    const int g = (int)threadIdx.x & 31, p = ((int)threadIdx.x >> 5) % N, r = (int)threadIdx.x / (32 * N);
+    const int64_t e0 = (int64_t)blockIdx.x * RC::EL + G * g;
     const int len = (splits + R - 1) / R;
     const int s0 = r * len, s1 = s0 + len < splits ? s0 + len : splits;
-    float v = 0.0f;
-    if (e < plane) {
-        const float* src = part + (int64_t)p * plane + e;
-        const int64_t step = (int64_t)N * plane;
+    V v = {};
+    if (e0 < pstride) {  // pstride is a multiple of 4: a group lies inside the padded plane
+        const V* src = reinterpret_cast<const V*>(part + (int64_t)p * pstride + e0);
+        const int64_t step = (int64_t)N * pstride / G;
         int s = s0;
         for (; s + 16 <= s1; s += 16) {
-            float t[16];
+            V t[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) t[j] = src[(int64_t)(s + j) * step];
 #pragma unroll
@@ -610,20 +625,40 @@ __global__ __launch_bounds__(BwReduceCfg<N>::kThreads) void bw_reduce_kernel(con
         }
         for (; s < s1; ++s) v += src[(int64_t)s * step];
     }
-    red[r][el][p] = v;
+    red[r][g][p] = v;
     __syncthreads();
-    if (r == 0 && p == 0 && e < plane) {
+    const int q = (int)threadIdx.x;  // element of the block
+    const int64_t e = (int64_t)blockIdx.x * RC::EL + q;
+    if (q < RC::EL && e < plane) {
+        auto comp = [&](const V& w) {
+            if constexpr (G == 4) return w[q & 3];
+            else return w;
+        };
         float P[N], y[N];
 #pragma unroll
-        for (int q = 0; q < N; ++q) {
-            float sum = red[0][el][q];
+        for (int k = 0; k < N; ++k) {
+            float sum = comp(red[0][q / G][k]);
 #pragma unroll
-            for (int rr = 1; rr < R; ++rr) sum += red[rr][el][q];
-            P[q] = sum;
+            for (int rr = 1; rr < R; ++rr) sum += comp(red[rr][q / G][k]);
+            P[k] = sum;
         }
         rdft_inverse<N>(P, y);
 #pragma unroll
         for (int m = 0; m < N; ++m) dw[e * N + m] = y[m];
+    }
+}
+
+template <int N>
+void launch_bw_reduce(const float* part, float* dw, int splits, int64_t plane, int64_t pstride,
+                      hipStream_t stream) {
+    if (plane >= 64 * BwReduceCfg<N, 4>::EL) {
+        using RC = BwReduceCfg<N, 4>;
+        hipLaunchKernelGGL((bw_reduce_kernel<N, 4>), dim3((uint32_t)((plane + RC::EL - 1) / RC::EL)),
+                           dim3(RC::kThreads), 0, stream, part, dw, splits, plane, pstride);
+    } else {
+        using RC = BwReduceCfg<N, 1>;
+        hipLaunchKernelGGL((bw_reduce_kernel<N, 1>), dim3((uint32_t)((plane + RC::EL - 1) / RC::EL)),
+                           dim3(RC::kThreads), 0, stream, part, dw, splits, plane, pstride);
     }
 }
 
@@ -658,7 +693,7 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
         sp = sp < 1 ? 1 : (sp > 256 ? 256 : sp);
         s.chunks_per_split = (s.nchunks + sp - 1) / sp;
         s.splits = (s.nchunks + s.chunks_per_split - 1) / s.chunks_per_split;
-        s.part_bytes = round256((size_t)s.splits * N * C_out * C_in * 4);
+        s.part_bytes = round256((size_t)s.splits * N * bw_pstride(C_in, C_out) * 4);
         s.total = s.part_bytes;
         return s;
     }
@@ -692,7 +727,7 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     s.splits = (s.nchunks + s.chunks_per_split - 1) / s.chunks_per_split;
     s.xp_bytes = round256((size_t)N * C_in * s.Tp * S);
     s.dyp_bytes = round256((size_t)N * C_out * s.Tp * S);
-    s.part_bytes = round256((size_t)s.splits * N * C_out * C_in * 4);
+    s.part_bytes = round256((size_t)s.splits * N * bw_pstride(C_in, C_out) * 4);
     s.total = s.xp_bytes + s.dyp_bytes + s.part_bytes;
     return s;
 }
@@ -701,13 +736,12 @@ template <int N, typename IO, int WG>
 hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t T, int C_in, int C_out,
                                char* ws, const BwShape& s, hipStream_t stream) {
     using Cfg = BwCfg<N, IO, WG>;
-    const int64_t plane = (int64_t)C_out * C_in;
+    const int64_t plane = (int64_t)C_out * C_in, pstride = bw_pstride(C_in, C_out);
     if (s.fused) {
         float* part = reinterpret_cast<float*>(ws);
         hipLaunchKernelGGL((bw_small_kernel<N, IO>), dim3((uint32_t)s.splits), dim3(256), 0, stream, (const IO*)x,
                            (const IO*)dy, part, T, C_in, C_out, s.chunks_per_split, s.nchunks);
-        hipLaunchKernelGGL((bw_reduce_kernel<N>), dim3((uint32_t)((plane + 31) / 32)),
-                           dim3(BwReduceCfg<N>::kThreads), 0, stream, (const float*)part, dw, s.splits, plane);
+        launch_bw_reduce<N>(part, dw, s.splits, plane, pstride, stream);
         return hipGetLastError();
     }
     IO* xp = reinterpret_cast<IO*>(ws);
@@ -722,8 +756,7 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
     hipLaunchKernelGGL((bw_gemm_kernel<Cfg>), dim3((uint32_t)wgs), dim3(Cfg::kThreads), 0, stream,
                        (const IO*)dyp, (const IO*)xp, part, C_out, C_in, s.Tp, s.n_i, s.tiles,
                        s.chunks_per_split, s.nchunks);
-    hipLaunchKernelGGL((bw_reduce_kernel<N>), dim3((uint32_t)((plane + 31) / 32)),
-                       dim3(BwReduceCfg<N>::kThreads), 0, stream, (const float*)part, dw, s.splits, plane);
+    launch_bw_reduce<N>(part, dw, s.splits, plane, pstride, stream);
     return hipGetLastError();
 }
 
