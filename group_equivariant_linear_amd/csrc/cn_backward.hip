@@ -408,6 +408,167 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
         }
 }
 
+// --- 2'. per-bin products over whole tiles ---------------------------------------------
+// Workgroup: one bin, one (o, i) tile of WM x WN waves (32 x 64 outputs per wave,
+// up to 16 waves), one range of tokens.  The tile spans as much of C_out x C_in
+// as the waves cover (all of it for 160 x 160), so each operand plane is read
+// once per tile column or row instead of once per 64-wide tile, and a bin's
+// workgroup reads only the bin's planes.  Stage q holds chunk q of the range:
+// the bin's planes (real and imaginary part, or the one real plane) of the
+// tile's TM dy rows (A) and TN x rows (B), each row 64 bytes, rows in LDS order
+// [A re][A im][B re][B im]; L direct 16-byte loads per thread fill a stage
+// (slots past the stage's rows, and planes a real bin lacks, read as zeros).
+// Three stages in flight round a ring; the stage size is a run-time value.
+template <int N_, typename IO_>
+struct BinCfg {
+    static constexpr int N = N_;
+    using IO = IO_;
+    static constexpr int S = (int)sizeof(IO);
+    static constexpr int H = (N - 1) / 2;
+    static constexpr int ST = 3;                // ring stages
+    static constexpr int kMaxStage = 53248;     // bytes: ST stages fit the CU's LDS
+};
+constexpr int kBinMaxL = 4;  // direct loads per thread and stage
+
+template <class C>
+__global__ __launch_bounds__(1024) void bw_bin_kernel(const char* __restrict__ ws, uint32_t xp_bytes,
+                                                      uint32_t span, float* __restrict__ part, int C_out,
+                                                      int C_in, int64_t Tp, int WM, int WN, int n_o, int n_i,
+                                                      int nb, int L, int stage_bytes, int chunks_per_split,
+                                                      int nchunks, int64_t pstride) {
+    using IO = typename C::IO;
+    using F = typename BwFrag<IO>::T;
+    constexpr int N = C::N, H = C::H, ST = C::ST, S = C::S;
+    __shared__ __attribute__((aligned(16))) char smem[ST * C::kMaxStage];
+
+    const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int ti = (int)(lb % (uint32_t)n_i);
+    const int to = (int)((lb / (uint32_t)n_i) % (uint32_t)n_o);
+    const uint32_t rest = lb / (uint32_t)(n_i * n_o);
+    const int bin = (int)(rest % (uint32_t)nb), split = (int)(rest / (uint32_t)nb);
+    const int TM = 32 * WM, TN = 64 * WN;
+    const int o0 = to * TM, i0 = ti * TN;
+    const bool cplx = bin >= 1 && bin <= H;
+    const int p0 = bin == 0 ? 0 : (bin <= H ? 2 * bin - 1 : N - 1);
+    const int c_begin = split * chunks_per_split;
+    const int c_end = c_begin + chunks_per_split < nchunks ? c_begin + chunks_per_split : nchunks;
+    const int nq = c_end - c_begin;
+
+    const int threads = 64 * WM * WN;
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    // one resource over both plane sets: x planes at 0, dy planes at xp_bytes
+    const __amdgpu_buffer_rsrc_t rw = bw_rsrc(ws, span);
+    const uint32_t row_bytes = (uint32_t)(Tp * S);
+    const int slots = 8 * (TM + TN);
+    uint32_t off[kBinMaxL];
+#pragma unroll
+    for (int l = 0; l < kBinMaxL; ++l) {
+        const int slot = l * threads + tid, u = slot & 3, rid = slot >> 2;
+        uint32_t o = kBwOOB;
+        if (l < L && slot < slots) {
+            if (rid < 2 * TM) {
+                const int pa = rid / TM, r = o0 + rid % TM;
+                if (r < C_out && (pa == 0 || cplx))
+                    o = xp_bytes + ((uint32_t)(p0 + pa) * (uint32_t)C_out + (uint32_t)r) * row_bytes + 16u * u;
+            } else {
+                const int rb = rid - 2 * TM, pb = rb / TN, r = i0 + rb % TN;
+                if (r < C_in && (pb == 0 || cplx))
+                    o = ((uint32_t)(p0 + pb) * (uint32_t)C_in + (uint32_t)r) * row_bytes + 16u * u;
+            }
+        }
+        off[l] = o;
+    }
+
+    auto dma = [&](int q) {
+        char* st = smem + (q % ST) * stage_bytes;
+        const bool live = q < nq;
+        const uint32_t soff = live ? (uint32_t)(c_begin + q) * 64u : 0u;
+#pragma unroll
+        for (int l = 0; l < kBinMaxL; ++l) {
+            if (l < L)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (__attribute__((address_space(3))) void*)(st + (l * threads + wave * 64) * 16), 16,
+                    live ? off[l] : kBwOOB, soff, 0, 0);
+        }
+    };
+    // this thread's loads of stage q are done once at most (ST - 2) L remain
+    auto wait_stage = [&]() {
+        switch (L) {
+            case 1: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 1)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 2)); break;
+            case 3: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 3)); break;
+            default: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 4)); break;
+        }
+    };
+
+    f32x4 acc[2][4][2];
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) acc[ob][ib][0] = acc[ob][ib][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int frag_off = (lane & 15) * 64 + (lane >> 4) * 16;
+    auto frag = [&](const char* region, int row) {
+        return *reinterpret_cast<const F*>(region + row * 64 + frag_off);
+    };
+
+#pragma unroll
+    for (int q = 0; q < ST - 1; ++q) dma(q);
+    for (int q = 0; q < nq; ++q) {
+        wait_stage();
+        asm volatile("s_barrier" ::: "memory");
+        dma(q + ST - 1);
+        const char* st = smem + (q % ST) * stage_bytes;
+        const char* sb = st + 2 * TM * 64;
+        F A0[2], B0[4];
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob) A0[ob] = frag(st, wm * 32 + ob * 16);
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) B0[ib] = frag(sb, wn * 64 + ib * 16);
+        if (cplx) {
+            F A1[2];
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob) A1[ob] = frag(st, TM + wm * 32 + ob * 16);
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                const F B1 = frag(sb, TN + wn * 64 + ib * 16), nB1 = bw_neg(B1);
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob) {
+                    bw_mma(acc[ob][ib][0], A0[ob], B0[ib]);   // a c
+                    bw_mma(acc[ob][ib][1], A1[ob], B0[ib]);   // b c
+                    bw_mma(acc[ob][ib][0], A1[ob], B1);       // + b d
+                    bw_mma(acc[ob][ib][1], A0[ob], nB1);      // - a d
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) bw_mma(acc[ob][ib][0], A0[ob], B0[ib]);
+        }
+    }
+
+    // this bin's partial planes of this token range: part[split][p][o][i]
+    float* dst = part + (int64_t)split * N * pstride;
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+            const int i = i0 + wn * 64 + ib * 16 + (lane & 15);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int o = o0 + wm * 32 + ob * 16 + 4 * (lane >> 4) + rr;
+                if (o < C_out && i < C_in) {
+                    dst[(int64_t)p0 * pstride + (int64_t)o * C_in + i] = acc[ob][ib][0][rr];
+                    if (cplx) dst[(int64_t)(p0 + 1) * pstride + (int64_t)o * C_in + i] = acc[ob][ib][1][rr];
+                }
+            }
+        }
+}
+
 // --- small layers: transforms and products in one launch ---------------------------------
 // For C_in, C_out <= 32 the plane round trip through HBM and the launches around
 // it dominate, so a workgroup (4 waves) does both steps for its token chunks
@@ -664,12 +825,41 @@ void launch_bw_reduce(const float* part, float* dw, int splits, int64_t plane, i
 
 // --- host side ---------------------------------------------------------------------------
 
+#ifndef EQL_BW_BIN
+#define EQL_BW_BIN 1
+#endif
+
 struct BwShape {
     int64_t Tp;
     int n_o, n_i, tiles, nchunks, splits, chunks_per_split;
     bool fused;  // small layers: transforms and products in one launch, no planes
+    bool bin;    // products per bin over whole tiles (bw_bin_kernel)
+    int WM, WN, nb, L, stage_bytes;
     size_t xp_bytes, dyp_bytes, part_bytes, total;
 };
+
+// Tile of the bin-major product kernel: WM x WN waves of 32 x 64 outputs (at most
+// 16 waves, one stage of at most kMaxStage bytes), the tile counts that stream
+// the fewest plane rows per token (n_i C_out + n_o C_in).  False if none fits.
+bool bw_bin_tile(int C_in, int C_out, BwShape& s) {
+    const int WMt = (C_out + 31) / 32, WNt = (C_in + 63) / 64;
+    int64_t best = -1;
+    for (int no = 1; no <= WMt; ++no)
+        for (int ni = 1; ni <= WNt; ++ni) {
+            const int WM = (WMt + no - 1) / no, WN = (WNt + ni - 1) / ni;
+            if (WM * WN > 16) continue;
+            const int threads = 64 * WM * WN, slots = 8 * (32 * WM + 64 * WN);
+            const int L = (slots + threads - 1) / threads;
+            if (L > kBinMaxL || L * threads * 16 > BinCfg<1, float>::kMaxStage) continue;
+            const int n_o = (C_out + 32 * WM - 1) / (32 * WM), n_i = (C_in + 64 * WN - 1) / (64 * WN);
+            const int64_t cost = (int64_t)n_i * C_out + (int64_t)n_o * C_in;
+            if (best < 0 || cost < best) {
+                best = cost;
+                s.WM = WM; s.WN = WN; s.n_o = n_o; s.n_i = n_i; s.L = L; s.stage_bytes = L * threads * 16;
+            }
+        }
+    return best >= 0;
+}
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
@@ -699,6 +889,8 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     }
     const int S = bf16 ? 2 : 4, KC = 64 / S;
     const int tm = 32 * bw_wg(C_in, C_out);
+    const int H = (N - 1) / 2;
+    s.nb = 1 + H + ((N % 2 == 0 && N > 1) ? 1 : 0);
     // plane rows: a whole number of 64-token blocks whose byte length is an odd
     // multiple of 256.  Rows of a power-of-two length (64 KiB at T = 32768 in
     // bf16) all start at the same offset modulo the memory interleave, so the 64
@@ -707,10 +899,27 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     int64_t m = (T + unit - 1) / unit;
     if (m % 2 == 0) ++m;
     s.Tp = m * unit;
+    s.nchunks = (int)(s.Tp / KC);
+    s.bin = EQL_BW_BIN != 0 && bw_bin_tile(C_in, C_out, s);
+    if (s.bin) {
+        // one workgroup per CU (the ring takes most of its LDS): bins x tiles x
+        // token ranges of at least two chunks, about 256 in all
+        s.tiles = s.n_o * s.n_i;
+        const int64_t per = (int64_t)s.nb * s.tiles;
+        int64_t sp = (256 + per - 1) / per;
+        const int64_t cap = s.nchunks / 2 > 0 ? s.nchunks / 2 : 1;
+        sp = sp < 1 ? 1 : (sp > cap ? cap : sp);
+        s.chunks_per_split = (int)((s.nchunks + sp - 1) / sp);
+        s.splits = (s.nchunks + s.chunks_per_split - 1) / s.chunks_per_split;
+        s.xp_bytes = round256((size_t)N * C_in * s.Tp * S);
+        s.dyp_bytes = round256((size_t)N * C_out * s.Tp * S);
+        s.part_bytes = round256((size_t)s.splits * N * bw_pstride(C_in, C_out) * 4);
+        s.total = s.xp_bytes + s.dyp_bytes + s.part_bytes;
+        return s;
+    }
     s.n_o = (C_out + tm - 1) / tm;
     s.n_i = (C_in + tm - 1) / tm;
     s.tiles = s.n_o * s.n_i;
-    s.nchunks = (int)(s.Tp / KC);
     // token ranges: enough waves to give every SIMD one (one-wave tiles, ranges
     // down to one chunk) or every CU two workgroups (ranges of four chunks or
     // more).  The product loop waits on its ring once per stage, and a second
@@ -752,6 +961,16 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
     const dim3 gp((uint32_t)(s.Tp / PC::TT), (uint32_t)((cmax + PC::TC - 1) / PC::TC), 2);
     hipLaunchKernelGGL((bw_planes_kernel<N, IO>), gp, dim3(256), 0, stream, (const IO*)x, xp, C_in, (const IO*)dy,
                        dyp, C_out, T, s.Tp);
+    if (s.bin) {
+        using BC = BinCfg<N, IO>;
+        const int64_t bwgs = (int64_t)s.nb * s.tiles * s.splits;
+        hipLaunchKernelGGL((bw_bin_kernel<BC>), dim3((uint32_t)bwgs), dim3(64 * s.WM * s.WN), 0, stream,
+                           (const char*)ws, (uint32_t)s.xp_bytes, (uint32_t)(s.xp_bytes + s.dyp_bytes), part, C_out,
+                           C_in, s.Tp, s.WM, s.WN, s.n_o, s.n_i, s.nb, s.L, s.stage_bytes, s.chunks_per_split,
+                           s.nchunks, pstride);
+        launch_bw_reduce<N>(part, dw, s.splits, plane, pstride, stream);
+        return hipGetLastError();
+    }
     const int64_t wgs = (int64_t)s.tiles * s.splits;
     hipLaunchKernelGGL((bw_gemm_kernel<Cfg>), dim3((uint32_t)wgs), dim3(Cfg::kThreads), 0, stream,
                        (const IO*)dyp, (const IO*)xp, part, C_out, C_in, s.Tp, s.n_i, s.tiles,
@@ -815,7 +1034,8 @@ hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const
     if (workspace_bytes < s.total) return hipErrorInvalidValue;
     // 32-bit buffer offsets over each operand's planes; grid dimensions
     const int S = dtype_bf16 ? 2 : 4;
-    if ((int64_t)N * C_in * s.Tp * S >= ((int64_t)1 << 31) || (int64_t)N * C_out * s.Tp * S >= ((int64_t)1 << 31))
+    if ((int64_t)N * C_in * s.Tp * S >= ((int64_t)1 << 31) || (int64_t)N * C_out * s.Tp * S >= ((int64_t)1 << 31) ||
+        (s.bin && s.xp_bytes + s.dyp_bytes >= ((size_t)1 << 31)))
         return hipErrorInvalidConfiguration;
     if (s.Tp / 64 > 0x7fffffff || (C_in + 7) / 8 > 65535 || (C_out + 7) / 8 > 65535 ||
         (int64_t)s.tiles * s.splits > 0x7fffffff)

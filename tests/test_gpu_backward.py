@@ -156,6 +156,22 @@ def test_backward_weight_small_layers_many_chunks(eq, N, C_in, C_out, dt):
 
 
 @pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("N", [1, 2, 3, 7, 8, 16])
+def test_backward_weight_whole_tile_bins(eq, N, dt):
+    """Wide layers whose (o, i) tile fits one workgroup of up to 16 waves take the
+    per-bin product kernel (one bin, whole tile, range of tokens per workgroup):
+    ragged tile edges on both axes (150 -> 140), exact ones (160 -> 160), and
+    two tiles along o (96 -> 384) or i (384 -> 96).  Also deterministic."""
+    for C_in, C_out, T in [(150, 140, 77), (160, 160, 300), (96, 384, 130), (384, 96, 64)]:
+        d = _inputs(N, C_in, C_out, T, dt, seed=3 * N + C_in)
+        dw = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
+        ref = oracle.cn_backward_weight(d["x64"], d["dy64"])
+        assert_close(dw, ref, dt, f"dw N={N} {dt} {C_in}->{C_out} T={T}")
+        if C_in == 150:
+            assert np.array_equal(dw, run_backward_weight(eq, N, C_in, C_out, T, dt, d))
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
 def test_gradients_satisfy_the_adjoint_identity(eq, dt):
     """<dy, y(x)> = <dx, x> = <dw, w> with all three computed on the GPU."""
     import torch
