@@ -18,11 +18,15 @@
 // a contraction over tokens for every kept bin (complex bins: Re C = a c + b d,
 // Im C = b c - a d with DY = a + ib, X = c + id).  Three launches:
 //   1. bw_planes_kernel: real DFT of every record of x and of dy, written as
-//      planes [plane][channel][token] (tokens contiguous, padded to Tp) through
-//      an LDS transpose, so that reads and writes are both contiguous runs;
-//   2. bw_gemm_kernel: per 64 x 64 (o, i) tile and range of tokens, all bins'
-//      products on the matrix cores with the operand planes streamed through
-//      an LDS ring by direct global->LDS loads; fp32 partial spectra per range;
+//      planes in chunk-major order [plane][chunk][channel][KC tokens] (64
+//      bytes per channel and chunk; tokens padded to Tp), through an LDS
+//      transpose.  A product stage, one chunk of some rows of one plane, then
+//      reads a few contiguous runs of C x 64 bytes, not one 64-byte piece per
+//      row from rows Tp S bytes apart (each piece a DRAM page of its own);
+//   2. bw_bin_kernel (whole tiles, one bin per workgroup) or bw_gemm_kernel
+//      (64 x 64 tiles, all bins): per tile and range of tokens, the products on
+//      the matrix cores with the operand planes streamed through an LDS ring by
+//      direct global->LDS loads; fp32 partial spectra per range;
 //   3. bw_reduce_kernel: partials summed in a fixed order, inverse real DFT
 //      per (o, i), dw written in fp32 [C_out][C_in][N].
 // Every step is deterministic (no atomics).
@@ -112,7 +116,9 @@ struct PlanesCfg {
     static constexpr int RAW = TT * RAW_PITCH;
     static constexpr int LDS = PLANES > RAW ? PLANES : RAW;
     static constexpr int PIECES = PLANES / 16;
+    static constexpr int KC = 64 / S;              // tokens of a plane chunk: 64 bytes
     static_assert(TC * N * S == PPT * 16, "a token's TC records are 4N pieces");
+    static_assert(TT % KC == 0, "a block covers whole chunks");
 };
 
 template <typename IO>
@@ -194,8 +200,11 @@ __global__ __launch_bounds__(256) void bw_planes_kernel(const IO* __restrict__ x
         const int p = row / P::TC, cl = row % P::TC;
         if (c0 + cl >= C) continue;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * P::ROW + piece * 16);
-        char* dst = reinterpret_cast<char*>(planes + ((int64_t)p * C + c0 + cl) * Tp + t0);
-        *reinterpret_cast<u32x4*>(dst + piece * 16) = v;
+        // chunk-major: [plane][chunk of KC tokens][channel][KC tokens]
+        const int64_t tk = t0 + piece * (16 / S), chunk = tk / P::KC;
+        char* dst = reinterpret_cast<char*>(planes) +
+                    (((int64_t)p * (Tp / P::KC) + chunk) * C + c0 + cl) * 64 + (tk % P::KC) * S;
+        *reinterpret_cast<u32x4*>(dst) = v;
     }
 }
 
@@ -288,8 +297,8 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
 #pragma unroll
     for (int l = 0; l < C::PL; ++l) {
         const int slot = l * C::kThreads + tid, r = slot >> 2, u = slot & 3;
-        offa[l] = o0 + r < C_out ? (uint32_t)(o0 + r) * row_bytes + (uint32_t)u * 16u : kBwOOB;
-        offb[l] = i0 + r < C_in ? (uint32_t)(i0 + r) * row_bytes + (uint32_t)u * 16u : kBwOOB;
+        offa[l] = o0 + r < C_out ? (uint32_t)(o0 + r) * 64u + (uint32_t)u * 16u : kBwOOB;
+        offb[l] = i0 + r < C_in ? (uint32_t)(i0 + r) * 64u + (uint32_t)u * 16u : kBwOOB;
     }
 
     // planes of bin b: first (real part, or the only plane), second (imaginary)
@@ -300,7 +309,8 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
         const int cq = live ? c_begin + q / NB : 0, b = live ? q % NB : 0;
         const int p0 = plane0(b);
         const bool cplx = b >= 1 && b <= H;
-        const uint32_t soff = (uint32_t)cq * 64u;  // KC tokens = 64 bytes along a row
+        // chunk cq of every plane row: C x 64 bytes per chunk (chunk-major planes)
+        const uint32_t soffa = (uint32_t)cq * (uint32_t)C_out * 64u, soffb = (uint32_t)cq * (uint32_t)C_in * 64u;
         // every thread issues LOADS loads for every stage, so vmcnt counts stages
 #pragma unroll
         for (int l = 0; l < C::PL; ++l) {
@@ -310,13 +320,13 @@ __global__ __launch_bounds__(C::kThreads) void bw_gemm_kernel(const typename C::
             const uint32_t b1 = live && cplx && offb[l] != kBwOOB ? b0 + pb : kBwOOB;
             char* d = st + (l * C::kThreads + wave * 64) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(d), 16, a0,
-                                                     soff, 0, 0);
+                                                     soffa, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(d + C::PBYTES), 16,
-                                                     a1, soff, 0, 0);
+                                                     a1, soffa, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (__attribute__((address_space(3))) void*)(d + 2 * C::PBYTES), 16, b0, soff, 0, 0);
+                rb, (__attribute__((address_space(3))) void*)(d + 2 * C::PBYTES), 16, b0, soffb, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (__attribute__((address_space(3))) void*)(d + 3 * C::PBYTES), 16, b1, soff, 0, 0);
+                rb, (__attribute__((address_space(3))) void*)(d + 3 * C::PBYTES), 16, b1, soffb, 0, 0);
         }
     };
 
@@ -434,18 +444,28 @@ template <class C>
 __global__ __launch_bounds__(1024) void bw_bin_kernel(const char* __restrict__ ws, uint32_t xp_bytes,
                                                       uint32_t span, float* __restrict__ part, int C_out,
                                                       int C_in, int64_t Tp, int WM, int WN, int n_o, int n_i,
-                                                      int nb, int L, int stage_bytes, int chunks_per_split,
-                                                      int nchunks, int64_t pstride) {
+                                                      int nb, int L, int stage_bytes, int splits_c, int cps_c,
+                                                      int cps_r, int nchunks, int64_t pstride) {
     using IO = typename C::IO;
     using F = typename BwFrag<IO>::T;
     constexpr int N = C::N, H = C::H, ST = C::ST, S = C::S;
     __shared__ __attribute__((aligned(16))) char smem[ST * C::kMaxStage];
 
+    // workgroups of the complex bins first (splits_c token ranges of cps_c chunks
+    // each), then those of the real bins (DC, Nyquist: half the bytes and a
+    // quarter of the products per chunk, so ranges of cps_r ~ 2 cps_c chunks)
     const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
-    const int ti = (int)(lb % (uint32_t)n_i);
-    const int to = (int)((lb / (uint32_t)n_i) % (uint32_t)n_o);
-    const uint32_t rest = lb / (uint32_t)(n_i * n_o);
-    const int bin = (int)(rest % (uint32_t)nb), split = (int)(rest / (uint32_t)nb);
+    const uint32_t tiles = (uint32_t)(n_i * n_o), ncw = (uint32_t)H * tiles * (uint32_t)splits_c;
+    const bool cw = lb < ncw;
+    const uint32_t t = cw ? lb : lb - ncw;
+    const int ti = (int)(t % (uint32_t)n_i);
+    const int to = (int)((t / (uint32_t)n_i) % (uint32_t)n_o);
+    const uint32_t rest = t / tiles;
+    const uint32_t nr = (uint32_t)(nb - H);  // real bins: 1 or 2
+    constexpr uint32_t HC = H > 0 ? H : 1;  // (no complex workgroups when H = 0)
+    const int bin = cw ? 1 + (int)(rest % HC) : ((rest % nr) == 0 ? 0 : H + 1);
+    const int split = cw ? (int)(rest / HC) : (int)(rest / nr);
+    const int chunks_per_split = cw ? cps_c : cps_r;
     const int TM = 32 * WM, TN = 64 * WN;
     const int o0 = to * TM, i0 = ti * TN;
     const bool cplx = bin >= 1 && bin <= H;
@@ -472,26 +492,32 @@ __global__ __launch_bounds__(1024) void bw_bin_kernel(const char* __restrict__ w
             if (rid < 2 * TM) {
                 const int pa = rid / TM, r = o0 + rid % TM;
                 if (r < C_out && (pa == 0 || cplx))
-                    o = xp_bytes + ((uint32_t)(p0 + pa) * (uint32_t)C_out + (uint32_t)r) * row_bytes + 16u * u;
+                    o = xp_bytes + (uint32_t)(p0 + pa) * (uint32_t)C_out * row_bytes + (uint32_t)r * 64u + 16u * u;
             } else {
                 const int rb = rid - 2 * TM, pb = rb / TN, r = i0 + rb % TN;
                 if (r < C_in && (pb == 0 || cplx))
-                    o = ((uint32_t)(p0 + pb) * (uint32_t)C_in + (uint32_t)r) * row_bytes + 16u * u;
+                    o = (uint32_t)(p0 + pb) * (uint32_t)C_in * row_bytes + (uint32_t)r * 64u + 16u * u;
             }
         }
         off[l] = o;
     }
 
+    // chunk c of a plane starts C x 64 bytes after chunk c - 1 (chunk-major
+    // planes); a wave's 64 slots of one load lie all in A or all in B (8 TM is
+    // a multiple of 64), so the chunk offset is uniform per load instruction
     auto dma = [&](int q) {
         char* st = smem + (q % ST) * stage_bytes;
         const bool live = q < nq;
-        const uint32_t soff = live ? (uint32_t)(c_begin + q) * 64u : 0u;
+        const uint32_t cq = live ? (uint32_t)(c_begin + q) : 0u;
 #pragma unroll
         for (int l = 0; l < kBinMaxL; ++l) {
-            if (l < L)
+            if (l < L) {
+                const bool in_a = l * threads + wave * 64 < 8 * TM;
+                const uint32_t soff = cq * (uint32_t)(in_a ? C_out : C_in) * 64u;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rw, (__attribute__((address_space(3))) void*)(st + (l * threads + wave * 64) * 16), 16,
                     live ? off[l] : kBwOOB, soff, 0, 0);
+            }
         }
     };
     // this thread's loads of stage q are done once at most (ST - 2) L remain
@@ -762,14 +788,17 @@ struct BwReduceCfg {
 
 template <int N, int G>
 __global__ __launch_bounds__((BwReduceCfg<N, G>::kThreads)) void bw_reduce_kernel(const float* __restrict__ part,
-                                                                                float* __restrict__ dw, int splits,
-                                                                                int64_t plane, int64_t pstride) {
+                                                                                float* __restrict__ dw, int splits_c,
+                                                                                int splits_r, int64_t plane,
+                                                                                int64_t pstride) {
     using RC = BwReduceCfg<N, G>;
     using V = typename RC::V;
     constexpr int R = RC::R;
     __shared__ V red[R][32][N];
     const int g = (int)threadIdx.x & 31, p = ((int)threadIdx.x >> 5) % N, r = (int)threadIdx.x / (32 * N);
     const int64_t e0 = (int64_t)blockIdx.x * RC::EL + G * g;
+    // the DC and Nyquist planes may have their own number of token ranges
+    const int splits = (p == 0 || (N % 2 == 0 && p == N - 1)) ? splits_r : splits_c;
     const int len = (splits + R - 1) / R;
     const int s0 = r * len, s1 = s0 + len < splits ? s0 + len : splits;
     V v = {};
@@ -810,16 +839,16 @@ __global__ __launch_bounds__((BwReduceCfg<N, G>::kThreads)) void bw_reduce_kerne
 }
 
 template <int N>
-void launch_bw_reduce(const float* part, float* dw, int splits, int64_t plane, int64_t pstride,
+void launch_bw_reduce(const float* part, float* dw, int splits, int splits_r, int64_t plane, int64_t pstride,
                       hipStream_t stream) {
     if (plane >= 64 * BwReduceCfg<N, 4>::EL) {
         using RC = BwReduceCfg<N, 4>;
         hipLaunchKernelGGL((bw_reduce_kernel<N, 4>), dim3((uint32_t)((plane + RC::EL - 1) / RC::EL)),
-                           dim3(RC::kThreads), 0, stream, part, dw, splits, plane, pstride);
+                           dim3(RC::kThreads), 0, stream, part, dw, splits, splits_r, plane, pstride);
     } else {
         using RC = BwReduceCfg<N, 1>;
         hipLaunchKernelGGL((bw_reduce_kernel<N, 1>), dim3((uint32_t)((plane + RC::EL - 1) / RC::EL)),
-                           dim3(RC::kThreads), 0, stream, part, dw, splits, plane, pstride);
+                           dim3(RC::kThreads), 0, stream, part, dw, splits, splits_r, plane, pstride);
     }
 }
 
@@ -835,6 +864,7 @@ struct BwShape {
     bool fused;  // small layers: transforms and products in one launch, no planes
     bool bin;    // products per bin over whole tiles (bw_bin_kernel)
     int WM, WN, nb, L, stage_bytes;
+    int splits_r, chunks_per_split_r;  // token ranges of the real bins (the others: splits)
     size_t xp_bytes, dyp_bytes, part_bytes, total;
 };
 
@@ -891,29 +921,27 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     const int tm = 32 * bw_wg(C_in, C_out);
     const int H = (N - 1) / 2;
     s.nb = 1 + H + ((N % 2 == 0 && N > 1) ? 1 : 0);
-    // plane rows: a whole number of 64-token blocks whose byte length is an odd
-    // multiple of 256.  Rows of a power-of-two length (64 KiB at T = 32768 in
-    // bf16) all start at the same offset modulo the memory interleave, so the 64
-    // rows a workgroup streams would queue on the same channels.
-    const int64_t unit = 256 / S;  // tokens per 256 bytes
-    int64_t m = (T + unit - 1) / unit;
-    if (m % 2 == 0) ++m;
-    s.Tp = m * unit;
+    s.Tp = (T + 63) / 64 * 64;
     s.nchunks = (int)(s.Tp / KC);
     s.bin = EQL_BW_BIN != 0 && bw_bin_tile(C_in, C_out, s);
     if (s.bin) {
         // one workgroup per CU (the ring takes most of its LDS): bins x tiles x
         // token ranges of at least two chunks, about 256 in all
+        // a real bin's workgroup costs about half a complex one, so it takes
+        // ranges twice as long: H S + nr S / 2 workgroups per tile in all
         s.tiles = s.n_o * s.n_i;
-        const int64_t per = (int64_t)s.nb * s.tiles;
-        int64_t sp = (256 + per - 1) / per;
+        const int nr = s.nb - H;
         const int64_t cap = s.nchunks / 2 > 0 ? s.nchunks / 2 : 1;
+        int64_t sp = (int64_t)(512 / (s.tiles * (2 * H + nr)));
         sp = sp < 1 ? 1 : (sp > cap ? cap : sp);
         s.chunks_per_split = (int)((s.nchunks + sp - 1) / sp);
         s.splits = (s.nchunks + s.chunks_per_split - 1) / s.chunks_per_split;
+        s.chunks_per_split_r = H > 0 ? 2 * s.chunks_per_split : s.chunks_per_split;
+        s.splits_r = (s.nchunks + s.chunks_per_split_r - 1) / s.chunks_per_split_r;
         s.xp_bytes = round256((size_t)N * C_in * s.Tp * S);
         s.dyp_bytes = round256((size_t)N * C_out * s.Tp * S);
-        s.part_bytes = round256((size_t)s.splits * N * bw_pstride(C_in, C_out) * 4);
+        const int smax = s.splits > s.splits_r ? s.splits : s.splits_r;
+        s.part_bytes = round256((size_t)smax * N * bw_pstride(C_in, C_out) * 4);
         s.total = s.xp_bytes + s.dyp_bytes + s.part_bytes;
         return s;
     }
@@ -950,7 +978,7 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
         float* part = reinterpret_cast<float*>(ws);
         hipLaunchKernelGGL((bw_small_kernel<N, IO>), dim3((uint32_t)s.splits), dim3(256), 0, stream, (const IO*)x,
                            (const IO*)dy, part, T, C_in, C_out, s.chunks_per_split, s.nchunks);
-        launch_bw_reduce<N>(part, dw, s.splits, plane, pstride, stream);
+        launch_bw_reduce<N>(part, dw, s.splits, s.splits, plane, pstride, stream);
         return hipGetLastError();
     }
     IO* xp = reinterpret_cast<IO*>(ws);
@@ -963,19 +991,20 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
                        dyp, C_out, T, s.Tp);
     if (s.bin) {
         using BC = BinCfg<N, IO>;
-        const int64_t bwgs = (int64_t)s.nb * s.tiles * s.splits;
+        constexpr int H = (N - 1) / 2;
+        const int64_t bwgs = (int64_t)s.tiles * (H * s.splits + (s.nb - H) * s.splits_r);
         hipLaunchKernelGGL((bw_bin_kernel<BC>), dim3((uint32_t)bwgs), dim3(64 * s.WM * s.WN), 0, stream,
                            (const char*)ws, (uint32_t)s.xp_bytes, (uint32_t)(s.xp_bytes + s.dyp_bytes), part, C_out,
-                           C_in, s.Tp, s.WM, s.WN, s.n_o, s.n_i, s.nb, s.L, s.stage_bytes, s.chunks_per_split,
-                           s.nchunks, pstride);
-        launch_bw_reduce<N>(part, dw, s.splits, plane, pstride, stream);
+                           C_in, s.Tp, s.WM, s.WN, s.n_o, s.n_i, s.nb, s.L, s.stage_bytes, s.splits,
+                           s.chunks_per_split, s.chunks_per_split_r, s.nchunks, pstride);
+        launch_bw_reduce<N>(part, dw, s.splits, s.splits_r, plane, pstride, stream);
         return hipGetLastError();
     }
     const int64_t wgs = (int64_t)s.tiles * s.splits;
     hipLaunchKernelGGL((bw_gemm_kernel<Cfg>), dim3((uint32_t)wgs), dim3(Cfg::kThreads), 0, stream,
                        (const IO*)dyp, (const IO*)xp, part, C_out, C_in, s.Tp, s.n_i, s.tiles,
                        s.chunks_per_split, s.nchunks);
-    launch_bw_reduce<N>(part, dw, s.splits, plane, pstride, stream);
+    launch_bw_reduce<N>(part, dw, s.splits, s.splits, plane, pstride, stream);
     return hipGetLastError();
 }
 
