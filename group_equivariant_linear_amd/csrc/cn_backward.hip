@@ -893,10 +893,6 @@ bool bw_bin_tile(int C_in, int C_out, BwShape& s) {
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Layers with at most 32 output and input channels take one-wave 32 x 32
-// tiles (a 64 x 64 tile would be three quarters padding); the others 2 x 2
-// waves over 64 x 64.
-int bw_wg(int C_in, int C_out) { return (C_in <= 32 && C_out <= 32) ? 1 : 2; }
 
 BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     BwShape s{};
@@ -918,7 +914,7 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
         return s;
     }
     const int S = bf16 ? 2 : 4, KC = 64 / S;
-    const int tm = 32 * bw_wg(C_in, C_out);
+    const int tm = 64;  // bw_gemm_kernel tiles: 2 x 2 waves of 32 x 32
     const int H = (N - 1) / 2;
     s.nb = 1 + H + ((N % 2 == 0 && N > 1) ? 1 : 0);
     s.Tp = (T + 63) / 64 * 64;
@@ -948,16 +944,14 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     s.n_o = (C_out + tm - 1) / tm;
     s.n_i = (C_in + tm - 1) / tm;
     s.tiles = s.n_o * s.n_i;
-    // token ranges: enough waves to give every SIMD one (one-wave tiles, ranges
-    // down to one chunk) or every CU two workgroups (ranges of four chunks or
-    // more).  The product loop waits on its ring once per stage, and a second
+    // token ranges: enough to give every CU two workgroups (ranges of four
+    // chunks or more).  The product loop waits on its ring once per stage, and a second
     // workgroup on the CU fills those waits: on MI355X 512 workgroups ran c4
     // (C7, 160 -> 160, T = 32768) in 132 us against 174 at 256 and 149 at 1024
     // (more ranges, more partial spectra to write and sum); a deeper ring at one
     // workgroup per CU instead was slower still (252 us at nine stages).
-    const bool small = bw_wg(C_in, C_out) == 1;
-    const int64_t want = ((small ? 1024 : 512) + s.tiles - 1) / s.tiles;
-    const int64_t cap = small ? s.nchunks : s.nchunks / 4;
+    const int64_t want = (512 + s.tiles - 1) / s.tiles;
+    const int64_t cap = s.nchunks / 4;
     int64_t sp = want < cap ? want : cap;
     sp = sp < 1 ? 1 : (sp > s.nchunks ? s.nchunks : sp);
     s.chunks_per_split = (int)((s.nchunks + sp - 1) / sp);
@@ -969,10 +963,10 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     return s;
 }
 
-template <int N, typename IO, int WG>
+template <int N, typename IO>
 hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t T, int C_in, int C_out,
                                char* ws, const BwShape& s, hipStream_t stream) {
-    using Cfg = BwCfg<N, IO, WG>;
+    using Cfg = BwCfg<N, IO, 2>;
     const int64_t plane = (int64_t)C_out * C_in, pstride = bw_pstride(C_in, C_out);
     if (s.fused) {
         float* part = reinterpret_cast<float*>(ws);
@@ -1014,8 +1008,7 @@ hipError_t dispatch_backward_weight(int N, const void* x, const void* dy, float*
     switch (N) {
 #define EQL_BW(n)                                                                           \
     case n:                                                                                 \
-        return bw_wg(C_in, C_out) == 1 ? run_backward_weight<n, IO, 1>(x, dy, dw, T, C_in, C_out, ws, s, stream) \
-                                        : run_backward_weight<n, IO, 2>(x, dy, dw, T, C_in, C_out, ws, s, stream);
+        return run_backward_weight<n, IO>(x, dy, dw, T, C_in, C_out, ws, s, stream);
         EQL_BW(1) EQL_BW(2) EQL_BW(3) EQL_BW(4) EQL_BW(5) EQL_BW(6) EQL_BW(7) EQL_BW(8)
         EQL_BW(9) EQL_BW(10) EQL_BW(11) EQL_BW(12) EQL_BW(13) EQL_BW(14) EQL_BW(15) EQL_BW(16)
 #undef EQL_BW

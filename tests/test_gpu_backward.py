@@ -161,8 +161,9 @@ def test_backward_weight_whole_tile_bins(eq, N, dt):
     """Wide layers whose (o, i) tile fits one workgroup of up to 16 waves take the
     per-bin product kernel (one bin, whole tile, range of tokens per workgroup):
     ragged tile edges on both axes (150 -> 140), exact ones (160 -> 160), and
-    two tiles along o (96 -> 384) or i (384 -> 96).  Also deterministic."""
-    for C_in, C_out, T in [(150, 140, 77), (160, 160, 300), (96, 384, 130), (384, 96, 64)]:
+    two tiles along o (96 -> 384) or i (384 -> 96), and a single token (one chunk,
+    one range per bin).  Also deterministic."""
+    for C_in, C_out, T in [(150, 140, 77), (160, 160, 300), (96, 384, 130), (384, 96, 64), (160, 160, 1)]:
         d = _inputs(N, C_in, C_out, T, dt, seed=3 * N + C_in)
         dw = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
         ref = oracle.cn_backward_weight(d["x64"], d["dy64"])
