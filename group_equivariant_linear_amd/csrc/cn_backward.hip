@@ -919,7 +919,10 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     s.nb = 1 + H + ((N % 2 == 0 && N > 1) ? 1 : 0);
     s.Tp = (T + 63) / 64 * 64;
     s.nchunks = (int)(s.Tp / KC);
-    s.bin = EQL_BW_BIN != 0 && bw_bin_tile(C_in, C_out, s);
+    // the per-bin kernel reaches both plane sets through one resource: under
+    // 2 GiB together (otherwise the 64 x 64 kernel, whose limit is per set)
+    const size_t both = round256((size_t)N * C_in * s.Tp * S) + round256((size_t)N * C_out * s.Tp * S);
+    s.bin = EQL_BW_BIN != 0 && both < ((size_t)1 << 31) && bw_bin_tile(C_in, C_out, s);
     if (s.bin) {
         // one workgroup per CU (the ring takes most of its LDS): bins x tiles x
         // token ranges of at least two chunks, about 256 in all
@@ -1054,14 +1057,16 @@ hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const
     }
     const BwShape s = bw_shape(N, dtype_bf16, T, C_in, C_out);
     if (workspace_bytes < s.total) return hipErrorInvalidValue;
-    // 32-bit buffer offsets over each operand's planes; grid dimensions
+    // 32-bit buffer offsets over each operand's planes (under 2 GiB per plane
+    // set); grid dimensions.  Past
+    // these limits the call is not supported (the caller can split the tokens
+    // and add the gradients).
     const int S = dtype_bf16 ? 2 : 4;
-    if ((int64_t)N * C_in * s.Tp * S >= ((int64_t)1 << 31) || (int64_t)N * C_out * s.Tp * S >= ((int64_t)1 << 31) ||
-        (s.bin && s.xp_bytes + s.dyp_bytes >= ((size_t)1 << 31)))
-        return hipErrorInvalidConfiguration;
+    if ((int64_t)N * C_in * s.Tp * S >= ((int64_t)1 << 31) || (int64_t)N * C_out * s.Tp * S >= ((int64_t)1 << 31))
+        return hipErrorNotSupported;
     if (s.Tp / 64 > 0x7fffffff || (C_in + 7) / 8 > 65535 || (C_out + 7) / 8 > 65535 ||
         (int64_t)s.tiles * s.splits > 0x7fffffff)
-        return hipErrorInvalidConfiguration;
+        return hipErrorNotSupported;
     char* ws = static_cast<char*>(workspace);
     if (dtype_bf16) return dispatch_backward_weight<__bf16>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
     return dispatch_backward_weight<float>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);

@@ -280,8 +280,9 @@ eqlinear_status eqlinear_backward_weight(eqlinear_plan_t p, const void* x, const
             overlaps(workspace, need, x, xb) || overlaps(workspace, need, dy, dyb))
             return EQL_ERR_INVALID;
     }
-    return hip_status(eql::launch_cn_backward_weight(p->N, p->dtype == EQL_BF16, x, dy, dw, T, p->C_in, p->C_out,
-                                                     workspace, workspace_bytes, (hipStream_t)stream));
+    const hipError_t e = eql::launch_cn_backward_weight(p->N, p->dtype == EQL_BF16, x, dy, dw, T, p->C_in, p->C_out,
+                                                        workspace, workspace_bytes, (hipStream_t)stream);
+    return e == hipErrorNotSupported ? EQL_ERR_UNSUPPORTED : hip_status(e);
 }
 
 eqlinear_status eqlinear_d8_forward(eqlinear_plan_t p, const void* x, const void* wb, void* y,

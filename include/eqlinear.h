@@ -283,7 +283,10 @@ size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t T);
  * not overlapping x, dy or dw; its contents are scratch.  x, dy, dw 16-byte
  * aligned.  T == 0 writes zeros to dw.  Asynchronous on stream; no allocation.
  * EQL_ERR_INVALID for a D8 plan, bad pointers, overlap or a short workspace;
- * EQL_ERR_UNSUPPORTED for an fp16 plan. */
+ * EQL_ERR_UNSUPPORTED for an fp16 plan, or when the transformed x or dy held in
+ * the workspace would reach 2 GiB (N C T S bytes each, S the element size; for
+ * N = 7, C = 160, bf16 that is about 958 000 tokens): split the tokens into
+ * parts and add the parts' gradients. */
 eqlinear_status eqlinear_backward_weight(eqlinear_plan_t plan, const void* x, const void* dy, float* dw,
                                          int64_t T, void* workspace, size_t workspace_bytes, void* stream);
 

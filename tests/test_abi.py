@@ -211,6 +211,13 @@ def test_backward_validation_before_any_hip_call(eq):
     assert lib.eqlinear_backward_weight(d8.handle, A, B, W, 100, S, need, None) == eq.EQL_ERR_INVALID
     # the workspace grows with T
     assert lib.eqlinear_backward_weight_workspace(h, 10000) > need
+    # transformed x or dy reaching 2 GiB: unsupported, refused before any HIP call
+    big = eq.eqlinear_plan(7, 160, 160, eq.EQL_BF16)
+    X, Y, D, WS = 1 << 40, 1 << 42, 1 << 44, 1 << 46  # farther apart than the big tensors
+    T = 1_000_000  # 7 * 160 * T * 2 bytes > 2 GiB
+    nb = lib.eqlinear_backward_weight_workspace(big.handle, T)
+    assert nb > 2 * (1 << 31)
+    assert lib.eqlinear_backward_weight(big.handle, X, Y, D, T, WS, nb, None) == eq.EQL_ERR_UNSUPPORTED
 
 
 def test_bias_act_validation_before_any_hip_call(eq):
