@@ -495,8 +495,34 @@ def op_kernel_name(wl, op):
         from dataclasses import replace
         return step_kernel_name(replace(wl, C_in=wl.C_out, C_out=wl.C_in))
     if op == "backward_weight":
-        return "bw_planes_kernel x2 + bw_gemm_kernel + bw_reduce_kernel"
+        if wl.C_in <= 32 and wl.C_out <= 32:
+            return "bw_small_kernel + bw_reduce_kernel"
+        return f"bw_planes_kernel + {_bw_products_kernel(wl)} + bw_reduce_kernel"
     return step_kernel_name(wl)
+
+
+def _bw_products_kernel(wl):
+    """Which product kernel the library picks for a wide layer's weight gradient:
+    the per-bin kernel when some tile of at most 16 waves (32 x 64 outputs each)
+    meets its load budget (4 loads per thread and stage above 8 waves, else 8;
+    stages up to 53248 bytes) and both plane sets stay under 2 GiB; otherwise
+    the 64 x 64 kernel.  A label only: the selection itself is the library's."""
+    import synthetic
+    S = 4 if wl.dtype == synthetic.F32 else 2
+    Tp = (wl.T + 63) // 64 * 64
+    if (wl.C_in + wl.C_out) * wl.N * Tp * S >= 1 << 31:
+        return "bw_gemm_kernel"
+    wmt, wnt = -(-wl.C_out // 32), -(-wl.C_in // 64)
+    for no in range(1, wmt + 1):
+        for ni in range(1, wnt + 1):
+            wm, wn = -(-wmt // no), -(-wnt // ni)
+            if wm * wn > 16:
+                continue
+            threads = 64 * wm * wn
+            loads = -(-8 * (32 * wm + 64 * wn) // threads)
+            if loads <= (8 if wm * wn <= 8 else 4) and loads * threads * 16 <= 53248:
+                return "bw_bin_kernel"
+    return "bw_gemm_kernel"
 
 
 def _dense_grad_agreement(L):

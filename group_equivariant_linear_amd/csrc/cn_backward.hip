@@ -438,10 +438,14 @@ struct BinCfg {
     static constexpr int ST = 3;                // ring stages
     static constexpr int kMaxStage = 53248;     // bytes: ST stages fit the CU's LDS
 };
-constexpr int kBinMaxL = 4;  // direct loads per thread and stage
+// Two instances: up to 16 waves (128 VGPRs a lane, so at most 4 direct loads
+// per thread and stage stay in registers) and up to 8 waves (256 VGPRs, up to
+// 8 loads: narrower tiles such as 96 x 96 need 5).
+template <int MAXT>
+constexpr int bin_max_loads() { return MAXT > 512 ? 4 : 8; }
 
-template <class C>
-__global__ __launch_bounds__(1024) void bw_bin_kernel(const char* __restrict__ ws, uint32_t xp_bytes,
+template <class C, int MAXT>
+__global__ __launch_bounds__(MAXT) void bw_bin_kernel(const char* __restrict__ ws, uint32_t xp_bytes,
                                                       uint32_t span, float* __restrict__ part, int C_out,
                                                       int C_in, int64_t Tp, int WM, int WN, int n_o, int n_i,
                                                       int nb, int L, int stage_bytes, int splits_c, int cps_c,
@@ -483,9 +487,9 @@ __global__ __launch_bounds__(1024) void bw_bin_kernel(const char* __restrict__ w
     const __amdgpu_buffer_rsrc_t rw = bw_rsrc(ws, span);
     const uint32_t row_bytes = (uint32_t)(Tp * S);
     const int slots = 8 * (TM + TN);
-    uint32_t off[kBinMaxL];
+    uint32_t off[8];  // the first bin_max_loads<MAXT>() are used
 #pragma unroll
-    for (int l = 0; l < kBinMaxL; ++l) {
+    for (int l = 0; l < bin_max_loads<MAXT>(); ++l) {
         const int slot = l * threads + tid, u = slot & 3, rid = slot >> 2;
         uint32_t o = kBwOOB;
         if (l < L && slot < slots) {
@@ -510,7 +514,7 @@ __global__ __launch_bounds__(1024) void bw_bin_kernel(const char* __restrict__ w
         const bool live = q < nq;
         const uint32_t cq = live ? (uint32_t)(c_begin + q) : 0u;
 #pragma unroll
-        for (int l = 0; l < kBinMaxL; ++l) {
+        for (int l = 0; l < bin_max_loads<MAXT>(); ++l) {
             if (l < L) {
                 const bool in_a = l * threads + wave * 64 < 8 * TM;
                 const uint32_t soff = cq * (uint32_t)(in_a ? C_out : C_in) * 64u;
@@ -526,7 +530,11 @@ __global__ __launch_bounds__(1024) void bw_bin_kernel(const char* __restrict__ w
             case 1: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 1)); break;
             case 2: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 2)); break;
             case 3: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 3)); break;
-            default: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 4)); break;
+            case 4: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 4)); break;
+            case 5: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 5)); break;
+            case 6: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 6)); break;
+            case 7: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 7)); break;
+            default: __builtin_amdgcn_s_waitcnt(bw_vmcnt((ST - 2) * 8)); break;
         }
     };
 
@@ -880,7 +888,8 @@ bool bw_bin_tile(int C_in, int C_out, BwShape& s) {
             if (WM * WN > 16) continue;
             const int threads = 64 * WM * WN, slots = 8 * (32 * WM + 64 * WN);
             const int L = (slots + threads - 1) / threads;
-            if (L > kBinMaxL || L * threads * 16 > BinCfg<1, float>::kMaxStage) continue;
+            const int max_loads = WM * WN <= 8 ? bin_max_loads<512>() : bin_max_loads<1024>();
+            if (L > max_loads || L * threads * 16 > BinCfg<1, float>::kMaxStage) continue;
             const int n_o = (C_out + 32 * WM - 1) / (32 * WM), n_i = (C_in + 64 * WN - 1) / (64 * WN);
             const int64_t cost = (int64_t)n_i * C_out + (int64_t)n_o * C_in;
             if (best < 0 || cost < best) {
@@ -990,10 +999,11 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
         using BC = BinCfg<N, IO>;
         constexpr int H = (N - 1) / 2;
         const int64_t bwgs = (int64_t)s.tiles * (H * s.splits + (s.nb - H) * s.splits_r);
-        hipLaunchKernelGGL((bw_bin_kernel<BC>), dim3((uint32_t)bwgs), dim3(64 * s.WM * s.WN), 0, stream,
-                           (const char*)ws, (uint32_t)s.xp_bytes, (uint32_t)(s.xp_bytes + s.dyp_bytes), part, C_out,
-                           C_in, s.Tp, s.WM, s.WN, s.n_o, s.n_i, s.nb, s.L, s.stage_bytes, s.splits,
-                           s.chunks_per_split, s.chunks_per_split_r, s.nchunks, pstride);
+        auto kern = s.WM * s.WN <= 8 ? bw_bin_kernel<BC, 512> : bw_bin_kernel<BC, 1024>;
+        hipLaunchKernelGGL(kern, dim3((uint32_t)bwgs), dim3(64 * s.WM * s.WN), 0, stream, (const char*)ws,
+                           (uint32_t)s.xp_bytes, (uint32_t)(s.xp_bytes + s.dyp_bytes), part, C_out, C_in, s.Tp, s.WM,
+                           s.WN, s.n_o, s.n_i, s.nb, s.L, s.stage_bytes, s.splits, s.chunks_per_split,
+                           s.chunks_per_split_r, s.nchunks, pstride);
         launch_bw_reduce<N>(part, dw, s.splits, s.splits_r, plane, pstride, stream);
         return hipGetLastError();
     }

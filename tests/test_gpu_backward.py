@@ -173,6 +173,19 @@ def test_backward_weight_whole_tile_bins(eq, N, dt):
 
 
 @pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("N", [1, 3, 8, 16])
+def test_backward_weight_64_tiles(eq, N, dt):
+    """At most 32 output channels with more than 32 input channels: no whole tile
+    fits the per-bin kernel's load budget, so the 64 x 64 product kernel (all
+    bins per workgroup) runs.  Ragged on both axes."""
+    for C_in, C_out, T in [(50, 20, 300), (130, 24, 77), (200, 9, 64)]:
+        d = _inputs(N, C_in, C_out, T, dt, seed=5 * N + C_in)
+        dw = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
+        ref = oracle.cn_backward_weight(d["x64"], d["dy64"])
+        assert_close(dw, ref, dt, f"dw N={N} {dt} {C_in}->{C_out} T={T}")
+
+
+@pytest.mark.parametrize("dt", [F32, BF16])
 def test_gradients_satisfy_the_adjoint_identity(eq, dt):
     """<dy, y(x)> = <dx, x> = <dw, w> with all three computed on the GPU."""
     import torch
