@@ -7,7 +7,7 @@
 // all of them.
 //
 // Workgroup: a grid of waves over TT tokens x CT output channels of one job.
-// Per chunk of 32 input channels both operands reach LDS by direct
+// Per chunk of 64 input channels both operands reach LDS by direct
 // global->LDS loads into an ST-stage ring (ST-1 chunks in flight, one barrier
 // per chunk): the W rows and the x rows of the tile, both in the XOR-swizzled
 // 16-byte-part order that makes the fragment reads conflict-free.
@@ -34,8 +34,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t d8_rsrc(const void* base, uint
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// 16-byte part q of row o of a 64-byte row chunk sits at part q ^ ((o >> 1) & 3).
-__device__ __forceinline__ int swz(int o, int q) { return o * 4 + (q ^ ((o >> 1) & 3)); }
+// 16-byte part q (0..7) of row o of a 128-byte row chunk sits at part
+// q ^ ((o >> 1) & 7): a fragment read (16 lanes, rows o..o+15, one part) then
+// touches 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int o, int q) { return o * 8 + (q ^ ((o >> 1) & 7)); }
 
 // Workgroup tile: WT x WN waves; wave (wt, wn) owns TPW 16-token blocks and
 // NPW 16-channel blocks, so each W fragment it reads from LDS feeds TPW
@@ -48,11 +50,11 @@ struct D8Cfg {
     static constexpr int kThreads = 64 * WAVES;
     static constexpr int TT = 16 * TPW * WT;  // tokens per workgroup
     static constexpr int CT = 16 * NPW * WN;  // output channels per workgroup
-    static constexpr int KC = 32;             // input channels per chunk
-    static constexpr int W_SLOTS = CT * 4;    // 16-byte parts of a W chunk
+    static constexpr int KC = 64;             // input channels per chunk: two 16x16x32 steps
+    static constexpr int W_SLOTS = CT * 8;    // 16-byte parts of a W chunk
     static constexpr int W_LOADS = (W_SLOTS + kThreads - 1) / kThreads;
     static constexpr int W_BUF = W_LOADS * kThreads * 16;
-    static constexpr int X_SLOTS = TT * 4;
+    static constexpr int X_SLOTS = TT * 8;
     static constexpr int X_LOADS = (X_SLOTS + kThreads - 1) / kThreads;
     static constexpr int X_BUF = X_LOADS * kThreads * 16;
     static constexpr int MAIN = ST * (W_BUF + X_BUF);
@@ -98,22 +100,22 @@ __device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, 
     char* wbuf = smem;
     char* xbuf = smem + C::ST * C::W_BUF;
 
-    // Slot s of a chunk tile (W: CT rows, x: TT rows, 64 bytes each) is row
-    // s/4, stored part s%4, holding part (s%4) ^ ((row >> 1) & 3).  W rows past
+    // Slot s of a chunk tile (W: CT rows, x: TT rows, 128 bytes each) is row
+    // s/8, stored part s%8, holding part (s%8) ^ ((row >> 1) & 7).  W rows past
     // Nn and slots past the tile read nothing (never used).
     uint32_t woff[C::W_LOADS], xoff[C::X_LOADS];
 #pragma unroll
     for (int it = 0; it < C::W_LOADS; ++it) {
-        const int sl = it * C::kThreads + tid, o = sl >> 2;
-        const int q = (sl & 3) ^ ((o >> 1) & 3);
+        const int sl = it * C::kThreads + tid, o = sl >> 3;
+        const int q = (sl & 7) ^ ((o >> 1) & 7);
         woff[it] = (sl < C::W_SLOTS && n0 + o < Nn)
                        ? (uint32_t)(((int64_t)job.w_off + (int64_t)(n0 + o) * job.ldw + q * 8) * 2)
                        : kD8OOB;
     }
 #pragma unroll
     for (int it = 0; it < C::X_LOADS; ++it) {
-        const int sl = it * C::kThreads + tid, r = sl >> 2;
-        const int q = (sl & 3) ^ ((r >> 1) & 3);
+        const int sl = it * C::kThreads + tid, r = sl >> 3;
+        const int q = (sl & 7) ^ ((r >> 1) & 7);
         xoff[it] = sl < C::X_SLOTS ? (uint32_t)r * row_x + (uint32_t)(job.x_col + q * 8) * 2u : kD8OOB;
     }
 
@@ -129,8 +131,8 @@ __device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, 
         for (int it = 0; it < C::W_LOADS; ++it) {
             uint32_t off = past ? kD8OOB : woff[it];
             if (tail && !past) {
-                const int sl = it * C::kThreads + tid, o = sl >> 2;
-                if (c * C::KC + ((sl & 3) ^ ((o >> 1) & 3)) * 8 >= K) off = kD8OOB;
+                const int sl = it * C::kThreads + tid, o = sl >> 3;
+                if (c * C::KC + ((sl & 7) ^ ((o >> 1) & 7)) * 8 >= K) off = kD8OOB;
             }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rw, (__attribute__((address_space(3))) void*)(wb + (it * C::kThreads + wave * 64) * 16), 16, off,
@@ -140,8 +142,8 @@ __device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, 
         for (int it = 0; it < C::X_LOADS; ++it) {
             uint32_t off = past ? kD8OOB : xoff[it];
             if (tail && !past) {
-                const int sl = it * C::kThreads + tid, r = sl >> 2;
-                if (c * C::KC + ((sl & 3) ^ ((r >> 1) & 3)) * 8 >= K) off = kD8OOB;
+                const int sl = it * C::kThreads + tid, r = sl >> 3;
+                if (c * C::KC + ((sl & 7) ^ ((r >> 1) & 7)) * 8 >= K) off = kD8OOB;
             }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rx, (__attribute__((address_space(3))) void*)(xb + (it * C::kThreads + wave * 64) * 16), 16, off,
@@ -155,7 +157,6 @@ __device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, 
 #pragma unroll
         for (int b = 0; b < TPW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int l_off = swz(tl, kg) * 16;  // this lane's part of a 16-row block
 #pragma unroll
     for (int c = 0; c < C::ST - 1; ++c) dma(c);
     for (int c = 0; c < nch; ++c) {
@@ -165,26 +166,32 @@ __device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, 
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::ST - 2) * C::LOADS));
         __builtin_amdgcn_s_barrier();
         dma(c + C::ST - 1);  // into the stage every wave finished with last step
-        const char* wb = wbuf + (c % C::ST) * C::W_BUF + wn * NPW * 1024;
-        const char* xb = xbuf + (c % C::ST) * C::X_BUF + wt * TPW * 1024;
-        bf16x8 A[NPW], B[TPW];
+        const char* wb = wbuf + (c % C::ST) * C::W_BUF + wn * NPW * 2048;
+        const char* xb = xbuf + (c % C::ST) * C::X_BUF + wt * TPW * 2048;
+        // two k-steps of 32 channels: parts 4 ks + kg of this lane's rows
 #pragma unroll
-        for (int a = 0; a < NPW; ++a) A[a] = *reinterpret_cast<const bf16x8*>(wb + a * 1024 + l_off);
+        for (int ks = 0; ks < 2; ++ks) {
+            if (c * C::KC + 32 * ks >= K) break;  // a last chunk's empty half (uniform per job)
+            const int l_off = swz(tl, 4 * ks + kg) * 16;
+            bf16x8 A[NPW], B[TPW];
 #pragma unroll
-        for (int b = 0; b < TPW; ++b) B[b] = *reinterpret_cast<const bf16x8*>(xb + b * 1024 + l_off);
-        if (c * C::KC + C::KC > K && c * C::KC + kg * 8 >= K) {
-            // input-channel tail: k-values past K are zero on both sides (the
-            // parts there were never loaded)
+            for (int a = 0; a < NPW; ++a) A[a] = *reinterpret_cast<const bf16x8*>(wb + a * 2048 + l_off);
 #pragma unroll
-            for (int a = 0; a < NPW; ++a) A[a] = bf16x8{};
+            for (int b = 0; b < TPW; ++b) B[b] = *reinterpret_cast<const bf16x8*>(xb + b * 2048 + l_off);
+            if (c * C::KC + C::KC > K && c * C::KC + 32 * ks + kg * 8 >= K) {
+                // input-channel tail: k-values past K are zero on both sides (the
+                // parts there were never loaded)
 #pragma unroll
-            for (int b = 0; b < TPW; ++b) B[b] = bf16x8{};
+                for (int a = 0; a < NPW; ++a) A[a] = bf16x8{};
+#pragma unroll
+                for (int b = 0; b < TPW; ++b) B[b] = bf16x8{};
+            }
+#pragma unroll
+            for (int a = 0; a < NPW; ++a)
+#pragma unroll
+                for (int b = 0; b < TPW; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[a], B[b], acc[a][b], 0, 0, 0);
         }
-#pragma unroll
-        for (int a = 0; a < NPW; ++a)
-#pragma unroll
-            for (int b = 0; b < TPW; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[a], B[b], acc[a][b], 0, 0, 0);
     }
 
     // Epilogue: lane (tl, kg) holds channels 16(wn NPW + a) + 4kg + i of token
