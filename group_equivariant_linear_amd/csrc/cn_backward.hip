@@ -863,10 +863,6 @@ void launch_bw_reduce(const float* part, float* dw, int splits, int splits_r, in
 
 // --- host side ---------------------------------------------------------------------------
 
-#ifndef EQL_BW_BIN
-#define EQL_BW_BIN 1
-#endif
-
 struct BwShape {
     int64_t Tp;
     int n_o, n_i, tiles, nchunks, splits, chunks_per_split;
@@ -932,7 +928,7 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
     // the per-bin kernel reaches both plane sets through one resource: under
     // 2 GiB together (otherwise the 64 x 64 kernel, whose limit is per set)
     const size_t both = round256((size_t)N * C_in * s.Tp * S) + round256((size_t)N * C_out * s.Tp * S);
-    s.bin = EQL_BW_BIN != 0 && both < ((size_t)1 << 31) && bw_bin_tile(C_in, C_out, s);
+    s.bin = both < ((size_t)1 << 31) && bw_bin_tile(C_in, C_out, s);
     if (s.bin) {
         // one workgroup per CU (the ring takes most of its LDS): bins x tiles x
         // token ranges of at least two chunks, about 256 in all
