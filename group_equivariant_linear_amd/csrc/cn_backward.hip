@@ -233,6 +233,9 @@ struct BwCfg {
 __device__ __forceinline__ void bw_mma(f32x4& acc, const bf16x8& a, const bf16x8& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
+__device__ __forceinline__ void bw_mma(f32x4& acc, const f16x8& a, const f16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
 __device__ __forceinline__ void bw_mma(f32x4& acc, const f32x4& a, const f32x4& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
@@ -244,6 +247,11 @@ __device__ __forceinline__ bf16x8 bw_neg(const bf16x8& v) {
     u ^= 0x80008000u;
     return __builtin_bit_cast(bf16x8, u);
 }
+__device__ __forceinline__ f16x8 bw_neg(const f16x8& v) {
+    u32x4 u = __builtin_bit_cast(u32x4, v);
+    u ^= 0x80008000u;
+    return __builtin_bit_cast(f16x8, u);
+}
 __device__ __forceinline__ f32x4 bw_neg(const f32x4& v) { return -v; }
 
 template <typename IO>
@@ -251,6 +259,10 @@ struct BwFrag;
 template <>
 struct BwFrag<__bf16> {
     using T = bf16x8;  // 8 tokens of one row: k-values of one 16x16x32 product
+};
+template <>
+struct BwFrag<_Float16> {
+    using T = f16x8;
 };
 template <>
 struct BwFrag<float> {
@@ -900,7 +912,7 @@ bool bw_bin_tile(int C_in, int C_out, BwShape& s) {
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 
-BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
+BwShape bw_shape(int N, int io, int64_t T, int C_in, int C_out) {
     BwShape s{};
     if (C_in <= 32 && C_out <= 32) {
         // one fused launch: token chunks of 16 over at most 256 workgroups, two
@@ -919,7 +931,7 @@ BwShape bw_shape(int N, int bf16, int64_t T, int C_in, int C_out) {
         s.total = s.part_bytes;
         return s;
     }
-    const int S = bf16 ? 2 : 4, KC = 64 / S;
+    const int S = io == kIoF32 ? 4 : 2, KC = 64 / S;
     const int tm = 64;  // bw_gemm_kernel tiles: 2 x 2 waves of 32 x 32
     const int H = (N - 1) / 2;
     s.nb = 1 + H + ((N % 2 == 0 && N > 1) ? 1 : 0);
@@ -1049,12 +1061,12 @@ hipError_t launch_w_hat_adjoint(int N, int io, const void* w_hat, void* w_hat_ad
     return hipGetLastError();
 }
 
-size_t backward_weight_workspace(int N, int dtype_bf16, int64_t T, int C_in, int C_out) {
+size_t backward_weight_workspace(int N, int io, int64_t T, int C_in, int C_out) {
     if (T <= 0) return 0;
-    return bw_shape(N, dtype_bf16, T, C_in, C_out).total;
+    return bw_shape(N, io, T, C_in, C_out).total;
 }
 
-hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const void* dy, float* dw, int64_t T,
+hipError_t launch_cn_backward_weight(int N, int io, const void* x, const void* dy, float* dw, int64_t T,
                                      int C_in, int C_out, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream) {
     if (T == 0) {  // no tokens: the gradient is zero (a fill kernel, also fine inside a captured graph)
@@ -1062,20 +1074,21 @@ hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const
         hipLaunchKernelGGL(bw_zero_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, dw, n);
         return hipGetLastError();
     }
-    const BwShape s = bw_shape(N, dtype_bf16, T, C_in, C_out);
+    const BwShape s = bw_shape(N, io, T, C_in, C_out);
     if (workspace_bytes < s.total) return hipErrorInvalidValue;
     // 32-bit buffer offsets over each operand's planes (under 2 GiB per plane
     // set); grid dimensions.  Past
     // these limits the call is not supported (the caller can split the tokens
     // and add the gradients).
-    const int S = dtype_bf16 ? 2 : 4;
+    const int S = io == kIoF32 ? 4 : 2;
     if ((int64_t)N * C_in * s.Tp * S >= ((int64_t)1 << 31) || (int64_t)N * C_out * s.Tp * S >= ((int64_t)1 << 31))
         return hipErrorNotSupported;
     if (s.Tp / 64 > 0x7fffffff || (C_in + 7) / 8 > 65535 || (C_out + 7) / 8 > 65535 ||
         (int64_t)s.tiles * s.splits > 0x7fffffff)
         return hipErrorNotSupported;
     char* ws = static_cast<char*>(workspace);
-    if (dtype_bf16) return dispatch_backward_weight<__bf16>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
+    if (io == kIoF16) return dispatch_backward_weight<_Float16>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
+    if (io == kIoBF16) return dispatch_backward_weight<__bf16>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
     return dispatch_backward_weight<float>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
 }
 

@@ -56,8 +56,8 @@ hipError_t launch_w_hat_adjoint(int N, int io, const void* w_hat, void* w_hat_ad
 
 // Weight gradient of the C_N layer into fp32 dw[C_out][C_in][N]; the workspace
 // holds the operand planes and the per-range partial spectra.
-size_t backward_weight_workspace(int N, int dtype_bf16, int64_t T, int C_in, int C_out);
-hipError_t launch_cn_backward_weight(int N, int dtype_bf16, const void* x, const void* dy, float* dw, int64_t T,
+size_t backward_weight_workspace(int N, int io, int64_t T, int C_in, int C_out);
+hipError_t launch_cn_backward_weight(int N, int io, const void* x, const void* dy, float* dw, int64_t T,
                                      int C_in, int C_out, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 

@@ -258,21 +258,20 @@ eqlinear_status eqlinear_backward_data(eqlinear_plan_t p, const void* dy, const 
 }
 
 size_t eqlinear_backward_weight_workspace(eqlinear_plan_t p, int64_t T) {
-    if (!p || p->kind != EQL_KIND_CN || T < 0 || p->dtype == EQL_F16) return 0;
-    return eql::backward_weight_workspace(p->N, p->dtype == EQL_BF16, T, p->C_in, p->C_out);
+    if (!p || p->kind != EQL_KIND_CN || T < 0) return 0;
+    return eql::backward_weight_workspace(p->N, p->dtype, T, p->C_in, p->C_out);
 }
 
 eqlinear_status eqlinear_backward_weight(eqlinear_plan_t p, const void* x, const void* dy, float* dw, int64_t T,
                                          void* workspace, size_t workspace_bytes, void* stream) {
     if (!p || p->kind != EQL_KIND_CN || !dw) return EQL_ERR_INVALID;
     if (T < 0) return EQL_ERR_INVALID;
-    if (p->dtype == EQL_F16) return EQL_ERR_UNSUPPORTED;  // the weight-gradient kernels are fp32 and bf16
     if (!aligned16(dw)) return EQL_ERR_INVALID;
     const size_t dwb = eqlinear_w_hat_elems(p) * sizeof(float);
     if (T > 0) {
         if (!x || !dy || !workspace) return EQL_ERR_INVALID;
         if (!aligned16(x) || !aligned16(dy) || ((uintptr_t)workspace & 255u) != 0) return EQL_ERR_INVALID;
-        const size_t need = eql::backward_weight_workspace(p->N, p->dtype == EQL_BF16, T, p->C_in, p->C_out);
+        const size_t need = eql::backward_weight_workspace(p->N, p->dtype, T, p->C_in, p->C_out);
         if (workspace_bytes < need) return EQL_ERR_INVALID;
         const size_t es = elem_size(p);
         const size_t xb = (size_t)T * in_width(p) * es, dyb = (size_t)T * out_width(p) * es;
@@ -280,7 +279,7 @@ eqlinear_status eqlinear_backward_weight(eqlinear_plan_t p, const void* x, const
             overlaps(workspace, need, x, xb) || overlaps(workspace, need, dy, dyb))
             return EQL_ERR_INVALID;
     }
-    const hipError_t e = eql::launch_cn_backward_weight(p->N, p->dtype == EQL_BF16, x, dy, dw, T, p->C_in, p->C_out,
+    const hipError_t e = eql::launch_cn_backward_weight(p->N, p->dtype, x, dy, dw, T, p->C_in, p->C_out,
                                                         workspace, workspace_bytes, (hipStream_t)stream);
     return e == hipErrorNotSupported ? EQL_ERR_UNSUPPORTED : hip_status(e);
 }

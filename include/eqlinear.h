@@ -24,11 +24,12 @@
  *    EQL_F16 = IEEE binary16 (accumulation is always fp32).  fp16 ("Flash
  *    EQ-Linear", Implementation: FP32 and FP16 kernels; "Quick ViTs", key
  *    findings, Table 2 in fp16) is taken by the C_N plans' weight spectrum,
- *    forward (every tile; with fused bias/GELU), adjoint spectrum, input
- *    gradient and expanded-dense comparator; the weight gradient and D8 plans
+ *    forward (every tile; with fused bias/GELU), adjoint spectrum, input and
+ *    weight gradients and expanded-dense comparator; D8 and dihedral plans
  *    return EQL_ERR_UNSUPPORTED for it.  fp16 holds values up to 65504: inputs,
- *    outputs and (in the matrix-core transform kernel) the Fourier-domain
- *    intermediates must stay within that range.
+ *    outputs and (in the matrix-core transform kernel and the weight
+ *    gradient's transformed x and dy) the Fourier-domain intermediates must
+ *    stay within that range.
  *  - Layouts are row-major with the last index contiguous:
  *      x [T][C_in][N], y [T][C_out][N], w [C_out][C_in][N]           (C_N)
  *      x [T][C_in], y [T][C_out] with features [A1|A2|B1|B2|E0|E1]  (D8)
@@ -268,7 +269,7 @@ eqlinear_status eqlinear_backward_data(eqlinear_plan_t plan, const void* dy, con
                                        void* dx, int64_t T, void* stream);
 
 /* Bytes of device workspace that eqlinear_backward_weight needs for T tokens
- * (0 for T <= 0, a non-C_N plan or an fp16 plan). */
+ * (0 for T <= 0 or a non-C_N plan). */
 size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t T);
 
 /* Weight gradient: dw [C_out][C_in][N] in fp32 (overwritten, for either plan
@@ -283,7 +284,7 @@ size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t T);
  * not overlapping x, dy or dw; its contents are scratch.  x, dy, dw 16-byte
  * aligned.  T == 0 writes zeros to dw.  Asynchronous on stream; no allocation.
  * EQL_ERR_INVALID for a D8 plan, bad pointers, overlap or a short workspace;
- * EQL_ERR_UNSUPPORTED for an fp16 plan, or when the transformed x or dy held in
+ * EQL_ERR_UNSUPPORTED when the transformed x or dy held in
  * the workspace would reach 2 GiB (N C T S bytes each, S the element size; for
  * N = 7, C = 160, bf16 that is about 958 000 tokens): split the tokens into
  * parts and add the parts' gradients. */

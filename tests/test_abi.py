@@ -90,8 +90,8 @@ def test_dihedral_plans(eq):
 
 
 def test_fp16_plans(eq):
-    """fp16 C_N plans exist (weight spectrum, forward, input gradient, comparator);
-    the weight gradient and D8 plans turn fp16 away before any HIP call."""
+    """fp16 C_N plans exist (weight spectrum, forward, both gradients, comparator);
+    D8 plans turn fp16 away before any HIP call."""
     lib = eq.load_library()
     p = eq.eqlinear_plan(8, 16, 24, eq.EQL_F16)
     assert p.info["dtype"] == eq.EQL_F16 and p.info["w_hat_elems"] == 8 * 16 * 24
@@ -99,8 +99,10 @@ def test_fp16_plans(eq):
         eq.eqlinear_d8_plan(16, 16, eq.EQL_F16)
     assert e.value.status == eq.EQL_ERR_UNSUPPORTED
     A, B, W, S = 1 << 20, 1 << 30, 1 << 34, 1 << 38
-    assert lib.eqlinear_backward_weight_workspace(p.handle, 100) == 0
-    assert lib.eqlinear_backward_weight(p.handle, A, B, W, 100, S, 1 << 20, None) == eq.EQL_ERR_UNSUPPORTED
+    # the weight gradient's workspace holds fp16 planes: the same size as a bf16 plan's
+    pb = eq.eqlinear_plan(8, 16, 24, eq.EQL_BF16)
+    need = lib.eqlinear_backward_weight_workspace(p.handle, 100)
+    assert need > 0 and need == lib.eqlinear_backward_weight_workspace(pb.handle, 100)
     # the forward's checks size fp16 tensors at 2 bytes: y one element into x's last row overlaps
     x_bytes = 5 * 16 * 8 * 2
     assert lib.eqlinear_forward(p.handle, A, W, A + x_bytes - 16, 5, None) == eq.EQL_ERR_INVALID

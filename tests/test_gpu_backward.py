@@ -1,10 +1,10 @@
 """GPU parity of the backward pass (input and weight gradients) against the fp64 oracle.
 
-Same bars as the forward (tests/gpu_util.py): rel-L2 <= 1e-5 (fp32 plans) or
-<= 2e-2 (bf16 plans) over the whole output, and the largest element error
-relative to the output's RMS under 2e-4 / 1e-1.  The weight gradient is fp32
-for both plan dtypes.  Inputs come from synthetic.py (seeded); expected values
-only from oracle/.
+Same bars as the forward (tests/gpu_util.py): rel-L2 <= 1e-5 (fp32 plans),
+<= 2e-2 (bf16 plans) or <= 2.5e-3 (fp16 plans) over the whole output, and the
+largest element error relative to the output's RMS under 2e-4 / 1e-1 /
+1.25e-2.  The weight gradient is fp32 for every plan dtype.  Inputs come from
+synthetic.py (seeded); expected values only from oracle/.
 """
 import numpy as np
 import pytest
@@ -109,7 +109,7 @@ def test_backward_data_sweep(eq, N, dt):
 
 # --- weight gradient --------------------------------------------------------------------
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 12, 16])
 def test_backward_weight_sweep(eq, N, dt):
     for C_in, C_out, T in SHAPES + [(16, 16, 1), (70, 66, 1000)]:
@@ -132,7 +132,7 @@ def test_backward_weight_zero_tokens_writes_zeros(eq):
     assert torch.count_nonzero(dw.t).item() == 0
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 def test_backward_weight_is_deterministic(eq, dt):
     N, C_in, C_out, T = 7, 40, 72, 3000
     d = _inputs(N, C_in, C_out, T, dt, seed=5)
@@ -141,7 +141,7 @@ def test_backward_weight_is_deterministic(eq, dt):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N,C_in,C_out", [(5, 24, 32), (8, 32, 32), (16, 32, 9)])
 def test_backward_weight_small_layers_many_chunks(eq, N, C_in, C_out, dt):
     """Layers with at most 32 channels each way take the one-launch path; at
@@ -155,7 +155,7 @@ def test_backward_weight_small_layers_many_chunks(eq, N, C_in, C_out, dt):
     assert np.array_equal(dw, run_backward_weight(eq, N, C_in, C_out, T, dt, d))
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N", [1, 2, 3, 7, 8, 16])
 def test_backward_weight_whole_tile_bins(eq, N, dt):
     """Wide layers whose (o, i) tile fits one workgroup of up to 16 waves take the
@@ -172,7 +172,7 @@ def test_backward_weight_whole_tile_bins(eq, N, dt):
             assert np.array_equal(dw, run_backward_weight(eq, N, C_in, C_out, T, dt, d))
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("N", [1, 3, 8, 16])
 def test_backward_weight_64_tiles(eq, N, dt):
     """At most 32 output channels with more than 32 input channels: no whole tile
@@ -185,7 +185,7 @@ def test_backward_weight_64_tiles(eq, N, dt):
         assert_close(dw, ref, dt, f"dw N={N} {dt} {C_in}->{C_out} T={T}")
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 def test_gradients_satisfy_the_adjoint_identity(eq, dt):
     """<dy, y(x)> = <dx, x> = <dw, w> with all three computed on the GPU."""
     import torch
