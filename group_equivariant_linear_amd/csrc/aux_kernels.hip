@@ -164,10 +164,13 @@ hipError_t launch_cn_expand(int N, int io, const void* w, void* w_dense, int C_i
     return hipGetLastError();
 }
 
-hipError_t launch_dn_expand(int n, int dtype_bf16, const void* wb, void* w_dense, int C_in, int C_out,
+hipError_t launch_dn_expand(int n, int io, const void* wb, void* w_dense, int C_in, int C_out,
                             hipStream_t stream) {
     const int64_t total = (int64_t)C_out * C_in;
-    if (dtype_bf16)
+    if (io == kIoF16)
+        hipLaunchKernelGGL(dn_expand_kernel<_Float16>, dim3(grid_for(total, 256)), dim3(256), 0,
+                           stream, (const _Float16*)wb, (_Float16*)w_dense, n, C_in, C_out, total);
+    else if (io == kIoBF16)
         hipLaunchKernelGGL(dn_expand_kernel<__bf16>, dim3(grid_for(total, 256)), dim3(256), 0,
                            stream, (const __bf16*)wb, (__bf16*)w_dense, n, C_in, C_out, total);
     else

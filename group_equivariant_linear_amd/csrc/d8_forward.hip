@@ -79,11 +79,20 @@ __device__ __forceinline__ int ypiece(int r, int k) {
     else return r * P + k;
 }
 
-// One tile: tokens t0 .. t0+TT-1, output channels n0 .. n0+CT-1 of job.
-template <class C>
-__device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, const __bf16* __restrict__ x,
-                                        const __bf16* __restrict__ w, __bf16* __restrict__ y, int64_t T, int ldx,
+__device__ __forceinline__ f32x4 d8_mma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 d8_mma(const f16x8& a, const f16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// One tile: tokens t0 .. t0+TT-1, output channels n0 .. n0+CT-1 of job.  IO is
+// __bf16 or _Float16 (the matrix-core product of the same shape for either).
+template <class C, typename IO>
+__device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, const IO* __restrict__ x,
+                                        const IO* __restrict__ w, IO* __restrict__ y, int64_t T, int ldx,
                                         int ldy, uint32_t w_bytes, char* smem) {
+    using F8 = typename Half<IO>::x8;
     constexpr int TPW = C::TPW, NPW = C::NPW;
     const int K = job.K, Nn = job.Nn;
 
@@ -173,24 +182,24 @@ __device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, 
         for (int ks = 0; ks < 2; ++ks) {
             if (c * C::KC + 32 * ks >= K) break;  // a last chunk's empty half (uniform per job)
             const int l_off = swz(tl, 4 * ks + kg) * 16;
-            bf16x8 A[NPW], B[TPW];
+            F8 A[NPW], B[TPW];
 #pragma unroll
-            for (int a = 0; a < NPW; ++a) A[a] = *reinterpret_cast<const bf16x8*>(wb + a * 2048 + l_off);
+            for (int a = 0; a < NPW; ++a) A[a] = *reinterpret_cast<const F8*>(wb + a * 2048 + l_off);
 #pragma unroll
-            for (int b = 0; b < TPW; ++b) B[b] = *reinterpret_cast<const bf16x8*>(xb + b * 2048 + l_off);
+            for (int b = 0; b < TPW; ++b) B[b] = *reinterpret_cast<const F8*>(xb + b * 2048 + l_off);
             if (c * C::KC + C::KC > K && c * C::KC + 32 * ks + kg * 8 >= K) {
                 // input-channel tail: k-values past K are zero on both sides (the
                 // parts there were never loaded)
 #pragma unroll
-                for (int a = 0; a < NPW; ++a) A[a] = bf16x8{};
+                for (int a = 0; a < NPW; ++a) A[a] = F8{};
 #pragma unroll
-                for (int b = 0; b < TPW; ++b) B[b] = bf16x8{};
+                for (int b = 0; b < TPW; ++b) B[b] = F8{};
             }
 #pragma unroll
             for (int a = 0; a < NPW; ++a)
 #pragma unroll
                 for (int b = 0; b < TPW; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[a], B[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = d8_mma(A[a], B[b], acc[a][b]);
         }
     }
 
@@ -204,7 +213,7 @@ __device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, 
         for (int b = 0; b < TPW; ++b) {
             const int by = (16 * a + 4 * kg) * 2;  // 8 bytes, inside one 16-byte piece
             *reinterpret_cast<u32x2*>(yst + ypiece<C::YROT, C::YP, C::YPITCH>(16 * b + tl, by / 16) * 16 + (by % 16)) =
-                u32x2{pack_bf16x2(acc[a][b][0], acc[a][b][1]), pack_bf16x2(acc[a][b][2], acc[a][b][3])};
+                u32x2{Half<IO>::pack2(acc[a][b][0], acc[a][b][1]), Half<IO>::pack2(acc[a][b][2], acc[a][b][3])};
         }
     const int nw0 = n0 + wn * NPW * 16;   // first channel of this wave
     const int lim = (Nn - nw0) * 2;       // valid bytes of a staged row
@@ -224,9 +233,9 @@ __device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, 
 // Workgroups take one tile each.  Jobs flagged narrow (the ones with twice the
 // input channels: W_E on an E coordinate) use the CN shape, the others CW, so
 // that every workgroup has the same number of products.
-template <class CW, class CN>
-__global__ __launch_bounds__(CW::kThreads) void d8_kernel(GemmJobs jobs, const __bf16* __restrict__ x,
-                                                          const __bf16* __restrict__ w, __bf16* __restrict__ y,
+template <class CW, class CN, typename IO>
+__global__ __launch_bounds__(CW::kThreads) void d8_kernel(GemmJobs jobs, const IO* __restrict__ x,
+                                                          const IO* __restrict__ w, IO* __restrict__ y,
                                                           int64_t T, int ldx, int ldy, uint32_t total_tiles,
                                                           uint32_t w_bytes) {
     static_assert(CW::TT == CN::TT && CW::kThreads == CN::kThreads, "one workgroup shape");
@@ -241,12 +250,12 @@ __global__ __launch_bounds__(CW::kThreads) void d8_kernel(GemmJobs jobs, const _
         if (j < jobs.njobs && jt >= jobs.j[j].tile_begin) ji = j;
     const GemmJob job = jobs.j[ji];
     if (job.narrow)
-        d8_tile<CN>(job, (jt - job.tile_begin) * CN::CT, t0, x, w, y, T, ldx, ldy, w_bytes, smem);
+        d8_tile<CN, IO>(job, (jt - job.tile_begin) * CN::CT, t0, x, w, y, T, ldx, ldy, w_bytes, smem);
     else
-        d8_tile<CW>(job, (jt - job.tile_begin) * CW::CT, t0, x, w, y, T, ldx, ldy, w_bytes, smem);
+        d8_tile<CW, IO>(job, (jt - job.tile_begin) * CW::CT, t0, x, w, y, T, ldx, ldy, w_bytes, smem);
 }
 
-template <class CW, class CN>
+template <class CW, class CN, typename IO>
 hipError_t launch_d8_cfg(GemmJobs jobs, const void* x, const void* w, void* y, int64_t T, int ldx, int ldy,
                          int64_t w_elems, hipStream_t stream) {
     int kmin = jobs.j[0].K;
@@ -261,18 +270,36 @@ hipError_t launch_d8_cfg(GemmJobs jobs, const void* x, const void* w, void* y, i
     jobs.tiles_per_row = tiles;
     const int64_t total = (T + CW::TT - 1) / CW::TT * tiles;
     if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((d8_kernel<CW, CN>), dim3((uint32_t)total), dim3(CW::kThreads), 0, stream, jobs,
-                       (const __bf16*)x, (const __bf16*)w, (__bf16*)y, T, ldx, ldy, (uint32_t)total,
+    hipLaunchKernelGGL((d8_kernel<CW, CN, IO>), dim3((uint32_t)total), dim3(CW::kThreads), 0, stream, jobs,
+                       (const IO*)x, (const IO*)w, (IO*)y, T, ldx, ldy, (uint32_t)total,
                        (uint32_t)(w_elems * 2));
     return hipGetLastError();
 }
 
+template <typename IO>
+hipError_t launch_d8_shape(GemmJobs jobs, const void* x, const void* w, void* y, int64_t T, int ldx, int ldy,
+                           int64_t w_elems, int cb, hipStream_t stream) {
+    // 128 tokens x 160 channels (2x2 waves), or x 80 channels (4x1 waves) for
+    // the jobs with twice the input channels; the smaller shapes use one tile
+    // for every job
+    using Wide = D8Cfg<2, 2, 4, 5, 2>;
+    using Narrow = D8Cfg<4, 1, 2, 5, 2>;
+    using Small = D8Cfg<4, 1, 1, 2, 2>;
+    switch (cb) {
+        case 5:
+            return launch_d8_cfg<D8Cfg<2, 1, 4, 5, 2>, D8Cfg<2, 1, 4, 5, 2>, IO>(jobs, x, w, y, T, ldx, ldy, w_elems,
+                                                                                stream);
+        case 2: return launch_d8_cfg<Small, Small, IO>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
+        default: return launch_d8_cfg<Wide, Narrow, IO>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
+    }
+}
+
 }  // namespace
 
-// The D8 jobs on the kernel above when every job column, width and W row is a
-// whole number of 16-byte pieces and all offsets fit 32 bits; otherwise
-// hipErrorNotSupported (the caller then uses gemm_rows).
-hipError_t launch_d8_fast(GemmJobs jobs, const void* x, const void* w, void* y, int64_t T, int ldx, int ldy,
+// The D8 jobs on the kernel above (bf16 or fp16) when every job column, width
+// and W row is a whole number of 16-byte pieces and all offsets fit 32 bits;
+// otherwise hipErrorNotSupported (the caller then uses gemm_rows).
+hipError_t launch_d8_fast(int io, GemmJobs jobs, const void* x, const void* w, void* y, int64_t T, int ldx, int ldy,
                           int64_t w_elems, int cb, hipStream_t stream) {
     const int64_t lim = (int64_t)1 << 30;
     if (ldx % 8 || ldy % 8 || w_elems * 2 >= lim || (int64_t)128 * ldx * 2 >= lim || (int64_t)128 * ldy * 2 >= lim)
@@ -281,17 +308,9 @@ hipError_t launch_d8_fast(GemmJobs jobs, const void* x, const void* w, void* y, 
         const GemmJob& g = jobs.j[j];
         if (g.x_col % 8 || g.y_col % 8 || g.K % 8 || g.Nn % 8 || g.ldw % 8 || g.w_off % 8) return hipErrorNotSupported;
     }
-    // 128 tokens x 160 channels (2x2 waves), or x 80 channels (4x1 waves) for
-    // the jobs with twice the input channels; the smaller shapes use one tile
-    // for every job
-    using Wide = D8Cfg<2, 2, 4, 5, 2>;
-    using Narrow = D8Cfg<4, 1, 2, 5, 2>;
-    using Small = D8Cfg<4, 1, 1, 2, 2>;
-    switch (cb) {
-        case 5: return launch_d8_cfg<D8Cfg<2, 1, 4, 5, 2>, D8Cfg<2, 1, 4, 5, 2>>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
-        case 2: return launch_d8_cfg<Small, Small>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
-        default: return launch_d8_cfg<Wide, Narrow>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
-    }
+    if (io == kIoF16) return launch_d8_shape<_Float16>(jobs, x, w, y, T, ldx, ldy, w_elems, cb, stream);
+    if (io == kIoBF16) return launch_d8_shape<__bf16>(jobs, x, w, y, T, ldx, ldy, w_elems, cb, stream);
+    return hipErrorNotSupported;
 }
 
 }  // namespace eql

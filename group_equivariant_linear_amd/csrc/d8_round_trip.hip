@@ -82,16 +82,16 @@ __device__ __forceinline__ void load_k(const IO* p, float (&o)[K]) {
             const u32x4 w = reinterpret_cast<const u32x4*>(p)[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                o[8 * i + 2 * e] = __uint_as_float(w[e] << 16);
-                o[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                o[8 * i + 2 * e] = Half<IO>::lo(w[e]);
+                o[8 * i + 2 * e + 1] = Half<IO>::hi(w[e]);
             }
         }
     } else if constexpr (sizeof(IO) == 2 && K == 4) {
         const u32x2 w = *reinterpret_cast<const u32x2*>(p);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            o[2 * e] = __uint_as_float(w[e] << 16);
-            o[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            o[2 * e] = Half<IO>::lo(w[e]);
+            o[2 * e + 1] = Half<IO>::hi(w[e]);
         }
     } else {
 #pragma unroll
@@ -110,15 +110,15 @@ __device__ __forceinline__ void store_k(IO* p, const float (&v)[K]) {
 #pragma unroll
         for (int i = 0; i < K / 8; ++i)
             reinterpret_cast<u32x4*>(p)[i] =
-                u32x4{pack_bf16x2(v[8 * i], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
-                      pack_bf16x2(v[8 * i + 4], v[8 * i + 5]), pack_bf16x2(v[8 * i + 6], v[8 * i + 7])};
+                u32x4{Half<IO>::pack2(v[8 * i], v[8 * i + 1]), Half<IO>::pack2(v[8 * i + 2], v[8 * i + 3]),
+                      Half<IO>::pack2(v[8 * i + 4], v[8 * i + 5]), Half<IO>::pack2(v[8 * i + 6], v[8 * i + 7])};
     } else if constexpr (sizeof(IO) == 2 && K == 4) {
-        *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(p) = u32x2{Half<IO>::pack2(v[0], v[1]), Half<IO>::pack2(v[2], v[3])};
     } else {
 #pragma unroll
         for (int e = 0; e < K; ++e) {
             if constexpr (sizeof(IO) == 4) p[e] = v[e];
-            else reinterpret_cast<uint16_t*>(p)[e] = (uint16_t)(pack_bf16x2(v[e], 0.f) & 0xffffu);
+            else reinterpret_cast<uint16_t*>(p)[e] = (uint16_t)(Half<IO>::pack2(v[e], 0.f) & 0xffffu);
         }
     }
 }
@@ -224,9 +224,10 @@ hipError_t launch_pass(const void* in, void* out, const void* bias, int act, int
 }
 
 template <int MODE>
-hipError_t launch_pass_dt(int dtype_bf16, const void* in, void* out, const void* bias, int act, int m, int64_t T,
+hipError_t launch_pass_dt(int io, const void* in, void* out, const void* bias, int act, int m, int64_t T,
                           hipStream_t stream) {
-    if (dtype_bf16) return launch_pass<__bf16, MODE>(in, out, bias, act, m, T, stream);
+    if (io == kIoF16) return launch_pass<_Float16, MODE>(in, out, bias, act, m, T, stream);
+    if (io == kIoBF16) return launch_pass<__bf16, MODE>(in, out, bias, act, m, T, stream);
     return launch_pass<float, MODE>(in, out, bias, act, m, T, stream);
 }
 
@@ -347,43 +348,44 @@ hipError_t launch_dn_pass(int n, const void* in, void* out, const void* bias, in
 
 // n == 4 (D8) takes the butterfly kernel above; other orders the table kernel
 template <int MODE>
-hipError_t launch_dihedral_pass(int n, int dtype_bf16, const void* in, void* out, const void* bias, int act, int m,
+hipError_t launch_dihedral_pass(int n, int io, const void* in, void* out, const void* bias, int act, int m,
                                 int64_t T, hipStream_t stream) {
-    if (n == 4) return launch_pass_dt<MODE>(dtype_bf16, in, out, bias, act, m, T, stream);
-    if (dtype_bf16) return launch_dn_pass<__bf16, MODE>(n, in, out, bias, act, m, T, stream);
+    if (n == 4) return launch_pass_dt<MODE>(io, in, out, bias, act, m, T, stream);
+    if (io == kIoF16) return launch_dn_pass<_Float16, MODE>(n, in, out, bias, act, m, T, stream);
+    if (io == kIoBF16) return launch_dn_pass<__bf16, MODE>(n, in, out, bias, act, m, T, stream);
     return launch_dn_pass<float, MODE>(n, in, out, bias, act, m, T, stream);
 }
 
 }  // namespace
 
-hipError_t launch_dn_round_trip(int n, int dtype_bf16, const void* y_in, void* y_out, const void* bias, int act,
+hipError_t launch_dn_round_trip(int n, int io, const void* y_in, void* y_out, const void* bias, int act,
                                 int m, int64_t T, hipStream_t stream) {
-    return launch_dihedral_pass<kRoundTrip>(n, dtype_bf16, y_in, y_out, bias, act, m, T, stream);
+    return launch_dihedral_pass<kRoundTrip>(n, io, y_in, y_out, bias, act, m, T, stream);
 }
 
-hipError_t launch_dn_to_fourier(int n, int dtype_bf16, const void* x_reg, void* x_four, int m, int64_t T,
+hipError_t launch_dn_to_fourier(int n, int io, const void* x_reg, void* x_four, int m, int64_t T,
                                 hipStream_t stream) {
-    return launch_dihedral_pass<kToFourier>(n, dtype_bf16, x_reg, x_four, nullptr, 0, m, T, stream);
+    return launch_dihedral_pass<kToFourier>(n, io, x_reg, x_four, nullptr, 0, m, T, stream);
 }
 
-hipError_t launch_dn_to_regular(int n, int dtype_bf16, const void* y_four, void* y_reg, int m, int64_t T,
+hipError_t launch_dn_to_regular(int n, int io, const void* y_four, void* y_reg, int m, int64_t T,
                                 hipStream_t stream) {
-    return launch_dihedral_pass<kToRegular>(n, dtype_bf16, y_four, y_reg, nullptr, 0, m, T, stream);
+    return launch_dihedral_pass<kToRegular>(n, io, y_four, y_reg, nullptr, 0, m, T, stream);
 }
 
-hipError_t launch_d8_round_trip(int dtype_bf16, const void* y_in, void* y_out, const void* bias, int act, int m,
+hipError_t launch_d8_round_trip(int io, const void* y_in, void* y_out, const void* bias, int act, int m,
                                 int64_t T, hipStream_t stream) {
-    return launch_pass_dt<kRoundTrip>(dtype_bf16, y_in, y_out, bias, act, m, T, stream);
+    return launch_pass_dt<kRoundTrip>(io, y_in, y_out, bias, act, m, T, stream);
 }
 
-hipError_t launch_d8_to_fourier(int dtype_bf16, const void* x_reg, void* x_four, int m, int64_t T,
+hipError_t launch_d8_to_fourier(int io, const void* x_reg, void* x_four, int m, int64_t T,
                                 hipStream_t stream) {
-    return launch_pass_dt<kToFourier>(dtype_bf16, x_reg, x_four, nullptr, 0, m, T, stream);
+    return launch_pass_dt<kToFourier>(io, x_reg, x_four, nullptr, 0, m, T, stream);
 }
 
-hipError_t launch_d8_to_regular(int dtype_bf16, const void* y_four, void* y_reg, int m, int64_t T,
+hipError_t launch_d8_to_regular(int io, const void* y_four, void* y_reg, int m, int64_t T,
                                 hipStream_t stream) {
-    return launch_pass_dt<kToRegular>(dtype_bf16, y_four, y_reg, nullptr, 0, m, T, stream);
+    return launch_pass_dt<kToRegular>(io, y_four, y_reg, nullptr, 0, m, T, stream);
 }
 
 }  // namespace eql

@@ -9,8 +9,7 @@ namespace eql {
 constexpr int kMaxGemmJobs = 16;  // D8: 6 jobs; D_n: n + 1 (odd n) or n + 2 (even n), n <= 12
 
 // Element type of a launch's tensors ("io" arguments), the codes of the C ABI's
-// eqlinear_dtype.  Launchers that take a plain "dtype_bf16" flag have no fp16
-// form; the C ABI turns fp16 plans away before it reaches them.
+// eqlinear_dtype.
 enum : int { kIoF32 = 0, kIoBF16 = 1, kIoF16 = 2 };
 
 // Fused neighbours of the C_N forward: y = act(y + bias[o]) in the epilogue.
@@ -47,7 +46,7 @@ hipError_t launch_gemm_rows(int io, GemmJobs jobs, const void* x, const void* w,
 // bf16 D8 jobs on the dedicated kernel (16*cb output channels per workgroup);
 // hipErrorNotSupported when a job column, width or W row is not a whole number
 // of 16-byte pieces (then use launch_gemm_rows).
-hipError_t launch_d8_fast(GemmJobs jobs, const void* x, const void* w, void* y, int64_t T, int ldx, int ldy,
+hipError_t launch_d8_fast(int io, GemmJobs jobs, const void* x, const void* w, void* y, int64_t T, int ldx, int ldy,
                           int64_t w_elems, int cb, hipStream_t stream);
 
 // Adjoint spectrum: w_hat_adj[p][i][o] = +-w_hat[p][o][i] (imaginary planes negated).
@@ -68,22 +67,22 @@ hipError_t launch_cn_expand(int N, int io, const void* w, void* w_dense, int C_i
                             int C_out, hipStream_t stream);
 
 // dihedral D_n block matrix (n = 4: D8)
-hipError_t launch_dn_expand(int n, int dtype_bf16, const void* wb, void* w_dense, int C_in, int C_out,
+hipError_t launch_dn_expand(int n, int io, const void* wb, void* w_dense, int C_in, int C_out,
                             hipStream_t stream);
 
 // d8_round_trip.hip: m = C/8 regular channels per token
-hipError_t launch_d8_round_trip(int dtype_bf16, const void* y_in, void* y_out, const void* bias, int act, int m,
+hipError_t launch_d8_round_trip(int io, const void* y_in, void* y_out, const void* bias, int act, int m,
                                 int64_t T, hipStream_t stream);
-hipError_t launch_d8_to_fourier(int dtype_bf16, const void* x_reg, void* x_four, int m, int64_t T,
+hipError_t launch_d8_to_fourier(int io, const void* x_reg, void* x_four, int m, int64_t T,
                                 hipStream_t stream);
-hipError_t launch_d8_to_regular(int dtype_bf16, const void* y_four, void* y_reg, int m, int64_t T,
+hipError_t launch_d8_to_regular(int io, const void* y_four, void* y_reg, int m, int64_t T,
                                 hipStream_t stream);
 // the same passes for D_n, m = C/2n regular channels (n = 4 takes the D8 kernels)
-hipError_t launch_dn_round_trip(int n, int dtype_bf16, const void* y_in, void* y_out, const void* bias, int act,
+hipError_t launch_dn_round_trip(int n, int io, const void* y_in, void* y_out, const void* bias, int act,
                                 int m, int64_t T, hipStream_t stream);
-hipError_t launch_dn_to_fourier(int n, int dtype_bf16, const void* x_reg, void* x_four, int m, int64_t T,
+hipError_t launch_dn_to_fourier(int n, int io, const void* x_reg, void* x_four, int m, int64_t T,
                                 hipStream_t stream);
-hipError_t launch_dn_to_regular(int n, int dtype_bf16, const void* y_four, void* y_reg, int m, int64_t T,
+hipError_t launch_dn_to_regular(int n, int io, const void* y_four, void* y_reg, int m, int64_t T,
                                 hipStream_t stream);
 
 }  // namespace eql

@@ -80,7 +80,6 @@ eqlinear_status eqlinear_dihedral_plan(eqlinear_plan_t* out, int n, int C_in, in
     if (n < 2 || n > 12) return EQL_ERR_INVALID;
     const int G = 2 * n;  // group order: the plan's N
     if (C_in < G || C_out < G || C_in % G || C_out % G || !dtype_ok((int)dt)) return EQL_ERR_INVALID;
-    if (dt == EQL_F16) return EQL_ERR_UNSUPPORTED;  // the dihedral kernels are fp32 and bf16
     if (C_in > kMaxWidth || C_out > kMaxWidth) return EQL_ERR_INVALID;
     eqlinear_plan_s* p = new (std::nothrow) eqlinear_plan_s{EQL_KIND_D8, (int)dt, G, C_in, C_out};
     if (!p) return EQL_ERR_NOMEM;
@@ -204,7 +203,7 @@ eqlinear_status eqlinear_d8_bias_act(eqlinear_plan_t p, const void* y_in, const 
     const size_t yb = (size_t)T * p->C_out * es, bb = (size_t)(p->C_out / p->N) * es;
     if (y_in != y_out && overlaps(y_in, yb, y_out, yb)) return EQL_ERR_INVALID;  // in place, or apart
     if (bias && (((uintptr_t)bias % es) != 0 || overlaps(bias, bb, y_out, yb))) return EQL_ERR_INVALID;
-    return hip_status(eql::launch_dn_round_trip(p->N / 2, p->dtype == EQL_BF16, y_in, y_out, bias, act,
+    return hip_status(eql::launch_dn_round_trip(p->N / 2, p->dtype, y_in, y_out, bias, act,
                                                 p->C_out / p->N, T, (hipStream_t)stream));
 }
 
@@ -216,7 +215,7 @@ eqlinear_status eqlinear_d8_to_fourier(eqlinear_plan_t p, const void* x_reg, voi
     if (!x_reg || !x_four || !aligned16(x_reg) || !aligned16(x_four)) return EQL_ERR_INVALID;
     const size_t b = (size_t)T * p->C_in * elem_size(p);
     if (overlaps(x_reg, b, x_four, b)) return EQL_ERR_INVALID;
-    return hip_status(eql::launch_dn_to_fourier(p->N / 2, p->dtype == EQL_BF16, x_reg, x_four, p->C_in / p->N,
+    return hip_status(eql::launch_dn_to_fourier(p->N / 2, p->dtype, x_reg, x_four, p->C_in / p->N,
                                                 T, (hipStream_t)stream));
 }
 
@@ -228,7 +227,7 @@ eqlinear_status eqlinear_d8_to_regular(eqlinear_plan_t p, const void* y_four, vo
     if (!y_four || !y_reg || !aligned16(y_four) || !aligned16(y_reg)) return EQL_ERR_INVALID;
     const size_t b = (size_t)T * p->C_out * elem_size(p);
     if (overlaps(y_four, b, y_reg, b)) return EQL_ERR_INVALID;
-    return hip_status(eql::launch_dn_to_regular(p->N / 2, p->dtype == EQL_BF16, y_four, y_reg, p->C_out / p->N,
+    return hip_status(eql::launch_dn_to_regular(p->N / 2, p->dtype, y_four, y_reg, p->C_out / p->N,
                                                 T, (hipStream_t)stream));
 }
 
@@ -306,10 +305,10 @@ eqlinear_status eqlinear_d8_forward(eqlinear_plan_t p, const void* x, const void
             jobs.j[n1 + 2 * k + c] =
                 eql::GemmJob{n1 * mi + 4 * k * mi + 2 * c * mi, n1 * mo + 4 * k * mo + 2 * c * mo, 2 * mi, 2 * mo,
                              (int64_t)n1 * mo * mi + (int64_t)k * 4 * mo * mi, 2 * mi, 0, 0, 0, 0};
-    if (p->dtype == EQL_BF16) {
+    if (p->dtype == EQL_BF16 || p->dtype == EQL_F16) {
         // widest output tile that the 1-D blocks fill: 160, 80 or 32 channels
         const int cb = mo % 160 == 0 ? 10 : (mo % 80 == 0 ? 5 : 2);
-        const hipError_t e = eql::launch_d8_fast(jobs, x, wb, y, T, p->C_in, p->C_out,
+        const hipError_t e = eql::launch_d8_fast(p->dtype, jobs, x, wb, y, T, p->C_in, p->C_out,
                                                  (int64_t)eqlinear_w_hat_elems(p), cb, (hipStream_t)stream);
         if (e != hipErrorNotSupported) return hip_status(e);
     }
@@ -330,7 +329,7 @@ eqlinear_status eqlinear_expand_dense(eqlinear_plan_t p, const void* w, void* w_
         e = eql::launch_cn_expand(p->N, p->dtype, w, w_dense, p->C_in, p->C_out,
                                   (hipStream_t)stream);
     else
-        e = eql::launch_dn_expand(p->N / 2, p->dtype == EQL_BF16, w, w_dense, p->C_in, p->C_out,
+        e = eql::launch_dn_expand(p->N / 2, p->dtype, w, w_dense, p->C_in, p->C_out,
                                   (hipStream_t)stream);
     return hip_status(e);
 }

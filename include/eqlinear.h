@@ -25,11 +25,11 @@
  *    EQ-Linear", Implementation: FP32 and FP16 kernels; "Quick ViTs", key
  *    findings, Table 2 in fp16) is taken by the C_N plans' weight spectrum,
  *    forward (every tile; with fused bias/GELU), adjoint spectrum, input and
- *    weight gradients and expanded-dense comparator; D8 and dihedral plans
- *    return EQL_ERR_UNSUPPORTED for it.  fp16 holds values up to 65504: inputs,
- *    outputs and (in the matrix-core transform kernel and the weight
- *    gradient's transformed x and dy) the Fourier-domain intermediates must
- *    stay within that range.
+ *    weight gradients and expanded-dense comparator, and by the D8 and
+ *    dihedral plans' layer, passes and comparator.  fp16 holds values up to
+ *    65504: inputs, outputs and (in the matrix-core transform kernel and the
+ *    weight gradient's transformed x and dy) the Fourier-domain intermediates
+ *    must stay within that range.
  *  - Layouts are row-major with the last index contiguous:
  *      x [T][C_in][N], y [T][C_out][N], w [C_out][C_in][N]           (C_N)
  *      x [T][C_in], y [T][C_out] with features [A1|A2|B1|B2|E0|E1]  (D8)
@@ -96,7 +96,7 @@ eqlinear_status eqlinear_plan(eqlinear_plan_t* out, int N, int C_in, int C_out,
 
 /* Create a D8 plan ("Quick ViTs", key design 2).  C_in and C_out are full
  * widths, multiples of 8 (C/8 channels per 1-D irrep, C/4 copies of E); dt in
- * {EQL_F32, EQL_BF16} (EQL_F16: EQL_ERR_UNSUPPORTED).  Same as
+ * {EQL_F32, EQL_BF16, EQL_F16}.  Same as
  * eqlinear_dihedral_plan(out, 4, C_in, C_out, dt). */
 eqlinear_status eqlinear_d8_plan(eqlinear_plan_t* out, int C_in, int C_out,
                                  eqlinear_dtype dt);

@@ -85,19 +85,18 @@ def test_dihedral_plans(eq):
     h = ctypes.c_void_p()
     for bad in ((1, 8, 8), (13, 26, 26), (3, 8, 12), (3, 12, 8), (6, 12, 18)):
         assert lib.eqlinear_dihedral_plan(ctypes.byref(h), *bad, eq.EQL_F32) == eq.EQL_ERR_INVALID
-    assert lib.eqlinear_dihedral_plan(ctypes.byref(h), 3, 12, 12, eq.EQL_F16) == eq.EQL_ERR_UNSUPPORTED
+    assert lib.eqlinear_dihedral_plan(ctypes.byref(h), 3, 12, 12, eq.EQL_F16) == eq.EQL_OK
+    lib.eqlinear_plan_destroy(h)
     assert lib.eqlinear_dihedral_plan(None, 3, 12, 12, eq.EQL_F32) == eq.EQL_ERR_INVALID
 
 
 def test_fp16_plans(eq):
-    """fp16 C_N plans exist (weight spectrum, forward, both gradients, comparator);
-    D8 plans turn fp16 away before any HIP call."""
+    """fp16 plans exist for every group: C_N (weight spectrum, forward, both
+    gradients, comparator) and D8 (layer, passes, comparator)."""
     lib = eq.load_library()
     p = eq.eqlinear_plan(8, 16, 24, eq.EQL_F16)
     assert p.info["dtype"] == eq.EQL_F16 and p.info["w_hat_elems"] == 8 * 16 * 24
-    with pytest.raises(eq.EqlError) as e:
-        eq.eqlinear_d8_plan(16, 16, eq.EQL_F16)
-    assert e.value.status == eq.EQL_ERR_UNSUPPORTED
+    assert eq.eqlinear_d8_plan(16, 16, eq.EQL_F16).info["dtype"] == eq.EQL_F16
     A, B, W, S = 1 << 20, 1 << 30, 1 << 34, 1 << 38
     # the weight gradient's workspace holds fp16 planes: the same size as a bf16 plan's
     pb = eq.eqlinear_plan(8, 16, 24, eq.EQL_BF16)

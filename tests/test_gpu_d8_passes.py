@@ -19,7 +19,7 @@ from gpu_util import Guarded, assert_close, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
-F32, BF16 = synthetic.F32, synthetic.BF16
+F32, BF16, F16 = synthetic.F32, synthetic.BF16, synthetic.F16
 # C/8 = 1, 3, 4, 12, 160 (LDS-tiled path); 2056 and 2049: rows wider than the
 # tiled path stages (more than 2048 16-byte pieces in bf16), one pass per thread
 # with four channels (C/8 a multiple of 4) or one
@@ -37,7 +37,7 @@ def eq():
 
 
 def _eqdt(eq, dt):
-    return eq.EQL_F32 if dt == F32 else eq.EQL_BF16
+    return {F32: eq.EQL_F32, BF16: eq.EQL_BF16, F16: eq.EQL_F16}[dt]
 
 
 def _features(T, C, dt, seed):
@@ -47,7 +47,7 @@ def _features(T, C, dt, seed):
     return d["x"], d["x64"], bd, b64
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("C", WIDTHS)
 def test_round_trip_matches_oracle(eq, C, dt):
     import torch
@@ -64,7 +64,7 @@ def test_round_trip_matches_oracle(eq, C, dt):
             assert_close(to_f64(out.t), ref, dt, f"C={C} {dt} T={T} bias={bias} act={act}")
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 def test_round_trip_in_place(eq, dt):
     import torch
     C, T = 96, 50
@@ -76,7 +76,7 @@ def test_round_trip_in_place(eq, dt):
     assert_close(to_f64(y), oracle.d8_bias_act(y64, b64, 1), dt, "in place")
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("C", WIDTHS)
 def test_transforms_match_oracle(eq, C, dt):
     import torch
@@ -118,7 +118,7 @@ def test_d8_layer_with_gelu_at_full_size(eq):
     print(f"c5 bias+GELU: rel-L2 {r:.3e} max/rms {m:.3e} over {len(rows)} tokens")
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 def test_d8_layer_on_regular_features(eq, dt):
     """A D8 layer between regular-representation features: to the Fourier
     layout, the block layer, back to the regular layout."""
@@ -126,7 +126,7 @@ def test_d8_layer_on_regular_features(eq, dt):
     C_in, C_out, T = 64, 96, 200
     d = synthetic.d8_inputs(C_in, C_out, T, dt, seed=8)
     plan = eq.eqlinear_d8_plan(C_in, C_out, _eqdt(eq, dt))
-    tdt = torch.float32 if dt == F32 else torch.bfloat16
+    tdt = {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[dt]
     xf = torch.empty(T, C_in, dtype=tdt, device="cuda")
     yf = torch.empty(T, C_out, dtype=tdt, device="cuda")
     yr = Guarded(T * C_out, dt, (T, C_out))

@@ -17,7 +17,7 @@ from gpu_util import Guarded, assert_close, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
-F32, BF16 = synthetic.F32, synthetic.BF16
+F32, BF16, F16 = synthetic.F32, synthetic.BF16, synthetic.F16
 ORDERS = [2, 3, 5, 6, 8, 12]
 
 
@@ -32,7 +32,7 @@ def eq():
 
 
 def _eqdt(eq, dt):
-    return eq.EQL_F32 if dt == F32 else eq.EQL_BF16
+    return {F32: eq.EQL_F32, BF16: eq.EQL_BF16, F16: eq.EQL_F16}[dt]
 
 
 def _shapes(n):
@@ -41,7 +41,7 @@ def _shapes(n):
     return [(G * 8, G * 16, 300), (G * 3, G * 5, 77), (G, G, 1)]
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("n", ORDERS)
 def test_dihedral_forward(eq, n, dt):
     import torch
@@ -57,7 +57,7 @@ def test_dihedral_forward(eq, n, dt):
         assert_close(to_f64(y.t), ref, dt, f"D_{n} {dt} {C_in}->{C_out} T={T}")
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("n", [3, 6, 12])
 def test_dihedral_comparator(eq, n, dt):
     import torch
@@ -88,7 +88,7 @@ def test_order_four_is_the_d8_layer(eq):
     assert torch.equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("n", ORDERS)
 def test_dihedral_passes(eq, n, dt):
     import torch

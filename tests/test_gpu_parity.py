@@ -220,7 +220,7 @@ def run_d8(eq, C_in, C_out, T, dt, seed=0, inputs=None):
     return to_f64(y.t), d
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("C_in,C_out,T", [(8, 8, 1), (16, 24, 33), (64, 64, 130), (160, 96, 257),
                                           (256, 512, 100), (1280, 1280, 77), (512, 320, 97),
                                           (192, 640, 200)])
@@ -261,7 +261,7 @@ def test_dense_comparator(eq, N, C_in, C_out, T, dt):
     assert_close(to_f64(y.t), ref, dt, "dense comparator")
 
 
-@pytest.mark.parametrize("dt", [F32, BF16])
+@pytest.mark.parametrize("dt", [F32, BF16, F16])
 def test_d8_dense_comparator(eq, dt):
     import torch
     C_in, C_out, T = 64, 48, 70
