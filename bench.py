@@ -95,7 +95,7 @@ def parse():
                     help="c1, c2, c3a, c3b, c3c, c3 (the three MLP layers), c4, c5")
     ap.add_argument("--cold-steps", type=int, default=100)
     ap.add_argument("--dtype", default="workload", choices=["workload", "f32", "bf16", "f16"],
-                    help="element type of a C_N workload (default: the workload's own)")
+                    help="element type of the workload's tensors (default: the workload's own)")
     ap.add_argument("--tile", type=int, default=-1,
                     help="fixed tile configuration of the C_N kernel (eqlinear_forward_tiled); -1 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -638,9 +638,6 @@ def main():
     wls = [synthetic.WORKLOADS[n] for n in names]
     if args.dtype != "workload":
         from dataclasses import replace
-        if any(wl.group != "C" for wl in wls) and args.dtype == "f16":
-            print("--dtype f16 applies to C_N workloads (the D8 kernels are fp32 and bf16)", file=sys.stderr)
-            sys.exit(2)
         wls = [replace(wl, dtype=args.dtype) for wl in wls]
     if args.traffic_from:
         summarize_traffic(args, wls)
