@@ -29,6 +29,8 @@
 //      direct global->LDS loads; fp32 partial spectra per range;
 //   3. bw_reduce_kernel: partials summed in a fixed order, inverse real DFT
 //      per (o, i), dw written in fp32 [C_out][C_in][N].
+// Layers of at most 32 channels each way run 1 and 2 as one launch
+// (bw_small_kernel: transforms into LDS, no planes in HBM), then 3.
 // Every step is deterministic (no atomics).
 #include "eq_device.h"
 #include "eq_launch.h"
