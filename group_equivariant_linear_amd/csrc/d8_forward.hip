@@ -289,6 +289,9 @@ hipError_t launch_d8_shape(GemmJobs jobs, const void* x, const void* w, void* y,
         case 5:
             return launch_d8_cfg<D8Cfg<2, 1, 4, 5, 2>, D8Cfg<2, 1, 4, 5, 2>, IO>(jobs, x, w, y, T, ldx, ldy, w_elems,
                                                                                 stream);
+        case 6:  // 96-channel blocks (D6 at width 1152): 64 tokens x 96 channels, 2x2 waves
+            return launch_d8_cfg<D8Cfg<2, 2, 2, 3, 2>, D8Cfg<2, 2, 2, 3, 2>, IO>(jobs, x, w, y, T, ldx, ldy,
+                                                                                w_elems, stream);
         case 2: return launch_d8_cfg<Small, Small, IO>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
         default: return launch_d8_cfg<Wide, Narrow, IO>(jobs, x, w, y, T, ldx, ldy, w_elems, stream);
     }

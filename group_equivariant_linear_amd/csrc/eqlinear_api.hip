@@ -306,8 +306,8 @@ eqlinear_status eqlinear_d8_forward(eqlinear_plan_t p, const void* x, const void
                 eql::GemmJob{n1 * mi + 4 * k * mi + 2 * c * mi, n1 * mo + 4 * k * mo + 2 * c * mo, 2 * mi, 2 * mo,
                              (int64_t)n1 * mo * mi + (int64_t)k * 4 * mo * mi, 2 * mi, 0, 0, 0, 0};
     if (p->dtype == EQL_BF16 || p->dtype == EQL_F16) {
-        // widest output tile that the 1-D blocks fill: 160, 80 or 32 channels
-        const int cb = mo % 160 == 0 ? 10 : (mo % 80 == 0 ? 5 : 2);
+        // widest output tile that the 1-D blocks fill: 160, 96, 80 or 32 channels
+        const int cb = mo % 160 == 0 ? 10 : (mo % 96 == 0 ? 6 : (mo % 80 == 0 ? 5 : 2));
         const hipError_t e = eql::launch_d8_fast(p->dtype, jobs, x, wb, y, T, p->C_in, p->C_out,
                                                  (int64_t)eqlinear_w_hat_elems(p), cb, (hipStream_t)stream);
         if (e != hipErrorNotSupported) return hip_status(e);

@@ -57,6 +57,45 @@ def test_dihedral_forward(eq, n, dt):
         assert_close(to_f64(y.t), ref, dt, f"D_{n} {dt} {C_in}->{C_out} T={T}")
 
 
+@pytest.mark.parametrize("dt", [BF16, F16])
+@pytest.mark.parametrize("n", [3, 6])
+def test_dihedral_forward_96_channel_tiles(eq, n, dt):
+    """1-D blocks of 96 or 192 output channels take the 64-token x 96-channel
+    tile of the matrix-core kernel (the D6 workload's shape at width 1152):
+    square and widening layers, ragged token counts."""
+    import torch
+    G = 2 * n
+    for C_in, C_out, T in [(G * 96, G * 96, 130), (G * 48, G * 192, 70)]:
+        d = synthetic.dn_inputs(n, C_in, C_out, T, dt, seed=7 * n + C_out)
+        plan = eq.eqlinear_dihedral_plan(n, C_in, C_out, _eqdt(eq, dt))
+        y = Guarded(T * C_out, dt, (T, C_out))
+        eq.eqlinear_d8_forward(plan, to_dev(d["x"], dt).reshape(T, C_in), to_dev(d["w"], dt), y.t, T=T)
+        torch.cuda.synchronize()
+        y.check_guards()
+        ref = oracle.dn_dense(n, d["x64"], d["w64"], C_out)
+        assert_close(to_f64(y.t), ref, dt, f"D_{n} {dt} {C_in}->{C_out} T={T}")
+
+
+def test_d6_workload_full_size(eq):
+    """The D6 benchmark workload (width 1152, T = 4112, bf16) in its bench launch,
+    checked on sampled token rows."""
+    import torch
+    wl = synthetic.WORKLOADS["d6"]
+    n = wl.N // 2
+    d = synthetic.dn_inputs(n, wl.C_in, wl.C_out, wl.T, wl.dtype, seed=0)
+    plan = eq.eqlinear_dihedral_plan(n, wl.C_in, wl.C_out, _eqdt(eq, wl.dtype))
+    y = Guarded(wl.T * wl.C_out, wl.dtype, (wl.T, wl.C_out))
+    eq.eqlinear_d8_forward(plan, to_dev(d["x"], wl.dtype).reshape(wl.T, wl.C_in), to_dev(d["w"], wl.dtype), y.t,
+                           T=wl.T)
+    torch.cuda.synchronize()
+    y.check_guards()
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(wl.T - 64, wl.T),
+                                     np.random.default_rng(0).choice(wl.T, 256, replace=False)]))
+    ref = oracle.dn_dense(n, d["x64"][rows], d["w64"], wl.C_out)
+    r, m = assert_close(to_f64(y.t)[rows], ref, wl.dtype, "d6")
+    print(f"d6: rel-L2 {r:.3e} max/rms {m:.3e} over {len(rows)} tokens")
+
+
 @pytest.mark.parametrize("dt", [F32, BF16, F16])
 @pytest.mark.parametrize("n", [3, 6, 12])
 def test_dihedral_comparator(eq, n, dt):
