@@ -946,8 +946,11 @@ BwShape bw_shape(int N, int io, int64_t T, int C_in, int C_out) {
     if (s.bin) {
         // one workgroup per CU (the ring takes most of its LDS): bins x tiles x
         // token ranges of at least two chunks, about 256 in all
-        // a real bin's workgroup costs about half a complex one, so it takes
-        // ranges twice as long: H S + nr S / 2 workgroups per tile in all
+        // a real bin's workgroup costs about half a complex one (half the bytes;
+        // its bytes, not its quarter of the products, set the pace), so it takes
+        // ranges twice as long: H S + nr S / 2 workgroups per tile in all (on
+        // MI355X three and four times as long were slower: c4 104 and 114 us
+        // against 95)
         s.tiles = s.n_o * s.n_i;
         const int nr = s.nb - H;
         const int64_t cap = s.nchunks / 2 > 0 ? s.nchunks / 2 : 1;
