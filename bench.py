@@ -628,7 +628,7 @@ def load_traffic(workload, group):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(tokens shard across GPUs with no exchange; see the sharding notes). "
               f"--gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)

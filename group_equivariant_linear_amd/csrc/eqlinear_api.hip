@@ -55,7 +55,7 @@ const char* eqlinear_status_string(eqlinear_status s) {
     switch (s) {
         case EQL_OK: return "EQL_OK";
         case EQL_ERR_INVALID: return "EQL_ERR_INVALID: invalid argument";
-        case EQL_ERR_UNSUPPORTED: return "EQL_ERR_UNSUPPORTED: not supported by this build";
+        case EQL_ERR_UNSUPPORTED: return "EQL_ERR_UNSUPPORTED: not supported by the library";
         case EQL_ERR_HIP: return "EQL_ERR_HIP: HIP runtime or kernel launch error";
         case EQL_ERR_NOMEM: return "EQL_ERR_NOMEM: host allocation failed";
     }

@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
     EQL_OK = 0,
     EQL_ERR_INVALID = 1,     /* bad argument: NULL, size, alignment, aliasing, kind */
-    EQL_ERR_UNSUPPORTED = 2, /* valid request outside what this build implements */
+    EQL_ERR_UNSUPPORTED = 2, /* valid request outside what the library implements */
     EQL_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
     EQL_ERR_NOMEM = 4        /* host allocation failed */
 } eqlinear_status;
