@@ -230,14 +230,16 @@ def test_d8_forward(eq, C_in, C_out, T, dt):
     assert_close(y, ref, dt, f"D8 {C_in}->{C_out} T={T} {dt}")
 
 
-def test_d8_workload_full_size(eq):
+@pytest.mark.parametrize("dt", [BF16, F16])
+def test_d8_workload_full_size(eq, dt):
+    """The c5 D8 layer at full size (bf16 as benchmarked, and fp16), sampled rows."""
     wl = synthetic.WORKLOADS["c5"]
-    y, d = run_d8(eq, wl.C_in, wl.C_out, wl.T, wl.dtype)
+    y, d = run_d8(eq, wl.C_in, wl.C_out, wl.T, dt)
     rows = _sample_rows(wl.T)
     W = oracle.d8_expand(d["w64"], wl.C_in, wl.C_out)
     ref = oracle.apply_dense(W, d["x64"][rows])
-    r, m = assert_close(y[rows], ref, wl.dtype, "c5")
-    print(f"c5: rel-L2 {r:.3e} max/rms {m:.3e} over {len(rows)} tokens")
+    r, m = assert_close(y[rows], ref, dt, f"c5 {dt}")
+    print(f"c5 {dt}: rel-L2 {r:.3e} max/rms {m:.3e} over {len(rows)} tokens")
 
 
 # --- expanded-dense comparator ------------------------------------------------------------
