@@ -135,23 +135,14 @@ def test_gelu_output_respects_its_lower_bound(eq):
     assert y.min() >= -0.1701 and y.min() < -0.15
 
 
-def _sample_rows(T, n=256, seed=0):
-    rng = np.random.default_rng(seed)
-    head = np.arange(min(T, 64))
-    tail = np.arange(max(0, T - 64), T)
-    mid = rng.choice(T, size=min(T, n), replace=False)
-    return np.unique(np.concatenate([head, tail, mid]))
-
-
 @pytest.mark.parametrize("name", ["c2", "c3a", "c3b", "c4"])
 def test_bias_gelu_workload_full_size(eq, name):
     """The benchmark layers at full size with bias + GELU (c3b is the ViT-B MLP's
-    first layer, the one that GELU follows), checked on sampled token rows."""
+    first layer, the one that GELU follows), every token row."""
     wl = synthetic.WORKLOADS[name]
     L = Layer(eq, wl.N, wl.C_in, wl.C_out, wl.T, wl.dtype, seed=0)
     y = to_f64(L.run(True, 1, -1).t)
-    rows = _sample_rows(wl.T)
-    ref = oracle.cn_dense_bias_act(L.d["x64"][rows], L.d["w64"], L.b64, 1)
-    r, m = assert_close(y[rows], ref, wl.dtype, f"{name} bias+GELU")
-    print(f"{name} bias+GELU: rel-L2 {r:.3e} max/rms {m:.3e} over {len(rows)} tokens")
+    ref = oracle.cn_dense_bias_act(L.d["x64"], L.d["w64"], L.b64, 1)
+    r, m = assert_close(y, ref, wl.dtype, f"{name} bias+GELU")
+    print(f"{name} bias+GELU: rel-L2 {r:.3e} max/rms {m:.3e} over all {wl.T} tokens")
     assert np.all(np.isfinite(y))

@@ -94,15 +94,9 @@ def test_transforms_match_oracle(eq, C, dt):
     assert_close(to_f64(reg.t), oracle.d8_to_regular(x64).reshape(T, C), dt, f"to_regular C={C}")
 
 
-def _sample_rows(T, n=256, seed=0):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([np.arange(min(T, 32)), np.arange(max(0, T - 32), T),
-                                     rng.choice(T, size=min(T, n), replace=False)]))
-
-
 def test_d8_layer_with_gelu_at_full_size(eq):
     """The c5 layer (D8, width 1280, 4112 tokens, bf16) followed by the fused
-    round trip with a bias and GELU: two launches, checked on sampled tokens."""
+    round trip with a bias and GELU: two launches, every token row."""
     import torch
     wl = synthetic.WORKLOADS["c5"]
     d = synthetic.d8_inputs(wl.C_in, wl.C_out, wl.T, wl.dtype, seed=0)
@@ -112,10 +106,9 @@ def test_d8_layer_with_gelu_at_full_size(eq):
     eq.eqlinear_d8_forward(plan, to_dev(d["x"], wl.dtype).reshape(wl.T, -1), to_dev(d["w"], wl.dtype), y, T=wl.T)
     eq.eqlinear_d8_bias_act(plan, y, to_dev(bd, wl.dtype), eq.EQL_ACT_GELU, y, T=wl.T)
     torch.cuda.synchronize()
-    rows = _sample_rows(wl.T)
-    ref = oracle.d8_dense_bias_act(d["x64"][rows], d["w64"], wl.C_out, b64, 1)
-    r, m = assert_close(to_f64(y)[rows], ref, wl.dtype, "c5 + bias + GELU")
-    print(f"c5 bias+GELU: rel-L2 {r:.3e} max/rms {m:.3e} over {len(rows)} tokens")
+    ref = oracle.d8_dense_bias_act(d["x64"], d["w64"], wl.C_out, b64, 1)
+    r, m = assert_close(to_f64(y), ref, wl.dtype, "c5 + bias + GELU")
+    print(f"c5 bias+GELU: rel-L2 {r:.3e} max/rms {m:.3e} over all {wl.T} tokens")
 
 
 @pytest.mark.parametrize("dt", [F32, BF16, F16])

@@ -79,7 +79,7 @@ def test_dihedral_forward_96_channel_tiles(eq, n, dt):
 @pytest.mark.parametrize("dt", [BF16, F16])
 def test_d6_workload_full_size(eq, dt):
     """The D6 benchmark workload (width 1152, T = 4112; bf16 as benchmarked, and
-    fp16) in its bench launch, checked on sampled token rows."""
+    fp16) in its bench launch, every token row."""
     import torch
     wl = synthetic.WORKLOADS["d6"]
     n = wl.N // 2
@@ -89,11 +89,9 @@ def test_d6_workload_full_size(eq, dt):
     eq.eqlinear_d8_forward(plan, to_dev(d["x"], dt).reshape(wl.T, wl.C_in), to_dev(d["w"], dt), y.t, T=wl.T)
     torch.cuda.synchronize()
     y.check_guards()
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(wl.T - 64, wl.T),
-                                     np.random.default_rng(0).choice(wl.T, 256, replace=False)]))
-    ref = oracle.dn_dense(n, d["x64"][rows], d["w64"], wl.C_out)
-    r, m = assert_close(to_f64(y.t)[rows], ref, dt, f"d6 {dt}")
-    print(f"d6 {dt}: rel-L2 {r:.3e} max/rms {m:.3e} over {len(rows)} tokens")
+    ref = oracle.dn_dense(n, d["x64"], d["w64"], wl.C_out)
+    r, m = assert_close(to_f64(y.t), ref, dt, f"d6 {dt}")
+    print(f"d6 {dt}: rel-L2 {r:.3e} max/rms {m:.3e} over all {wl.T} tokens")
 
 
 @pytest.mark.parametrize("dt", [F32, BF16, F16])
