@@ -31,6 +31,7 @@ ABI_FUNCTIONS = (
     "eqlinear_dense_forward", "eqlinear_w_hat_adjoint", "eqlinear_backward_data",
     "eqlinear_backward_weight_workspace", "eqlinear_backward_weight", "eqlinear_forward_bias_act",
     "eqlinear_d8_bias_act", "eqlinear_d8_to_fourier", "eqlinear_d8_to_regular", "eqlinear_dihedral_plan",
+    "eqlinear_d8_regular_forward",
 )
 
 
@@ -91,6 +92,7 @@ def load_library(path: str | None = None):
             "eqlinear_d8_bias_act": ([vp, vp, vp, i32, vp, i64, vp], st),
             "eqlinear_dihedral_plan": ([ctypes.POINTER(ctypes.c_void_p), i32, i32, i32, i32], st),
             "eqlinear_d8_to_fourier": ([vp, vp, vp, i64, vp], st),
+            "eqlinear_d8_regular_forward": ([vp, vp, vp, vp, i32, vp, i64, vp], st),
             "eqlinear_d8_to_regular": ([vp, vp, vp, i64, vp], st),
         }
         for name, (args, res) in sig.items():
@@ -276,6 +278,19 @@ def eqlinear_d8_bias_act(plan: Plan, y_in, bias, act: int, y_out, T: int | None 
                                           _ptr(bias, plan, plan.info["C_out"] // plan.info["N"], "bias"), int(act),
                                           _ptr(y_out, plan, T * M, "y_out"), T, _stream(stream)),
            "eqlinear_d8_bias_act")
+
+
+def eqlinear_d8_regular_forward(plan: Plan, x_reg, wb, bias, act: int, y_reg, T: int | None = None,
+                                stream=None):
+    """y_reg = act(to_regular(layer(to_fourier(x_reg))) + bias[j]) in one launch; bias None or
+    [C_out / group order]."""
+    K, M = _widths(plan)
+    T = _tokens(x_reg, T, K)
+    _check(plan._lib.eqlinear_d8_regular_forward(plan.handle, _ptr(x_reg, plan, T * K, "x_reg"),
+                                                 _ptr(wb, plan, eqlinear_w_hat_elems(plan), "wb"),
+                                                 _ptr(bias, plan, plan.info["C_out"] // plan.info["N"], "bias"),
+                                                 int(act), _ptr(y_reg, plan, T * M, "y_reg"), T, _stream(stream)),
+           "eqlinear_d8_regular_forward")
 
 
 def eqlinear_d8_to_fourier(plan: Plan, x_reg, x_four, T: int | None = None, stream=None):

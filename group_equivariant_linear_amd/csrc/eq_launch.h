@@ -77,6 +77,11 @@ hipError_t launch_d8_to_fourier(int io, const void* x_reg, void* x_four, int m, 
                                 hipStream_t stream);
 hipError_t launch_d8_to_regular(int io, const void* y_four, void* y_reg, int m, int64_t T,
                                 hipStream_t stream);
+// dn_regular.hip: the dihedral layer between regular-representation features in
+// one launch, y_reg = act(F^T W F x_reg + b); 16-bit I/O, m_in and m_out multiples
+// of 8 (hipErrorNotSupported otherwise)
+hipError_t launch_dn_regular(int n, int io, const void* x_reg, const void* wb, const void* bias, int act,
+                             void* y_reg, int64_t T, int m_in, int m_out, int64_t w_elems, hipStream_t stream);
 // the same passes for D_n, m = C/2n regular channels (n = 4 takes the D8 kernels)
 hipError_t launch_dn_round_trip(int n, int io, const void* y_in, void* y_out, const void* bias, int act,
                                 int m, int64_t T, hipStream_t stream);

@@ -207,6 +207,27 @@ eqlinear_status eqlinear_d8_bias_act(eqlinear_plan_t p, const void* y_in, const 
                                                 p->C_out / p->N, T, (hipStream_t)stream));
 }
 
+eqlinear_status eqlinear_d8_regular_forward(eqlinear_plan_t p, const void* x_reg, const void* wb, const void* bias,
+                                            int act, void* y_reg, int64_t T, void* stream) {
+    if (!p || p->kind != EQL_KIND_D8) return EQL_ERR_INVALID;
+    if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (p->dtype == EQL_F32) return EQL_ERR_UNSUPPORTED;
+    const int mi = p->C_in / p->N, mo = p->C_out / p->N;
+    if (mi % 8 || mo % 8) return EQL_ERR_UNSUPPORTED;
+    if (T == 0) return EQL_OK;
+    if (!x_reg || !wb || !y_reg) return EQL_ERR_INVALID;
+    if (!aligned16(x_reg) || !aligned16(wb) || !aligned16(y_reg)) return EQL_ERR_INVALID;
+    const size_t es = elem_size(p);
+    const size_t xb = (size_t)T * p->C_in * es, yb = (size_t)T * p->C_out * es;
+    const size_t wbb = eqlinear_w_hat_elems(p) * es, bb = (size_t)mo * es;
+    if (overlaps(x_reg, xb, y_reg, yb) || overlaps(wb, wbb, y_reg, yb)) return EQL_ERR_INVALID;
+    if (bias && (((uintptr_t)bias % es) != 0 || overlaps(bias, bb, y_reg, yb))) return EQL_ERR_INVALID;
+    const hipError_t e = eql::launch_dn_regular(p->N / 2, p->dtype, x_reg, wb, bias, act, y_reg, T, mi, mo,
+                                                (int64_t)eqlinear_w_hat_elems(p), (hipStream_t)stream);
+    return e == hipErrorNotSupported ? EQL_ERR_UNSUPPORTED : hip_status(e);
+}
+
 eqlinear_status eqlinear_d8_to_fourier(eqlinear_plan_t p, const void* x_reg, void* x_four, int64_t T,
                                        void* stream) {
     if (!p || p->kind != EQL_KIND_D8) return EQL_ERR_INVALID;

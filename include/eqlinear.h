@@ -242,6 +242,31 @@ eqlinear_status eqlinear_d8_to_fourier(eqlinear_plan_t plan, const void* x_reg, 
 eqlinear_status eqlinear_d8_to_regular(eqlinear_plan_t plan, const void* y_four, void* y_reg, int64_t T,
                                        void* stream);
 
+/* The dihedral layer between regular-representation features, in one launch
+ * ("Quick ViTs", key design 2: the MLP keeps its features in the regular
+ * representation, where the group only permutes each channel's values and
+ * GELU acts pointwise; the linear map is block-diagonal in the group-Fourier
+ * basis; the page fuses the transforms and GELU around the products):
+ *   y_reg = act( to_regular( layer( to_fourier(x_reg) ) ) + b )
+ * i.e. eqlinear_d8_to_fourier, eqlinear_d8_forward, and the regular half of
+ * eqlinear_d8_bias_act, with no Fourier-domain tensor in memory.
+ *   x_reg [T][C_in/G][G], y_reg [T][C_out/G][G] (G = the plan's group order;
+ *     regular channel j's values at the G group elements, as for
+ *     eqlinear_d8_to_fourier);
+ *   wb    the packed blocks, as for eqlinear_d8_forward;
+ *   bias  NULL or C_out/G values, one per output regular channel (constant
+ *         over the group elements, so the block stays equivariant);
+ *   act   EQL_ACT_NONE or EQL_ACT_GELU (the erf form).
+ * The group-Fourier transform and its inverse run in fp32; the Fourier
+ * features of x are rounded once to the plan dtype for the matrix-core
+ * products (fp32 accumulation); y is rounded once.  Device pointers, plan
+ * dtype, 16-byte aligned (bias: element-aligned); y_reg must not overlap
+ * x_reg, wb or bias.  Asynchronous on stream; no allocation; T == 0: EQL_OK.
+ * EQL_ERR_UNSUPPORTED for fp32 plans and for C_in/G or C_out/G not a multiple
+ * of 8 (use the three separate calls); EQL_ERR_INVALID for C_N plans. */
+eqlinear_status eqlinear_d8_regular_forward(eqlinear_plan_t plan, const void* x_reg, const void* wb,
+                                            const void* bias, int act, void* y_reg, int64_t T, void* stream);
+
 /* Backward pass ("Flash EQ-Linear", Implementation: the kernels cover forward
  * and backward; Experimental Results, Operator Level, backward pass).  The
  * pages give no formulas; these are the derivatives of the layer

@@ -247,6 +247,31 @@ def test_bias_act_validation_before_any_hip_call(eq):
     assert f(pf.handle, X, W, Bz + 2, G, Y, 5, None, -1) == eq.EQL_ERR_INVALID  # fp32 bias needs 4 bytes
 
 
+def test_regular_forward_validation_before_any_hip_call(eq):
+    lib = eq.load_library()
+    f = lib.eqlinear_d8_regular_forward
+    d8 = eq.eqlinear_d8_plan(64, 128, eq.EQL_BF16)  # 8 -> 16 regular channels
+    h = d8.handle
+    X, W, Bz, Y = 1 << 20, 1 << 30, 1 << 34, 1 << 38
+    G, NONE = eq.EQL_ACT_GELU, eq.EQL_ACT_NONE
+    assert f(h, X, W, Bz, 2, Y, 5, None) == eq.EQL_ERR_INVALID           # unknown activation
+    assert f(h, X, W, Bz, G, Y, -1, None) == eq.EQL_ERR_INVALID          # negative T
+    assert f(h, None, None, None, G, None, 0, None) == eq.EQL_OK         # T == 0
+    assert f(h, X, W, Bz, G, X + 64, 5, None) == eq.EQL_ERR_INVALID      # y over x
+    assert f(h, X, W, Bz, G, W, 5, None) == eq.EQL_ERR_INVALID           # y over the blocks
+    assert f(h, X, W, Y + 2, G, Y, 5, None) == eq.EQL_ERR_INVALID        # bias inside y
+    assert f(h, X + 2, W, Bz, G, Y, 5, None) == eq.EQL_ERR_INVALID       # misaligned
+    assert f(h, X, W, Bz + 1, G, Y, 5, None) == eq.EQL_ERR_INVALID       # bias misaligned for bf16
+    assert f(h, None, W, Bz, NONE, Y, 5, None) == eq.EQL_ERR_INVALID
+    cn = eq.eqlinear_plan(8, 8, 16, eq.EQL_BF16)
+    assert f(cn.handle, X, W, Bz, G, Y, 5, None) == eq.EQL_ERR_INVALID   # C_N plan
+    # not on this path: fp32 plans, regular channel counts that are not multiples of 8
+    f32 = eq.eqlinear_d8_plan(64, 128, eq.EQL_F32)
+    assert f(f32.handle, X, W, Bz, G, Y, 5, None) == eq.EQL_ERR_UNSUPPORTED
+    odd = eq.eqlinear_dihedral_plan(6, 12 * 12, 12 * 8, eq.EQL_F16)  # 12 -> 8 regular channels
+    assert f(odd.handle, X, W, Bz, G, Y, 5, None) == eq.EQL_ERR_UNSUPPORTED
+
+
 def test_d8_passes_validation_before_any_hip_call(eq):
     lib = eq.load_library()
     d8 = eq.eqlinear_d8_plan(32, 64, eq.EQL_BF16)  # y rows: 64 bf16 = 128 bytes; bias: 8 bf16
