@@ -31,8 +31,11 @@ ABI_FUNCTIONS = (
     "eqlinear_dense_forward", "eqlinear_w_hat_adjoint", "eqlinear_backward_data",
     "eqlinear_backward_weight_workspace", "eqlinear_backward_weight", "eqlinear_forward_bias_act",
     "eqlinear_d8_bias_act", "eqlinear_d8_to_fourier", "eqlinear_d8_to_regular", "eqlinear_dihedral_plan",
-    "eqlinear_d8_regular_forward",
+    "eqlinear_backward_weight_noalloc", "eqlinear_d8_regular_forward",
 )
+
+# Size of the library-held scratch array of eqlinear_backward_weight_noalloc.
+EQL_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class EqlError(RuntimeError):
@@ -88,6 +91,7 @@ def load_library(path: str | None = None):
             "eqlinear_backward_data": ([vp, vp, vp, vp, i64, vp], st),
             "eqlinear_backward_weight_workspace": ([vp, i64], ctypes.c_size_t),
             "eqlinear_backward_weight": ([vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp], st),
+            "eqlinear_backward_weight_noalloc": ([vp, vp, vp, vp, i64, vp], st),
             "eqlinear_forward_bias_act": ([vp, vp, vp, vp, i32, vp, i64, vp, i32], st),
             "eqlinear_d8_bias_act": ([vp, vp, vp, i32, vp, i64, vp], st),
             "eqlinear_dihedral_plan": ([ctypes.POINTER(ctypes.c_void_p), i32, i32, i32, i32], st),
@@ -377,6 +381,23 @@ def eqlinear_backward_weight(plan: Plan, x, dy, dw, workspace, T: int | None = N
                                               _raw_ptr(dw, "dw", torch.float32, n),
                                               T, _raw_ptr(workspace, "workspace"), wbytes, _stream(stream)),
            "eqlinear_backward_weight")
+
+
+def eqlinear_backward_weight_noalloc(plan: Plan, x, dy, dw, T: int | None = None, stream=None):
+    """dw (fp32, N*C_in*C_out elements) from x and dy, with the workspace in the
+    library's own scratch array on the current GPU (no allocation anywhere)."""
+    import torch
+    K, M = _widths(plan)
+    T = _tokens(x, T, K)
+    n = eqlinear_w_hat_elems(plan)
+    st = plan._lib.eqlinear_backward_weight_noalloc(plan.handle, _ptr(x, plan, T * K, "x"),
+                                                    _ptr(dy, plan, T * M, "dy"),
+                                                    _raw_ptr(dw, "dw", torch.float32, n), T, _stream(stream))
+    if st == EQL_ERR_UNSUPPORTED:
+        need = eqlinear_backward_weight_workspace(plan, T)
+        raise EqlError(st, f"eqlinear_backward_weight_noalloc (workspace {need} bytes > the "
+                           f"{EQL_NOALLOC_SCRATCH_BYTES}-byte library scratch, or past the 2 GiB plane limit)")
+    _check(st, "eqlinear_backward_weight_noalloc")
 
 
 def built() -> bool:

@@ -32,10 +32,19 @@
 // Layers of at most 32 channels each way run 1 and 2 as one launch
 // (bw_small_kernel: transforms into LDS, no planes in HBM), then 3.
 // Every step is deterministic (no atomics).
+#include <mutex>
+
 #include "eq_device.h"
 #include "eq_launch.h"
 
 namespace eql {
+
+// Scratch memory of the weight gradient for callers that cannot allocate
+// (launch_cn_backward_weight_noalloc): one array per GPU, held by the loaded
+// code object until the process ends.  Host code never passes the array's name
+// to a kernel: it takes the device address from hipGetSymbolAddress, once per
+// device, and passes that.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -1071,6 +1080,29 @@ size_t backward_weight_workspace(int N, int io, int64_t T, int C_in, int C_out) 
     return bw_shape(N, io, T, C_in, C_out).total;
 }
 
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch` on each device, once known
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 hipError_t launch_cn_backward_weight(int N, int io, const void* x, const void* dy, float* dw, int64_t T,
                                      int C_in, int C_out, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream) {
@@ -1095,6 +1127,18 @@ hipError_t launch_cn_backward_weight(int N, int io, const void* x, const void* d
     if (io == kIoF16) return dispatch_backward_weight<_Float16>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
     if (io == kIoBF16) return dispatch_backward_weight<__bf16>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
     return dispatch_backward_weight<float>(N, x, dy, dw, T, C_in, C_out, ws, s, stream);
+}
+
+hipError_t launch_cn_backward_weight_noalloc(int N, int io, const void* x, const void* dy, float* dw, int64_t T,
+                                             int C_in, int C_out, hipStream_t stream) {
+    const size_t need = T > 0 ? bw_shape(N, io, T, C_in, C_out).total : 0;
+    if (need > kNoAllocScratchBytes) return hipErrorOutOfMemory;  // before any HIP call
+    void* ws = nullptr;
+    if (T > 0) {
+        const hipError_t e = noalloc_scratch(&ws);
+        if (e != hipSuccess) return e;
+    }
+    return launch_cn_backward_weight(N, io, x, dy, dw, T, C_in, C_out, ws, kNoAllocScratchBytes, stream);
 }
 
 }  // namespace eql

@@ -60,6 +60,13 @@ hipError_t launch_cn_backward_weight(int N, int io, const void* x, const void* d
                                      int C_in, int C_out, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+// The same weight gradient with the workspace in a library-held per-GPU array of
+// kNoAllocScratchBytes (no allocation); hipErrorOutOfMemory, before any HIP
+// call, when the shape needs more.  Calls that overlap on one GPU race.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t launch_cn_backward_weight_noalloc(int N, int io, const void* x, const void* dy, float* dw, int64_t T,
+                                             int C_in, int C_out, hipStream_t stream);
+
 hipError_t launch_weight_dft(int N, int io, const void* w, void* w_hat, int C_in,
                              int C_out, hipStream_t stream);
 

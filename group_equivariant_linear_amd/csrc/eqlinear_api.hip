@@ -304,6 +304,35 @@ eqlinear_status eqlinear_backward_weight(eqlinear_plan_t p, const void* x, const
     return e == hipErrorNotSupported ? EQL_ERR_UNSUPPORTED : hip_status(e);
 }
 
+eqlinear_status eqlinear_backward_weight_noalloc(eqlinear_plan_t p, const void* x, const void* dy, float* dw,
+                                                 int64_t T, void* stream) {
+    if (!p || p->kind != EQL_KIND_CN || !dw) return EQL_ERR_INVALID;
+    if (T < 0) return EQL_ERR_INVALID;
+    if (!aligned16(dw)) return EQL_ERR_INVALID;
+    const size_t dwb = eqlinear_w_hat_elems(p) * sizeof(float);
+    if (T > 0) {
+        if (!x || !dy) return EQL_ERR_INVALID;
+        if (!aligned16(x) || !aligned16(dy)) return EQL_ERR_INVALID;
+        const size_t es = elem_size(p);
+        const size_t xb = (size_t)T * in_width(p) * es, dyb = (size_t)T * out_width(p) * es;
+        if (overlaps(dw, dwb, x, xb) || overlaps(dw, dwb, dy, dyb)) return EQL_ERR_INVALID;
+        // the library-held scratch has a fixed size: larger shapes are refused here
+        if (eql::backward_weight_workspace(p->N, p->dtype, T, p->C_in, p->C_out) > eql::kNoAllocScratchBytes)
+            return EQL_ERR_UNSUPPORTED;
+    }
+    // the scratch array used is the current device's: the stream must be one of its streams
+    if (stream) {
+        int cur = -1, sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess)
+            return EQL_ERR_HIP;
+        if (cur != sdev) return EQL_ERR_INVALID;
+    }
+    const hipError_t e = eql::launch_cn_backward_weight_noalloc(p->N, p->dtype, x, dy, dw, T, p->C_in, p->C_out,
+                                                                (hipStream_t)stream);
+    if (e == hipErrorOutOfMemory) return EQL_ERR_UNSUPPORTED;
+    return e == hipErrorNotSupported ? EQL_ERR_UNSUPPORTED : hip_status(e);
+}
+
 eqlinear_status eqlinear_d8_forward(eqlinear_plan_t p, const void* x, const void* wb, void* y,
                                     int64_t T, void* stream) {
     if (!p || p->kind != EQL_KIND_D8) return EQL_ERR_INVALID;

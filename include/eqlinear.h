@@ -316,6 +316,31 @@ size_t eqlinear_backward_weight_workspace(eqlinear_plan_t plan, int64_t T);
 eqlinear_status eqlinear_backward_weight(eqlinear_plan_t plan, const void* x, const void* dy, float* dw,
                                          int64_t T, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Largest workspace eqlinear_backward_weight_noalloc can serve: the size of
+ * its library-held scratch array on each GPU. */
+#define EQL_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* Weight gradient without allocation and without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Computes exactly what
+ * eqlinear_backward_weight computes (same kernels, same fixed summation order,
+ * so the same bits), with the workspace taken from a device array of
+ * EQL_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  It calls no hipMalloc/hipFree.
+ *   x, dy, dw, T: as for eqlinear_backward_weight.
+ *   stream: a stream of the current device (NULL: the null stream); the
+ *   current device's array is used.
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents (nothing in it needs to start at zero).  Calls that overlap
+ * on one GPU (several streams, or host threads) race on it: serialise them.
+ * EQL_ERR_UNSUPPORTED, before any launch, when the shape's workspace
+ * (eqlinear_backward_weight_workspace) exceeds EQL_NOALLOC_SCRATCH_BYTES (use
+ * eqlinear_backward_weight, or split the tokens and add the gradients);
+ * EQL_ERR_INVALID as for eqlinear_backward_weight, or for a stream of another
+ * device.  Asynchronous on stream.  T == 0 writes zeros to dw. */
+eqlinear_status eqlinear_backward_weight_noalloc(eqlinear_plan_t plan, const void* x, const void* dy, float* dw,
+                                                 int64_t T, void* stream);
+
 /* D8 forward: y_rho = W_rho x_rho for rho in A1, A2, B1, B2 and
  * y_Ec = W_E x_Ec for both E coordinates c ("Quick ViTs", key design 2).
  *   x  [T][C_in], y [T][C_out], features laid out [A1|A2|B1|B2|E0|E1] with

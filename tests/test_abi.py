@@ -212,6 +212,16 @@ def test_backward_validation_before_any_hip_call(eq):
     assert lib.eqlinear_backward_weight(d8.handle, A, B, W, 100, S, need, None) == eq.EQL_ERR_INVALID
     # the workspace grows with T
     assert lib.eqlinear_backward_weight_workspace(h, 10000) > need
+    # the weight gradient without allocation: the same checks, no workspace argument
+    assert lib.eqlinear_backward_weight_noalloc(h, A, B, W, -1, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_backward_weight_noalloc(h, A, B, A, 100, None) == eq.EQL_ERR_INVALID  # dw aliases x
+    assert lib.eqlinear_backward_weight_noalloc(h, A, B, None, 100, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_backward_weight_noalloc(h, A + 2, B, W, 100, None) == eq.EQL_ERR_INVALID
+    assert lib.eqlinear_backward_weight_noalloc(d8.handle, A, B, W, 100, None) == eq.EQL_ERR_INVALID
+    # a workspace past the library-held scratch: refused before any HIP call
+    wide = eq.eqlinear_plan(8, 96, 96, eq.EQL_BF16)
+    assert lib.eqlinear_backward_weight_workspace(wide.handle, 12608) > eq.EQL_NOALLOC_SCRATCH_BYTES
+    assert lib.eqlinear_backward_weight_noalloc(wide.handle, A, B, W, 12608, None) == eq.EQL_ERR_UNSUPPORTED
     # transformed x or dy reaching 2 GiB: unsupported, refused before any HIP call
     big = eq.eqlinear_plan(7, 160, 160, eq.EQL_BF16)
     X, Y, D, WS = 1 << 40, 1 << 42, 1 << 44, 1 << 46  # farther apart than the big tensors
