@@ -41,6 +41,8 @@ OP_METRIC = {
     "forward": METRIC,
     "backward_data": "EQ-Linear bwd (input gradient) tokens/sec + TFLOP/s and % roofline vs expanded-dense GEMM",
     "backward_weight": "EQ-Linear bwd (weight gradient) tokens/sec + TFLOP/s and % roofline vs expanded-dense GEMM",
+    "regular": "EQ-Linear (dihedral, regular features in and out, one launch) fwd tokens/sec + TFLOP/s and "
+               "% roofline vs expanded-dense GEMM",
 }
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}
@@ -108,8 +110,10 @@ def parse():
                     help="fixed tile configuration of the C_N kernel (eqlinear_forward_tiled); -1 = automatic")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample (0 disables)")
-    ap.add_argument("--op", default="forward", choices=["forward", "backward_data", "backward_weight"],
-                    help="which pass of a C_N workload to time (the default line is the forward)")
+    ap.add_argument("--op", default="forward", choices=["forward", "backward_data", "backward_weight", "regular"],
+                    help="which pass of a C_N workload to time (the default line is the forward); "
+                         "regular: a dihedral workload between regular-representation features in one "
+                         "launch (eqlinear_d8_regular_forward; --epilogue sets bias/GELU)")
     ap.add_argument("--epilogue", default="none", choices=["none", "bias", "bias_gelu"],
                     help="forward with its pointwise neighbours: C_N workloads through "
                          "eqlinear_forward_bias_act (bias and GELU fused into the store), D8 through "
@@ -118,9 +122,9 @@ def parse():
     ap.add_argument("--mode", default="bench", choices=["bench", "cold", "traffic"],
                     help="cold: only the timed cache-cold steps (for rocprofv3 --kernel-trace); "
                          "traffic: a few forwards and a copy of known size, for rocprofv3 --pmc")
-    ap.add_argument("--counters-from", metavar="PMC_DIR",
-                    help="read the counter_collection.csv of a rocprofv3 --pmc run of --mode cold and "
-                         "write profiles/counters_<workload>.md")
+    ap.add_argument("--counters-from", nargs="+", metavar="PMC_DIR",
+                    help="read the counter_collection.csv of one or more rocprofv3 --pmc runs (one pass "
+                         "each) of --mode cold and write profiles/counters_<workload>.md")
     ap.add_argument("--trace-from", metavar="TRACE_DIR",
                     help="read the kernel_trace.csv of a rocprofv3 --kernel-trace run of --mode cold "
                          "and write profiles/kernel_trace_<workload>.md")
@@ -199,7 +203,9 @@ class Layer:
         # for the cache-cold timing) and those of the comparators
         self.rot = ("x", "y")
         self.rot_dense = ("x", "y_dense", "y_lin")
-        if op != "forward":
+        if op == "regular":
+            self._regular(eq, wl, d, dev, es, epilogue)
+        elif op != "forward":
             self._backward(eq, wl, d, dev, eqdt, es)
         elif epilogue != "none":
             self._epilogue(eq, wl, d, dev, es, tile, epilogue)
@@ -283,6 +289,70 @@ class Layer:
             return u.float()
         self.post = post
 
+    def _regular(self, eq, wl, d, dev, es, epilogue):
+        """Dihedral layer between regular features in one launch: x_reg -> group
+        Fourier transform -> blocks -> inverse -> bias (+ GELU) -> y_reg.  The
+        comparators: the chain of the library's separate passes it replaces
+        (to_fourier, d8_forward, the round trip, to_regular: four launches) and
+        torch's dense GEMM on the equivalent regular-basis matrix with the bias in
+        the GEMM and an in-place GELU after it."""
+        import numpy as np
+        import torch
+
+        import synthetic
+        assert wl.group != "C", "--op regular applies to the dihedral workloads"
+        G, n = wl.N, wl.N // 2
+        m = wl.C_out // G
+        bd, d["b64"] = synthetic.channel_bias(m, wl.dtype, 500)
+        self.bias = dev(bd) if epilogue != "none" else None
+        act = eq.EQL_ACT_GELU if epilogue == "bias_gelu" else eq.EQL_ACT_NONE
+        d["act"], d["regular"], d["bias_on"] = act, True, epilogue != "none"
+        self.step = lambda: eq.eqlinear_d8_regular_forward(self.plan, self.x, self.w_hat, self.bias, act, self.y,
+                                                           T=wl.T)
+        self.bytes_per_launch += (m * es if epilogue != "none" else 0)
+        self.xf = torch.empty_like(self.x)
+        self.yf = torch.empty_like(self.y)
+        self.y_chain = torch.empty_like(self.y)
+
+        def chain():
+            eq.eqlinear_d8_to_fourier(self.plan, self.x, self.xf, T=wl.T)
+            eq.eqlinear_d8_forward(self.plan, self.xf, self.w_hat, self.yf, T=wl.T)
+            eq.eqlinear_d8_bias_act(self.plan, self.yf, self.bias, act, self.yf, T=wl.T)
+            eq.eqlinear_d8_to_regular(self.plan, self.yf, self.y_chain, T=wl.T)
+        self.chain = chain
+        self.rot_chain = ("x", "xf", "yf", "y_chain")
+        # the regular-basis dense matrix: W_reg = R_out^T W_four R_in, with R the
+        # map from regular features to the Fourier layout (per channel F, then the
+        # layout's columns)
+        Fm, n1, n2 = _dihedral_fourier_matrix(n)
+
+        def to_four(width):
+            mm = width // G
+            j = np.arange(mm)[:, None]
+            cols = [b * mm + j for b in range(n1)]
+            for k in range(n2):
+                base = n1 * mm + 4 * mm * k
+                cols += [base + 2 * j, base + 2 * j + 1, base + 2 * mm + 2 * j, base + 2 * mm + 2 * j + 1]
+            idx = np.concatenate(cols, axis=1)  # [mm][G]: Fourier column of (channel, feature p)
+            R = np.zeros((width, width))
+            for jj in range(mm):
+                for p in range(G):
+                    R[idx[jj, p], jj * G:(jj + 1) * G] = Fm[p]
+            return torch.tensor(R, dtype=torch.float32, device="cuda")
+        W_reg = to_four(wl.C_out).t() @ self.W_dense.float() @ to_four(wl.C_in)
+        self.W_dense = W_reg.to(self.tdt).contiguous()
+        bias_cols = (self.bias.repeat_interleave(G) if self.bias is not None
+                     else torch.zeros(wl.C_out, dtype=self.tdt, device="cuda"))
+        gelu_ = torch._C._nn.gelu_
+
+        def dense_torch():
+            torch.addmm(bias_cols, self.x, self.W_dense.t(), out=self.y_lin)
+            if act == eq.EQL_ACT_GELU:
+                gelu_(self.y_lin)
+        self.dense_torch = dense_torch
+        self.dense_own = None
+        self.rot_dense = ("x", "y_lin")
+
     def _backward(self, eq, wl, d, dev, eqdt, es):
         """Buffers and step callables of the input- or weight-gradient pass; the
         upstream gradient dy is a second seeded standard normal tensor."""
@@ -331,7 +401,7 @@ class Layer:
 
     def make_copies(self, n):
         """n copies of the rotated tensors (copy 0 is the original)."""
-        keys = sorted(set(self.rot) | set(self.rot_dense))
+        keys = sorted(set(self.rot) | set(self.rot_dense) | set(getattr(self, "rot_chain", ())))
         self.copies = [{k: getattr(self, k) for k in keys}]
         for _ in range(n - 1):
             self.copies.append({k: getattr(self, k).clone() for k in keys})
@@ -486,6 +556,34 @@ def _median(v):
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
+def profile_tag(args):
+    """The workload and the options that change the timed step, as a file-name part."""
+    parts = [args.workload]
+    if args.op != "forward":
+        parts.append(args.op)
+    if args.epilogue != "none":
+        parts.append(args.epilogue)
+    if args.dtype != "workload":
+        parts.append(args.dtype)
+    if args.tile != -1:
+        parts.append(f"tile{args.tile}")
+    return "_".join(parts)
+
+
+def step_flags(args):
+    """The command-line options that select the timed step, for the recorded commands."""
+    f = f"--workload {args.workload}"
+    if args.op != "forward":
+        f += f" --op {args.op}"
+    if args.epilogue != "none":
+        f += f" --epilogue {args.epilogue}"
+    if args.dtype != "workload":
+        f += f" --dtype {args.dtype}"
+    if args.tile != -1:
+        f += f" --tile {args.tile}"
+    return f
+
+
 def summarize_trace(args, wls):
     """Per-dispatch durations of a rocprofv3 --kernel-trace run of --mode cold:
     the step kernel's dispatches in launch order, the eager warm-up and warmup
@@ -500,7 +598,7 @@ def summarize_trace(args, wls):
     step = [r for r in rows if any(k in r["Kernel_Name"] for k in STEP_KERNELS)]
     names = sorted({r["Kernel_Name"] for r in step})
     nl = len(wls)
-    nbytes = sum(algorithmic_bytes(w) for w in wls)
+    nbytes = sum(algorithmic_bytes(w, args.op, args.epilogue) for w in wls)
     R, S = rotation_plan(nbytes, nbytes / 2.5e6)
     skip = R + -(-args.warmup // S) * S  # eager warm-up of each graph's steps, then the warmup replays
     timed = -(-args.steps // S) * S
@@ -513,11 +611,12 @@ def summarize_trace(args, wls):
         per_layer[i % nl].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
         if i:
             gaps.append((int(r["Start_Timestamp"]) - int(step[i - 1]["End_Timestamp"])) * 1e-3)
-    lines = [f"# Kernel trace, cache-cold steps, workload {args.workload}", "",
+    flags = step_flags(args)
+    lines = [f"# Kernel trace, cache-cold steps, {profile_tag(args)}", "",
              "Commands:", "", "```",
              f"rocprofv3 --kernel-trace --stats -d {args.trace_from} -o run -f csv -- "
-             f"python3 bench.py --workload {args.workload} --mode cold --steps {args.steps} --warmup {args.warmup}",
-             f"python3 bench.py --workload {args.workload} --trace-from {args.trace_from} "
+             f"python3 bench.py {flags} --mode cold --steps {args.steps} --warmup {args.warmup}",
+             f"python3 bench.py {flags} --trace-from {args.trace_from} "
              f"--steps {args.steps} --warmup {args.warmup}", "```", "",
              f"Each step launches the layers on one of {R} copies of their per-token tensors, in rotation "
              f"({R * nbytes >> 20} MiB, over 3x the 256 MiB Infinity Cache), {S} step(s) per HIP graph; "
@@ -530,7 +629,7 @@ def summarize_trace(args, wls):
         d = per_layer[li]
         grid = {r["Grid_Size_X"] for r in step[li::nl]}
         mean = sum(d) / max(len(d), 1)
-        b = algorithmic_bytes(wl)
+        b = algorithmic_bytes(wl, args.op, args.epilogue)
         tot_mean += mean
         lines.append(f"| {wl.name} | {','.join(sorted(grid))} | {len(d)} | {mean:.2f} | {_median(d):.2f} | "
                      f"{min(d):.2f} | {b} | {b / mean / 1e3:.0f} | {b / mean / 1e3 / HBM_PEAK_GBS:.3f} |")
@@ -538,7 +637,7 @@ def summarize_trace(args, wls):
                   f"{tot_mean / nl:.2f} us); {nbytes} algorithmic bytes: {nbytes / tot_mean / 1e3:.0f} GB/s = "
                   f"{nbytes / tot_mean / 1e3 / HBM_PEAK_GBS:.3f} of 8 TB/s.",
               f"Gaps between consecutive dispatches under the profiler: median {_median(gaps):.2f} us."]
-    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{args.workload}.md"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{profile_tag(args)}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -574,7 +673,13 @@ def cpu_baseline(layers, target_s, op="forward"):
 
 def _run_oracle(wl, d, n, op="forward"):
     import oracle
-    if "b64" in d and wl.group != "C":
+    if d.get("regular"):
+        nd, G = wl.N // 2, wl.N
+        xr = d["x64"][:n].reshape(n, wl.C_in // G, G)
+        yf = oracle.dn_dense_bias_act(nd, oracle.dn_to_fourier(nd, xr), d["w64"], wl.C_out,
+                                      d["b64"] if d.get("bias_on") else None, d["act"])
+        oracle.dn_to_regular(nd, yf)
+    elif "b64" in d and wl.group != "C":
         oracle.dn_dense_bias_act(wl.N // 2, d["x64"][:n], d["w64"], wl.C_out, d["b64"], d["act"])
     elif "b64" in d:
         oracle.cn_dense_bias_act(d["x64"][:n], d["w64"], d["b64"], d["act"])
@@ -588,7 +693,8 @@ def _run_oracle(wl, d, n, op="forward"):
         oracle.dn_dense(wl.N // 2, d["x64"][:n], d["w64"], wl.C_out)
 
 
-STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "cn_split_kernel", "d8_kernel",
+STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "cn_split_kernel", "cn_stream_kernel",
+                "dn_regular_kernel", "d8_kernel",
                 "gemm_rows_kernel")
 TRAFFIC_WARM = 5   # back-to-back forwards (inputs partly cached from the previous launch)
 TRAFFIC_COLD = 5   # forwards each after a 512 MiB read that evicts the L2s
@@ -633,6 +739,8 @@ def op_kernel_name(wl, op):
     if op == "backward_data":
         from dataclasses import replace
         return step_kernel_name(replace(wl, C_in=wl.C_out, C_out=wl.C_in))
+    if op == "regular":
+        return "dn_regular_kernel"
     if op == "backward_weight":
         if wl.C_in <= 32 and wl.C_out <= 32:
             return "bw_small_kernel + bw_reduce_kernel"
@@ -696,46 +804,54 @@ def algorithmic_bytes(wl, op="forward", epilogue="none"):
 
 
 def summarize_counters(args, wls):
-    """Per-layer means of a rocprofv3 --pmc run of --mode cold (derived counters
-    MfmaUtil, VALUBusy, LdsUtil, LDSBankConflict, OccupancyPercent and raw
-    instruction counts), written to profiles/counters_<workload>.md."""
+    """Per-layer means of one or more rocprofv3 --pmc runs of --mode cold, one
+    counter pass each (derived counters such as MfmaUtil, VALUBusy, LdsUtil,
+    LDSBankConflict, OccupancyPercent, or raw ones), merged into one table and
+    written to profiles/counters_<workload>.md."""
     import collections
     import csv
     import glob
-    files = glob.glob(os.path.join(args.counters_from, "**", "*counter_collection.csv"), recursive=True)
-    if len(files) != 1:
-        raise SystemExit(f"expected one counter_collection.csv under {args.counters_from}, found {files}")
-    rows = [r for r in csv.DictReader(open(files[0])) if any(k in r["Kernel_Name"] for k in STEP_KERNELS)]
-    counters = sorted({r["Counter_Name"] for r in rows})
-    disp = sorted({int(r["Dispatch_Id"]) for r in rows})
     nl = len(wls)
-    nbytes = sum(algorithmic_bytes(w) for w in wls)
+    nbytes = sum(algorithmic_bytes(w, args.op, args.epilogue) for w in wls)
     R, S = rotation_plan(nbytes, nbytes / 2.5e6)
     skip = (R + -(-args.warmup // S) * S) * nl
-    keep = {d: i % nl for i, d in enumerate(disp) if i >= skip}
     vals = collections.defaultdict(list)
     kname = {}
-    for r in rows:
-        d = int(r["Dispatch_Id"])
-        if d in keep:
-            vals[(keep[d], r["Counter_Name"])].append(float(r["Counter_Value"]))
-            kname[keep[d]] = r["Kernel_Name"]
-    cmd = (f"rocprofv3 --pmc {' '.join(counters)} -d {args.counters_from} -o run -f csv -- "
-           f"python3 bench.py --workload {args.workload} --mode cold --steps {args.steps} --warmup {args.warmup}")
-    lines = [f"# Counters of the step kernel, cache-cold steps, workload {args.workload}", "", "Commands:", "",
-             "```", cmd, f"python3 bench.py --workload {args.workload} --counters-from {args.counters_from} "
+    counters = []
+    flags = step_flags(args)
+    cmds = []
+    for d in args.counters_from:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if len(files) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {d}, found {files}")
+        rows = [r for r in csv.DictReader(open(files[0])) if any(k in r["Kernel_Name"] for k in STEP_KERNELS)]
+        names = sorted({r["Counter_Name"] for r in rows})
+        disp = sorted({int(r["Dispatch_Id"]) for r in rows})
+        keep = {dd: i % nl for i, dd in enumerate(disp) if i >= skip}
+        for r in rows:
+            dd = int(r["Dispatch_Id"])
+            if dd in keep:
+                vals[(keep[dd], r["Counter_Name"])].append(float(r["Counter_Value"]))
+                kname[keep[dd]] = r["Kernel_Name"]
+        counters += [c for c in names if c not in counters]
+        cmds.append(f"rocprofv3 --pmc {' '.join(names)} -d {d} -o run -f csv -- "
+                    f"python3 bench.py {flags} --mode cold --steps {args.steps} --warmup {args.warmup}")
+    tag = profile_tag(args)
+    lines = [f"# Counters of the step kernel, cache-cold steps, {tag}", "", "Commands (one counter pass each):",
+             "", "```", *cmds, f"python3 bench.py {flags} --counters-from {' '.join(args.counters_from)} "
              f"--steps {args.steps} --warmup {args.warmup}", "```", "",
              "Derived counters as rocprofv3 defines them: MfmaUtil = matrix-core busy cycles over all SIMDs / "
              "(GPU active cycles x SIMDs), in %; VALUBusy and LdsUtil likewise for the vector ALU and LDS; "
              "OccupancyPercent = resident waves over the CU's maximum; LDSBankConflict = conflict cycles per "
-             "CU-cycle, in %.  Means over the timed dispatches.", "",
+             "CU-cycle, in %.  Raw SQ_/TA_/TCP_ counters are sums over the dispatch.  Means over the timed "
+             "dispatches.", "",
              "| layer | kernel | dispatches | " + " | ".join(counters) + " |",
              "|---|---|---|" + "---|" * len(counters)]
     for li, wl in enumerate(wls):
         n = len(vals[(li, counters[0])])
         cells = [f"{sum(vals[(li, c)]) / max(len(vals[(li, c)]), 1):.4g}" for c in counters]
         lines.append(f"| {wl.name} | `{kname.get(li, '?')[:60]}` | {n} | " + " | ".join(cells) + " |")
-    out = os.path.join(ROOT, "profiles", f"counters_{args.workload}.md")
+    out = os.path.join(ROOT, "profiles", f"counters_{tag}.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -839,6 +955,10 @@ def precision_note(wl, kernel):
                                      f"spectrum rounded to {io} for the products",
                 "inverse_transform": f"on the matrix cores: the fp32 spectrum of y rounded to {io}, "
                                      f"{io} coefficients (1/N folded in), fp32 out, y rounded to {io} once"}
+    if kernel == "dn_regular_kernel":
+        return {"io": io, "products": f"{io} x {io} -> fp32 (matrix cores)",
+                "transforms": f"group Fourier transform and its inverse in fp32 (VALU); the Fourier features of x "
+                              f"rounded to {io} for the products; y rounded to {io} once"}
     if kernel in ("d8_kernel", "gemm_rows_kernel"):
         return {"io": io, "products": f"{io} x {io} -> fp32 (matrix cores)", "transforms": "none"}
     return {"io": io, "products": f"{io} x {io} -> fp32 (matrix cores)",
@@ -878,7 +998,7 @@ def main():
     eq.load_library()
     torch.cuda.set_device(0)
 
-    if args.epilogue != "none" and args.op != "forward":
+    if args.epilogue != "none" and args.op not in ("forward", "regular"):
         print("--epilogue applies to the forward pass", file=sys.stderr)
         sys.exit(2)
     layers = [Layer(eq, wl, tile=args.tile, op=args.op, epilogue=args.epilogue) for wl in wls]
@@ -930,6 +1050,14 @@ def main():
     ms_own_cold = (rotation_timing(layers, "dense_own", args.steps, args.warmup, dense_bytes, est(dense_bytes))[0]
                    if has_own else None)
     ms_dense_cold = min(t for t in (ms_lin_cold, ms_own_cold) if t is not None)
+    chain = None
+    if all(hasattr(L, "chain") for L in layers):
+        # the separate passes the one-launch path replaces, timed the same way
+        ms_chain = rotation_timing(layers, "chain", args.steps, args.warmup, 3 * bytes_launch, est(3 * bytes_launch))[0]
+        ms_chain_warm = time_graph([L.chain for L in layers], [L.y_chain for L in layers], dsteps, dwarm)
+        chain = {"what": "eqlinear_d8_to_fourier + eqlinear_d8_forward + eqlinear_d8_bias_act + "
+                         "eqlinear_d8_to_regular (four launches, the Fourier tensors through memory)",
+                 "ms_cold": ms_chain, "ms_warm": ms_chain_warm, "speedup_cold": ms_chain / ms}
     # a device copy moving the same number of bytes (half read, half written): the
     # practical floor of a launch of this size, warm (graph) and cold (rotation)
     cp = CopyStep(bytes_launch)
@@ -1008,6 +1136,7 @@ def main():
                            "ms_best_cold": ms_dense_cold, "speedup_vs_best_cold": ms_dense_cold / ms,
                            "expand_ms_once": sum(L.expand_ms for L in layers),
                            "agreement_rel_l2": agree},
+        "chain_of_passes": chain,
         "copy_same_bytes": {"ms_warm": ms_copy, "ms_cold": ms_copy_cold,
                             "frac_hbm_cold": bytes_launch / (ms_copy_cold * 1e-3) / 1e9 / HBM_PEAK_GBS,
                             "frac_hbm_warm": bytes_launch / (ms_copy * 1e-3) / 1e9 / HBM_PEAK_GBS},
@@ -1019,7 +1148,8 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": kname + (" + d8_pass_kernel" if group != "C" and args.epilogue != "none" else ""),
+            "kernel": kname + (" + d8_pass_kernel" if group != "C" and args.epilogue != "none"
+                               and args.op != "regular" else ""),
             "launches_per_step": len(layers),
             "mean_launch_us": ms * 1e3 / len(layers),
             "bytes_per_launch": bytes_launch,

@@ -199,7 +199,8 @@ __global__ __launch_bounds__(256) void bw_planes_kernel(const IO* __restrict__ x
         rdft_forward<N>(xv, Pv);
 #pragma unroll
         for (int p = 0; p < N; ++p)
-            *reinterpret_cast<IO*>(stage + (p * P::TC + wave * R + r) * P::ROW + lane * S) = (IO)Pv[p];
+            *reinterpret_cast<IO*>(stage + (p * P::TC + wave * R + r) * P::ROW + lane * S) =
+                (IO)(Pv[p] * spec_scale<IO, N>);
     }
     __syncthreads();
     constexpr int RP = P::ROW / 16;  // pieces per row
@@ -822,7 +823,7 @@ template <int N, int G>
 __global__ __launch_bounds__((BwReduceCfg<N, G>::kThreads)) void bw_reduce_kernel(const float* __restrict__ part,
                                                                                 float* __restrict__ dw, int splits_c,
                                                                                 int splits_r, int64_t plane,
-                                                                                int64_t pstride) {
+                                                                                int64_t pstride, float post) {
     using RC = BwReduceCfg<N, G>;
     using V = typename RC::V;
     constexpr int R = RC::R;
@@ -862,7 +863,7 @@ __global__ __launch_bounds__((BwReduceCfg<N, G>::kThreads)) void bw_reduce_kerne
             float sum = comp(red[0][q / G][k]);
 #pragma unroll
             for (int rr = 1; rr < R; ++rr) sum += comp(red[rr][q / G][k]);
-            P[k] = sum;
+            P[k] = sum * post;
         }
         rdft_inverse<N>(P, y);
 #pragma unroll
@@ -871,16 +872,18 @@ __global__ __launch_bounds__((BwReduceCfg<N, G>::kThreads)) void bw_reduce_kerne
 }
 
 template <int N>
+// post: the scale of the summed spectra (N^2 for fp16 planes, which hold the
+// spectra of x/N and dy/N; 1 otherwise)
 void launch_bw_reduce(const float* part, float* dw, int splits, int splits_r, int64_t plane, int64_t pstride,
-                      hipStream_t stream) {
+                      hipStream_t stream, float post = 1.0f) {
     if (plane >= 128 * BwReduceCfg<N, 4>::EL) {
         using RC = BwReduceCfg<N, 4>;
         hipLaunchKernelGGL((bw_reduce_kernel<N, 4>), dim3((uint32_t)((plane + RC::EL - 1) / RC::EL)),
-                           dim3(RC::kThreads), 0, stream, part, dw, splits, splits_r, plane, pstride);
+                           dim3(RC::kThreads), 0, stream, part, dw, splits, splits_r, plane, pstride, post);
     } else {
         using RC = BwReduceCfg<N, 1>;
         hipLaunchKernelGGL((bw_reduce_kernel<N, 1>), dim3((uint32_t)((plane + RC::EL - 1) / RC::EL)),
-                           dim3(RC::kThreads), 0, stream, part, dw, splits, splits_r, plane, pstride);
+                           dim3(RC::kThreads), 0, stream, part, dw, splits, splits_r, plane, pstride, post);
     }
 }
 
@@ -1027,14 +1030,16 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
                            (uint32_t)s.xp_bytes, (uint32_t)(s.xp_bytes + s.dyp_bytes), part, C_out, C_in, s.Tp, s.WM,
                            s.WN, s.n_o, s.n_i, s.nb, s.L, s.stage_bytes, s.splits, s.chunks_per_split,
                            s.chunks_per_split_r, s.nchunks, pstride);
-        launch_bw_reduce<N>(part, dw, s.splits, s.splits_r, plane, pstride, stream);
+        launch_bw_reduce<N>(part, dw, s.splits, s.splits_r, plane, pstride, stream,
+                            spec_unscale<IO, N> * spec_unscale<IO, N>);
         return hipGetLastError();
     }
     const int64_t wgs = (int64_t)s.tiles * s.splits;
     hipLaunchKernelGGL((bw_gemm_kernel<Cfg>), dim3((uint32_t)wgs), dim3(Cfg::kThreads), 0, stream,
                        (const IO*)dyp, (const IO*)xp, part, C_out, C_in, s.Tp, s.n_i, s.tiles,
                        s.chunks_per_split, s.nchunks);
-    launch_bw_reduce<N>(part, dw, s.splits, s.splits, plane, pstride, stream);
+    launch_bw_reduce<N>(part, dw, s.splits, s.splits, plane, pstride, stream,
+                        spec_unscale<IO, N> * spec_unscale<IO, N>);
     return hipGetLastError();
 }
 

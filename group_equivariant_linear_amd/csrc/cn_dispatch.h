@@ -11,6 +11,22 @@ namespace eql {
 
 constexpr int kMfFirstTile = 7;     // tiles 7..13: entries 0..6 on the matrix-core transform kernel
 constexpr int kSplitFirstTile = 14;  // tiles 14, 15: fp32, input channels split over 2 or 4 waves
+constexpr int kStreamTile = 16;      // 16-bit, N <= 8: the persistent kernel (cn_stream.h)
+
+// cn_stream_{bf16,f16}.hip; hipErrorNotSupported for shapes the kernel does not take
+hipError_t launch_cn_stream_bf16(int N, const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
+                                 hipStream_t stream, Epi epi);
+hipError_t launch_cn_stream_f16(int N, const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
+                                hipStream_t stream, Epi epi);
+
+// The automatic choice does not take the persistent kernel: on MI355X its
+// lane-scattered x loads (16 bytes per lane, 128 bytes apart, the layout the
+// 16x16x32 operands ask for) thrash the CUs' L1 and it ran the c3 trio in
+// 148 us against 97.5 us for tile 10 (cache-cold).  EQL_STREAM_MIN_T sets a
+// token count from which it would.
+#ifndef EQL_STREAM_MIN_T
+#define EQL_STREAM_MIN_T (int64_t)0x7fffffffffffffff
+#endif
 constexpr int kSplitMaxN = 10;       // larger orders: the split kernel's registers do not fit
 
 #ifndef EQL_SPLIT_AUTO_KS
@@ -38,8 +54,10 @@ int choose_shape(int64_t T, int C_in, int C_out) {
 
 template <int N, typename IO>
 int choose_fused(int64_t T, int C_in, int C_out) {
-    // 16-bit orders up to 8 take the matrix-core transform kernel, same shapes
+    // 16-bit orders up to 8: the persistent kernel for long token batches of
+    // whole 8-channel groups, else the matrix-core transform kernel
     if constexpr (mf_supported<N, IO>) {
+        if (T >= EQL_STREAM_MIN_T && C_in % 8 == 0 && C_out % 8 == 0) return kStreamTile;
         return kMfFirstTile + choose_shape<N>(T, C_in, C_out);
     } else {
         const int s = choose_shape<N>(T, C_in, C_out);
@@ -55,6 +73,19 @@ template <int N, typename IO>
 hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
                         hipStream_t stream, int tile, Epi epi) {
     int i = tile >= 0 ? tile : choose_fused<N, IO>(T, C_in, C_out);
+    if (i == kStreamTile) {
+        if constexpr (mf_supported<N, IO>) {
+            const hipError_t e = std::is_same_v<IO, __bf16>
+                                     ? launch_cn_stream_bf16(N, x, w_hat, y, T, C_in, C_out, stream, epi)
+                                     : launch_cn_stream_f16(N, x, w_hat, y, T, C_in, C_out, stream, epi);
+            if (e != hipErrorNotSupported) return e;
+        }
+        // shapes it does not take: the other kernels' automatic choice
+        i = choose_shape<N>(T, C_in, C_out);
+        if constexpr (mf_supported<N, IO>) i += kMfFirstTile;
+        else if (std::is_same_v<IO, float> && N <= kSplitMaxN && i == 6 && split_ok<N>(C_in, C_out))
+            i = kSplitFirstTile + (EQL_SPLIT_AUTO_KS == 4 ? 1 : 0);
+    }
     if (i >= kSplitFirstTile) {
         if constexpr (std::is_same_v<IO, float> && N <= kSplitMaxN) {
             if (split_ok<N>(C_in, C_out)) {

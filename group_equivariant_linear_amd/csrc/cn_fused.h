@@ -284,7 +284,8 @@ __device__ __forceinline__ void x_to_planes(const uint32_t (&xr)[C::XW],
             rdft_forward<N>(xa, Pa);
             rdft_forward<N>(xb, Pb);
 #pragma unroll
-            for (int p = 0; p < N; ++p) pk[p][r / 2] = Half<IO>::pack2(Pa[p], Pb[p]);
+            for (int p = 0; p < N; ++p)
+                pk[p][r / 2] = Half<IO>::pack2(Pa[p] * spec_scale<IO, N>, Pb[p] * spec_scale<IO, N>);
         }
 #pragma unroll
         for (int p = 0; p < N; ++p) {
@@ -419,7 +420,7 @@ __device__ __forceinline__ void store_y(const f32x4 (&acc)[C::N][C::CB], typenam
             const int o = o0 + b * 16 + (lane & 15);
             float P[N], yv[N];
 #pragma unroll
-            for (int p = 0; p < N; ++p) P[p] = acc[p][b][r];
+            for (int p = 0; p < N; ++p) P[p] = acc[p][b][r] * spec_unscale<IO, N>;
             rdft_inverse<N>(P, yv);
             if (epi_on(epi)) epi_apply<N>(yv, epi.bias != nullptr ? lbias[o - o0] : 0.0f, epi.act);
             if (t >= T || o >= C_out) continue;
@@ -773,7 +774,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
                 const int tl = (lane >> 4) * 4 + r, ol = b * 16 + (lane & 15);
                 float P[N], yv[N];
 #pragma unroll
-                for (int p = 0; p < N; ++p) P[p] = acc[p][b][r];
+                for (int p = 0; p < N; ++p) P[p] = acc[p][b][r] * spec_unscale<IO, N>;
                 rdft_inverse<N>(P, yv);
                 if (epi_on(epi)) epi_apply<N>(yv, bias_of(b), epi.act);
                 // record bytes [ol*N*S, ol*N*S + N*S) of row tl, piece-rotated like x
@@ -827,7 +828,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
                 const uint32_t off = o < C_out ? tl * row_y + (uint32_t)o * (N * S) : kOOB;
                 float P[N], yv[N];
 #pragma unroll
-                for (int p = 0; p < N; ++p) P[p] = acc[p][b][r];
+                for (int p = 0; p < N; ++p) P[p] = acc[p][b][r] * spec_unscale<IO, N>;
                 rdft_inverse<N>(P, yv);
                 if (epi_on(epi)) epi_apply<N>(yv, bias_of(b), epi.act);
 #pragma unroll

@@ -36,8 +36,9 @@
 // twiddles carry a rounding of at most 2^-9 (bf16) or 2^-12 (fp16) relative,
 // and the Fourier-domain outputs one more rounding to that type before the
 // inverse -- both of the order of the rounding of Xhat and of y that the fused
-// kernel already makes.  (In fp16 the Fourier-domain values must also stay
-// within its range, 65504: a bin can reach N times the largest |y|.)
+// kernel already makes.  The forward coefficients carry 1/N and the inverse
+// ones N, so the 16-bit spectra are those of x/N and y/N: a bin is at most the
+// largest |x| (|y|), and fp16 stays within its range whenever x and y do.
 #pragma once
 
 #include "cn_fused.h"
@@ -91,7 +92,8 @@ struct MfCfg : FastCfg<N_, IO_, WAVES_, CB_> {
 };
 
 // The MQ block-diagonal transform fragments (A operand) of this lane:
-// row (gr, ir) of fragment m, k-values (kg, e): coef(4m + ir, e) if kg == gr.
+// row (gr, ir) of fragment m, k-values (kg, e): coef(4m + ir, e) / N if kg == gr
+// (the inverse: N coef).
 // INV selects the inverse transform (rows = group elements, k = planes).
 template <class C, bool INV>
 __device__ __forceinline__ void make_frags(typename C::F8 (&Fa)[C::MQ]) {
@@ -111,7 +113,7 @@ __device__ __forceinline__ void make_frags(typename C::F8 (&Fa)[C::MQ]) {
             if constexpr (p < N) {
                 static_for<0, N>([&](auto hc) {
                     constexpr int h = decltype(hc)::value;
-                    constexpr float c = (float)(INV ? inv_coef<N>(p, h) : fwd_coef<N>(p, h));
+                    constexpr float c = (float)(INV ? N * inv_coef<N>(p, h) : fwd_coef<N>(p, h) / N);
                     v[h] = (ir == i) ? c : v[h];
                 });
             }
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
                 const uint32_t off = o < C_out ? trow * row_y + (uint32_t)o * (N * S) : kOOB;
                 float P[N], yv[N];
 #pragma unroll
-                for (int p = 0; p < N; ++p) P[p] = acc[p][b][i];
+                for (int p = 0; p < N; ++p) P[p] = acc[p][b][i] * (float)N;  // the spectrum of y/N
                 rdft_inverse<N>(P, yv);
                 if (epi_on(epi)) epi_apply<N>(yv, epi.bias != nullptr ? lbias[o - o0] : 0.0f, epi.act);
 #pragma unroll

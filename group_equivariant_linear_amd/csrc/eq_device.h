@@ -318,6 +318,17 @@ struct Half<_Float16> {
     }
 };
 
+// fp16 spectra held in 16 bits (the VALU-transform kernels, the
+// weight-gradient planes) are those of x/N (so that a bin never exceeds the largest |x|:
+// fp16 keeps its range wherever x and y do); the accumulators then hold the
+// spectrum of y/N, and the inverse transform first multiplies by N.  (Exact
+// for N a power of two; one fp32 rounding otherwise.)  bf16 and fp32 have the
+// range of fp32 and keep the unscaled spectra.
+template <typename IO, int N>
+constexpr float spec_scale = std::is_same_v<IO, _Float16> ? (float)(1.0 / N) : 1.0f;
+template <typename IO, int N>
+constexpr float spec_unscale = std::is_same_v<IO, _Float16> ? (float)N : 1.0f;
+
 // ---------------------------------------------------------------------------
 // Workgroup ids are handed to the 8 XCDs round-robin.  Remap them so that a
 // run of consecutive logical tiles executes on one XCD and shares its L2.

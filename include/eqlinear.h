@@ -151,7 +151,7 @@ eqlinear_status eqlinear_weight_fft(eqlinear_plan_t plan, const void* w, void* w
  * dtype before the matrix cores and round y once from fp32; for 2 <= N <= 8
  * the transforms run on the matrix cores too, with coefficients in the plan
  * dtype, and the frequency-domain outputs are rounded to it before the inverse
- * transform. */
+ * transform (see eqlinear_forward_tiled for which kernel takes which shape). */
 eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                  void* y, int64_t T, void* stream);
 
@@ -174,7 +174,15 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
  * their results differ from the other tiles by fp32 rounding.  The automatic
  * choice uses tile 14 for fp32 layers too small for one wave per SIMD.  Shapes
  * with C_in not a multiple of 16 bytes of channels use a generic kernel with
- * fewer shapes.  Other tile values -> EQL_ERR_INVALID. */
+ * fewer shapes.  Tile 16 (bf16 and fp16 plans with 2 <= N <= 8 and C_in, C_out
+ * multiples of 8; otherwise the automatic choice among the others) is the
+ * persistent kernel: one workgroup per CU and output slice of 48 channels, x
+ * streamed into registers ahead of use, w_hat held in LDS; its transforms run
+ * on the matrix cores like tiles 7..13, with 1/N folded into the forward
+ * coefficients (and N into the inverse ones) so that no 16-bit intermediate
+ * exceeds the range of x and y.  The automatic choice does not use it (it
+ * measured slower than tiles 7..13 on MI355X).  Other tile values ->
+ * EQL_ERR_INVALID. */
 eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                        void* y, int64_t T, void* stream, int tile);
 

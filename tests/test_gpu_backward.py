@@ -205,6 +205,20 @@ def test_gradients_satisfy_the_adjoint_identity(eq, dt):
     assert abs(np.sum(dw * d["w64"]) - lhs) <= tol * scale
 
 
+@pytest.mark.parametrize("N,C_in,C_out,T", [(8, 96, 96, 700), (7, 40, 72, 333), (8, 24, 16, 500)])
+def test_backward_weight_fp16_loss_scaled(eq, N, C_in, C_out, T):
+    """A loss-scaled upstream gradient in fp16 (dy scaled by 2^13, exactly): the
+    transformed dy held in fp16 would pass 65504 unscaled.  dw (fp32) must match
+    the oracle on the plane paths and the narrow-layer path alike."""
+    d = _inputs(N, C_in, C_out, T, F16, seed=N + C_in)
+    dyd, dy64 = synthetic.quantize(d["dy64"] * 8192.0, F16)
+    assert np.array_equal(dy64, d["dy64"] * 8192.0)
+    dd = dict(d, dy=dyd, dy64=dy64)
+    dw = run_backward_weight(eq, N, C_in, C_out, T, F16, dd)
+    assert np.all(np.isfinite(dw))
+    assert_close(dw, oracle.cn_backward_weight(d["x64"], dy64), F16, f"dw fp16 loss-scaled N={N}")
+
+
 # --- the benchmark workloads at full size ------------------------------------------------
 
 def _shift_route_dw(x64, dy64):

@@ -91,7 +91,7 @@ def test_forward_sweep(eq, N, dt):
     for (C_in, C_out, T) in SHAPES:
         d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=N * 100 + C_in)
         ref = oracle.cn_dense(d["x64"], d["w64"])
-        for tile in range(-1, 16):
+        for tile in range(-1, 17):
             y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
             assert_close(y, ref, dt, f"N={N} {dt} C_in={C_in} C_out={C_out} T={T} tile={tile}")
 
@@ -101,11 +101,14 @@ def test_forward_sweep(eq, N, dt):
     (8, 96, 96, 1000), (7, 160, 160, 777), (8, 96, 384, 300), (8, 384, 96, 300),
     (4, 8, 8, 64), (8, 32, 32, 4096), (5, 64, 64, 129), (16, 48, 80, 97), (12, 20, 36, 200),
     (6, 48, 40, 150), (3, 64, 24, 90), (2, 16, 48, 70),
+    # whole 8-channel input groups with token rows of y that are not whole
+    # 16-byte pieces (the transform kernel's element-wise store path)
+    (2, 32, 21, 150), (4, 24, 3, 77), (6, 16, 7, 50), (7, 8, 4, 60),
 ])
 def test_forward_multi_tile_shapes(eq, N, C_in, C_out, T, dt):
     d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=7)
     ref = oracle.cn_dense(d["x64"], d["w64"])
-    for tile in range(-1, 16):
+    for tile in range(-1, 17):
         y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
         assert_close(y, ref, dt, f"N={N} {dt} {C_in}->{C_out} T={T} tile={tile}")
 
@@ -139,6 +142,24 @@ def test_fp16_workload_full_size(eq, name):
     ref = oracle.cn_dense(d["x64"], d["w64"])
     r, m = assert_close(y, ref, F16, f"{name} fp16")
     print(f"{name} fp16: rel-L2 {r:.3e} max/rms {m:.3e} over all {wl.T} tokens")
+
+
+@pytest.mark.parametrize("N", [3, 4, 7, 8, 12])
+def test_fp16_large_inputs_keep_their_range(eq, N):
+    """fp16 x of magnitude up to ~4e4 (x ~ N(0, 1) scaled by 2^13, exactly): y
+    stays below 65504, but an unscaled spectrum bin (a sum of N values) would
+    not.  Every tile must still match the oracle and produce finite values."""
+    C_in, C_out, T = 64, 48, 300
+    d = synthetic.cn_inputs(N, C_in, C_out, T, F16, seed=N + 40)
+    xd, x64 = synthetic.quantize(d["x64"] * 8192.0, F16)
+    assert np.array_equal(x64, d["x64"] * 8192.0)  # the scaling is exact
+    assert np.abs(x64).max() * 3 > 65504  # a DC bin of 3+ such values would overflow
+    dd = dict(d, x=xd, x64=x64)
+    ref = oracle.cn_dense(x64, d["w64"])
+    assert np.abs(ref).max() < 65504
+    for tile in range(-1, 17):
+        y, _ = run_cn(eq, N, C_in, C_out, T, F16, tile=tile, inputs=dd)
+        assert_close(y, ref, F16, f"N={N} fp16 x*2^13 tile={tile}")
 
 
 @pytest.mark.parametrize("dt", [F32, BF16, F16])
