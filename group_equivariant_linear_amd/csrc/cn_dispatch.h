@@ -19,11 +19,11 @@ hipError_t launch_cn_stream_bf16(int N, const void* x, const void* w_hat, void* 
 hipError_t launch_cn_stream_f16(int N, const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
                                 hipStream_t stream, Epi epi);
 
-// The automatic choice does not take the persistent kernel: on MI355X its
-// lane-scattered x loads (16 bytes per lane, 128 bytes apart, the layout the
-// 16x16x32 operands ask for) thrash the CUs' L1 and it ran the c3 trio in
-// 148 us against 97.5 us for tile 10 (cache-cold).  EQL_STREAM_MIN_T sets a
-// token count from which it would.
+// The automatic choice does not take the persistent kernel: on MI355X it ran
+// the c3 trio (C8, 12608 tokens, 768->768, 768->3072, 3072->768 channels x
+// group elements, bf16) in 116 us cache-cold and 95 us warm, against 99 us and
+// 73 us for tile 10, and the C7 layer of 32768 tokens x 1120 in 96 us against
+// 71 us.  EQL_STREAM_MIN_T sets a token count from which it would.
 #ifndef EQL_STREAM_MIN_T
 #define EQL_STREAM_MIN_T (int64_t)0x7fffffffffffffff
 #endif

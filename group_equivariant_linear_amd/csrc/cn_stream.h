@@ -4,21 +4,23 @@
 // products over the kept half of the spectrum, inverse DFT, one pass with no
 // intermediate tensor in memory), scheduled for the memory system.
 //
-// One workgroup per CU, one wave per SIMD, so that a wave may hold ~500
-// registers.  A workgroup owns one slice of CT = 16 CB output channels for the
-// whole launch and walks the token axis in 16-token blocks, one block per wave
-// at a time (the workgroups of all output slices walk the same blocks in the
-// same order, so a block's x is fetched from HBM once and read from L2 by the
-// other slices; the slices of one block share an XCD).  Per wave, the input
-// channels of a block are consumed in chunks of 32, and the chunks of
-// successive blocks form one stream:
-//   - x goes from memory straight into registers, PF chunks ahead of use: the
-//     lane that multiplies channels 8kg .. 8kg+7 of token tl loads exactly
-//     their 8 records (16 N contiguous bytes), which are the B operands of the
-//     transform products -- no LDS exchange and no barrier;
+// One workgroup of eight waves per CU (two waves per SIMD).  A workgroup owns
+// one slice of CT = 16 CB output channels for the whole launch and walks the
+// token axis in 16-token blocks, one block per wave at a time (the workgroups
+// of all output slices walk the same blocks in the same order, so a block's x
+// is fetched from HBM once and read from L2 by the other slices; the slices of
+// one block share an XCD).  Per wave, the input channels of a block are
+// consumed in chunks of 32, and the chunks of successive blocks form one
+// stream:
+//   - x goes from memory straight into the wave's own exchange rows in LDS
+//     (direct loads of whole 16-byte pieces, cn_mf's row layout); as soon as
+//     the wave has read a chunk's channel records into registers it starts the
+//     next chunk into the same rows, so one chunk per wave is always in flight
+//     and the transform, the products and any epilogue run under its latency;
 //   - the w_hat slice of the workgroup sits in LDS for the whole launch when
-//     all of C_in fits (WSTAT: loaded once, then the waves run independently);
-//     otherwise it streams through a two-stage LDS ring, one barrier per chunk;
+//     all of C_in fits (WSTAT: loaded once, then the waves run independently,
+//     with no barrier); otherwise it streams through a two-stage LDS ring, one
+//     barrier per chunk;
 //   - group DFT on the matrix cores (block-diagonal 16 x 32 coefficient
 //     fragments, as in cn_mf.h), the spectrum rounded once to the I/O type;
 //     the per-bin products as the real 2 x 2 block form, fp32 accumulation;
@@ -35,28 +37,34 @@
 
 namespace eql {
 
-#ifndef EQL_STREAM_PF
-#define EQL_STREAM_PF 1  // chunks of x in flight ahead of the one being multiplied
-#endif
-
 // s_waitcnt immediate: vmcnt <= n (0..63), lgkmcnt and expcnt unconstrained.
 constexpr int vmcnt_imm_st(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-template <int N_, typename IO_, int CB_, int PF_, bool WSTAT_, bool EPI_, int WPE_ = 2>
+// WSTAT: the w_hat slice stays in LDS for the whole launch; otherwise it
+// streams through a two-stage ring.
+template <int N_, typename IO_, int CB_, bool WSTAT_, bool EPI_>
 struct StCfg {
     using IO = IO_;
     using F8 = typename Half<IO_>::x8;
-    static constexpr int N = N_, CB = CB_, PF = PF_;
+    static constexpr int N = N_, CB = CB_;
     static constexpr bool WSTAT = WSTAT_;
-    static constexpr bool EPI = EPI_;  // the fused bias/GELU epilogue is compiled in
-    static constexpr int WPE = WPE_;   // workgroups per CU (waves per SIMD)
+    static constexpr bool EPI = EPI_;    // the fused bias/GELU epilogue is compiled in
     static constexpr int CT = 16 * CB_;  // output channels of a workgroup
     static constexpr int KC = 32;        // input channels per chunk
-    static constexpr int WAVES = 4, kThreads = 256;
+    static constexpr int WAVES = 8, kThreads = 512;
     static constexpr int MQ = (N_ + 3) / 4;  // transform products per four channels
     static constexpr int H = (N_ - 1) / 2;   // complex bins
     static constexpr int NB = 1 + H + (N_ % 2 == 0 ? 1 : 0);
-    static constexpr int XL = N_;              // 16-byte loads of a lane's records per chunk
+    // x: a chunk of a 16-token block is 16 rows of XP 16-byte pieces, held in
+    // the wave's exchange rows as in cn_mf.h (rotated rows for N = 2, 4, 8,
+    // else rows padded to an odd pitch)
+    static constexpr int XP = 4 * N_;
+    static constexpr bool XALIGN = (16 % (2 * N_)) == 0;  // records inside one piece
+    static constexpr bool XROT = XALIGN && (XP % 8) == 0;
+    static constexpr int XPITCH = XROT ? XP : (XP | 1);
+    // slot s of the rows is written by lane s % 64 of load s / 64: whole loads
+    static constexpr int XDMA = (16 * XPITCH + 63) / 64;
+    static constexpr int XEX = XDMA * 1024;  // exchange bytes of one wave
     static constexpr int WSLOTS = N_ * CT * 4;  // 16-byte parts of one w_hat chunk
     static constexpr int WDMA = (WSLOTS + kThreads - 1) / kThreads;  // direct loads per thread and chunk
     static constexpr int WCH = WDMA * kThreads * 16;  // LDS bytes of a chunk, padded to whole loads
@@ -102,29 +110,11 @@ __device__ __forceinline__ void st_frags(typename C::F8 (&Fa)[C::MQ]) {
     });
 }
 
-// Record J (elements 0..N-1, zeros after) of a lane's 8 records, held as 4N
-// dwords (16N contiguous bytes).
-template <int N, int J, typename F8>
-__device__ __forceinline__ F8 st_record(const u32x4 (&xr)[N]) {
-    u32x4 e = {0u, 0u, 0u, 0u};
-    constexpr int B0 = 2 * N * J, SH = B0 % 4, D0 = B0 / 4;
-    auto dw = [&](int d) -> uint32_t { return xr[d / 4][d % 4]; };
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (2 * q + 1 < N) {
-            e[q] = SH == 0 ? dw(D0 + q) : __builtin_amdgcn_alignbit(dw(D0 + q + 1), dw(D0 + q), 16);
-        } else if (2 * q < N) {
-            e[q] = SH == 0 ? (dw(D0 + q) & 0xffffu) : (dw(D0 + q) >> 16);
-        }
-    }
-    return __builtin_bit_cast(F8, e);
-}
-
 template <class C>
-__global__ __launch_bounds__(C::kThreads, C::WPE) void cn_stream_kernel(
+__global__ __launch_bounds__(C::kThreads, 1) void cn_stream_kernel(
     const typename C::IO* __restrict__ x, const typename C::IO* __restrict__ w_hat, typename C::IO* __restrict__ y,
     int64_t T, int C_in, int C_out, int n_ct, int P, uint32_t n_wg, Epi epi) {
-    constexpr int N = C::N, CB = C::CB, PF = C::PF, MQ = C::MQ, H = C::H, NB = C::NB, XL = C::XL;
+    constexpr int N = C::N, CB = C::CB, MQ = C::MQ, H = C::H, NB = C::NB, WAVES = C::WAVES;
     constexpr int S = 2;  // bytes per element
     using IO = typename C::IO;
     using F8 = typename C::F8;
@@ -139,12 +129,12 @@ __global__ __launch_bounds__(C::kThreads, C::WPE) void cn_stream_kernel(
     const int kg = lane >> 4, tl = lane & 15;
     const int nch = (C_in + C::KC - 1) / C::KC;
     const int64_t nblk = (T + 15) / 16;
-    // this wave's token blocks: (m P + wi) 4 + wave, m = 0, 1, ...; in the ring
-    // mode every wave runs the count of wave 0 (the largest), so that all take
-    // part in every barrier
-    const int64_t b0 = (int64_t)wi * 4 + wave, stride = (int64_t)P * 4;
+    // this wave's token blocks: (m P + wi) WAVES + wave, m = 0, 1, ...; in the
+    // ring mode every wave runs the count of wave 0 (the largest), so that all
+    // take part in every barrier
+    const int64_t b0 = (int64_t)wi * WAVES + wave, stride = (int64_t)P * WAVES;
     const int64_t nmine = b0 < nblk ? (nblk - b0 + stride - 1) / stride : 0;
-    const int64_t nlead = (int64_t)wi * 4 < nblk ? (nblk - (int64_t)wi * 4 + stride - 1) / stride : 0;
+    const int64_t nlead = (int64_t)wi * WAVES < nblk ? (nblk - (int64_t)wi * WAVES + stride - 1) / stride : 0;
     const int64_t nsteps = (C::WSTAT ? nmine : nlead) * nch;
 
     const uint32_t row_x = (uint32_t)C_in * (N * S), row_y = (uint32_t)C_out * (N * S);
@@ -181,9 +171,9 @@ __global__ __launch_bounds__(C::kThreads, C::WPE) void cn_stream_kernel(
     };
     // parts never loaded (rows past C_out, channels past C_in) must be finite
     // (their x side is zero, or their rows are dropped): clear the LDS first
+    const int wbytes = (C::WSTAT ? nch : 2) * C::WCH;
     if ((C_in % C::KC) != 0 || (C_out - o0) < C::CT) {
-        const int bytes = (C::WSTAT ? nch : 2) * C::WCH;
-        for (int i = (int)threadIdx.x; i < bytes / 16; i += C::kThreads)
+        for (int i = (int)threadIdx.x; i < wbytes / 16; i += C::kThreads)
             reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
     }
@@ -193,29 +183,61 @@ __global__ __launch_bounds__(C::kThreads, C::WPE) void cn_stream_kernel(
         dma_w(0, smem);
     }
 
-    // --- x: step s = (block index m, chunk c); this lane's 8 records of chunk c
-    // of block (m P + wi) 4 + wave are 16N bytes at (t C_in + 32c + 8kg) 2N.
-    // The prefetch cursor (mp, cp) runs PF steps ahead of the step's (m, c);
-    // both advance by one chunk per step (no divisions in the loop).
-    u32x4 xr[PF + 1][XL];
+    // --- x: step s = (block index m, chunk c).  Chunk c of block (m P + wi)
+    // WAVES + wave: token rows t0 .. t0+15, bytes 64 N c .. 64 N (c+1) of each
+    // row.  Load j of this lane fills slot 64 j + lane of the exchange rows:
+    // row r = slot / XPITCH, rotated position -> piece k (cn_mf's layout).  The
+    // load cursor (mp, cp) runs one step ahead of the step's (m, c).
+    char* xex = smem + wbytes + wave * C::XEX;
+    uint32_t xoff[C::XDMA];  // offset of the slot's piece within a chunk's rows
+#pragma unroll
+    for (int j = 0; j < C::XDMA; ++j) {
+        const int sl = 64 * j + lane, r = sl / C::XPITCH, pos = sl % C::XPITCH;
+        const int k = C::XROT ? (pos + C::XP - r % C::XP) % C::XP : pos;
+        xoff[j] = (r < 16 && k < C::XP) ? (uint32_t)r * row_x + (uint32_t)k * 16u : kOOB;
+    }
     int64_t mp = 0;
     int cp = 0, sp = 0;  // cursor chunk; steps issued (saturates at nsteps)
-    auto load_x = [&](auto slotc) {
-        constexpr int sl = decltype(slotc)::value;
-        uint32_t off = kOOB;
+    auto load_x = [&]() {
+        bool on = false;
+        uint32_t base = 0;
+        int64_t t0 = 0;
+        uint32_t valid = 0;  // bytes of the chunk's rows that hold channels < C_in
         if (sp < nsteps) {
-            const int64_t t = (b0 + mp * stride) * 16 + tl;
-            if (t < T && cp * C::KC + 8 * kg < C_in)
-                off = (uint32_t)t * row_x + (uint32_t)(cp * C::KC + 8 * kg) * (uint32_t)(N * S);
+            t0 = (b0 + mp * stride) * 16;
+            on = t0 < T;
+            base = (uint32_t)t0 * row_x + (uint32_t)(cp * C::KC) * (uint32_t)(N * S);
+            valid = (uint32_t)(C_in - cp * C::KC) * (uint32_t)(N * S);
             ++sp;
             if (++cp == nch) {
                 cp = 0;
                 ++mp;
             }
         }
+        if (on && t0 + 16 <= T && valid >= (uint32_t)(C::XP * 16)) {
+            // (the offsets pass through locals: an array element given straight
+            // to the builtin makes the host compilation drop the kernel's stub)
 #pragma unroll
-        for (int q = 0; q < XL; ++q)
-            xr[sl][q] = __builtin_amdgcn_raw_buffer_load_b128(rx, off == kOOB ? kOOB : off + 16u * q, 0, 0);
+            for (int j = 0; j < C::XDMA; ++j) {
+                const uint32_t off = xoff[j] == kOOB ? kOOB : xoff[j] + base;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(xex + j * 1024), 16, off, 0, 0, 0);
+            }
+        } else {
+            // a partial block, a partial chunk or past the end: rows past T and
+            // pieces past C_in are not read (every slot still gets one load, so
+            // that the count of loads in flight stays the same)
+            const uint32_t rows = on ? (uint32_t)(T - t0 < 16 ? T - t0 : 16) : 0u;
+#pragma unroll
+            for (int j = 0; j < C::XDMA; ++j) {
+                const int sl = 64 * j + lane, r = sl / C::XPITCH, pos = sl % C::XPITCH;
+                const int k = C::XROT ? (pos + C::XP - r % C::XP) % C::XP : pos;
+                const bool ok = xoff[j] != kOOB && (uint32_t)r < rows && (uint32_t)k * 16u < valid;
+                const uint32_t off = ok ? xoff[j] + base : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (__attribute__((address_space(3))) void*)(xex + j * 1024), 16, off, 0, 0, 0);
+            }
+        }
     };
 
     // bias of this lane's output channels (the slice is fixed for the launch)
@@ -240,48 +262,54 @@ __global__ __launch_bounds__(C::kThreads, C::WPE) void cn_stream_kernel(
     const int o_l = lane & 15;
     const int lane_off = (o_l * 4 + (kg ^ ((o_l >> 1) & 3))) * 16;
 
-    // the first PF chunks of x
-    static_for<0, PF>([&](auto kc) { load_x(kc); });
+    // the first chunk of x
+    load_x();
     // the slice (or the first ring stage) has landed for every wave
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // One step: wait for x(s) (and, in ring mode, w_hat(s)), start x(s + PF),
-    // transform, products; after a block's last chunk the epilogue.
+    // One step: wait for x(s) (and, in ring mode, w_hat(s)); read its records,
+    // start x(s + 1) into the rows they leave; transform, products; after a
+    // block's last chunk the epilogue and its stores.  Loads and stores retire
+    // in issue order, so a wait names the number of younger operations that may
+    // stay in flight: x(s) went out in step s - 1 after its records were read,
+    // and only the stores of step s - 1 (a block that ended there) are younger.
     int64_t m = 0;  // this step's block index (in the wave's sequence) and chunk
     int c = 0;
-    auto step = [&](auto kc, int64_t s) {
-        constexpr int k = decltype(kc)::value;  // ring slot of x(s)
-        constexpr int kn = (k + PF) % (PF + 1);  // ring slot of x(s + PF)
-        const bool after_epi = c == 0 && s > 0;  // the previous step stored y
+    for (int64_t s = 0; s < nsteps; ++s) {
+        const bool ended = m > 0 && c == 0;  // step s - 1 ended a block and stored it
+        if (ended) __builtin_amdgcn_s_waitcnt(vmcnt_imm_st(C::E));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm_st(0));
         const char* wbuf;
         if constexpr (C::WSTAT) {
-            // x(s) is older than the PF-1 younger chunks (and than the stores
-            // of the previous step, if any)
-            if (after_epi) __builtin_amdgcn_s_waitcnt(vmcnt_imm_st((PF - 1) * XL + C::E));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm_st((PF - 1) * XL));
             wbuf = smem + c * C::WCH;
         } else {
-            // w_hat(s) was started in the previous step, just before x(s + PF - 1):
-            // with PF >= 2 that x chunk may stay in flight, with PF = 1 it is x(s)
-            constexpr int YOUNG = PF >= 2 ? XL : 0;
-            if (after_epi) __builtin_amdgcn_s_waitcnt(vmcnt_imm_st(YOUNG + C::E));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm_st(YOUNG));
+            // w_hat(s) went out in step s - 1 before x(s): it has landed too
             __builtin_amdgcn_s_barrier();  // every wave's share of w_hat(s) is in; stage (s+1)%2 is free
             const int cn = c + 1 == nch ? 0 : c + 1;
             dma_w(s + 1 < nsteps ? cn : nch, smem + ((s + 1) & 1) * C::WCH);  // nch: no access, same count
             wbuf = smem + (s & 1) * C::WCH;
         }
-        load_x(std::integral_constant<int, kn>{});
+
+        // records of channels 8kg + j (j = 0..7) of token tl
+        F8 rec[8];
+        static_for<0, 8>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            rec[j] = read_record<C, j>(xex, tl, kg);
+        });
+        // the records are in registers: the exchange rows may be refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        load_x();
+        if (c * C::KC + C::KC > C_in) {  // channel tail: records past C_in are zero
+            const int left = C_in - c * C::KC;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (8 * kg + j >= left) rec[j] = F8{};
+        }
 
         // transform: Xh[p] = planes p / N of channels 8kg .. 8kg+7 of token tl
         F8 Xh[N];
         {
-            F8 rec[8];
-            static_for<0, 8>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                rec[j] = st_record<N, j, F8>(xr[k]);
-            });
             uint32_t pk[N][4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -403,21 +431,20 @@ __global__ __launch_bounds__(C::kThreads, C::WPE) void cn_stream_kernel(
             c = 0;
             ++m;
         }
-    };
-
-    for (int64_t s0 = 0; s0 < nsteps; s0 += PF + 1) {
-        static_for<0, PF + 1>([&](auto kc) {
-            constexpr int k = decltype(kc)::value;
-            if (s0 + k < nsteps) step(kc, s0 + k);
-        });
     }
 }
 
 // --- host side ----------------------------------------------------------------------
 
+// LDS bytes of one workgroup: the w_hat slice or ring, then the exchange rows.
+template <class C>
+constexpr int64_t stream_lds(int nch) {
+    return (C::WSTAT ? (int64_t)nch * C::WCH : 2 * (int64_t)C::WCH) + (int64_t)C::WAVES * C::XEX;
+}
+
 // The launch: one workgroup per CU, the output slices spread evenly over them.
 // hipErrorNotSupported when the shape does not suit the kernel (channel counts
-// not multiples of 8, tensors of 2 GiB or more, a w_hat ring past the LDS).
+// not multiples of 8, tensors of 2 GiB or more, LDS past the CU's 160 KiB).
 template <class C>
 hipError_t launch_stream_cfg(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
                              hipStream_t stream, Epi epi) {
@@ -427,8 +454,8 @@ hipError_t launch_stream_cfg(const void* x, const void* w_hat, void* y, int64_t 
         (int64_t)C::N * C_in * C_out * S >= ((int64_t)1 << 31))
         return hipErrorNotSupported;
     const int nch = (C_in + C::KC - 1) / C::KC;
-    const int64_t lds = C::WSTAT ? (int64_t)nch * C::WCH : 2 * (int64_t)C::WCH;
-    if (lds * C::WPE > 160 * 1024) return hipErrorNotSupported;
+    const int64_t lds = stream_lds<C>(nch);
+    if (lds > 160 * 1024) return hipErrorNotSupported;
     static int cus = 0;
     static bool attr = false;
     if (!attr) {
@@ -437,13 +464,12 @@ hipError_t launch_stream_cfg(const void* x, const void* w_hat, void* y, int64_t 
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
             e = hipFuncSetAttribute((const void*)cn_stream_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    160 * 1024 / C::WPE);
+                                    160 * 1024);
         if (e != hipSuccess) return e;
         attr = true;
     }
     const int n_ct = (C_out + C::CT - 1) / C::CT;
-    const int slots = cus * C::WPE;
-    const int P = n_ct >= slots ? 1 : slots / n_ct;
+    const int P = n_ct >= cus ? 1 : cus / n_ct;
     const uint32_t n_wg = (uint32_t)P * (uint32_t)n_ct;
     hipLaunchKernelGGL((cn_stream_kernel<C>), dim3(n_wg), dim3(C::kThreads), (uint32_t)lds, stream,
                        (const typename C::IO*)x, (const typename C::IO*)w_hat, (typename C::IO*)y, T, C_in, C_out,
@@ -455,16 +481,14 @@ hipError_t launch_stream_cfg(const void* x, const void* w_hat, void* y, int64_t 
 template <int N, typename IO, int CB>
 hipError_t launch_stream(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
                          hipStream_t stream, Epi epi) {
-    constexpr int PF = EQL_STREAM_PF;
     const int nch = (C_in + 31) / 32;
-    using Probe = StCfg<N, IO, CB, PF, true, false>;
-    const bool stat = (int64_t)nch * Probe::WCH * Probe::WPE <= 160 * 1024;
+    const bool stat = stream_lds<StCfg<N, IO, CB, true, false>>(nch) <= 160 * 1024;
     if (epi.bias != nullptr || epi.act != 0) {
-        if (stat) return launch_stream_cfg<StCfg<N, IO, CB, PF, true, true>>(x, w_hat, y, T, C_in, C_out, stream, epi);
-        return launch_stream_cfg<StCfg<N, IO, CB, PF, false, true>>(x, w_hat, y, T, C_in, C_out, stream, epi);
+        if (stat) return launch_stream_cfg<StCfg<N, IO, CB, true, true>>(x, w_hat, y, T, C_in, C_out, stream, epi);
+        return launch_stream_cfg<StCfg<N, IO, CB, false, true>>(x, w_hat, y, T, C_in, C_out, stream, epi);
     }
-    if (stat) return launch_stream_cfg<StCfg<N, IO, CB, PF, true, false>>(x, w_hat, y, T, C_in, C_out, stream, epi);
-    return launch_stream_cfg<StCfg<N, IO, CB, PF, false, false>>(x, w_hat, y, T, C_in, C_out, stream, epi);
+    if (stat) return launch_stream_cfg<StCfg<N, IO, CB, true, false>>(x, w_hat, y, T, C_in, C_out, stream, epi);
+    return launch_stream_cfg<StCfg<N, IO, CB, false, false>>(x, w_hat, y, T, C_in, C_out, stream, epi);
 }
 
 }  // namespace eql
