@@ -57,6 +57,9 @@ KERNEL_SOURCES = {
     "D8": ["group_equivariant_linear_amd/csrc/d8_forward.hip",
            "group_equivariant_linear_amd/csrc/gemm_rows.hip",
            "group_equivariant_linear_amd/csrc/eq_device.h"],
+    "REG": ["group_equivariant_linear_amd/csrc/dn_regular.hip",
+            "group_equivariant_linear_amd/csrc/dn_group.h",
+            "group_equivariant_linear_amd/csrc/eq_device.h"],
 }
 KERNEL_SOURCES["D"] = KERNEL_SOURCES["D8"]  # the dihedral layers of other orders: same kernels
 
@@ -495,14 +498,18 @@ ROTATE_BYTES = 3 * CACHE_BYTES     # bytes a tensor copy waits before it is used
 MAX_COPIES = 64
 
 
-def rotation_plan(bytes_per_step, est_us_per_step):
+def rotation_plan(bytes_per_step, est_us_per_step, steps):
     """(copies, steps per graph): enough copies that R x bytes >= 3x the
-    Infinity Cache, and enough steps per graph that a replay keeps the GPU busy
-    for ~100 us (the host's launch cost then hides behind it)."""
+    Infinity Cache, and up to ~400 us of work per graph (the host's launch
+    cost, ~10 us a graph, then hides behind the replay and the gap between
+    graphs is spread over S steps), S a divisor of the timed step count so that
+    exactly that many steps are timed; R is rounded up to a multiple of S so
+    that every graph holds S distinct copies."""
     R = min(MAX_COPIES, max(2, -(-ROTATE_BYTES // max(bytes_per_step, 1))))
-    S = max(1, min(R, int(100.0 // max(est_us_per_step, 1e-3))))
-    while R % S:
+    S = max(1, min(R, int(400.0 // max(est_us_per_step, 1e-3))))
+    while steps % S:
         S -= 1
+    R = -(-R // S) * S
     return R, S
 
 
@@ -516,7 +523,7 @@ def rotation_timing(layers, fn_name, steps, warmup, bytes_per_step, est_us):
     the launch stream bracket the whole region, which synchronizes on both sides.
     Returns (ms per step, steps timed, R, S)."""
     import torch
-    R, S = rotation_plan(bytes_per_step, est_us)
+    R, S = rotation_plan(bytes_per_step, est_us, steps)
     for L in layers:
         if not hasattr(L, "copies") or len(L.copies) < R:
             L.make_copies(R)
@@ -536,7 +543,7 @@ def rotation_timing(layers, fn_name, steps, warmup, bytes_per_step, est_us):
         graphs.append(gr)
     for L in layers:
         L.use(0)
-    nrep = -(-steps // S)
+    nrep = steps // S
     for k in range(-(-warmup // S)):
         graphs[k % len(graphs)].replay()
     torch.cuda.synchronize()
@@ -595,20 +602,25 @@ def summarize_trace(args, wls):
         raise SystemExit(f"expected one kernel_trace.csv under {args.trace_from}, found {files}")
     rows = list(csv.DictReader(open(files[0])))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    step = [r for r in rows if any(k in r["Kernel_Name"] for k in STEP_KERNELS)]
+    step = [r for r in rows if any(k in r["Kernel_Name"] for k in STEP_KERNELS + BW_KERNELS)]
     names = sorted({r["Kernel_Name"] for r in step})
     nl = len(wls)
     nbytes = sum(algorithmic_bytes(w, args.op, args.epilogue) for w in wls)
-    R, S = rotation_plan(nbytes, nbytes / 2.5e6)
+    R, S = rotation_plan(nbytes, nbytes / 2.5e6, args.steps)
     skip = R + -(-args.warmup // S) * S  # eager warm-up of each graph's steps, then the warmup replays
     timed = -(-args.steps // S) * S
-    if len(step) != (skip + timed) * nl:
-        raise SystemExit(f"{len(step)} step-kernel dispatches; expected ({skip} + {timed}) x {nl}")
-    step = step[skip * nl:]
-    per_layer = [[] for _ in range(nl)]
+    # kernels per layer and step: 1 for a forward, 2 or 3 for the weight gradient
+    kpl = len(step) // ((skip + timed) * nl)
+    if kpl < 1 or len(step) != (skip + timed) * nl * kpl:
+        raise SystemExit(f"{len(step)} step-kernel dispatches; expected ({skip} + {timed}) x {nl} x k")
+    step = step[skip * nl * kpl:]
+    per = {}  # (layer, position in the step) -> durations
+    kname = {}
     gaps = []
     for i, r in enumerate(step):
-        per_layer[i % nl].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        key = ((i // kpl) % nl, i % kpl)
+        per.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        kname[key] = r["Kernel_Name"]
         if i:
             gaps.append((int(r["Start_Timestamp"]) - int(step[i - 1]["End_Timestamp"])) * 1e-3)
     flags = step_flags(args)
@@ -621,22 +633,38 @@ def summarize_trace(args, wls):
              f"Each step launches the layers on one of {R} copies of their per-token tensors, in rotation "
              f"({R * nbytes >> 20} MiB, over 3x the 256 MiB Infinity Cache), {S} step(s) per HIP graph; "
              f"the {skip} warm-up steps are dropped, {timed} steps remain.", "",
-             "Kernel: " + ", ".join(f"`{n[:160]}`" for n in names), "",
-             "| layer | grid | dispatches | mean us | median us | min us | algorithmic bytes | GB/s (mean) | frac of 8 TB/s |",
-             "|---|---|---|---|---|---|---|---|---|"]
-    tot_mean = 0.0
-    for li, wl in enumerate(wls):
-        d = per_layer[li]
-        grid = {r["Grid_Size_X"] for r in step[li::nl]}
+             "Kernels: " + ", ".join(f"`{n[:160]}`" for n in names), "",
+             "| layer | kernel | grid | dispatches | mean us | median us | min us |",
+             "|---|---|---|---|---|---|---|"]
+    layer_mean = [0.0] * nl
+    for (li, k), d in sorted(per.items()):
+        grid = {r["Grid_Size_X"] for r in step[li * kpl + k::nl * kpl]}
         mean = sum(d) / max(len(d), 1)
+        layer_mean[li] += mean
+        short = next((n for n in STEP_KERNELS + BW_KERNELS if n in kname[(li, k)]), kname[(li, k)][:40])
+        lines.append(f"| {wls[li].name} | {short} | {','.join(sorted(grid))} | {len(d)} | {mean:.2f} | "
+                     f"{_median(d):.2f} | {min(d):.2f} |")
+    lines += ["", "| layer | step us (sum of its kernels' means) | algorithmic bytes | GB/s | frac of 8 TB/s |",
+              "|---|---|---|---|---|"]
+    for li, wl in enumerate(wls):
         b = algorithmic_bytes(wl, args.op, args.epilogue)
-        tot_mean += mean
-        lines.append(f"| {wl.name} | {','.join(sorted(grid))} | {len(d)} | {mean:.2f} | {_median(d):.2f} | "
-                     f"{min(d):.2f} | {b} | {b / mean / 1e3:.0f} | {b / mean / 1e3 / HBM_PEAK_GBS:.3f} |")
-    lines += ["", f"Sum of the layers' mean durations: {tot_mean:.2f} us per step ({nl} launches, mean "
-                  f"{tot_mean / nl:.2f} us); {nbytes} algorithmic bytes: {nbytes / tot_mean / 1e3:.0f} GB/s = "
+        lines.append(f"| {wl.name} | {layer_mean[li]:.2f} | {b} | {b / layer_mean[li] / 1e3:.0f} | "
+                     f"{b / layer_mean[li] / 1e3 / HBM_PEAK_GBS:.3f} |")
+    tot_mean = sum(layer_mean)
+    lines += ["", f"Sum of the layers' mean durations: {tot_mean:.2f} us per step ({nl * kpl} launches, mean "
+                  f"{tot_mean / (nl * kpl):.2f} us); {nbytes} algorithmic bytes: {nbytes / tot_mean / 1e3:.0f} GB/s = "
                   f"{nbytes / tot_mean / 1e3 / HBM_PEAK_GBS:.3f} of 8 TB/s.",
               f"Gaps between consecutive dispatches under the profiler: median {_median(gaps):.2f} us."]
+    stats = glob.glob(os.path.join(args.trace_from, "**", "*kernel_stats.csv"), recursive=True)
+    if len(stats) == 1:
+        # the profiler's own --stats summary of the same run (every dispatch of
+        # the process: the eager warm-up and the comparators' setup included)
+        srows = list(csv.DictReader(open(stats[0])))
+        lines += ["", "rocprofv3 `--stats` (kernel_stats.csv of the same run, all dispatches of the process):", "",
+                  "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+        for r in srows[:6]:
+            lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} % |")
     with open(os.path.join(ROOT, "profiles", f"kernel_trace_{profile_tag(args)}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -696,6 +724,7 @@ def _run_oracle(wl, d, n, op="forward"):
 STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "cn_split_kernel", "cn_stream_kernel",
                 "dn_regular_kernel", "d8_kernel",
                 "gemm_rows_kernel")
+BW_KERNELS = ("bw_planes_kernel", "bw_bin_kernel", "bw_gemm_kernel", "bw_small_kernel", "bw_reduce_kernel")
 TRAFFIC_WARM = 5   # back-to-back forwards (inputs partly cached from the previous launch)
 TRAFFIC_COLD = 5   # forwards each after a 512 MiB read that evicts the L2s
 TRAFFIC_COPIES = 5
@@ -813,26 +842,33 @@ def summarize_counters(args, wls):
     import glob
     nl = len(wls)
     nbytes = sum(algorithmic_bytes(w, args.op, args.epilogue) for w in wls)
-    R, S = rotation_plan(nbytes, nbytes / 2.5e6)
-    skip = (R + -(-args.warmup // S) * S) * nl
+    R, S = rotation_plan(nbytes, nbytes / 2.5e6, args.steps)
+    skip_steps = R + -(-args.warmup // S) * S
+    total_steps = skip_steps + args.steps
     vals = collections.defaultdict(list)
     kname = {}
     counters = []
     flags = step_flags(args)
     cmds = []
+    keys = set()
     for d in args.counters_from:
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         if len(files) != 1:
             raise SystemExit(f"expected one counter_collection.csv under {d}, found {files}")
-        rows = [r for r in csv.DictReader(open(files[0])) if any(k in r["Kernel_Name"] for k in STEP_KERNELS)]
+        rows = [r for r in csv.DictReader(open(files[0]))
+                if any(k in r["Kernel_Name"] for k in STEP_KERNELS + BW_KERNELS)]
         names = sorted({r["Counter_Name"] for r in rows})
         disp = sorted({int(r["Dispatch_Id"]) for r in rows})
-        keep = {dd: i % nl for i, dd in enumerate(disp) if i >= skip}
+        kpl = len(disp) // (total_steps * nl)  # kernels per layer and step
+        if kpl < 1 or len(disp) != total_steps * nl * kpl:
+            raise SystemExit(f"{d}: {len(disp)} step-kernel dispatches; expected {total_steps} x {nl} x k")
+        keep = {dd: ((i // kpl) % nl, i % kpl) for i, dd in enumerate(disp) if i >= skip_steps * nl * kpl}
         for r in rows:
             dd = int(r["Dispatch_Id"])
             if dd in keep:
                 vals[(keep[dd], r["Counter_Name"])].append(float(r["Counter_Value"]))
                 kname[keep[dd]] = r["Kernel_Name"]
+                keys.add(keep[dd])
         counters += [c for c in names if c not in counters]
         cmds.append(f"rocprofv3 --pmc {' '.join(names)} -d {d} -o run -f csv -- "
                     f"python3 bench.py {flags} --mode cold --steps {args.steps} --warmup {args.warmup}")
@@ -847,20 +883,30 @@ def summarize_counters(args, wls):
              "dispatches.", "",
              "| layer | kernel | dispatches | " + " | ".join(counters) + " |",
              "|---|---|---|" + "---|" * len(counters)]
-    for li, wl in enumerate(wls):
-        n = len(vals[(li, counters[0])])
-        cells = [f"{sum(vals[(li, c)]) / max(len(vals[(li, c)]), 1):.4g}" for c in counters]
-        lines.append(f"| {wl.name} | `{kname.get(li, '?')[:60]}` | {n} | " + " | ".join(cells) + " |")
+    for key in sorted(keys):
+        n = len(vals[(key, counters[0])])
+        cells = [f"{sum(vals[(key, c)]) / max(len(vals[(key, c)]), 1):.4g}" for c in counters]
+        lines.append(f"| {wls[key[0]].name} | `{kname.get(key, '?')[:60]}` | {n} | " + " | ".join(cells) + " |")
     out = os.path.join(ROOT, "profiles", f"counters_{tag}.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
+def source_group(wl, op):
+    """Which kernel sources the step of this workload and pass runs."""
+    if op == "backward_weight":
+        return "BW"
+    if op == "regular":
+        return "REG"
+    return wl.group
+
+
 def summarize_traffic(args, wls):
     """Calibrated HBM bytes per launch of the step kernel from two rocprofv3 --pmc runs
     of --mode traffic (FETCH_SIZE, then WRITE_SIZE; both count KiB per dispatch)."""
-    wl = args.workload
+    wl = profile_tag(args)
+    flags = step_flags(args)
     layers = wls
     res = {}
     for counter, d in zip(("FETCH_SIZE", "WRITE_SIZE"), args.traffic_from):
@@ -881,25 +927,25 @@ def summarize_traffic(args, wls):
     f, w = res["FETCH_SIZE"], res["WRITE_SIZE"]
     cold = f["kib_cold"] * 1024 * f["scale"] + w["kib_cold"] * 1024 * w["scale"]
     warm = f["kib_warm"] * 1024 * f["scale"] + w["kib_warm"] * 1024 * w["scale"]
-    algo = sum(algorithmic_bytes(w) for w in wls)
-    group = wls[0].group
+    algo = sum(algorithmic_bytes(w, args.op, args.epilogue) for w in wls)
+    group = source_group(wls[0], args.op)
     rec = {"workload": wl, "kernel": f["kernel"], "kernel_source_sha": kernel_source_hash(group),
            "hbm_bytes_per_launch": cold, "hbm_bytes_per_launch_warm": warm,
            "algorithmic_bytes_per_launch": algo, "traffic_over_algorithmic": cold / algo,
            "fetch": f, "write": w, "copy_bytes": TRAFFIC_COPY_BYTES,
            "command_fetch": f"rocprofv3 --pmc FETCH_SIZE -d {args.traffic_from[0]} -o run -f csv -- "
-                            f"python3 bench.py --workload {wl} --mode traffic",
+                            f"python3 bench.py {flags} --mode traffic",
            "command_write": f"rocprofv3 --pmc WRITE_SIZE -d {args.traffic_from[1]} -o run -f csv -- "
-                            f"python3 bench.py --workload {wl} --mode traffic",
-           "command_summary": f"python3 bench.py --workload {wl} --traffic-from "
+                            f"python3 bench.py {flags} --mode traffic",
+           "command_summary": f"python3 bench.py {flags} --traffic-from "
                               f"{args.traffic_from[0]} {args.traffic_from[1]}"}
     with open(os.path.join(ROOT, "profiles", f"traffic_{wl}.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
-    md = [f"# HBM traffic of the step kernel, workload {wl}", "",
+    md = [f"# HBM traffic of the step kernel, {wl}", "",
           f"Kernel: `{f['kernel']}`", "",
           "Commands (each counter in its own pass):", "",
           "```", rec["command_fetch"], rec["command_write"], rec["command_summary"], "```", "",
-          f"`--mode traffic` launches {TRAFFIC_WARM} back-to-back forwards, {TRAFFIC_COLD} forwards "
+          f"`--mode traffic` launches {TRAFFIC_WARM} back-to-back steps, {TRAFFIC_COLD} steps "
           f"each after a 512 MiB read (L2s evicted, clean), then {TRAFFIC_COPIES} device copies of "
           f"{TRAFFIC_COPY_BYTES >> 20} MiB that calibrate the counters.", "",
           "| counter | KiB/launch warm | KiB/launch cold | copy KiB (expected "
@@ -909,14 +955,14 @@ def summarize_traffic(args, wls):
         md.append(f"| {c} | {r['kib_warm']:.1f} | {r['kib_cold']:.1f} | {r['copy_kib']:.1f} | {r['scale']:.4f} |")
     md += ["", f"Calibrated HBM bytes per launch: cold {cold:.0f}, warm {warm:.0f}; "
                f"algorithmic {algo} (x once, y once, w_hat once): cold/algorithmic = {cold / algo:.3f}.",
-           f"Kernel source sha (cn path headers): `{rec['kernel_source_sha']}`."]
+           f"Kernel source sha (the step kernel's sources): `{rec['kernel_source_sha']}`."]
     with open(os.path.join(ROOT, "profiles", f"traffic_{wl}.md"), "w") as fh:
         fh.write("\n".join(md) + "\n")
     print(json.dumps({"hbm_bytes_per_launch": cold, "algorithmic": algo, "ratio": cold / algo}))
 
 
-def load_traffic(workload, group):
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+def load_traffic(tag, group):
+    p = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -1092,8 +1138,8 @@ def main():
     dt = wls[0].dtype
     best_dense = min(t for t in (ms_own, ms_lin) if t is not None)
 
-    same = args.op == "forward" and args.epilogue == "none" and args.dtype == "workload"
-    traffic = load_traffic(args.workload, group) if same else None
+    same = args.tile == -1 and args.op in ("forward", "regular")
+    traffic = load_traffic(profile_tag(args), source_group(wls[0], args.op)) if same else None
     out = {
         "metric": OP_METRIC[args.op],
         "value": tokens / (ms * 1e-3),
@@ -1154,7 +1200,7 @@ def main():
             "mean_launch_us": ms * 1e3 / len(layers),
             "bytes_per_launch": bytes_launch,
             "timing": "cache-cold steps (rotated copies), HIP events on the launch stream around the K steps",
-            "kernel_source_sha": kernel_source_hash(group if args.op != "backward_weight" else "BW"),
+            "kernel_source_sha": kernel_source_hash(source_group(wls[0], args.op)),
         },
     }
     if args.cpu_seconds > 0:
