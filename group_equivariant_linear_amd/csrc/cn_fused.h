@@ -810,7 +810,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_fast_kernel(
             const uint32_t off = ((uint32_t)k * 16u < cols)
                                      ? (uint32_t)(wave * 16 + r) * row_y + (uint32_t)o0 * (N * S) + (uint32_t)k * 16u
                                      : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, kYStoreAux);
         }
     } else {
         if (kLdsBias && !BiasT::OWN && epi.bias != nullptr) {

@@ -43,6 +43,15 @@
 
 #include "cn_fused.h"
 
+// y leaves the kernel once and is not read again by it: the store phase
+// writes whole 128-byte lines (8 lanes per tile row) with the non-temporal
+// hint (kYStoreAux).  Measured on MI355X, cache-cold: c3 96.3 ->
+// 91.6 us, C7 x 1120 70.7-72.3 -> 68.3-69.0 us; either change alone moved
+// neither by more than run-to-run noise.
+#ifndef EQL_MF_STORE_LPR
+#define EQL_MF_STORE_LPR 8  // lanes per y row in the store phase (4 or 8)
+#endif
+
 namespace eql {
 
 // Real-DFT coefficient of plane p at group element h (planes as in rdft_forward).
@@ -460,41 +469,49 @@ __global__ __launch_bounds__(C::kThreads) void cn_mf_kernel(
                     u32x2{pk[2 * q], pk[2 * q + 1]};
             }
         }
-        // Lane (r = lane/4, u = lane%4) stores pieces u, u+4, u+8, ... of tile
-        // row r: 64 contiguous bytes of each of the 16 rows per instruction, and
-        // no per-piece index arithmetic beyond the rotation's single wrap.
+        // LPR lanes per tile row: lane (r = lane / LPR, u = lane % LPR) stores
+        // pieces u, u + LPR, ... of rows r, r + 64/LPR, ...: every instruction
+        // writes 64/LPR rows x 16 LPR contiguous bytes, with no per-piece index
+        // arithmetic beyond the rotation's single wrap.
+        constexpr int LPR = EQL_MF_STORE_LPR, RPI = 64 / LPR, RG = 16 / RPI;
+        constexpr int NIT = (C::YP + LPR - 1) / LPR;
         const uint32_t cols = (uint32_t)(C_out - o0) * (N * S);  // valid bytes of a tile row
         const bool full = cols >= (uint32_t)(C::YP * 16);
-        const int r = lane >> 2, u = lane & 3;
-        const uint32_t gbase = (uint32_t)(wave * 16 + r) * row_y + (uint32_t)o0 * (N * S) + (uint32_t)u * 16u;
-        const char* lrow = yst + r * C::YPITCH * 16;
-        const int rot0 = C::YROT ? (u + r) % C::YP : u;  // rotated position of piece u
-        constexpr int NIT = (C::YP + 3) / 4;
+        const int r_in = lane / LPR, u = lane % LPR;
         constexpr int G = 6;  // LDS reads issued ahead of their stores
         auto store_rows = [&](auto fullc) {
             constexpr bool FULL = decltype(fullc)::value;
 #pragma unroll
-            for (int i0 = 0; i0 < NIT; i0 += G) {
-                u32x4 v[G];
+            for (int rg = 0; rg < RG; ++rg) {
+                const int r = rg * RPI + r_in;
+                const uint32_t gbase =
+                    (uint32_t)(wave * 16 + r) * row_y + (uint32_t)o0 * (N * S) + (uint32_t)u * 16u;
+                const char* lrow = yst + r * C::YPITCH * 16;
+                const int rot0 = C::YROT ? (u + r) % C::YP : u;  // rotated position of piece u
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const int it = i0 + g;
-                    if (it < NIT) {
-                        int pos = rot0 + 4 * it;
-                        if constexpr (C::YROT) pos = pos >= C::YP ? pos - C::YP : pos;
-                        v[g] = *reinterpret_cast<const u32x4*>(lrow + pos * 16);
+                for (int i0 = 0; i0 < NIT; i0 += G) {
+                    u32x4 v[G];
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const int it = i0 + g;
+                        if (it < NIT) {
+                            int pos = rot0 + LPR * it;
+                            if constexpr (C::YROT) pos = pos >= C::YP ? pos - C::YP : pos;
+                            v[g] = *reinterpret_cast<const u32x4*>(lrow + pos * 16);
+                        }
                     }
-                }
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const int it = i0 + g;
-                    if (it < NIT) {
-                        const uint32_t k = (uint32_t)(u + 4 * it);
-                        // pieces past the row (YP not a multiple of 4) and
-                        // columns past C_out are dropped by an out-of-range offset
-                        const bool ok = (C::YP % 4 == 0 || it < NIT - 1 || k < (uint32_t)C::YP) &&
-                                        (FULL || k * 16u < cols);
-                        __builtin_amdgcn_raw_buffer_store_b128(v[g], ry, ok ? gbase + 64u * it : kOOB, 0, 0);
+                    for (int g = 0; g < G; ++g) {
+                        const int it = i0 + g;
+                        if (it < NIT) {
+                            const uint32_t k = (uint32_t)(u + LPR * it);
+                            // pieces past the row (YP not a multiple of LPR) and
+                            // columns past C_out are dropped by an out-of-range offset
+                            const bool ok = (C::YP % LPR == 0 || it < NIT - 1 || k < (uint32_t)C::YP) &&
+                                            (FULL || k * 16u < cols);
+                            __builtin_amdgcn_raw_buffer_store_b128(v[g], ry, ok ? gbase + 16u * LPR * it : kOOB, 0,
+                                                                   kYStoreAux);
+                        }
                     }
                 }
             }

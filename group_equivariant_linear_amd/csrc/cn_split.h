@@ -329,7 +329,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
             const uint32_t off = (uint32_t)k * 16u < cols
                                      ? (uint32_t)r * row_y + (uint32_t)o0 * (N * 4) + (uint32_t)k * 16u
                                      : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, kYStoreAux);
         }
     } else {
 #pragma unroll

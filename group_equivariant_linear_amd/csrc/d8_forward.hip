@@ -226,7 +226,7 @@ __device__ __forceinline__ void d8_tile(const GemmJob& job, int n0, int64_t t0, 
         const int r = pc / C::YP, k = pc % C::YP;
         const u32x4 v = *reinterpret_cast<const u32x4*>(yst + ypiece<C::YROT, C::YP, C::YPITCH>(r, k) * 16);
         const uint32_t off = k * 16 < lim ? (uint32_t)(tw0 + r) * row_y + col + (uint32_t)k * 16u : kD8OOB;
-        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, kYStoreAux);
     }
 }
 

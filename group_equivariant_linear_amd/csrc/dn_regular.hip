@@ -406,7 +406,7 @@ __global__ __launch_bounds__(C::kThreads) void dn_regular_kernel(
         const uint32_t off = (k * 16 < valid && (uint32_t)(tw + r) < rows)
                                  ? (uint32_t)(tw + r) * row_y + (uint32_t)jw * (uint32_t)(G * 2) + (uint32_t)k * 16u
                                  : kOOB;
-        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, kYStoreAux);
     }
 }
 

@@ -12,6 +12,15 @@
 
 namespace eql {
 
+// Cache-policy bits of the stores that write a layer's output: y is written
+// once and not read again by the kernel that writes it, so it carries the
+// non-temporal hint (nt, bit 1 of the gfx950 cache policy).
+#ifndef EQL_Y_STORE_AUX
+#define EQL_Y_STORE_AUX 2
+#endif
+constexpr int kYStoreAux = EQL_Y_STORE_AUX;
+
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
