@@ -432,8 +432,9 @@ template <int n, typename IO>
 hipError_t launch_dnr_n(const void* x, const void* w, const void* bias, int act, void* y, int64_t T, int m_in,
                         int m_out, int64_t w_elems, hipStream_t stream) {
     // 4 waves over 32 tokens x 32 output channels (2 x 2 waves of 16 x 16)
-    // Wider tiles (64 x 32 and 128 x 32 per workgroup) measured slower on
-    // both the D5 and the D6 layer, so every n uses this one.
+    // Wider tiles (64 x 32, 128 x 32, 32 x 64 and 64 x 64 per workgroup)
+    // measured slower on both the D8 and the D6 layer, so every n uses this
+    // one: the larger tiles leave one wave per SIMD or one workgroup per CU.
     using C = DnrCfg<n, IO, 2, 2, 1, 1>;
     return launch_dnr_cfg<C>(x, w, bias, act, y, T, m_in, m_out, w_elems, stream);
 }
