@@ -15,6 +15,15 @@
 // fixed order (each wave finishes 4/KS of the accumulator rows of its block),
 // inverse-transformed, staged in LDS and written as contiguous 16-byte pieces.
 //
+// Grids of a few workgroups (XD) are pure latency: there every lane loads its
+// own records (R channels of one token, R N contiguous floats) straight into
+// registers, with no LDS tile and no barrier before the transform, and writes
+// its N outputs of a token from registers as 16-byte pieces when N % 4 == 0.
+// (Measured on MI355X, cache-cold: the C4 layer of 64 tokens x 8 channels
+// 2.74 -> 2.27 us; the C8 layer of 4096 tokens x 32 channels, 256 workgroups,
+// 5.72 -> 5.95 us, where the per-lane loads touch eight times the cache lines
+// of the coalesced tile: it keeps the tile.)
+//
 // Complex bins use three real products instead of four (Gauss's method):
 //   t1 = Xr Wr^T, t2 = Xi Wi^T, t3 = (Xr + Xi)(Wr + Wi)^T,
 //   Re = t1 - t2, Im = t3 - t1 - t2.
@@ -28,9 +37,10 @@ namespace eql {
 #define EQL_SPLIT_GAUSS 1
 #endif
 
-template <int N_, int OB_, int KS_, int R_>
+template <int N_, int OB_, int KS_, int R_, bool XD_ = false>
 struct SplitCfg {
     static constexpr int N = N_, OB = OB_, KS = KS_, R = R_;
+    static constexpr bool XD = XD_;  // records straight into registers (few workgroups)
     static constexpr int H = (N - 1) / 2;  // complex bins
     static constexpr bool GAUSS = EQL_SPLIT_GAUSS != 0 && H > 0;
     static constexpr int kWaves = OB * KS, kThreads = 64 * kWaves;
@@ -42,15 +52,22 @@ struct SplitCfg {
     static constexpr int XPITCH = XROT ? XP : (XP | 1);
     static constexpr int XBUF = 16 * XPITCH * 16;
     static constexpr int XL = (16 * XP + kThreads - 1) / kThreads;  // x loads per thread per step
+    // XD: a lane's records of one step, R N contiguous floats, 16-byte aligned
+    // for R = 4 (8-byte for R = 2), loaded 16 or 8 bytes at a time
+    static constexpr int RF = R * N;
+    static constexpr int XW = R == 4 ? 4 : 2;
+    static constexpr int XLD = RF / XW;
     static constexpr int ROWS = 4 / KS;                // accumulator rows each wave finishes
-    static constexpr int RED = N * 4 * 64 * 4;           // one wave's partial spectra
+    static constexpr int RED = N * 64 * 16;            // one wave's partial spectra: N f32x4 per lane
+    static constexpr bool YDIRECT = XD_ && N % 4 == 0;  // y stored from registers
     static constexpr int YROW = CT * N * 4;
     static constexpr int YP = YROW / 16;
     static constexpr bool YROT = YP % 8 == 0;
     static constexpr int YPITCH = YROT ? YP : (YP | 1);
-    static constexpr int YST = 16 * YPITCH * 16;
+    static constexpr int YST = YDIRECT ? 0 : 16 * YPITCH * 16;
+    static constexpr int XTILES = XD_ ? 0 : 2 * XBUF;
     // the y staging overlaps the x tiles (both at offset 0); the partials follow
-    static constexpr int PART_OFF = 2 * XBUF > YST ? 2 * XBUF : YST;
+    static constexpr int PART_OFF = XTILES > YST ? XTILES : YST;
     // the tile's bias (fp32) has a slice of its own when that keeps as many
     // workgroups per CU; otherwise each lane fetches its one value in the epilogue
     static constexpr int BIAS_OFF = PART_OFF + kWaves * RED;
@@ -111,11 +128,35 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
             xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, (uint32_t)s * step_x, 0);
         }
     };
+    // XD: this lane's records of step s are token row l16, channels
+    // s KSTEP + ch_lane .. + R-1.  C_in is a multiple of four, so the R channels
+    // of a lane are all inside C_in or all past it; rows past T lie past the
+    // resource.  Either way the loads return zeros.
+    const int ch_lane = kh * C::KW + q * R;
+    constexpr int XR = C::XD ? C::RF : 1;
+    auto load_xd = [&](int s, float (&xv)[XR]) {
+        if constexpr (C::XD) {
+            const uint32_t off = s * C::KSTEP + ch_lane < C_in ? (uint32_t)l16 * row_x + (uint32_t)ch_lane * (N * 4)
+                                                                : kOOB;
+            const uint32_t soff = (uint32_t)s * step_x;
+#pragma unroll
+            for (int j = 0; j < C::XLD; ++j) {
+                if constexpr (C::XW == 4) {
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16u * j, soff, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) xv[4 * j + e] = __uint_as_float(v[e]);
+                } else {
+                    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rx, off + 8u * j, soff, 0);
+                    xv[2 * j] = __uint_as_float(v[0]);
+                    xv[2 * j + 1] = __uint_as_float(v[1]);
+                }
+            }
+        }
+    };
 
     // B fragments (weights): lane (column l16, k-group q) holds channels
     // ch .. ch+R-1 of output row orow in every plane
     const int orow = o0 + ob * 16 + l16;
-    const int ch_lane = kh * C::KW + q * R;
     const uint32_t plane_w = (uint32_t)C_out * (uint32_t)C_in * 4u;
     const uint32_t wbase = (uint32_t)orow * (uint32_t)C_in * 4u + (uint32_t)ch_lane * 4u;
     auto load_w = [&](int s, float (&B)[N][R]) {
@@ -143,9 +184,11 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
 #pragma unroll
     for (int k = 0; k < (H > 0 ? H : 1); ++k) gs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 xr[C::XL];
+    u32x4 xr[C::XD ? 1 : C::XL];
+    float X0[XR], X1[XR];
     float B0[N][R], B1[N][R];
-    load_x(0, xr);
+    if constexpr (C::XD) load_xd(0, X0);
+    else load_x(0, xr);
     __builtin_amdgcn_sched_barrier(0);  // x first: it is needed first
     load_w(0, B0);
     // The tile's bias to its LDS slice, fetched after the first step's loads (the
@@ -159,7 +202,17 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
     // work placed between fp32 MFMAs stretches each of them by about half, so
     // everything the products read (transforms, Gauss sums) is computed first
     // and the products issue as one uninterrupted run.
-    auto step = [&](int s, const float (&B)[N][R], float (&Bnext)[N][R]) {
+    auto step = [&](int s, const float (&B)[N][R], float (&Bnext)[N][R], const float (&X)[XR], float (&Xn)[XR]) {
+        // this lane's records: token row l16, channels ch_lane .. ch_lane+R-1
+        float rec[R * N];
+        if constexpr (C::XD) {
+            if (s + 1 < steps) {
+                load_xd(s + 1, Xn);
+                load_w(s + 1, Bnext);
+            }
+#pragma unroll
+            for (int j = 0; j < R * N; ++j) rec[j] = X[j];
+        } else {
         char* xbuf = smem + (s & 1) * C::XBUF;
 #pragma unroll
         for (int j = 0; j < C::XL; ++j) {
@@ -172,8 +225,6 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
         if (s + 1 < steps) load_w(s + 1, Bnext);
         lds_barrier();
 
-        // this lane's records: token row l16, channels ch_lane .. ch_lane+R-1
-        float rec[R * N];
         const int byte0 = ch_lane * N * 4;
         if constexpr ((R * N) % 4 == 0) {
 #pragma unroll
@@ -192,6 +243,7 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
                 rec[2 * j] = __uint_as_float(v[0]);
                 rec[2 * j + 1] = __uint_as_float(v[1]);
             }
+        }
         }
         float A[N][R];
 #pragma unroll
@@ -248,9 +300,9 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
     // C_in >= 1: at least one step, no branch ahead of the first loads; the two
     // weight buffers alternate without register copies
     for (int s = 0;;) {
-        step(s, B0, B1);
+        step(s, B0, B1, X0, X1);
         if (++s >= steps) break;
-        step(s, B1, B0);
+        step(s, B1, B0, X1, X0);
         if (++s >= steps) break;
     }
     if constexpr (C::GAUSS) {
@@ -263,17 +315,15 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
     }
 
     // Sum the KS partial spectra of each block through LDS: every wave leaves
-    // all its accumulator rows there, and row i is finished by the wave with
-    // kh == i / ROWS, adding the KS partials in order (no per-lane selects).
-    // The partials have a region of their own, so they are written as soon as
-    // the products are done; the barrier after them also ends every wave's use
-    // of the x tiles, which the y staging then overwrites.
+    // its accumulators there ([plane][lane], 16 bytes each), and row i is
+    // finished by the wave with kh == i / ROWS, adding the KS partials in order
+    // (no per-lane selects).  The partials have a region of their own, so they
+    // are written as soon as the products are done; the barrier after them also
+    // ends every wave's use of the x tiles, which the y staging then overwrites.
     {
-        float* mine = reinterpret_cast<float*>(smem + C::PART_OFF + wave * C::RED);
+        f32x4* mine = reinterpret_cast<f32x4*>(smem + C::PART_OFF + wave * C::RED);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int p = 0; p < N; ++p) mine[(i * N + p) * 64 + lane] = acc[p][i];
+        for (int p = 0; p < N; ++p) mine[p * 64 + lane] = acc[p];
     }
     __syncthreads();
     // this lane's bias: from the slice, or fetched now (its latency overlaps the sums)
@@ -283,20 +333,48 @@ __global__ __launch_bounds__(C::kThreads) void cn_split_kernel(
         else bias_v = bias_value<float>(bias_fetch<float>(epi, C_out, orow));
     }
     const float* red =
-        reinterpret_cast<const float*>(smem + C::PART_OFF) + ob * (C::RED / 4) + kh * C::ROWS * N * 64 + lane;
+        reinterpret_cast<const float*>(smem + C::PART_OFF) + ob * (C::RED / 4) + lane * 4 + kh * C::ROWS;
     float P[C::ROWS][N];
 #pragma unroll
-    for (int ii = 0; ii < C::ROWS; ++ii)
+    for (int p = 0; p < N; ++p) {
+        float v[C::ROWS];
 #pragma unroll
-        for (int p = 0; p < N; ++p) {
-            float v = red[(ii * N + p) * 64];
+        for (int src = 0; src < C::KS; ++src) {
+            const float* pp = red + src * C::OB * (C::RED / 4) + p * 256;
+            float u[C::ROWS];
+            if constexpr (C::ROWS == 2) {
+                const f32x2 t = *reinterpret_cast<const f32x2*>(pp);
+                u[0] = t[0];
+                u[1] = t[1];
+            } else {
 #pragma unroll
-            for (int src = 1; src < C::KS; ++src) v += red[src * C::OB * (C::RED / 4) + (ii * N + p) * 64];
-            P[ii][p] = v;
+                for (int ii = 0; ii < C::ROWS; ++ii) u[ii] = pp[ii];
+            }
+#pragma unroll
+            for (int ii = 0; ii < C::ROWS; ++ii) v[ii] = src == 0 ? u[ii] : v[ii] + u[ii];
         }
+#pragma unroll
+        for (int ii = 0; ii < C::ROWS; ++ii) P[ii][p] = v[ii];
+    }
 
     // Epilogue: inverse DFT of each finished (token, channel) record, y written once.
-    if (y_coalesced) {
+    if constexpr (C::YDIRECT) {
+        // N contiguous floats per lane, stored as 16-byte pieces
+#pragma unroll
+        for (int ii = 0; ii < C::ROWS; ++ii) {
+            const uint32_t tl = (uint32_t)(q * 4 + kh * C::ROWS + ii);
+            const uint32_t off = orow < C_out ? tl * row_y + (uint32_t)orow * (N * 4) : kOOB;
+            float yv[N];
+            rdft_inverse<N>(P[ii], yv);
+            if (epi_on(epi)) epi_apply<N>(yv, bias_v, epi.act);
+#pragma unroll
+            for (int j = 0; j < N / 4; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{__float_as_uint(yv[4 * j]), __float_as_uint(yv[4 * j + 1]), __float_as_uint(yv[4 * j + 2]),
+                          __float_as_uint(yv[4 * j + 3])},
+                    ry, off + 16u * j, 0, kYStoreAux);
+        }
+    } else if (y_coalesced) {
         char* yst = smem;
 #pragma unroll
         for (int ii = 0; ii < C::ROWS; ++ii) {
@@ -369,6 +447,9 @@ hipError_t launch_split_cfg(const void* x, const void* w_hat, void* y, int64_t T
     return hipGetLastError();
 }
 
+// Grids below this many workgroups take the register-loaded form (XD).
+constexpr int64_t kSplitDirectBelow = 128;
+
 // KS input-channel slices: 2 (four channels per lane up to N = 8, else two) or
 // 4 (two per lane); one output block per workgroup when C_out fits in 16
 // channels, else two.
@@ -376,7 +457,13 @@ template <int N, int KS>
 hipError_t launch_split(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
                         hipStream_t stream, Epi epi) {
     constexpr int R = (KS == 2 && N <= 8) ? 4 : 2;
-    if (C_out <= 16) return launch_split_cfg<SplitCfg<N, 1, KS, R>>(x, w_hat, y, T, C_in, C_out, stream, epi);
+    const int OB = C_out <= 16 ? 1 : 2;
+    const int64_t total = (T + 15) / 16 * ((C_out + 16 * OB - 1) / (16 * OB));
+    if (total < kSplitDirectBelow) {
+        if (OB == 1) return launch_split_cfg<SplitCfg<N, 1, KS, R, true>>(x, w_hat, y, T, C_in, C_out, stream, epi);
+        return launch_split_cfg<SplitCfg<N, 2, KS, R, true>>(x, w_hat, y, T, C_in, C_out, stream, epi);
+    }
+    if (OB == 1) return launch_split_cfg<SplitCfg<N, 1, KS, R>>(x, w_hat, y, T, C_in, C_out, stream, epi);
     return launch_split_cfg<SplitCfg<N, 2, KS, R>>(x, w_hat, y, T, C_in, C_out, stream, epi);
 }
 
