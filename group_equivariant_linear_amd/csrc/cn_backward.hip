@@ -30,7 +30,9 @@
 //   3. bw_reduce_kernel: partials summed in a fixed order, inverse real DFT
 //      per (o, i), dw written in fp32 [C_out][C_in][N].
 // Layers of at most 32 channels each way run 1 and 2 as one launch
-// (bw_small_kernel: transforms into LDS, no planes in HBM), then 3.
+// (bw_small_kernel: transforms into LDS, no planes in HBM), then 3; so do the
+// other 16-bit layers of even order up to 8 (bw_xf_kernel: 64 x 64 tiles, the
+// transforms on the matrix cores inside the product kernel).
 // Every step is deterministic (no atomics).
 #include <mutex>
 
@@ -798,6 +800,250 @@ __global__ __launch_bounds__(256) void bw_small_kernel(const IO* __restrict__ x,
     });
 }
 
+// --- 2b. transforms and products in one launch (16-bit, N = 2, 4, 6, 8) ------------
+// Workgroup: one 64 x 64 (o, i) tile, every kept bin, one range of 32-token
+// chunks; eight waves, wave (wm, wn) owning outputs o in 32 wm + [0, 32) and
+// i in 16 wn + [0, 16).  Per chunk, the tile's 64 dy rows and 64 x rows are
+// transformed on the matrix cores straight from their records, and every plane
+// of both operands goes to LDS; the products then read them from there.  No
+// plane reaches HBM: x and dy are read once per tile row or column of the
+// output (the planes path writes both plane sets out and reads them back).
+//
+// Transform: a record fragment is 16 tokens x 4 channels of one operand, one
+// record per lane (token l%16, channel l/16; its N elements as the lane's
+// k-values, zeros after).  As the A operand against the coefficient fragment
+//   B[(g', h)][(g, i)] = coef(plane 4m + i, element h) if g == g' else 0
+// it returns, per lane, 4 consecutive tokens (rows 4(l/16) .. +3) of one
+// channel g = (l%16)/4 and one plane 4m + i, i = l%4: 8 bytes of that plane's
+// row in LDS.  The coefficients are those of the planes path (the spectrum of
+// x and dy; of x/N and dy/N for fp16) rounded to the I/O type, and the
+// operands of the products are the transform's fp32 outputs rounded once.
+//
+// LDS: per chunk N planes x {dy, x} x 64 rows x 64 bytes (32 tokens), for two
+// chunks (one multiplied while the next is written); the 16-byte parts of a
+// row of plane p sit at part ^ (p & 3).  A lane reads each record (2N bytes, N
+// even: dword-aligned) with one 16-byte load, two chunks ahead, into
+// registers; window bytes past the record are masked off, and those past the
+// operand's end read as zeros.
+//
+// Measured on MI355X, cache-cold, against the planes path (planes, per-bin
+// products, reduction): N = 8, 12608 tokens, 96 -> 96 38 -> 32 us, 96 -> 384
+// 74 -> 66 us, 384 -> 96 70 -> 67 us; but C7 160 -> 160 (32768 tokens, odd N:
+// records on 2-byte boundaries) 101 -> 106 us.  Odd orders keep the planes
+// path.  The per-lane record loads read rows 2 N C bytes apart, and each x and
+// dy row is read once per 64-wide tile of the other axis.
+template <int N_, typename IO_>
+struct BwXfCfg {
+    static constexpr int N = N_;
+    using IO = IO_;
+    using F8 = typename Half<IO_>::x8;
+    static constexpr int KC = 32;               // tokens per chunk: the K of one product
+    static constexpr int TM = 64, TN = 64;      // output rows (o) and columns (i) per workgroup
+    static constexpr int kWaves = 8, kThreads = 64 * kWaves;
+    static constexpr int H = (N_ - 1) / 2;
+    static constexpr bool NYQ = N_ % 2 == 0;
+    static constexpr int MQ = (N_ + 3) / 4;     // transform products per record fragment
+    static constexpr int NF = 64 / kWaves;      // record fragments per wave and chunk
+    static constexpr int REGION = 64 * 64;      // one plane of one operand: 64 rows x 64 bytes
+    static constexpr int BUF = N_ * 2 * REGION;
+    static constexpr int LDS = 2 * BUF;
+    static_assert(N_ >= 2 && N_ <= 8 && N_ % 2 == 0, "one dword-aligned record per 8 k-values");
+    static_assert(LDS <= 163840, "two chunks of planes fit the CU's LDS");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void bw_xf_kernel(const typename C::IO* __restrict__ x,
+                                                            const typename C::IO* __restrict__ dy,
+                                                            float* __restrict__ part, int64_t T, int C_out, int C_in,
+                                                            int n_i, int tiles, int chunks_per_split, int nchunks) {
+    using IO = typename C::IO;
+    using F8 = typename C::F8;
+    constexpr int N = C::N, H = C::H, MQ = C::MQ, NF = C::NF;
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+    // the tiles of one token range are consecutive logical blocks, kept on one
+    // XCD: they read the same x and dy rows, which its L2 then serves once
+    const uint32_t lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = (int)(lb % (uint32_t)tiles), split = (int)(lb / (uint32_t)tiles);
+    const int o0 = (tile / n_i) * C::TM, i0 = (tile % n_i) * C::TN;
+    const int c_begin = split * chunks_per_split;
+    const int c_end = c_begin + chunks_per_split < nchunks ? c_begin + chunks_per_split : nchunks;
+    const int nq = c_end - c_begin;
+
+    const int tid = (int)threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+
+    // Record fragments: wave w transforms fragments F = w NF + f: operand
+    // F / 32 (0: dy rows o, waves 0-3; 1: x rows i, waves 4-7), channel group
+    // (F % 32) / 2 of four rows, token half F % 2.
+    const int rs = wave >= 4 ? 1 : 0;
+    const int Crs = rs ? C_in : C_out, r0 = rs ? i0 : o0;
+    constexpr uint32_t rec_b = 2u * N;  // bytes of one record
+    const uint32_t row_b = (uint32_t)Crs * rec_b;
+    const uint32_t rbytes = (uint32_t)(T * Crs) * rec_b;  // the operand's extent
+    const __amdgpu_buffer_rsrc_t rr = rs ? bw_rsrc(x, rbytes) : bw_rsrc(dy, rbytes);
+    uint32_t roff[NF];  // this lane's record at chunk 0 (or out of range)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const int F = wave * NF + f, g16 = (F & 31) >> 1, th = F & 1;
+        const int row = r0 + 4 * g16 + (lane >> 4), tok = 16 * th + (lane & 15);
+        roff[f] = row < Crs ? (uint32_t)tok * row_b + (uint32_t)row * rec_b : kBwOOB;
+    }
+    // a fragment whose four channels all lie past the operand's rows is skipped
+    // (uniform across the wave): its rows are never read
+    auto frag_live = [&](int f) { return r0 + 4 * (((wave * NF + f) & 31) >> 1) < Crs; };
+    const uint32_t chunk_b = (uint32_t)C::KC * row_b;  // chunk advance (scalar)
+    auto load = [&](int q, u32x4 (&W)[NF]) {
+        const bool live = q < nq;
+        // (uniform: a scalar offset; stated, or the compiler loops over lanes)
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(live ? (uint32_t)(c_begin + q) * chunk_b : 0u);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+            W[f] = __builtin_amdgcn_raw_buffer_load_b128(rr, live && frag_live(f) ? roff[f] : kBwOOB, soff, 0);
+    };
+    // coefficient fragments (B operand): lane (k-group g' = l/16, column
+    // j = l%16 = (g, i)) holds coef(4m + i, h), h = 0..7, if g == g'
+    F8 Fb[MQ];
+    {
+        const int gp = lane >> 4, j = lane & 15, g = j >> 2, i = j & 3;
+        static_for<0, MQ>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            float v[8];
+#pragma unroll
+            for (int h = 0; h < 8; ++h) v[h] = 0.0f;
+            static_for<0, 4>([&](auto ic) {
+                constexpr int ii = decltype(ic)::value;
+                constexpr int p = 4 * m + ii;
+                if constexpr (p < N) {
+                    static_for<0, N>([&](auto hc) {
+                        constexpr int h = decltype(hc)::value;
+                        constexpr float c = (float)(fwd_coef<N>(p, h) * (double)spec_scale<IO, N>);
+                        v[h] = i == ii ? c : v[h];
+                    });
+                }
+            });
+            u32x4 u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) u[q] = g == gp ? Half<IO>::pack2(v[2 * q], v[2 * q + 1]) : 0u;
+            Fb[m] = __builtin_bit_cast(F8, u);
+        });
+    }
+
+    // LDS address of part u of row r of plane p of operand o_ (0: dy, 1: x)
+    auto plane_at = [&](char* buf, int p, int o_, int r, int u) {
+        return buf + (p * 2 + o_) * C::REGION + r * 64 + ((u ^ (p & 3)) << 4);
+    };
+
+    // transform the chunk held in W into buf
+    auto transform = [&](const u32x4 (&W)[NF], char* buf) {
+        const int j = lane & 15, g = j >> 2, ii = j & 3, kq = lane >> 4;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (!frag_live(f)) continue;
+            const int F = wave * NF + f, g16 = (F & 31) >> 1, th = F & 1;
+            // the record's N elements, zeros after
+            u32x4 e = W[f];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (2 * q >= N) e[q] = 0u;
+            const F8 a = __builtin_bit_cast(F8, e);
+            const int r = 4 * g16 + g;
+            // tokens 16 th + 4 kq .. + 3: part 2 th + kq / 2, half kq % 2
+            const int u = 2 * th + (kq >> 1);
+            static_for<0, MQ>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                bw_mma(d, a, Fb[m]);
+                const int p = 4 * m + ii;
+                if (p < N)
+                    *reinterpret_cast<u32x2*>(plane_at(buf, p, rs, r, u) + ((kq & 1) << 3)) =
+                        u32x2{Half<IO>::pack2(d[0], d[1]), Half<IO>::pack2(d[2], d[3])};
+            });
+        }
+    };
+
+    f32x4 acc[2][N];
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int p = 0; p < N; ++p) acc[ob][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // fragment of 16-row block blk of plane p of operand o_: row 16 blk + l%16,
+    // tokens 8 (l/16) .. + 7
+    auto frag = [&](char* buf, int p, int o_, int blk) {
+        return *reinterpret_cast<const F8*>(plane_at(buf, p, o_, 16 * blk + (lane & 15), lane >> 4));
+    };
+    auto products = [&](char* buf) {
+        static_for<0, H + 1 + (C::NYQ ? 1 : 0)>([&](auto bc) {
+            constexpr int b = decltype(bc)::value;
+            constexpr bool cplx = b >= 1 && b <= H;
+            constexpr int pr = b == 0 ? 0 : (cplx ? 2 * b - 1 : N - 1), pi = pr + 1;
+            F8 A0[2];
+            const F8 B0 = frag(buf, pr, 1, wn);
+#pragma unroll
+            for (int ob = 0; ob < 2; ++ob) A0[ob] = frag(buf, pr, 0, 2 * wm + ob);
+            if constexpr (cplx) {
+                F8 A1[2];
+                const F8 B1 = frag(buf, pi, 1, wn);
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob) A1[ob] = frag(buf, pi, 0, 2 * wm + ob);
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob) {
+                    bw_mma(acc[ob][pr], A0[ob], B0);          // a c
+                    bw_mma(acc[ob][pi], A1[ob], B0);          // b c
+                    bw_mma(acc[ob][pr], A1[ob], B1);          // + b d
+                    bw_mma(acc[ob][pi], bw_neg(A0[ob]), B1);  // - a d
+                }
+            } else {
+#pragma unroll
+                for (int ob = 0; ob < 2; ++ob) bw_mma(acc[ob][pr], A0[ob], B0);
+            }
+        });
+    };
+
+    // Two chunks in flight: the records of chunk q + 2 load while chunk q's
+    // planes are multiplied.  One barrier per chunk: after it chunk q's planes
+    // are in, and every wave is done with chunk q - 1's, whose buffer chunk
+    // q + 1 then takes.
+    u32x4 W0[NF], W1[NF];
+    load(0, W0);
+    load(1, W1);
+    for (int q = 0; q < nq;) {
+        {
+            char* buf = smem + (q & 1) * C::BUF;
+            transform(W0, buf);
+            load(q + 2, W0);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            products(buf);
+        }
+        if (++q >= nq) break;
+        {
+            char* buf = smem + (q & 1) * C::BUF;
+            transform(W1, buf);
+            load(q + 2, W1);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            products(buf);
+        }
+        ++q;
+    }
+
+    // partial spectra of this token range: part[split][p][o][i]
+    const int64_t plane = bw_pstride(C_in, C_out);  // partial planes padded to whole 16-byte groups
+    float* dst = part + (int64_t)split * N * plane;
+    const int i = i0 + 16 * wn + (lane & 15);
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int o = o0 + 32 * wm + 16 * ob + 4 * (lane >> 4) + r;
+            if (o < C_out && i < C_in) {
+#pragma unroll
+                for (int p = 0; p < N; ++p) dst[p * plane + (int64_t)o * C_in + i] = acc[ob][p][r];
+            }
+        }
+}
+
 // --- 3. reduction and inverse transform ------------------------------------------------
 // Block: 32 G consecutive (o, i) elements (G = 4 per lane, 16-byte loads, for
 // planes of at least 128 such blocks; else G = 1.  Measured on MI355X: 96 x 96
@@ -893,6 +1139,7 @@ struct BwShape {
     int64_t Tp;
     int n_o, n_i, tiles, nchunks, splits, chunks_per_split;
     bool fused;  // small layers: transforms and products in one launch, no planes
+    bool xf;     // 16-bit, N = 2, 4, 6, 8: transforms inside the product kernel (bw_xf_kernel)
     bool bin;    // products per bin over whole tiles (bw_bin_kernel)
     int WM, WN, nb, L, stage_bytes;
     int splits_r, chunks_per_split_r;  // token ranges of the real bins (the others: splits)
@@ -946,6 +1193,27 @@ BwShape bw_shape(int N, int io, int64_t T, int C_in, int C_out) {
         return s;
     }
     const int S = io == kIoF32 ? 4 : 2, KC = 64 / S;
+    if (io != kIoF32 && N >= 2 && N <= 8 && N % 2 == 0) {
+        // one launch of 64 x 64 tiles over 32-token chunks, then the reduction;
+        // token ranges give about one workgroup per CU (two chunks or more each)
+        const int64_t Tp = (T + 31) / 32 * 32;
+        if ((int64_t)N * C_in * Tp * S < ((int64_t)1 << 31) && (int64_t)N * C_out * Tp * S < ((int64_t)1 << 31)) {
+            s.xf = true;
+            s.Tp = Tp;
+            s.nchunks = (int)(Tp / 32);
+            s.n_o = (C_out + 63) / 64;
+            s.n_i = (C_in + 63) / 64;
+            s.tiles = s.n_o * s.n_i;
+            const int64_t cap = s.nchunks / 2 > 0 ? s.nchunks / 2 : 1;
+            int64_t sp = 256 / s.tiles;
+            sp = sp < 1 ? 1 : (sp > cap ? cap : sp);
+            s.chunks_per_split = (int)((s.nchunks + sp - 1) / sp);
+            s.splits = (s.nchunks + s.chunks_per_split - 1) / s.chunks_per_split;
+            s.part_bytes = round256((size_t)s.splits * N * bw_pstride(C_in, C_out) * 4);
+            s.total = s.part_bytes;
+            return s;
+        }
+    }
     const int tm = 64;  // bw_gemm_kernel tiles: 2 x 2 waves of 32 x 32
     const int H = (N - 1) / 2;
     s.nb = 1 + H + ((N % 2 == 0 && N > 1) ? 1 : 0);
@@ -1012,6 +1280,18 @@ hipError_t run_backward_weight(const void* x, const void* dy, float* dw, int64_t
                            (const IO*)dy, part, T, C_in, C_out, s.chunks_per_split, s.nchunks);
         launch_bw_reduce<N>(part, dw, s.splits, s.splits, plane, pstride, stream);
         return hipGetLastError();
+    }
+    if constexpr (!std::is_same_v<IO, float> && N >= 2 && N <= 8 && N % 2 == 0) {
+        if (s.xf) {
+            using XC = BwXfCfg<N, IO>;
+            float* part = reinterpret_cast<float*>(ws);
+            hipLaunchKernelGGL((bw_xf_kernel<XC>), dim3((uint32_t)(s.tiles * s.splits)), dim3(XC::kThreads), 0, stream,
+                               (const IO*)x, (const IO*)dy, part, T, C_out, C_in, s.n_i, s.tiles, s.chunks_per_split,
+                               s.nchunks);
+            launch_bw_reduce<N>(part, dw, s.splits, s.splits, plane, pstride, stream,
+                                spec_unscale<IO, N> * spec_unscale<IO, N>);
+            return hipGetLastError();
+        }
     }
     IO* xp = reinterpret_cast<IO*>(ws);
     IO* dyp = reinterpret_cast<IO*>(ws + s.xp_bytes);

@@ -54,15 +54,6 @@
 
 namespace eql {
 
-// Real-DFT coefficient of plane p at group element h (planes as in rdft_forward).
-template <int N>
-constexpr double fwd_coef(int p, int h) {
-    if (p == 0) return 1.0;
-    if (N % 2 == 0 && p == N - 1) return (h % 2) ? -1.0 : 1.0;
-    const int k = (p + 1) / 2;
-    return (p % 2) ? turn_trig((long)h * k, N, false) : -turn_trig((long)h * k, N, true);
-}
-
 // Inverse real-DFT coefficient of group element g from plane p, 1/N included
 // (as in rdft_inverse: DC and Nyquist weigh 1/N, the other bins 2/N).
 template <int N>

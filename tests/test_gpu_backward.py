@@ -185,6 +185,25 @@ def test_backward_weight_64_tiles(eq, N, dt):
         assert_close(dw, ref, dt, f"dw N={N} {dt} {C_in}->{C_out} T={T}")
 
 
+@pytest.mark.parametrize("dt", [BF16, F16])
+@pytest.mark.parametrize("N,C_in,C_out,T", [
+    (8, 37, 45, 101), (6, 65, 33, 1), (4, 65, 33, 77), (2, 33, 70, 95), (8, 64, 64, 32),
+    (6, 100, 36, 63), (2, 40, 130, 99), (4, 129, 66, 250), (6, 160, 160, 2000), (8, 96, 200, 1500),
+    (8, 1, 200, 33), (2, 3, 130, 29),
+])
+def test_backward_weight_transforms_in_the_product_kernel(eq, N, C_in, C_out, T, dt):
+    """16-bit layers of even order up to 8 with more than 32 channels one way:
+    x and dy are transformed inside the product kernel (64 x 64 tiles, 32-token
+    chunks, records read by 16-byte windows).  Ragged tiles, token tails, one
+    or three input channels (windows that run past the operand's end), a single
+    token, and ranges of many chunks.  Also deterministic."""
+    d = _inputs(N, C_in, C_out, T, dt, seed=13 * N + C_in + T)
+    dw = run_backward_weight(eq, N, C_in, C_out, T, dt, d)
+    ref = oracle.cn_backward_weight(d["x64"], d["dy64"])
+    assert_close(dw, ref, dt, f"dw N={N} {dt} {C_in}->{C_out} T={T}")
+    assert np.array_equal(dw, run_backward_weight(eq, N, C_in, C_out, T, dt, d))
+
+
 @pytest.mark.parametrize("dt", [F32, BF16, F16])
 def test_gradients_satisfy_the_adjoint_identity(eq, dt):
     """<dy, y(x)> = <dx, x> = <dw, w> with all three computed on the GPU."""

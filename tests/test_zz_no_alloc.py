@@ -48,9 +48,9 @@ def _grads(eq, plan, N, C_in, C_out, T, dt, seed):
 @pytest.mark.parametrize("N,C_in,C_out,T1,T2", [
     (8, 32, 32, 4096, 1000),     # one-launch path for narrow layers
     (7, 24, 16, 777, 65),
-    (8, 96, 96, 1200, 300),      # planes + per-bin products + reduction
-    (7, 160, 160, 640, 129),
-    (6, 100, 24, 900, 17),       # 64 x 64 product tiles
+    (8, 96, 96, 1200, 300),      # fp32: planes + per-bin products + reduction;
+    (7, 160, 160, 640, 129),     # 16-bit: transforms inside the product kernel
+    (6, 100, 24, 900, 17),       # fp32: 64 x 64 product tiles
 ])
 def test_noalloc_matches_the_workspace_entry(eq, N, C_in, C_out, T1, T2, dt):
     plan = eq.eqlinear_plan(N, C_in, C_out, _eqdt(eq, dt))
@@ -73,10 +73,10 @@ def test_noalloc_zero_tokens_writes_zeros(eq):
 
 def test_noalloc_refuses_shapes_past_its_scratch(eq):
     import torch
-    plan = eq.eqlinear_plan(8, 96, 96, eq.EQL_BF16)
-    T = 12608  # about 53 MiB of workspace
+    plan = eq.eqlinear_plan(8, 96, 96, eq.EQL_F32)
+    T = 12608  # fp32 planes of x and dy: about 80 MiB of workspace
     assert eq.eqlinear_backward_weight_workspace(plan, T) > eq.EQL_NOALLOC_SCRATCH_BYTES
-    x = torch.zeros(T * 96 * 8, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros(T * 96 * 8, dtype=torch.float32, device="cuda")
     dw = torch.zeros(8 * 96 * 96, dtype=torch.float32, device="cuda")
     with pytest.raises(eq.EqlError):
         eq.eqlinear_backward_weight_noalloc(plan, x, x, dw, T=T)
