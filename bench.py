@@ -51,8 +51,10 @@ KERNEL_SOURCES = {
           "group_equivariant_linear_amd/csrc/cn_mf.h",
           "group_equivariant_linear_amd/csrc/cn_split.h",
           "group_equivariant_linear_amd/csrc/cn_dispatch.h",
+          "group_equivariant_linear_amd/csrc/dft_coef.h",
           "group_equivariant_linear_amd/csrc/eq_device.h"],
     "BW": ["group_equivariant_linear_amd/csrc/cn_backward.hip",
+           "group_equivariant_linear_amd/csrc/dft_coef.h",
            "group_equivariant_linear_amd/csrc/eq_device.h"],
     "D8": ["group_equivariant_linear_amd/csrc/d8_forward.hip",
            "group_equivariant_linear_amd/csrc/gemm_rows.hip",
@@ -724,7 +726,8 @@ def _run_oracle(wl, d, n, op="forward"):
 STEP_KERNELS = ("cn_fast_kernel", "cn_fused_kernel", "cn_mf_kernel", "cn_split_kernel", "cn_stream_kernel",
                 "dn_regular_kernel", "d8_kernel",
                 "gemm_rows_kernel")
-BW_KERNELS = ("bw_planes_kernel", "bw_bin_kernel", "bw_gemm_kernel", "bw_small_kernel", "bw_reduce_kernel")
+BW_KERNELS = ("bw_planes_kernel", "bw_bin_kernel", "bw_gemm_kernel", "bw_small_kernel", "bw_xf_kernel",
+              "bw_reduce_kernel")
 TRAFFIC_WARM = 5   # back-to-back forwards (inputs partly cached from the previous launch)
 TRAFFIC_COLD = 5   # forwards each after a 512 MiB read that evicts the L2s
 TRAFFIC_COPIES = 5
@@ -773,6 +776,10 @@ def op_kernel_name(wl, op):
     if op == "backward_weight":
         if wl.C_in <= 32 and wl.C_out <= 32:
             return "bw_small_kernel + bw_reduce_kernel"
+        if wl.dtype in ("bf16", "f16") and wl.N in (2, 4, 6, 8):
+            Tp = (wl.T + 31) // 32 * 32
+            if max(wl.C_in, wl.C_out) * wl.N * Tp * 2 < 1 << 31:
+                return "bw_xf_kernel + bw_reduce_kernel"
         return f"bw_planes_kernel + {_bw_products_kernel(wl)} + bw_reduce_kernel"
     return step_kernel_name(wl)
 

@@ -36,6 +36,7 @@
 // Every step is deterministic (no atomics).
 #include <mutex>
 
+#include "dft_coef.h"
 #include "eq_device.h"
 #include "eq_launch.h"
 
@@ -831,7 +832,9 @@ __global__ __launch_bounds__(256) void bw_small_kernel(const IO* __restrict__ x,
 // 74 -> 66 us, 384 -> 96 70 -> 67 us; but C7 160 -> 160 (32768 tokens, odd N:
 // records on 2-byte boundaries) 101 -> 106 us.  Odd orders keep the planes
 // path.  The per-lane record loads read rows 2 N C bytes apart, and each x and
-// dy row is read once per 64-wide tile of the other axis.
+// dy row is read once per 64-wide tile of the other axis.  (A row-dependent
+// swizzle that halved the fragment reads' bank conflicts, 15 -> 12 % of
+// cycles, made the kernel 20 % slower: the reads lost their immediate offsets.)
 template <int N_, typename IO_>
 struct BwXfCfg {
     static constexpr int N = N_;

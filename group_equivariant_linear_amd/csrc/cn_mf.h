@@ -42,6 +42,7 @@
 #pragma once
 
 #include "cn_fused.h"
+#include "dft_coef.h"
 
 // y leaves the kernel once and is not read again by it: the store phase
 // writes whole 128-byte lines (8 lanes per tile row) with the non-temporal

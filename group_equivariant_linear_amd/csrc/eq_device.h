@@ -137,16 +137,6 @@ struct fconst { static constexpr T value = V; };
 //   Im X[k] = -sum_h d_h sin(2 pi hk/N).
 // For N = 4 every coefficient is 0 or +-1: adds and subtracts only
 // ("Flash EQ-Linear", Specialization for p4 Rotation Group).
-
-// Coefficient of plane p at group element h in this packing (double).
-template <int N>
-constexpr double fwd_coef(int p, int h) {
-    if (p == 0) return 1.0;
-    if (N % 2 == 0 && p == N - 1) return (h % 2) ? -1.0 : 1.0;
-    const int k = (p + 1) / 2;
-    return (p % 2) ? turn_trig((long)h * k, N, false) : -turn_trig((long)h * k, N, true);
-}
-
 template <int N>
 __device__ __forceinline__ void rdft_forward(const float (&x)[N], float (&P)[N]) {
     constexpr int H = (N - 1) / 2;  // symmetric pairs == complex bins
