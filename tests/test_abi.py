@@ -219,7 +219,8 @@ def test_backward_validation_before_any_hip_call(eq):
     assert lib.eqlinear_backward_weight_noalloc(h, A + 2, B, W, 100, None) == eq.EQL_ERR_INVALID
     assert lib.eqlinear_backward_weight_noalloc(d8.handle, A, B, W, 100, None) == eq.EQL_ERR_INVALID
     # a workspace past the library-held scratch: refused before any HIP call
-    wide = eq.eqlinear_plan(8, 96, 96, eq.EQL_BF16)
+    # (an fp32 plan: its transformed x and dy still go through the workspace)
+    wide = eq.eqlinear_plan(8, 96, 96, eq.EQL_F32)
     assert lib.eqlinear_backward_weight_workspace(wide.handle, 12608) > eq.EQL_NOALLOC_SCRATCH_BYTES
     assert lib.eqlinear_backward_weight_noalloc(wide.handle, A, B, W, 12608, None) == eq.EQL_ERR_UNSUPPORTED
     # transformed x or dy reaching 2 GiB: unsupported, refused before any HIP call
