@@ -1205,7 +1205,8 @@ def main():
                                and args.op != "regular" else ""),
             "launches_per_step": len(layers),
             "mean_launch_us": ms * 1e3 / len(layers),
-            "bytes_per_launch": bytes_launch,
+            "bytes_per_step": bytes_launch,
+            "bytes_per_launch": [L.bytes_per_launch for L in layers],
             "timing": "cache-cold steps (rotated copies), HIP events on the launch stream around the K steps",
             "kernel_source_sha": kernel_source_hash(source_group(wls[0], args.op)),
         },
