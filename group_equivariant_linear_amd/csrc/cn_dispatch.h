@@ -12,6 +12,7 @@ namespace eql {
 constexpr int kMfFirstTile = 7;     // tiles 7..13: entries 0..6 on the matrix-core transform kernel
 constexpr int kSplitFirstTile = 14;  // tiles 14, 15: fp32, input channels split over 2 or 4 waves
 constexpr int kStreamTile = 16;      // 16-bit, N <= 8: the persistent kernel (cn_stream.h)
+constexpr int kWideTile = 17;        // 16-bit, N <= 8: the transform kernel with 8 waves, 128 tokens x 48 channels
 
 // cn_stream_{bf16,f16}.hip; hipErrorNotSupported for shapes the kernel does not take
 hipError_t launch_cn_stream_bf16(int N, const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
@@ -63,6 +64,13 @@ int choose_fused(int64_t T, int C_in, int C_out) {
         // once (cache-cold on MI355X, 12608 tokens, 96 output channels at N = 8:
         // 13.7 against 14.1 us from 96 inputs, 34.8 against 35.7 us from 384)
         const int nblk = (C_out + 15) / 16;
+        // Six output blocks over that many token tiles: the 8-wave tile of 128
+        // tokens x 48 channels instead.  Each weight chunk then serves 128
+        // tokens, which halves the weight reloads; x is read once more, from L2
+        // (cache-cold on MI355X, 12608 tokens at N = 8: 96 -> 96 13.6 -> 12.5 us,
+        // 384 -> 96 32.2 -> 30.6 us; it is slower on 96 -> 384, 36.4 -> 39.7 us,
+        // and on the C7 layer of 160 channels, 63.9 -> 70.2 us)
+        if (nblk == 6 && (T + 63) / 64 >= 192) return kWideTile;
         if (nblk <= 6 && (T + 63) / 64 >= 192) return kMfFirstTile + 6 - (nblk < 2 ? 2 : nblk);
         return kMfFirstTile + choose_shape<N>(T, C_in, C_out);
     } else {
@@ -79,6 +87,16 @@ template <int N, typename IO>
 hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
                         hipStream_t stream, int tile, Epi epi) {
     int i = tile >= 0 ? tile : choose_fused<N, IO>(T, C_in, C_out);
+    if (i == kWideTile) {
+        if constexpr (mf_supported<N, IO>) {
+            using Cfg = MfCfg<N, 8, 3, IO>;
+            if (fast_ok<N, IO>(C_in, C_out, Cfg::TT))
+                return launch_mf_cfg<Cfg>(x, w_hat, y, T, C_in, C_out, stream, epi);
+            i = kMfFirstTile + choose_shape<N>(T, C_in, C_out);  // shapes it does not take
+        } else {
+            i = choose_fused<N, IO>(T, C_in, C_out);
+        }
+    }
     if (i == kStreamTile) {
         if constexpr (mf_supported<N, IO>) {
             const hipError_t e = std::is_same_v<IO, __bf16>

@@ -164,7 +164,7 @@ eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t p, const void* x, const v
     const size_t xb = (size_t)T * in_width(p) * es, yb = (size_t)T * out_width(p) * es;
     const size_t wb = eqlinear_w_hat_elems(p) * es;
     if (overlaps(x, xb, y, yb) || overlaps(w_hat, wb, y, yb)) return EQL_ERR_INVALID;
-    if (tile < -1 || tile > 16) return EQL_ERR_INVALID;
+    if (tile < -1 || tile > 17) return EQL_ERR_INVALID;
     return hip_status(eql::launch_cn_forward(p->N, p->dtype, x, w_hat, y, T, p->C_in,
                                              p->C_out, (hipStream_t)stream, tile));
 }
@@ -187,7 +187,7 @@ eqlinear_status eqlinear_forward_bias_act(eqlinear_plan_t p, const void* x, cons
     const size_t wb = eqlinear_w_hat_elems(p) * es, bb = (size_t)p->C_out * es;
     if (overlaps(x, xb, y, yb) || overlaps(w_hat, wb, y, yb)) return EQL_ERR_INVALID;
     if (bias && (((uintptr_t)bias % es) != 0 || overlaps(bias, bb, y, yb))) return EQL_ERR_INVALID;
-    if (tile < -1 || tile > 16) return EQL_ERR_INVALID;
+    if (tile < -1 || tile > 17) return EQL_ERR_INVALID;
     return hip_status(eql::launch_cn_forward(p->N, p->dtype, x, w_hat, y, T, p->C_in, p->C_out,
                                              (hipStream_t)stream, tile, eql::Epi{bias, act}));
 }

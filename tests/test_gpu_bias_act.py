@@ -17,7 +17,7 @@ from gpu_util import Guarded, assert_close, to_dev, to_f64
 pytestmark = pytest.mark.gpu
 
 F32, BF16, F16 = synthetic.F32, synthetic.BF16, synthetic.F16
-TILES = range(-1, 17)
+TILES = range(-1, 18)
 # (C_in, C_out, T): ragged C_out blocks and token tail; C_in % 4 == 0 for the split
 # kernel; 7 -> 5 takes the generic path (rows not a multiple of 16 bytes)
 SHAPES = [(32, 21, 150), (24, 48, 97), (7, 5, 37)]

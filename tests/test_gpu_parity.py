@@ -91,7 +91,7 @@ def test_forward_sweep(eq, N, dt):
     for (C_in, C_out, T) in SHAPES:
         d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=N * 100 + C_in)
         ref = oracle.cn_dense(d["x64"], d["w64"])
-        for tile in range(-1, 17):
+        for tile in range(-1, 18):
             y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
             assert_close(y, ref, dt, f"N={N} {dt} C_in={C_in} C_out={C_out} T={T} tile={tile}")
 
@@ -108,7 +108,7 @@ def test_forward_sweep(eq, N, dt):
 def test_forward_multi_tile_shapes(eq, N, C_in, C_out, T, dt):
     d = synthetic.cn_inputs(N, C_in, C_out, T, dt, seed=7)
     ref = oracle.cn_dense(d["x64"], d["w64"])
-    for tile in range(-1, 17):
+    for tile in range(-1, 18):
         y, _ = run_cn(eq, N, C_in, C_out, T, dt, tile=tile, inputs=d)
         assert_close(y, ref, dt, f"N={N} {dt} {C_in}->{C_out} T={T} tile={tile}")
 
@@ -157,7 +157,7 @@ def test_fp16_large_inputs_keep_their_range(eq, N):
     dd = dict(d, x=xd, x64=x64)
     ref = oracle.cn_dense(x64, d["w64"])
     assert np.abs(ref).max() < 65504
-    for tile in range(-1, 17):
+    for tile in range(-1, 18):
         y, _ = run_cn(eq, N, C_in, C_out, T, F16, tile=tile, inputs=dd)
         assert_close(y, ref, F16, f"N={N} fp16 x*2^13 tile={tile}")
 
