@@ -12,7 +12,13 @@ namespace eql {
 constexpr int kMfFirstTile = 7;     // tiles 7..13: entries 0..6 on the matrix-core transform kernel
 constexpr int kSplitFirstTile = 14;  // tiles 14, 15: fp32, input channels split over 2 or 4 waves
 constexpr int kStreamTile = 16;      // 16-bit, N <= 8: the persistent kernel (cn_stream.h)
-constexpr int kWideTile = 17;        // 16-bit, N <= 8: the transform kernel with 8 waves, 128 tokens x 48 channels
+constexpr int kWideTile = 17;        // 16-bit, N <= 8: the transform kernel with 8 waves over 128 tokens
+
+// Output blocks per wave of the 8-wave tile: the most that keep two waves per
+// SIMD without spilling (4 x N x CB accumulators beside the operands: N = 7
+// takes four blocks in 251 VGPRs; five spill, as do four at N = 8).
+template <int N>
+constexpr int wide_cb() { return N == 7 ? 4 : 3; }
 
 // cn_stream_{bf16,f16}.hip; hipErrorNotSupported for shapes the kernel does not take
 hipError_t launch_cn_stream_bf16(int N, const void* x, const void* w_hat, void* y, int64_t T, int C_in, int C_out,
@@ -71,6 +77,11 @@ int choose_fused(int64_t T, int C_in, int C_out) {
         // 384 -> 96 32.2 -> 30.6 us; it is slower on 96 -> 384, 36.4 -> 39.7 us,
         // and on the C7 layer of 160 channels, 63.9 -> 70.2 us)
         if (nblk == 6 && (T + 63) / 64 >= 192) return kWideTile;
+        // C7 layers wider than six blocks: 128 tokens x 64 channels, which
+        // halves the weight reloads and cuts x's re-reads, when the tiles fill
+        // every CU (cache-cold on MI355X, 32768 tokens x 160 channels:
+        // 65.5-66.2 -> 56.9-59.9 us)
+        if (N == 7 && nblk > 6 && ((T + 127) / 128) * ((nblk + 3) / 4) >= 256) return kWideTile;
         if (nblk <= 6 && (T + 63) / 64 >= 192) return kMfFirstTile + 6 - (nblk < 2 ? 2 : nblk);
         return kMfFirstTile + choose_shape<N>(T, C_in, C_out);
     } else {
@@ -89,7 +100,7 @@ hipError_t launch_fused(const void* x, const void* w_hat, void* y, int64_t T, in
     int i = tile >= 0 ? tile : choose_fused<N, IO>(T, C_in, C_out);
     if (i == kWideTile) {
         if constexpr (mf_supported<N, IO>) {
-            using Cfg = MfCfg<N, 8, 3, IO>;
+            using Cfg = MfCfg<N, 8, wide_cb<N>(), IO>;
             if (fast_ok<N, IO>(C_in, C_out, Cfg::TT))
                 return launch_mf_cfg<Cfg>(x, w_hat, y, T, C_in, C_out, stream, epi);
             i = kMfFirstTile + choose_shape<N>(T, C_in, C_out);  // shapes it does not take

@@ -183,10 +183,12 @@ eqlinear_status eqlinear_forward(eqlinear_plan_t plan, const void* x, const void
  * exceeds the range of x and y.  The automatic choice does not use it (it
  * measured slower than tiles 7..13 on MI355X).  Tile 17 (bf16 and fp16 plans
  * with 2 <= N <= 8; otherwise the automatic choice) is the kernel of tiles
- * 7..13 with 8 waves over 128 tokens x 48 output channels: each weight chunk
- * serves twice the tokens of the 4-wave tiles.  The automatic choice takes it
- * for layers of 81..96 output channels when the token batch gives at least 192
- * tiles of 64 tokens.  Other tile values -> EQL_ERR_INVALID. */
+ * 7..13 with 8 waves over 128 tokens x 48 output channels (64 for N = 7):
+ * each weight chunk serves twice the tokens of the 4-wave tiles.  The
+ * automatic choice takes it for layers of 81..96 output channels when the
+ * token batch gives at least 192 tiles of 64 tokens, and for N = 7 layers of
+ * more than 96 output channels whose tiles number at least 256.  Other tile
+ * values -> EQL_ERR_INVALID. */
 eqlinear_status eqlinear_forward_tiled(eqlinear_plan_t plan, const void* x, const void* w_hat,
                                        void* y, int64_t T, void* stream, int tile);
 
